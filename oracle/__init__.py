@@ -1,0 +1,165 @@
+"""fp64 CPU oracle for Gated DeltaNet replay, chunk operators and composition.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+CPU-baseline leg of the benchmark, never by the product path.  It shares no
+code with the HIP library and imports nothing from it.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain sequential loops in double
+precision); this module only builds it with gcc and marshals numpy arrays.
+
+Sources: "Tail-Replay: Escaping the Curse of Linear Attention in Prefix Caching
+for Hybrid LLMs", section 2 Eq. (1) and section 3 Eq. (2); "LinearKV: One
+Cached State Suffices for Position-Independent Caching in Hybrid LLMs", the
+affine chunk operator and its back-to-back composition in context order.
+
+Parity pins (tests/test_oracle_pins.py) tie every function here to facts the
+pages and the mathematics fix; none of the three functions is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile gdn_oracle.c into liboracle.so with gcc (OpenMP over heads)."""
+    if force or not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+               "-Wall", "-o", tmp, _SRC]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        lib.gdn_oracle_replay.argtypes = [dp, dp, dp, dp, dp, dp, ip,
+                                          ctypes.c_int, ctypes.c_int64,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          dp, dp, ctypes.c_int]
+        lib.gdn_oracle_chunk_operator.argtypes = [dp, dp, dp, dp, ip, ctypes.c_int,
+                                                  ctypes.c_int64, ctypes.c_int,
+                                                  ctypes.c_int, ctypes.c_int,
+                                                  dp, dp, ctypes.c_int]
+        lib.gdn_oracle_compose.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, dp, ctypes.c_int]
+        lib.gdn_oracle_threads.argtypes = []
+        for f in (lib.gdn_oracle_replay, lib.gdn_oracle_chunk_operator,
+                  lib.gdn_oracle_compose, lib.gdn_oracle_threads):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    """Default OpenMP thread count the oracle uses."""
+    return int(_load().gdn_oracle_threads())
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _iptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, n_threads=0):
+    """Sequential per-token replay (Tail-Replay Eq. (1); Eq. (2) when S0 is None).
+
+    Shapes: q, k [T, H, dk]; v [T, H, dv]; alpha, beta [T, H];
+    cu_seqlens int [N+1]; S0 [N, H, dv, dk] or None (zero state).
+    Returns (o [T, H, dv] or None, S_final [N, H, dv, dk]) in float64.
+    """
+    k, v, alpha, beta = _f64(k), _f64(v), _f64(alpha), _f64(beta)
+    q = _f64(q) if (want_o and q is not None) else None
+    if want_o and q is None:
+        raise ValueError("o requested without q")
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    N = cu.shape[0] - 1
+    S0 = _f64(S0)
+    o = np.empty((T, H, dv), np.float64) if want_o else None
+    S = np.empty((N, H, dv, dk), np.float64)
+    rc = _load().gdn_oracle_replay(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                   _ptr(S0), _iptr(cu), N, T, H, dk, dv,
+                                   _ptr(o), _ptr(S), int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle replay rejected its arguments")
+    return o, S
+
+
+def chunk_operator(k, alpha, beta, cu_chunks, v=None, n_threads=0):
+    """Per-chunk transition product and local state (LinearKV chunk operator).
+
+    Returns (T_C [C, H, dk, dk], S_local [C, H, dv, dk] or None) in float64.
+    """
+    k, alpha, beta = _f64(k), _f64(alpha), _f64(beta)
+    v = _f64(v)
+    cu = np.ascontiguousarray(np.asarray(cu_chunks, dtype=np.int32))
+    T, H, dk = k.shape
+    C = cu.shape[0] - 1
+    dv = v.shape[2] if v is not None else dk
+    TC = np.empty((C, H, dk, dk), np.float64)
+    SL = np.empty((C, H, dv, dk), np.float64) if v is not None else None
+    rc = _load().gdn_oracle_chunk_operator(_ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                           _iptr(cu), C, T, H, dk, dv,
+                                           _ptr(TC), _ptr(SL), int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle chunk_operator rejected its arguments")
+    return TC, SL
+
+
+def compose(T_C, S_local, S_in=None, n_threads=0):
+    """Back-to-back composition S <- S T_C[c] + S_local[c] in context order.
+
+    T_C [C, H, dk, dk], S_local [C, H, dv, dk], S_in [H, dv, dk] or None.
+    Returns S_out [H, dv, dk] in float64.
+    """
+    T_C, S_local, S_in = _f64(T_C), _f64(S_local), _f64(S_in)
+    C, H, dk, _ = T_C.shape
+    dv = S_local.shape[2]
+    out = np.empty((H, dv, dk), np.float64)
+    rc = _load().gdn_oracle_compose(_ptr(S_in), _ptr(T_C), _ptr(S_local), C, H, dk, dv,
+                                    _ptr(out), int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle compose rejected its arguments")
+    return out
+
+
+def rel_fro(x, ref) -> float:
+    """Relative Frobenius error ||x - ref||_F / ||ref||_F over the whole tensor.
+
+    The error measure of the LinearKV state probe (relative state error
+    against the full-prefix state).  When ||ref|| is 0 the absolute norm of
+    x is returned instead.
+    """
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = float(np.linalg.norm(ref.ravel()))
+    num = float(np.linalg.norm((x - ref).ravel()))
+    return num / den if den > 0 else num

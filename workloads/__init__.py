@@ -1,0 +1,181 @@
+"""Seeded synthetic inputs for Gated DeltaNet replay (numpy only).
+
+This module holds no part of the method's arithmetic: it only draws random
+inputs with the shapes and value distributions of the workloads and rounds
+them to the input dtype.  Both the HIP path (through the tests and the
+benchmark) and the fp64 oracle receive exactly the arrays made here.
+
+Recipe (one numpy PCG64 generator per call, seeded by the caller):
+  1. varlen only: tail lengths = rng.integers(lo, hi, size=n, endpoint=True);
+  2. q, k, v ~ N(0, 1) in float64 with shape [T_tot, H, d];
+  3. beta-logit then alpha-logit ~ N(0, 1) with shape [T_tot, H];
+  4. q and k are L2-normalised per (token, head); beta = sigmoid(x_beta);
+     alpha = exp(-c * softplus(x_alpha)) with c = 0.1 by default;
+  5. values are rounded to float32 (round to nearest even) and, for bf16
+     inputs, further to bfloat16 (round to nearest even).  The oracle is fed
+     the rounded values, upcast exactly.
+
+The tail length of a replay follows the Tail-Replay rule (section 3,
+"Independent Tail-Replay"): the latest k = ceil(r * m) tokens of an m-token
+matched prefix, with r a fraction such as 5% or 10%.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from fractions import Fraction
+from typing import Optional
+
+import numpy as np
+
+
+def tail_length(m: int, r) -> int:
+    """ceil(r * m) computed exactly (r given as a float, str or Fraction)."""
+    fr = Fraction(str(r)) if not isinstance(r, Fraction) else r
+    return int(math.ceil(fr * int(m)))
+
+
+def f32_round(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, np.float64).astype(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round to float32 then to bfloat16 (both round-to-nearest-even).
+
+    Returns the uint16 bit patterns.  NaN is not expected in these inputs.
+    """
+    f = f32_round(x)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    u = (u + 0x7FFF + lsb) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    u = np.asarray(bits, np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+@dataclass
+class Inputs:
+    """One batch of replay inputs.
+
+    ``q``, ``k``, ``v``, ``alpha``, ``beta`` are numpy arrays in the input
+    dtype's storage: float32, or uint16 bf16 bit patterns when dtype == 'bf16'.
+    ``f64`` holds the same values upcast exactly to float64.
+    """
+    dtype: str
+    H: int
+    dk: int
+    dv: int
+    cu_seqlens: np.ndarray
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    alpha: np.ndarray
+    beta: np.ndarray
+    f64: dict = field(default_factory=dict)
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def n_seqs(self) -> int:
+        return int(self.cu_seqlens.shape[0] - 1)
+
+    @property
+    def lengths(self) -> np.ndarray:
+        return np.diff(self.cu_seqlens)
+
+
+def _softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def generate(lengths, H: int, dk: int, dv: int, dtype: str = "bf16",
+             seed: int = 0, gate_scale: float = 0.1, rng=None,
+             alpha_one: bool = False, beta_value: Optional[float] = None) -> Inputs:
+    """Draw one packed batch with the recipe in the module docstring.
+
+    ``lengths``: per-sequence token counts (any may be 0).
+    ``gate_scale``: c in alpha = exp(-c * softplus(x)); 0.1 is the workload law,
+    0.001 the slow-decay stress law.  ``alpha_one`` forces alpha = 1 and
+    ``beta_value`` forces a constant beta (stress / invariant cases).
+    """
+    if dtype not in ("f32", "bf16"):
+        raise ValueError("dtype must be 'f32' or 'bf16'")
+    rng = np.random.Generator(np.random.PCG64(seed)) if rng is None else rng
+    lengths = np.asarray(lengths, np.int64)
+    cu = np.zeros(lengths.shape[0] + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+    q = rng.standard_normal((T, H, dk))
+    k = rng.standard_normal((T, H, dk))
+    v = rng.standard_normal((T, H, dv))
+    xb = rng.standard_normal((T, H))
+    xa = rng.standard_normal((T, H))
+    q = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    k = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    beta = 1.0 / (1.0 + np.exp(-xb)) if beta_value is None else np.full((T, H), beta_value)
+    alpha = np.ones((T, H)) if alpha_one else np.exp(-gate_scale * _softplus(xa))
+    arrs = dict(q=q, k=k, v=v, alpha=alpha, beta=beta)
+    store, f64 = {}, {}
+    for name, a in arrs.items():
+        if dtype == "bf16":
+            bits = bf16_bits(a)
+            store[name] = bits
+            f64[name] = bf16_to_f64(bits)
+        else:
+            f = f32_round(a)
+            store[name] = f
+            f64[name] = f.astype(np.float64)
+    return Inputs(dtype=dtype, H=H, dk=dk, dv=dv, cu_seqlens=cu, f64=f64, **store)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads.  Shapes follow the pages: a 32768-token prefix with a
+# 10% tail (ceil(0.1 * 32768) = 3277), tails of 5-10% of 8K-32K prefixes
+# (bounds ceil(0.05 * 8192) = 410 and 3277), a full 32K prefill, and 64
+# fixed contiguous 512-token chunks (the LinearKV chunking).
+# ---------------------------------------------------------------------------
+
+WORKLOADS = {
+    0: dict(name="single-head-T256-d64-f32", H=1, d=64, dtype="f32", lengths=[256]),
+    1: dict(name="tail-replay-T3277-H32-d128-bf16", H=32, d=128, dtype="bf16",
+            lengths=[tail_length(32768, "0.1")], state_only=True),
+    2: dict(name="varlen-16x[410,3277]-H32-d128-bf16", H=32, d=128, dtype="bf16",
+            n_varlen=16, lo=tail_length(8192, "0.05"), hi=tail_length(32768, "0.1")),
+    3: dict(name="full-prefill-T32768-H32-d128-bf16", H=32, d=128, dtype="bf16",
+            lengths=[32768]),
+    4: dict(name="chunk-ops-64x512-H32-d128-bf16", H=32, d=128, dtype="bf16",
+            lengths=[64 * 512], chunk=512),
+}
+
+
+def workload_lengths(cfg_id: int, rng) -> list:
+    w = WORKLOADS[cfg_id]
+    if "n_varlen" in w:
+        return [int(x) for x in rng.integers(w["lo"], w["hi"], size=w["n_varlen"],
+                                             endpoint=True)]
+    return list(w["lengths"])
+
+
+def make_workload(cfg_id: int, seed: Optional[int] = None, H: Optional[int] = None) -> Inputs:
+    """Inputs of workload ``cfg_id`` (seed defaults to the workload index).
+
+    ``H`` may reduce the head count (heads are independent and identically
+    distributed, so fewer heads is a sample of the same workload).
+    """
+    w = WORKLOADS[cfg_id]
+    seed = cfg_id if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = workload_lengths(cfg_id, rng)
+    return generate(lengths, H=w["H"] if H is None else H, dk=w["d"], dv=w["d"],
+                    dtype=w["dtype"], rng=rng)
+
+
+def chunk_bounds(n_tokens: int, chunk: int) -> np.ndarray:
+    """cu_chunks for fixed contiguous chunks of ``chunk`` tokens (last may be short)."""
+    starts = list(range(0, n_tokens, chunk)) + [n_tokens]
+    return np.asarray(starts, np.int32)
