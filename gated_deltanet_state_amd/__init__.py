@@ -1,0 +1,204 @@
+"""Gated DeltaNet state replay for MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/gdn.h`` (``libgdn.so``,
+built in-tree by ``gated_deltanet_state_amd.build``).  The binding only
+marshals arguments: every step of the computation runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.
+
+If ``libgdn.so`` is missing or cannot be loaded, every call raises: there is
+no fallback implementation.
+
+Functions (same names as the C entry points, without the ``gdn_`` prefix):
+  replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=float32)
+  chunk_operator(k, alpha, beta, cu_chunks, v=None)
+  compose(T_C, S_local, S_in=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["replay", "chunk_operator", "compose", "GdnError", "library", "LIB_PATH"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__("%s (%d): %s" % (name, status, detail))
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+def library():
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libgdn.so is not built (run python -m gated_deltanet_state_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cint = ctypes.c_int
+    lib.gdn_replay.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint,
+                               vp, cint, vp, vp, sz, vp]
+    lib.gdn_replay_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
+    lib.gdn_chunk_operator.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint,
+                                       vp, vp, vp, sz, vp]
+    lib.gdn_chunk_operator_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
+    lib.gdn_compose.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]
+    lib.gdn_compose_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    for f in (lib.gdn_replay, lib.gdn_chunk_operator, lib.gdn_compose):
+        f.restype = cint
+    for f in (lib.gdn_replay_workspace_bytes, lib.gdn_chunk_operator_workspace_bytes,
+              lib.gdn_compose_workspace_bytes):
+        f.restype = sz
+    lib.gdn_status_string.argtypes = [cint]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_abi_version.argtypes = []
+    lib.gdn_abi_version.restype = cint
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = library()
+        raise GdnError(status, lib.gdn_status_string(status).decode(),
+                       lib.gdn_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    if dt == torch.float32:
+        return GDN_F32
+    if dt == torch.bfloat16:
+        return GDN_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % dt)
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _workspace(nbytes, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=None,
+           out=None, S_out=None, stream=None):
+    """Replay packed sequences through the gated delta rule.
+
+    q, k [T, H, dk]; v [T, H, dv]; alpha, beta [T, H] (all float32 or all
+    bfloat16); cu_seqlens int32 [N+1] on the device; S0 [N, H, dv, dk]
+    float32 or None (zero state).  Returns (o [T, H, dv] or None,
+    S_final [N, H, dv, dk] float32).  ``out`` / ``S_out`` may supply the
+    output tensors (S_out may be S0: the update is then in place).
+    """
+    torch = _torch()
+    lib = library()
+    for name, t in (("k", k), ("v", v), ("alpha", alpha), ("beta", beta),
+                    ("cu_seqlens", cu_seqlens), ("S0", S0)):
+        _dev(t, name)
+    if want_o:
+        _dev(q, "q")
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    in_code = _dtype_code(k.dtype)
+    for name, t in (("q", q if want_o else None), ("v", v), ("alpha", alpha), ("beta", beta)):
+        if t is not None and t.dtype != k.dtype:
+            raise TypeError("%s must have the dtype of k" % name)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if S0 is not None and S0.dtype != torch.float32:
+        raise TypeError("S0 must be float32")
+    o = None
+    if want_o:
+        o_dt = torch.float32 if o_dtype is None else o_dtype
+        o = out if out is not None else torch.empty((T, H, dv), dtype=o_dt, device=k.device)
+        _dev(o, "out")
+        o_code = _dtype_code(o.dtype)
+    else:
+        o_code = GDN_F32
+    S = S_out if S_out is not None else torch.empty((N, H, dv, dk), dtype=torch.float32,
+                                                    device=k.device)
+    _dev(S, "S_out")
+    ws_bytes = lib.gdn_replay_workspace_bytes(N, T, H, dk, dv)
+    ws, ws_bytes = _workspace(ws_bytes, k.device)
+    _check(lib.gdn_replay(_ptr(q) if want_o else None, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                          _ptr(S0), _ptr(cu_seqlens), N, T, H, dk, dv, in_code, _ptr(o),
+                          o_code, _ptr(S), _ptr(ws), ws_bytes, _stream_ptr(stream)))
+    return o, S
+
+
+def chunk_operator(k, alpha, beta, cu_chunks, v=None, stream=None):
+    """Per-chunk transition product T_C [C, H, dk, dk] and local state
+    S_local [C, H, dv, dk] (None when v is None), both float32."""
+    torch = _torch()
+    lib = library()
+    for name, t in (("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("cu_chunks", cu_chunks)):
+        _dev(t, name)
+    T, H, dk = k.shape
+    dv = v.shape[2] if v is not None else dk
+    C = cu_chunks.shape[0] - 1
+    in_code = _dtype_code(k.dtype)
+    if cu_chunks.dtype != torch.int32:
+        raise TypeError("cu_chunks must be int32")
+    TC = torch.empty((C, H, dk, dk), dtype=torch.float32, device=k.device)
+    SL = torch.empty((C, H, dv, dk), dtype=torch.float32, device=k.device) if v is not None else None
+    ws_bytes = lib.gdn_chunk_operator_workspace_bytes(C, T, H, dk, dv)
+    ws, ws_bytes = _workspace(ws_bytes, k.device)
+    _check(lib.gdn_chunk_operator(_ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_chunks), C, T,
+                                  H, dk, dv, in_code, _ptr(TC), _ptr(SL), _ptr(ws), ws_bytes,
+                                  _stream_ptr(stream)))
+    return TC, SL
+
+
+def compose(T_C, S_local, S_in=None, out=None, stream=None):
+    """S <- S_in (or 0); S <- S T_C[c] + S_local[c] for c in context order.
+    Returns S_out [H, dv, dk] float32."""
+    torch = _torch()
+    lib = library()
+    for name, t in (("T_C", T_C), ("S_local", S_local), ("S_in", S_in)):
+        _dev(t, name)
+    C, H, dk, _ = T_C.shape
+    dv = S_local.shape[2]
+    S = out if out is not None else torch.empty((H, dv, dk), dtype=torch.float32, device=T_C.device)
+    _dev(S, "out")
+    ws_bytes = lib.gdn_compose_workspace_bytes(C, H, dk, dv)
+    ws, ws_bytes = _workspace(ws_bytes, T_C.device)
+    _check(lib.gdn_compose(_ptr(S_in), _ptr(T_C), _ptr(S_local), C, H, dk, dv, _ptr(S),
+                           _ptr(ws), ws_bytes, _stream_ptr(stream)))
+    return S

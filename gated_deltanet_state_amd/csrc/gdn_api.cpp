@@ -1,0 +1,202 @@
+// gdn_api.cpp -- the C ABI declared in include/gdn.h: argument checks,
+// workspace sizing and kernel launches on the caller's stream.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+gdn_status fail(gdn_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+gdn_status ok() {
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_dim(int32_t d) { return d == 64 || d == 128; }
+
+bool valid_dtype(gdn_dtype t) { return t == GDN_F32 || t == GDN_BF16; }
+
+// Largest token count whose (token, head) indexing stays within the 32-bit
+// arithmetic of the chunk loop.
+constexpr int64_t kMaxTokens = (int64_t(1) << 31) - 64;
+
+gdn_status check_align(const char *name, const void *p) {
+  if (p && !aligned16(p)) return fail(GDN_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
+  return GDN_OK;
+}
+
+gdn_status launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_replay_workspace_bytes(int32_t, int64_t, int32_t, int32_t, int32_t) { return 0; }
+
+size_t gdn_chunk_operator_workspace_bytes(int32_t, int64_t, int32_t, int32_t, int32_t) { return 0; }
+
+size_t gdn_compose_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return 0; }
+
+gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *alpha, const void *beta,
+                      const float *S0, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
+                      int32_t n_heads, int32_t dk, int32_t dv, gdn_dtype in_dtype, void *o, gdn_dtype o_dtype,
+                      float *S_final, void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
+  if (!k || !v || !alpha || !beta || !cu_seqlens || !S_final)
+    return fail(GDN_ERR_NULL_POINTER, "gdn_replay: k, v, alpha, beta, cu_seqlens and S_final are required");
+  if (o && !q) return fail(GDN_ERR_NULL_POINTER, "gdn_replay: o requested without q");
+  if (n_seqs < 1 || n_tokens < 0 || n_heads < 1 || dk < 1 || dv < 1)
+    return fail(GDN_ERR_BAD_SHAPE, "gdn_replay: need n_seqs >= 1, n_tokens >= 0, n_heads >= 1 (got %d, %lld, %d)",
+                n_seqs, (long long)n_tokens, n_heads);
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_replay: dk and dv must be 64 or 128 (got %d, %d)", dk, dv);
+  if (!valid_dtype(in_dtype) || (o && !valid_dtype(o_dtype)))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_replay: dtypes must be GDN_F32 or GDN_BF16");
+  if (n_tokens > kMaxTokens || (int64_t)n_seqs * n_heads * (dv / 16) > (int64_t(1) << 30))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_replay: problem too large for one call");
+  gdn_status s;
+  if ((s = check_align("q", q)) || (s = check_align("k", k)) || (s = check_align("v", v)) ||
+      (s = check_align("alpha", alpha)) || (s = check_align("beta", beta)) || (s = check_align("S0", S0)) ||
+      (s = check_align("cu_seqlens", cu_seqlens)) || (s = check_align("o", o)) ||
+      (s = check_align("S_final", S_final)))
+    return s;
+  if (workspace_bytes < gdn_replay_workspace_bytes(n_seqs, n_tokens, n_heads, dk, dv) ||
+      (gdn_replay_workspace_bytes(n_seqs, n_tokens, n_heads, dk, dv) > 0 && !workspace))
+    return fail(GDN_ERR_WORKSPACE, "gdn_replay: workspace too small");
+  (void)workspace;
+  gdn::ChainLaunch p{};
+  p.q = o ? q : nullptr;
+  p.k = k;
+  p.v = v;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.S0 = S0;
+  p.cu = cu_seqlens;
+  p.n_seqs = n_seqs;
+  p.H = n_heads;
+  p.dk = dk;
+  p.dv = dv;
+  p.in_bf16 = in_dtype == GDN_BF16;
+  p.o = o;
+  p.o_bf16 = o_dtype == GDN_BF16;
+  p.S_out = S_final;
+  p.T_out = nullptr;
+  p.tiles_T = 0;
+  p.tiles_S = dv / 16;
+  p.precise_state = 0;
+  return launched(gdn::launch_chain(p, reinterpret_cast<hipStream_t>(stream)), "gdn_replay launch");
+}
+
+gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, const void *beta,
+                              const int32_t *cu_chunks, int32_t n_chunks, int64_t n_tokens, int32_t n_heads,
+                              int32_t dk, int32_t dv, gdn_dtype in_dtype, float *T_C, float *S_local,
+                              void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
+  if (!k || !alpha || !beta || !cu_chunks || !T_C)
+    return fail(GDN_ERR_NULL_POINTER, "gdn_chunk_operator: k, alpha, beta, cu_chunks and T_C are required");
+  if ((v == nullptr) != (S_local == nullptr))
+    return fail(GDN_ERR_NULL_POINTER, "gdn_chunk_operator: v and S_local must be given together");
+  if (n_chunks < 0 || n_tokens < 0 || n_heads < 1 || dk < 1 || dv < 1)
+    return fail(GDN_ERR_BAD_SHAPE, "gdn_chunk_operator: bad sizes (n_chunks %d, n_tokens %lld, n_heads %d)",
+                n_chunks, (long long)n_tokens, n_heads);
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_operator: dk and dv must be 64 or 128 (got %d, %d)", dk, dv);
+  if (!valid_dtype(in_dtype)) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_operator: bad dtype");
+  if (n_tokens > kMaxTokens || (int64_t)n_chunks * n_heads * ((dk + dv) / 16) > (int64_t(1) << 30))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_operator: problem too large for one call");
+  gdn_status s;
+  if ((s = check_align("k", k)) || (s = check_align("v", v)) || (s = check_align("alpha", alpha)) ||
+      (s = check_align("beta", beta)) || (s = check_align("cu_chunks", cu_chunks)) ||
+      (s = check_align("T_C", T_C)) || (s = check_align("S_local", S_local)))
+    return s;
+  if (workspace_bytes < gdn_chunk_operator_workspace_bytes(n_chunks, n_tokens, n_heads, dk, dv))
+    return fail(GDN_ERR_WORKSPACE, "gdn_chunk_operator: workspace too small");
+  (void)workspace;
+  if (n_chunks == 0) return ok();
+  gdn::ChainLaunch p{};
+  p.k = k;
+  p.v = v;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.cu = cu_chunks;
+  p.n_seqs = n_chunks;
+  p.H = n_heads;
+  p.dk = dk;
+  p.dv = dv;
+  p.in_bf16 = in_dtype == GDN_BF16;
+  p.S_out = S_local;
+  p.T_out = T_C;
+  p.tiles_T = dk / 16;
+  p.tiles_S = v ? dv / 16 : 0;
+  p.precise_state = 1;
+  return launched(gdn::launch_chain(p, reinterpret_cast<hipStream_t>(stream)), "gdn_chunk_operator launch");
+}
+
+gdn_status gdn_compose(const float *S_in, const float *T_C, const float *S_local, int32_t n_chunks,
+                       int32_t n_heads, int32_t dk, int32_t dv, float *S_out, void *workspace,
+                       size_t workspace_bytes, gdn_stream_t stream) {
+  if (!S_out || (n_chunks > 0 && (!T_C || !S_local)))
+    return fail(GDN_ERR_NULL_POINTER, "gdn_compose: T_C, S_local and S_out are required");
+  if (n_chunks < 0 || n_heads < 1 || dk < 1 || dv < 1)
+    return fail(GDN_ERR_BAD_SHAPE, "gdn_compose: bad sizes (n_chunks %d, n_heads %d)", n_chunks, n_heads);
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_compose: dk and dv must be 64 or 128 (got %d, %d)", dk, dv);
+  gdn_status s;
+  if ((s = check_align("S_in", S_in)) || (s = check_align("T_C", T_C)) || (s = check_align("S_local", S_local)) ||
+      (s = check_align("S_out", S_out)))
+    return s;
+  if (workspace_bytes < gdn_compose_workspace_bytes(n_chunks, n_heads, dk, dv))
+    return fail(GDN_ERR_WORKSPACE, "gdn_compose: workspace too small");
+  (void)workspace;
+  gdn::ComposeLaunch p{};
+  p.S_in = S_in;
+  p.T_C = T_C;
+  p.S_local = S_local;
+  p.n_chunks = n_chunks;
+  p.H = n_heads;
+  p.dk = dk;
+  p.dv = dv;
+  p.S_out = S_out;
+  return launched(gdn::launch_compose(p, reinterpret_cast<hipStream_t>(stream)), "gdn_compose launch");
+}
+
+const char *gdn_status_string(gdn_status status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL_POINTER: return "GDN_ERR_NULL_POINTER";
+    case GDN_ERR_BAD_SHAPE: return "GDN_ERR_BAD_SHAPE";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_ALIGNMENT: return "GDN_ERR_ALIGNMENT";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+  }
+  return "GDN_ERR_UNKNOWN";
+}
+
+const char *gdn_last_error(void) { return g_last_error.c_str(); }
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+}  // extern "C"

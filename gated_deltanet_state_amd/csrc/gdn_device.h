@@ -1,0 +1,175 @@
+// gdn_device.h -- device-side building blocks for the gfx950 GDN kernels:
+// MFMA fragment loaders over LDS-resident operands, split-bfloat16 products
+// and small lane utilities.
+//
+// MFMA lane layouts used (gfx950, wave64; checked on the device):
+//   v_mfma_f32_16x16x32_bf16:  A[16 x 32]: lane l holds row (l & 15),
+//     k = 8*(l >> 4) .. +7;  B[32 x 16]: lane l holds column (l & 15), the
+//     same 8 k;  C/D[16 x 16]: lane l holds column (l & 15), rows
+//     4*(l >> 4) .. +3.
+//   v_mfma_f32_16x16x4_f32:    A: row (l & 15), k = l >> 4;  B: column
+//     (l & 15), k = l >> 4;  C/D as above.
+//
+// Split bfloat16 (Henry, Tang and Heinecke, "Leveraging the bfloat16
+// Artificial Intelligence Datatype For Higher-Precision Computations",
+// ARITH 2019): an fp32 value x is carried as hi = bf16(x) and
+// lo = bf16(x - hi); a product a*b is approximated by up to three bf16
+// products a_hi b_hi + a_hi b_lo + a_lo b_hi accumulated in fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+// ---------------------------------------------------------------------------
+// LDS operand views.  An operand of an MFMA tile is addressed as
+// element(row, k): "row" runs over the 16 M (or N) positions of the tile and
+// k over the contraction.
+//   RowMajor<T>:  p[row * ld + k]           (k contiguous: 8-wide loads)
+//   ColMajor<T>:  p[k * ld + row]           (only single-element loads)
+//   RowScaled:    fp32 p[row * ld + k] * s[k]  (column scaling on load)
+// ---------------------------------------------------------------------------
+template <class T>
+struct RowMajor {
+  const T *p;
+  int ld;
+  __device__ float one(int row, int k) const { return to_f32(p[row * ld + k]); }
+};
+
+template <class T>
+struct ColMajor {
+  const T *p;
+  int ld;
+  __device__ float one(int row, int k) const { return to_f32(p[k * ld + row]); }
+};
+
+struct RowScaled {
+  const float *p;
+  int ld;
+  const float *s;
+  __device__ float one(int row, int k) const { return p[row * ld + k] * s[k]; }
+};
+
+struct RowNeg {  // -p[row * ld + k], fp32
+  const float *p;
+  int ld;
+  __device__ float one(int row, int k) const { return -p[row * ld + k]; }
+};
+
+// 8 consecutive k of one row as split bf16 (hi, lo).
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    bf16 h = (bf16)x[i];
+    hi[i] = h;
+    lo[i] = (bf16)(x[i] - (float)h);
+  }
+}
+
+template <bool NEED_LO>
+__device__ __forceinline__ void load8f(const float *src, const float *scale, float sign, bf16x8 &hi,
+                                       bf16x8 &lo) {
+  f32x4 x0 = *reinterpret_cast<const f32x4 *>(src);
+  f32x4 x1 = *reinterpret_cast<const f32x4 *>(src + 4);
+  float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  if (scale) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] *= scale[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] *= sign;
+  if (NEED_LO) {
+    split8(x, hi, lo);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hi[i] = (bf16)x[i];
+  }
+}
+
+template <bool NEED_LO>
+__device__ __forceinline__ void load8(const RowMajor<float> &a, int row, int k, bf16x8 &hi, bf16x8 &lo) {
+  load8f<NEED_LO>(a.p + row * a.ld + k, nullptr, 1.f, hi, lo);
+}
+template <bool NEED_LO>
+__device__ __forceinline__ void load8(const RowScaled &a, int row, int k, bf16x8 &hi, bf16x8 &lo) {
+  load8f<NEED_LO>(a.p + row * a.ld + k, a.s + k, 1.f, hi, lo);
+}
+template <bool NEED_LO>
+__device__ __forceinline__ void load8(const RowNeg &a, int row, int k, bf16x8 &hi, bf16x8 &lo) {
+  load8f<NEED_LO>(a.p + row * a.ld + k, nullptr, -1.f, hi, lo);
+}
+template <bool NEED_LO>
+__device__ __forceinline__ void load8(const RowMajor<bf16> &a, int row, int k, bf16x8 &hi, bf16x8 &lo) {
+  hi = *reinterpret_cast<const bf16x8 *>(a.p + row * a.ld + k);
+  (void)lo;
+}
+
+template <class Op>
+struct IsExactBf16 {
+  static constexpr bool value = false;
+};
+template <>
+struct IsExactBf16<RowMajor<bf16>> {
+  static constexpr bool value = true;
+};
+
+// C[16x16] += A[m0.., k] * B[k, n0..] for k in [k0, k1) (multiple of 32), with
+// A given as opA(m, k) and B given through its transpose opB(n, k).
+// PA / PB: 2 = split that operand into hi + lo (ignored for exact bf16 data).
+// Products formed: hi*hi, plus hi_A*lo_B if PB == 2, plus lo_A*hi_B if PA == 2.
+template <int PA, int PB, class OA, class OB>
+__device__ __forceinline__ void mma_bf16(f32x4 &c, const OA &opA, const OB &opB, int m0, int n0, int k0,
+                                         int k1) {
+  constexpr bool LA = (PA == 2) && !IsExactBf16<OA>::value;
+  constexpr bool LB = (PB == 2) && !IsExactBf16<OB>::value;
+  const int l = lane_id();
+  const int r = l & 15, kq = (l >> 4) * 8;
+  for (int k = k0; k < k1; k += 32) {
+    bf16x8 ah, al, bh, bl;
+    load8<LA>(opA, m0 + r, k + kq, ah, al);
+    load8<LB>(opB, n0 + r, k + kq, bh, bl);
+    c = mfma_bf16(ah, bh, c);
+    if (LB) c = mfma_bf16(ah, bl, c);
+    if (LA) c = mfma_bf16(al, bh, c);
+  }
+}
+
+// Same contract with fp32 operands on the fp32 MFMA (k step 4).
+template <class OA, class OB>
+__device__ __forceinline__ void mma_f32(f32x4 &c, const OA &opA, const OB &opB, int m0, int n0, int k0,
+                                        int k1) {
+  const int l = lane_id();
+  const int r = l & 15, kk = l >> 4;
+  for (int k = k0; k < k1; k += 4) c = mfma_f32(opA.one(m0 + r, k + kk), opB.one(n0 + r, k + kk), c);
+}
+
+// Store a C-layout tile into a row-major fp32 LDS array (optionally scaled per column).
+__device__ __forceinline__ void store_tile(float *dst, int ld, int m0, int n0, const f32x4 &c) {
+  const int l = lane_id();
+  const int col = n0 + (l & 15), row = m0 + 4 * (l >> 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[(row + i) * ld + col] = c[i];
+}
+
+}  // namespace gdn

@@ -1,0 +1,44 @@
+// gdn_internal.h -- host-side launch descriptors shared by the C ABI and the
+// kernel translation units (not part of the public interface).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// One launch of the chunked recurrence kernel.  A work item is one tile of
+// 16 rows of the state of one (sequence, head).  Row tiles come in two kinds:
+//   * tiles_T "transition" tiles (chunk-operator mode): rows of a dk x dk
+//     matrix that starts as the identity and receives no value input; after
+//     the sequence they hold rows of the transition product T_C.
+//   * tiles_S "state" tiles: rows of the dv x dk state, starting from S0 (or
+//     zero) and receiving the value input; they end as S_final / S_local.
+struct ChainLaunch {
+  const void *q, *k, *v, *alpha, *beta;
+  const float *S0;          // [n_seqs, H, dv, dk] or null
+  const int32_t *cu;        // [n_seqs + 1] (device)
+  int32_t n_seqs;
+  int32_t H;
+  int32_t dk, dv;
+  int in_bf16;              // inputs are bf16 (else fp32)
+  void *o;                  // [T, H, dv] or null
+  int o_bf16;
+  float *S_out;             // [n_seqs, H, dv, dk] (state tiles) or null
+  float *T_out;             // [n_seqs, H, dk, dk] (transition tiles) or null
+  int32_t tiles_T, tiles_S;
+  int precise_state;        // split the state operand of the state x W product
+};
+
+struct ComposeLaunch {
+  const float *S_in;        // [H, dv, dk] or null
+  const float *T_C;         // [n, H, dk, dk]
+  const float *S_local;     // [n, H, dv, dk]
+  int32_t n_chunks, H, dk, dv;
+  float *S_out;             // [H, dv, dk]
+};
+
+hipError_t launch_chain(const ChainLaunch &p, hipStream_t stream);
+hipError_t launch_compose(const ComposeLaunch &p, hipStream_t stream);
+
+}  // namespace gdn

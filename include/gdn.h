@@ -1,0 +1,152 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet state-replay library.
+ *
+ * Three operations, each an asynchronous, stream-ordered sequence of HIP
+ * kernel launches on the caller's stream.  No call allocates or frees device
+ * memory, synchronises the device, or keeps a pointer after it returns; every
+ * buffer belongs to the caller and must stay alive until the stream work is
+ * done.  All argument checks happen on the host before any launch; on an
+ * error nothing is launched and a status other than GDN_OK is returned (a
+ * longer message is available from gdn_last_error(), per calling thread).
+ * Device-side data are not validated: cu_seqlens / cu_chunks must be
+ * nondecreasing with first entry 0 and last entry n_tokens, and every gate
+ * alpha must lie in (0, 1].
+ *
+ * Pointer arguments are DEVICE pointers unless stated otherwise, 16-byte
+ * aligned (GDN_ERR_ALIGNMENT otherwise), row-major and contiguous.
+ * Shapes below use T = n_tokens, H = n_heads.
+ *
+ * The recurrence (page "Tail-Replay: Escaping the Curse of Linear Attention
+ * in Prefix Caching for Hybrid LLMs", section 2, Eq. (1)), per head, with
+ * the state S a dv x dk matrix:
+ *     S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t.
+ * (The page writes the transition on the left of S; with S stored dv x dk it
+ * acts from the right.  The transition is symmetric, so this only fixes the
+ * storage orientation.)
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL_POINTER = 1, /* a required pointer is NULL                        */
+  GDN_ERR_BAD_SHAPE = 2,    /* negative / inconsistent sizes                     */
+  GDN_ERR_UNSUPPORTED = 3,  /* a size or dtype this build has no kernel for      */
+  GDN_ERR_ALIGNMENT = 4,    /* a pointer is not 16-byte aligned                  */
+  GDN_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required        */
+  GDN_ERR_HIP = 6           /* a HIP launch failed; see gdn_last_error()         */
+} gdn_status;
+
+typedef enum gdn_dtype {
+  GDN_F32 = 0,  /* IEEE binary32                                    */
+  GDN_BF16 = 1  /* bfloat16 (upper half of a binary32)              */
+} gdn_dtype;
+
+/* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
+typedef void *gdn_stream_t;
+
+/*
+ * gdn_replay -- replay packed token sequences through the recurrence.
+ * Page: Tail-Replay, section 2 Eq. (1) (the update) and section 3 Eq. (2)
+ * (tail replay from a zero state: pass S0 = NULL).
+ *
+ *   q      [T, H, dk]  in_dtype   may be NULL when o is NULL
+ *   k      [T, H, dk]  in_dtype   keys (used as given: no normalisation, no scale)
+ *   v      [T, H, dv]  in_dtype
+ *   alpha  [T, H]      in_dtype   gates in (0, 1]
+ *   beta   [T, H]      in_dtype
+ *   S0     [n_seqs, H, dv, dk] fp32 starting states, or NULL for zero
+ *   cu_seqlens [n_seqs + 1] int32 (device): sequence n is tokens
+ *          cu_seqlens[n] .. cu_seqlens[n+1]-1; sequences may be empty
+ *   o      [T, H, dv]  o_dtype    o_t = S_t q_t with the state after token t,
+ *          or NULL for a state-only replay
+ *   S_final [n_seqs, H, dv, dk] fp32 (may alias S0: read fully before written)
+ *   workspace / workspace_bytes: device scratch of at least
+ *          gdn_replay_workspace_bytes(...) bytes (may be NULL if that is 0)
+ *
+ * Supported: dk, dv in {64, 128}; in_dtype F32 or BF16 (q, k, v, alpha,
+ * beta all of it); o_dtype F32 or BF16; n_seqs >= 1; n_heads >= 1.
+ * Deterministic: equal inputs give bitwise-equal outputs.
+ */
+gdn_status gdn_replay(const void *q, const void *k, const void *v,
+                      const void *alpha, const void *beta, const float *S0,
+                      const int32_t *cu_seqlens, int32_t n_seqs,
+                      int64_t n_tokens, int32_t n_heads, int32_t dk,
+                      int32_t dv, gdn_dtype in_dtype, void *o,
+                      gdn_dtype o_dtype, float *S_final, void *workspace,
+                      size_t workspace_bytes, gdn_stream_t stream);
+
+size_t gdn_replay_workspace_bytes(int32_t n_seqs, int64_t n_tokens,
+                                  int32_t n_heads, int32_t dk, int32_t dv);
+
+/*
+ * gdn_chunk_operator -- the affine operator of each chunk.
+ * Page: "LinearKV: One Cached State Suffices for Position-Independent
+ * Caching in Hybrid LLMs", the paragraph on the affine chunk operator: a
+ * chunk maps an incoming state S_in to S_in T_C + S_local, where T_C is the
+ * product of the chunk's per-token transitions in token order and S_local
+ * the state the chunk reaches from a zero start.
+ *
+ *   k      [T, H, dk], alpha, beta [T, H], v [T, H, dv]  in_dtype
+ *   cu_chunks [n_chunks + 1] int32 (device): chunk c is tokens
+ *          cu_chunks[c] .. cu_chunks[c+1]-1 (an empty chunk gives T_C = I)
+ *   T_C     [n_chunks, H, dk, dk] fp32 out
+ *   S_local [n_chunks, H, dv, dk] fp32 out
+ *   v and S_local may both be NULL: only T_C is built (T_C needs only the
+ *   key / gate stream).
+ */
+gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha,
+                              const void *beta, const int32_t *cu_chunks,
+                              int32_t n_chunks, int64_t n_tokens,
+                              int32_t n_heads, int32_t dk, int32_t dv,
+                              gdn_dtype in_dtype, float *T_C, float *S_local,
+                              void *workspace, size_t workspace_bytes,
+                              gdn_stream_t stream);
+
+size_t gdn_chunk_operator_workspace_bytes(int32_t n_chunks, int64_t n_tokens,
+                                          int32_t n_heads, int32_t dk,
+                                          int32_t dv);
+
+/*
+ * gdn_compose -- apply chunk operators back to back in context order.
+ * Page: LinearKV, the composition paragraph (chunk c's output is chunk
+ * c+1's input; the closed form adds no approximation of its own):
+ *     S <- S_in (or zero);  for c = 0 .. n_chunks-1:  S <- S T_C[c] + S_local[c]
+ *
+ *   S_in    [H, dv, dk] fp32 or NULL (zero)
+ *   T_C     [n_chunks, H, dk, dk] fp32,  S_local [n_chunks, H, dv, dk] fp32
+ *   S_out   [H, dv, dk] fp32 (may alias S_in)
+ * n_chunks may be 0 (S_out = S_in, or zero).
+ */
+gdn_status gdn_compose(const float *S_in, const float *T_C,
+                       const float *S_local, int32_t n_chunks, int32_t n_heads,
+                       int32_t dk, int32_t dv, float *S_out, void *workspace,
+                       size_t workspace_bytes, gdn_stream_t stream);
+
+size_t gdn_compose_workspace_bytes(int32_t n_chunks, int32_t n_heads,
+                                   int32_t dk, int32_t dv);
+
+/* Human-readable name of a status code (static storage). */
+const char *gdn_status_string(gdn_status status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* GDN_ABI_VERSION of the loaded library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

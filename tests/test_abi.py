@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every declared entry point and rejects
+bad arguments on the host before launching anything (CPU only: none of
+these calls reaches a HIP API)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+import gated_deltanet_state_amd as gdn  # noqa: E402
+
+OK, NULLP, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gdn.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"gdn_replay", "gdn_chunk_operator", "gdn_compose"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.gdn_abi_version() == 1
+    for code, name in [(0, b"GDN_OK"), (1, b"GDN_ERR_NULL_POINTER"), (2, b"GDN_ERR_BAD_SHAPE"),
+                       (3, b"GDN_ERR_UNSUPPORTED"), (4, b"GDN_ERR_ALIGNMENT"),
+                       (5, b"GDN_ERR_WORKSPACE"), (6, b"GDN_ERR_HIP")]:
+        assert lib.gdn_status_string(code) == name
+
+
+P = 0x10000  # a 16-byte aligned fake address; never dereferenced (checks fail first)
+
+
+def replay(lib, q=P, k=P, v=P, a=P, b=P, S0=None, cu=P, N=1, T=10, H=2, dk=64, dv=64,
+           dt=F32, o=P, odt=F32, S=P):
+    return lib.gdn_replay(q, k, v, a, b, S0, cu, N, T, H, dk, dv, dt, o, odt, S, None, 0, None)
+
+
+def test_replay_argument_checks(lib):
+    assert replay(lib, k=None) == NULLP
+    assert b"required" in lib.gdn_last_error()
+    assert replay(lib, S=None) == NULLP
+    assert replay(lib, cu=None) == NULLP
+    assert replay(lib, q=None) == NULLP             # o requested without q
+    assert replay(lib, N=0) == SHAPE
+    assert replay(lib, T=-1) == SHAPE
+    assert replay(lib, H=0) == SHAPE
+    assert replay(lib, dk=96) == UNSUP
+    assert replay(lib, dv=32) == UNSUP
+    assert replay(lib, dt=7) == UNSUP
+    assert replay(lib, odt=9) == UNSUP
+    assert replay(lib, T=1 << 31) == UNSUP
+    assert replay(lib, k=P + 2) == ALIGN
+    assert b"k is not 16-byte aligned" in lib.gdn_last_error()
+    assert replay(lib, S0=P + 8) == ALIGN
+    assert replay(lib, o=P + 4) == ALIGN
+
+
+def test_chunk_operator_argument_checks(lib):
+    def co(k=P, v=P, a=P, b=P, cu=P, C=2, T=10, H=2, dk=64, dv=64, dt=BF16, TC=P, SL=P):
+        return lib.gdn_chunk_operator(k, v, a, b, cu, C, T, H, dk, dv, dt, TC, SL, None, 0, None)
+    assert co(TC=None) == NULLP
+    assert co(v=None) == NULLP                      # v without S_local
+    assert co(SL=None) == NULLP
+    assert co(C=-1) == SHAPE
+    assert co(dk=100) == UNSUP
+    assert co(b=P + 2) == ALIGN
+    assert co(C=0) == OK                            # nothing to do, nothing launched
+
+
+def test_compose_argument_checks(lib):
+    def cp(Si=None, TC=P, SL=P, C=3, H=2, dk=128, dv=64, So=P):
+        return lib.gdn_compose(Si, TC, SL, C, H, dk, dv, So, None, 0, None)
+    assert cp(So=None) == NULLP
+    assert cp(TC=None) == NULLP
+    assert cp(C=-2) == SHAPE
+    assert cp(dv=48) == UNSUP
+    assert cp(Si=P + 4) == ALIGN
+
+
+def test_workspace_queries(lib):
+    assert lib.gdn_replay_workspace_bytes(16, 30000, 32, 128, 128) == 0
+    assert lib.gdn_chunk_operator_workspace_bytes(64, 32768, 32, 128, 128) == 0
+    assert lib.gdn_compose_workspace_bytes(64, 32, 128, 128) == 0
