@@ -1,0 +1,202 @@
+"""Benchmark of the Gated DeltaNet replay path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ID] [--no-cpu]
+
+One step is one pass of the whole path over one batch of synthetic input
+already resident in HBM.  The default workload is a tail replay of one
+request: the latest 3277 tokens (10% of a 32768-token prefix) through 32
+heads with dk = dv = 128, bf16 inputs, fp32 state, zero start state, final
+state only (the "replay to rebuild the state" use of the Tail-Replay page,
+section 3, Eq. (2)).  Other workloads: 2 = 16 packed tails of 410..3277
+tokens with outputs; 3 = a 32768-token prefill with outputs; 4 = 64
+chunk operators of 512 tokens and their composition; 0 = one fp32 head.
+
+Prints ONE JSON line.  ``value`` is replayed tokens x heads per second;
+``roofline`` compares the dominant kernel's algorithmic HBM bytes per launch
+over its average launch time (HIP events on the launch stream) against the
+8 TB/s HBM3E peak; ``cpu_baseline`` is the fp64 oracle timed on this host's
+cores on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN replay tokens·heads/s (H=32,d=128) + % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2516.6
+
+
+def algorithmic(inp, want_o: bool, o_bytes: int, C: int = 64):
+    """Algorithmic HBM bytes and flops of one replay launch.
+
+    Bytes: every input read once (q only with outputs), o written once,
+    S_final written once (no S0).  Flops: the chunked form's products,
+    2C(3dk + 2dv) + 6 dk dv per token x head with outputs, 2C(2dk + dv) +
+    4 dk dv state-only.
+    """
+    import numpy as np
+    T, H, dk, dv = inp.n_tokens, inp.H, inp.dk, inp.dv
+    es = 2 if inp.dtype == "bf16" else 4
+    per_tok = (dk + dv) * es + 2 * es + ((dk * es + dv * o_bytes) if want_o else 0)
+    byt = T * H * per_tok + inp.n_seqs * H * dv * dk * 4
+    if want_o:
+        fl = T * H * (2 * C * (3 * dk + 2 * dv) + 6 * dk * dv)
+    else:
+        fl = T * H * (2 * C * (2 * dk + dv) + 4 * dk * dv)
+    return int(byt), int(fl)
+
+
+def to_dev(inp, torch, np):
+    def t(a):
+        if inp.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return dict(q=t(inp.q), k=t(inp.k), v=t(inp.v), alpha=t(inp.alpha), beta=t(inp.beta),
+                cu=torch.from_numpy(inp.cu_seqlens.astype(np.int32)).cuda())
+
+
+def cpu_baseline(inp, want_o, wid, min_seconds=3.0):
+    """fp64 oracle on the same workload: whole heads, repeated to >= min_seconds,
+    or a subset of heads when one full pass would be long."""
+    import oracle
+    f = inp.f64
+    heads = list(range(inp.H))
+    # estimate: ~1.2 GFLOP/s per thread for the plain fp64 loops
+    thr = oracle.threads()
+    est = inp.n_tokens * inp.H * (6 if want_o else 4) * inp.dk * inp.dv / (1.2e9 * thr)
+    if est > 20.0:
+        keep = max(1, int(inp.H * 20.0 / est))
+        heads = heads[:keep]
+    sel = heads
+    args = (f["q"][:, sel] if want_o else None, f["k"][:, sel], f["v"][:, sel],
+            f["alpha"][:, sel], f["beta"][:, sel], inp.cu_seqlens)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.replay(*args, want_o=want_o)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    th = reps * inp.n_tokens * len(heads) / el
+    sample = "%d full pass(es) of the workload over %d of %d heads, %s, fp64" % (
+        reps, len(heads), inp.H, "with o" if want_o else "state only")
+    return dict(value=th, unit="tokens·heads/s", cores=thr, kind="oracle", sample=sample,
+                seconds=el)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--o-bf16", action="store_true", help="write o in bf16 (workloads 2, 3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the replay path is a single-GPU kernel library "
+              "(heads and requests shard across GPUs without any exchange); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_deltanet_state_amd as gdn
+    import workloads
+
+    wid = args.workload
+    wdef = workloads.WORKLOADS[wid]
+    inp = workloads.make_workload(wid)
+    d = to_dev(inp, torch, np)
+    H, dk, dv, T = inp.H, inp.dk, inp.dv, inp.n_tokens
+    want_o = wid in (0, 2, 3)
+    o_dtype = torch.bfloat16 if args.o_bf16 else torch.float32
+    o_bytes = 2 if args.o_bf16 else 4
+    stream = torch.cuda.current_stream()
+    dev = torch.device("cuda:0")
+
+    if wid == 4:
+        cu_chunks = torch.from_numpy(workloads.chunk_bounds(T, wdef["chunk"])).cuda()
+        n_chunks = cu_chunks.shape[0] - 1
+
+        def launches():
+            TC, SL = gdn.chunk_operator(d["k"], d["alpha"], d["beta"], cu_chunks, v=d["v"])
+            return TC, SL
+        # bytes of the chunk-operator kernel: k, v, alpha, beta read; T_C, S_local written
+        byt = T * H * (dk + dv + 2) * 2 + n_chunks * H * (dk * dk + dv * dk) * 4
+        fl = T * H * (2 * 64 * (2 * dk + dv) + 4 * dk * (dk + dv))
+    else:
+        o_buf = torch.empty((T, H, dv), dtype=o_dtype, device=dev) if want_o else None
+        S_buf = torch.empty((inp.n_seqs, H, dv, dk), dtype=torch.float32, device=dev)
+
+        def launches():
+            return gdn.replay(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu"],
+                              want_o=want_o, out=o_buf, S_out=S_buf)
+        byt, fl = algorithmic(inp, want_o, o_bytes)
+
+    for _ in range(args.warmup):
+        res = launches()
+    torch.cuda.synchronize()
+    if wid == 4:
+        TC, SL = res
+        comp_out = torch.empty((H, dv, dk), dtype=torch.float32, device=dev)
+
+    # ---- timed region: K steps, one event pair per dominant launch ----
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    cstarts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    cends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        res = launches()
+        ends[i].record(stream)
+        if wid == 4:
+            TC, SL = res
+            cstarts[i].record(stream)
+            gdn.compose(TC, SL, out=comp_out)
+            cends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    step_ms = wall * 1e3 / args.steps
+    comp_ms = [s.elapsed_time(e) for s, e in zip(cstarts, cends)] if wid == 4 else []
+    avg_kern = sum(kern_ms) / len(kern_ms)
+    med_kern = sorted(kern_ms)[len(kern_ms) // 2]
+    gpu_ms = avg_kern + (sum(comp_ms) / len(comp_ms) if comp_ms else 0.0)
+    tok_heads = T * H
+    value = tok_heads / (step_ms / 1e3)
+    achieved = byt / (avg_kern / 1e3) / 1e9
+    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                algorithmic_bytes=byt, kernel_ms_avg=round(avg_kern, 5),
+                kernel_ms_median=round(med_kern, 5), kernel_ms_min=round(min(kern_ms), 5),
+                mfma_frac=round(fl / (avg_kern / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                algorithmic_flops=fl)
+    config = dict(workload=wdef["name"], n_seqs=inp.n_seqs, n_tokens=T, heads=H, dk=dk, dv=dv,
+                  outputs=("T_C,S_local" if wid == 4 else ("o,S_final" if want_o else "S_final")),
+                  chunk=64)
+    if wid == 4:
+        config["compose_ms_avg"] = round(sum(comp_ms) / len(comp_ms), 5)
+    line = dict(metric=METRIC, value=round(value, 1), unit="tokens·heads/s", n_gpus=1,
+                steps=args.steps, warmup=args.warmup, ms_per_step=round(step_ms, 5),
+                higher_is_better=True, scaling="weak", vs_baseline=None,
+                dtype="bf16" if inp.dtype == "bf16" else "f32", data="synthetic",
+                config=config, roofline=roof)
+    line["gpu_ms_per_step"] = round(gpu_ms, 5)
+    if not args.no_cpu and wid != 4:
+        line["cpu_baseline"] = cpu_baseline(inp, want_o, wid)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -55,9 +55,16 @@ gdn_status launched(hipError_t e, const char *what) {
 
 extern "C" {
 
-size_t gdn_replay_workspace_bytes(int32_t, int64_t, int32_t, int32_t, int32_t) { return 0; }
+size_t gdn_replay_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t, int32_t) {
+  if (n_seqs < 1 || n_tokens < 0 || n_heads < 1) return 0;
+  return gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads);
+}
 
-size_t gdn_chunk_operator_workspace_bytes(int32_t, int64_t, int32_t, int32_t, int32_t) { return 0; }
+size_t gdn_chunk_operator_workspace_bytes(int32_t n_chunks, int64_t n_tokens, int32_t n_heads, int32_t,
+                                          int32_t) {
+  if (n_chunks < 1 || n_tokens < 0 || n_heads < 1) return 0;
+  return gdn::tau_workspace_bytes(n_tokens, n_chunks, n_heads);
+}
 
 size_t gdn_compose_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return 0; }
 
@@ -83,11 +90,25 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
       (s = check_align("cu_seqlens", cu_seqlens)) || (s = check_align("o", o)) ||
       (s = check_align("S_final", S_final)))
     return s;
-  if (workspace_bytes < gdn_replay_workspace_bytes(n_seqs, n_tokens, n_heads, dk, dv) ||
-      (gdn_replay_workspace_bytes(n_seqs, n_tokens, n_heads, dk, dv) > 0 && !workspace))
-    return fail(GDN_ERR_WORKSPACE, "gdn_replay: workspace too small");
-  (void)workspace;
+  const size_t need = gdn_replay_workspace_bytes(n_seqs, n_tokens, n_heads, dk, dv);
+  if (workspace_bytes < need || !workspace)
+    return fail(GDN_ERR_WORKSPACE, "gdn_replay: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  if ((s = check_align("workspace", workspace))) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  gdn::PrepLaunch pp{};
+  pp.k = k;
+  pp.alpha = alpha;
+  pp.beta = beta;
+  pp.cu = cu_seqlens;
+  pp.n_seqs = n_seqs;
+  pp.H = n_heads;
+  pp.dk = dk;
+  pp.in_bf16 = in_dtype == GDN_BF16;
+  pp.tau = static_cast<float *>(workspace);
+  pp.n_slots = gdn::slot_count(n_tokens, n_seqs);
+  if ((s = launched(gdn::launch_prep(pp, st), "gdn_replay prep launch"))) return s;
   gdn::ChainLaunch p{};
+  p.tau = pp.tau;
   p.q = o ? q : nullptr;
   p.k = k;
   p.v = v;
@@ -106,8 +127,7 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   p.T_out = nullptr;
   p.tiles_T = 0;
   p.tiles_S = dv / 16;
-  p.precise_state = 0;
-  return launched(gdn::launch_chain(p, reinterpret_cast<hipStream_t>(stream)), "gdn_replay launch");
+  return launched(gdn::launch_chain(p, st), "gdn_replay launch");
 }
 
 gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, const void *beta,
@@ -131,11 +151,27 @@ gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, c
       (s = check_align("beta", beta)) || (s = check_align("cu_chunks", cu_chunks)) ||
       (s = check_align("T_C", T_C)) || (s = check_align("S_local", S_local)))
     return s;
-  if (workspace_bytes < gdn_chunk_operator_workspace_bytes(n_chunks, n_tokens, n_heads, dk, dv))
-    return fail(GDN_ERR_WORKSPACE, "gdn_chunk_operator: workspace too small");
-  (void)workspace;
   if (n_chunks == 0) return ok();
+  const size_t need = gdn_chunk_operator_workspace_bytes(n_chunks, n_tokens, n_heads, dk, dv);
+  if (workspace_bytes < need || !workspace)
+    return fail(GDN_ERR_WORKSPACE, "gdn_chunk_operator: workspace of %zu bytes required (got %zu)", need,
+                workspace_bytes);
+  if ((s = check_align("workspace", workspace))) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  gdn::PrepLaunch pp{};
+  pp.k = k;
+  pp.alpha = alpha;
+  pp.beta = beta;
+  pp.cu = cu_chunks;
+  pp.n_seqs = n_chunks;
+  pp.H = n_heads;
+  pp.dk = dk;
+  pp.in_bf16 = in_dtype == GDN_BF16;
+  pp.tau = static_cast<float *>(workspace);
+  pp.n_slots = gdn::slot_count(n_tokens, n_chunks);
+  if ((s = launched(gdn::launch_prep(pp, st), "gdn_chunk_operator prep launch"))) return s;
   gdn::ChainLaunch p{};
+  p.tau = pp.tau;
   p.k = k;
   p.v = v;
   p.alpha = alpha;
@@ -150,8 +186,7 @@ gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, c
   p.T_out = T_C;
   p.tiles_T = dk / 16;
   p.tiles_S = v ? dv / 16 : 0;
-  p.precise_state = 1;
-  return launched(gdn::launch_chain(p, reinterpret_cast<hipStream_t>(stream)), "gdn_chunk_operator launch");
+  return launched(gdn::launch_chain(p, st), "gdn_chunk_operator launch");
 }
 
 gdn_status gdn_compose(const float *S_in, const float *T_C, const float *S_local, int32_t n_chunks,

@@ -1,31 +1,40 @@
-// gdn_chain.hip -- chunkwise-parallel Gated DeltaNet recurrence for gfx950.
+// gdn_chain.hip -- chunkwise Gated DeltaNet recurrence for gfx950.
 //
 // The recurrence (page "Tail-Replay: Escaping the Curse of Linear Attention
 // in Prefix Caching for Hybrid LLMs", section 2 Eq. (1); state S dv x dk):
 //     S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t.
 // Unrolled over a chunk of L <= 64 tokens with cumulative log-gates
-// g_r = sum_{s<=r} log alpha_s it becomes (derivation: substitute the state
-// before each token into the delta-rule correction of the next one):
-//     A    = strictly lower part of  beta_r exp(g_r - g_s) (k_r . k_s)
-//     Tau  = (I + A)^{-1}                         (unit lower triangular)
-//     W    = Tau diag(beta e^g) K,   U = Tau diag(beta) V
-//     D    = U - W S^T                            (per-token corrections)
-//     O    = diag(e^g) Q S^T + (M o Q K^T) D,     M_rs = e^{g_r - g_s}, s <= r
+// g_r = sum_{s<=r} log alpha_s (substitute the state before each token into
+// the delta-rule correction of the next one), with Tau = (I + A)^{-1} built
+// per chunk by the prep kernel (gdn_prep.hip):
+//     R    = diag(beta) (V - diag(e^g) K S^T)
+//     D    = Tau R                                     (per-token corrections)
+//     O    = diag(e^g) Q S^T + (M o Q K^T) D,          M_rs = e^{g_r - g_s}, s <= r
 //     S   <- e^{g_L} S + (diag(e^{g_L - g}) D)^T K
-// Rows of S evolve independently, so a workgroup owns 16 rows of one
-// (sequence, head) state and walks its chunks in order; the dv-independent
-// factors (A, Tau, W, P = M o QK^T) are rebuilt by every row tile.
+// Rows of S evolve independently: a workgroup owns 16 rows of one
+// (sequence, head) state and walks its chunks in order; all products are
+// computed transposed (the 16 state rows are the MFMA M dimension).
 //
 // The same kernel builds the affine chunk operator of the page "LinearKV:
 // One Cached State Suffices for Position-Independent Caching in Hybrid
 // LLMs" (affine chunk operator paragraph): rows of the transition product
-// T_C are the rows of a "state" that starts as the identity and receives no
-// value input (T_C = e^{g_L} I - W^T diag(e^{g_L-g}) K per 64-token step).
+// T_C are rows of a "state" that starts as the identity and receives no
+// value input.
 //
-// Precision (bf16 inputs, fp32 state): every MFMA operand that is an input
-// (K, Q, V) is exact in bf16; fp32-derived operands are split into bf16
-// hi + lo where their rounding would show in the result (see mma_bf16).
-// fp32 inputs use the fp32 MFMA throughout.
+// Precision (bf16 inputs, fp32 state): K, Q, V are exact in bf16; the
+// state, R, D, Tau and M o QK^T enter products as split bf16 (hi + lo), so
+// every product is within a few fp32 ulps (split-bfloat16, gdn_device.h).
+// fp32 inputs use the fp32 MFMA.
+//
+// Four waves; wave w owns token block w (16 tokens) of every 16 x 64 tile
+// (Y, R, D, O) and state column tiles w, w + 4.  Per chunk, four phases
+// separated by LDS-only barriers (global loads of the next chunk stay in
+// flight across them):
+//   P0  store the prefetched keys (and queries) to LDS, gates, state planes;
+//       issue the next chunk's loads (keys, queries, V, gates, Tau rows)
+//   P1  Y = S K^T -> R;  [o] Z = e^g S Q^T,  P = M o Q K^T
+//   P2  D = R Tau^T (Tau rows straight from registers)
+//   P3  [o] O = Z + D P^T -> o;  S = e^{g_L} S + (e^{g_L - g} D)^T K
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -35,85 +44,70 @@ namespace gdn {
 
 namespace {
 
-constexpr int CH = 64;      // tokens per chunk
-constexpr int RT = 16;      // state rows per workgroup
-constexpr int NW = 8;       // waves per workgroup
+constexpr int CH = kChunk;  // tokens per chunk
+constexpr int NW = 4;       // waves per workgroup
 constexpr int NT = NW * 64; // threads per workgroup
+constexpr int RT = 16;      // state rows per workgroup
 
-template <class Tin, int DK>
-struct Smem {
+template <class Tin, int DK, bool WANT_O>
+struct Cfg {
   static constexpr bool BF = std::is_same<Tin, bf16>::value;
-  // leading dimensions (elements); bf16 paths need 16-byte aligned rows,
-  // fp32 paths read single elements and use odd strides against bank conflicts
-  static constexpr int LDK = BF ? DK + 8 : DK + 1;   // sK, sQ  [CH][LDK]   Tin
-  static constexpr int LDKT = CH + 8;                // sKt     [DK][LDKT]  bf16 only
-  static constexpr int LDVT = BF ? CH + 8 : CH + 1;  // sVt     [RT][LDVT]  Tin
-  static constexpr int LDC = BF ? CH + 4 : CH + 1;   // sA(=sP), sTau [CH][LDC] fp32
-  static constexpr int LDW = BF ? DK + 4 : DK + 1;   // sW [CH][LDW], sS [RT][LDW] fp32
-  static constexpr int LDD = LDC;                    // sD, sDd [RT][LDD] fp32
-  static constexpr int LDX = 17;                     // solve scratch [3][16][LDX]
+  using PT = typename std::conditional<BF, bf16, float>::type;  // plane element type
+  // leading dimensions (elements): bf16 paths read 16-byte rows; fp32 paths
+  // read single elements and use odd strides against bank conflicts
+  static constexpr int LDK = BF ? DK + 8 : DK + 1;   // sK, sQ [CH][LDK] Tin
+  static constexpr int LDC = BF ? CH + 4 : CH + 1;   // sP [CH][LDC] fp32
+  static constexpr int LDSP = BF ? DK + 8 : DK + 1;  // state planes [RT][LDSP]
+  static constexpr int LDRP = BF ? CH + 8 : CH + 1;  // R, D, Dd planes [RT][LDRP]
+  static constexpr int NPL = BF ? 2 : 1;             // planes per split operand
 
   static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
   static constexpr size_t oK = 0;
   static constexpr size_t oQ = oK + al(sizeof(Tin) * CH * LDK);
-  static constexpr size_t oKt = oQ + al(sizeof(Tin) * CH * LDK);
-  static constexpr size_t oVt = oKt + (BF ? al(sizeof(bf16) * DK * LDKT) : 0);
-  static constexpr size_t oA = oVt + al(sizeof(Tin) * RT * LDVT);
-  static constexpr size_t oTau = oA + al(4 * CH * LDC);
-  static constexpr size_t oW = oTau + al(4 * CH * LDC);
-  static constexpr size_t oS = oW + al(4 * CH * LDW);
-  static constexpr size_t oD = oS + al(4 * RT * LDW);
-  static constexpr size_t oDd = oD + al(4 * RT * LDD);
-  static constexpr size_t oGate = oDd + al(4 * RT * LDD);  // 8 arrays of CH floats
-  static constexpr size_t TOTAL = oGate + al(4 * 8 * CH);
-  static_assert(3 * 16 * LDX * 4 <= 2 * 4 * RT * LDD, "solve scratch must fit in sD/sDd");
+  static constexpr size_t oP = oQ + (WANT_O ? al(sizeof(Tin) * CH * LDK) : 0);
+  static constexpr size_t oS = oP + (WANT_O ? al(4 * CH * LDC) : 0);
+  static constexpr size_t oR = oS + NPL * al(sizeof(PT) * RT * LDSP);
+  static constexpr size_t oD = oR + NPL * al(sizeof(PT) * RT * LDRP);
+  static constexpr size_t oDd = oD + (WANT_O ? NPL * al(sizeof(PT) * RT * LDRP) : 0);
+  static constexpr size_t oGate = oDd + NPL * al(sizeof(PT) * RT * LDRP);
+  static constexpr size_t TOTAL = oGate + al(4 * 5 * CH);
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
+
+  static constexpr int NST = DK / 16;          // state column tiles
+  static constexpr int SPW = (NST + NW - 1) / NW;
+  static constexpr int VEC = 16 / sizeof(Tin);
+  static constexpr int KSEG = DK / VEC;        // 16-byte segments per key row
+  static constexpr int NKP = (CH * KSEG + NT - 1) / NT;
+  // Tau row fragments per lane: bf16 policy 2 k-steps of 8 floats, fp32
+  // policy 16 single elements (k step 4)
+  static constexpr int NTF = 4;
 };
 
-__device__ __forceinline__ float ld_in(const float *p, int64_t i) { return p[i]; }
-__device__ __forceinline__ float ld_in(const bf16 *p, int64_t i) { return (float)p[i]; }
 
-// C += A * B over k in [k0, k1); fp32 policy ignores the pass counts.
-template <bool BF, int PA, int PB, class OA, class OB>
-__device__ __forceinline__ void mma(f32x4 &c, const OA &a, const OB &b, int m0, int n0, int k0, int k1) {
-  if constexpr (BF)
-    mma_bf16<PA, PB>(c, a, b, m0, n0, k0, k1);
-  else
-    mma_f32(c, a, b, m0, n0, k0, k1);
-}
 
-// k range [0, kend) covering the lower-triangular blocks up to block b
-// (inclusive): 16 (b + 1) rounded up to the MFMA k step.
-template <bool BF>
-__device__ __forceinline__ int tri_kend(int b) {
-  return BF ? 32 * ((b + 2) >> 1) : 16 * (b + 1);
-}
-
-template <class Tin, int DK, bool WANT_O, bool PRECISE_S>
+template <class Tin, int DK, bool WANT_O>
 __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
-  using L = Smem<Tin, DK>;
-  constexpr bool BF = L::BF;
-  __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-  Tin *sK = reinterpret_cast<Tin *>(smem + L::oK);
-  Tin *sQ = reinterpret_cast<Tin *>(smem + L::oQ);
-  bf16 *sKt = reinterpret_cast<bf16 *>(smem + L::oKt);
-  Tin *sVt = reinterpret_cast<Tin *>(smem + L::oVt);
-  float *sA = reinterpret_cast<float *>(smem + L::oA);  // A, later P
-  float *sTau = reinterpret_cast<float *>(smem + L::oTau);
-  float *sW = reinterpret_cast<float *>(smem + L::oW);
-  float *sS = reinterpret_cast<float *>(smem + L::oS);
-  float *sD = reinterpret_cast<float *>(smem + L::oD);
-  float *sDd = reinterpret_cast<float *>(smem + L::oDd);
-  float *sX = sD;  // solve scratch (sD / sDd are idle during the solve)
-  float *sGate = reinterpret_cast<float *>(smem + L::oGate);
-  float *sG = sGate;               // g_r
-  float *sBeta = sGate + CH;       // beta_r (0 past the chunk end)
-  float *sBG = sGate + 2 * CH;     // beta_r e^{g_r}
-  float *sDec = sGate + 3 * CH;    // e^{g_L - g_r} (0 past the end)
-  float *sGam = sGate + 4 * CH;    // e^{g_r}
-  float *sRawA = sGate + 5 * CH;   // alpha as loaded
-  float *sRawB = sGate + 6 * CH;   // beta as loaded
-  float *sScal = sGate + 7 * CH;   // [0] = e^{g_L}
+  using C = Cfg<Tin, DK, WANT_O>;
+  constexpr bool BF = C::BF;
+  using PT = typename C::PT;
+  __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
+  Tin *sK = reinterpret_cast<Tin *>(smem + C::oK);
+  Tin *sQ = reinterpret_cast<Tin *>(smem + C::oQ);
+  float *sP = reinterpret_cast<float *>(smem + C::oP);
+  PT *sSh = reinterpret_cast<PT *>(smem + C::oS);
+  PT *sSl = sSh + (BF ? RT * C::LDSP : 0);
+  PT *sRh = reinterpret_cast<PT *>(smem + C::oR);
+  PT *sRl = sRh + (BF ? RT * C::LDRP : 0);
+  PT *sDh = reinterpret_cast<PT *>(smem + C::oD);
+  PT *sDl = sDh + (BF ? RT * C::LDRP : 0);
+  PT *sDdh = reinterpret_cast<PT *>(smem + C::oDd);
+  PT *sDdl = sDdh + (BF ? RT * C::LDRP : 0);
+  float *sGate = reinterpret_cast<float *>(smem + C::oGate);
+  float *sG = sGate;             // g_r
+  float *sBeta = sGate + CH;     // beta_r (0 past the chunk end)
+  float *sGam = sGate + 2 * CH;  // e^{g_r}
+  float *sDec = sGate + 3 * CH;  // e^{g_L - g_r} (0 past the end)
+  float *sScal = sGate + 4 * CH; // [0] = e^{g_L}
 
   // ---- work item: XCD-aware order (block b runs on XCD b % 8; each XCD
   // takes a contiguous range of items so the row tiles of one head share
@@ -125,250 +119,260 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
   const int unit = item / tiles, tile = item % tiles;
   const int n = unit / p.H, h = unit % p.H;
   const bool is_T = tile < p.tiles_T;
-  const int row0 = is_T ? 16 * tile : 16 * (tile - p.tiles_T);
+  const int row0 = is_T ? RT * tile : RT * (tile - p.tiles_T);
   const int H = p.H, DV = p.dv;
 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int cb = w;  // token block of this wave
   const Tin *gq = reinterpret_cast<const Tin *>(p.q);
   const Tin *gk = reinterpret_cast<const Tin *>(p.k);
   const Tin *gv = reinterpret_cast<const Tin *>(p.v);
   const Tin *ga = reinterpret_cast<const Tin *>(p.alpha);
   const Tin *gb = reinterpret_cast<const Tin *>(p.beta);
 
-  // ---- state tile in registers: wave w owns columns [16w, 16w + 16) ----
-  constexpr int NST = DK / 16;  // state column tiles (4 or 8 <= NW)
-  const bool owns = w < NST;
-  f32x4 sacc = zero4();
-  if (owns) {
-    const int col = 16 * w + (l & 15);
+  // ---- state column tiles ct = w + NW u in registers (C layout) ----
+  f32x4 sacc[C::SPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = row0 + 4 * (l >> 4) + i;
-      if (is_T) {
-        sacc[i] = (r == col) ? 1.f : 0.f;
-      } else if (p.S0) {
-        sacc[i] = p.S0[(((int64_t)n * H + h) * DV + r) * DK + col];
+  for (int u = 0; u < C::SPW; ++u) {
+    sacc[u] = zero4();
+    const int ct = w + u * NW;
+    if (ct < C::NST) {
+      const int col = 16 * ct + (l & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + 4 * (l >> 4) + i;
+        if (is_T)
+          sacc[u][i] = (r == col) ? 1.f : 0.f;
+        else if (p.S0)
+          sacc[u][i] = p.S0[(((int64_t)n * H + h) * DV + r) * DK + col];
       }
     }
   }
 
+  // ---- prefetch registers (next chunk) and current-chunk copies ----
+  f32x4 pk[C::NKP], pq[C::NKP];
+  f32x4 ptau[C::NTF], ctau[C::NTF];
+  f32x4 pvv, cvv;  // V[t0 + 16 cb + (l & 15)][row0 + 4 (l >> 4) .. + 3] (bf16: first half used)
+  float pa = 1.f, pb = 0.f;
   const int tbeg = p.cu[n], tend = p.cu[n + 1];
-  for (int t0 = tbeg; t0 < tend; t0 += CH) {
+  const int64_t slot0 = (int64_t)(tbeg / CH) + n;
+
+  auto prefetch = [&](int t0, int Lc, int64_t slot) {
+#pragma unroll
+    for (int i = 0; i < C::NKP; ++i) {
+      const int s = tid + i * NT;
+      const int r = s / C::KSEG, seg = s % C::KSEG;
+      pk[i] = zero4();
+      pq[i] = zero4();
+      if (s < CH * C::KSEG && r < Lc) {
+        const int64_t goff = ((int64_t)(t0 + r) * H + h) * DK + seg * C::VEC;
+        pk[i] = *reinterpret_cast<const f32x4 *>(gk + goff);
+        if (WANT_O) pq[i] = *reinterpret_cast<const f32x4 *>(gq + goff);
+      }
+    }
+    // Tau rows 16 cb + (l & 15) of this chunk
+    const float *tau = p.tau + (slot * H + h) * (int64_t)kTauFloats + tau_off(cb) + (l & 15) * 16 * (cb + 1);
+    const int ncol = 16 * (cb + 1);
+    if constexpr (BF) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int s0 = 32 * ks + 8 * (l >> 4);
+        ptau[2 * ks] = zero4();
+        ptau[2 * ks + 1] = zero4();
+        if (s0 < ncol) {
+          ptau[2 * ks] = *reinterpret_cast<const f32x4 *>(tau + s0);
+          ptau[2 * ks + 1] = *reinterpret_cast<const f32x4 *>(tau + s0 + 4);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int s = 4 * i + (l >> 4);
+        ptau[i >> 2][i & 3] = (s < ncol) ? tau[s] : 0.f;
+      }
+    }
+    pvv = zero4();
+    const int r = 16 * cb + (l & 15);
+    if (!is_T && r < Lc) {
+      const Tin *src = gv + ((int64_t)(t0 + r) * H + h) * DV + row0 + 4 * (l >> 4);
+      if constexpr (BF) {
+        const uint2 u2 = *reinterpret_cast<const uint2 *>(src);
+        pvv[0] = __uint_as_float(u2.x);
+        pvv[1] = __uint_as_float(u2.y);
+      } else {
+        pvv = *reinterpret_cast<const f32x4 *>(src);
+      }
+    }
+    if (w == 0) {
+      pa = 1.f;
+      pb = 0.f;
+      if (l < Lc) {
+        const int64_t gi = (int64_t)(t0 + l) * H + h;
+        pa = ld_in(ga, gi);
+        pb = ld_in(gb, gi);
+      }
+    }
+  };
+
+  if (tbeg < tend) prefetch(tbeg, min(CH, tend - tbeg), slot0);
+
+  int64_t slot = slot0;
+  for (int t0 = tbeg; t0 < tend; t0 += CH, ++slot) {
     const int Lc = min(CH, tend - t0);
 
-    // ---------------- phase 1: loads, state to LDS ----------------
-    if (owns) store_tile(sS, L::LDW, 0, 16 * w, sacc);
-    {
-      constexpr int VEC = 16 / sizeof(Tin);  // elements per 16-byte load
-      constexpr int SEGS = DK / VEC;
-      for (int s = tid; s < CH * SEGS; s += NT) {
-        const int r = s / SEGS, seg = s % SEGS;
-        const int64_t goff = ((int64_t)(t0 + r) * H + h) * DK + seg * VEC;
-        f32x4 kraw = zero4(), qraw = zero4();
-        if (r < Lc) {
-          kraw = *reinterpret_cast<const f32x4 *>(gk + goff);
-          if (WANT_O) qraw = *reinterpret_cast<const f32x4 *>(gq + goff);
-        }
-        const Tin *kv = reinterpret_cast<const Tin *>(&kraw);
-        const Tin *qv = reinterpret_cast<const Tin *>(&qraw);
-        if constexpr (BF) {
-          *reinterpret_cast<f32x4 *>(sK + r * L::LDK + seg * VEC) = kraw;
-          if (WANT_O) *reinterpret_cast<f32x4 *>(sQ + r * L::LDK + seg * VEC) = qraw;
+    // ================= P0 =================
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) sKt[(seg * VEC + e) * L::LDKT + r] = kv[e];
+    for (int i = 0; i < C::NKP; ++i) {
+      const int s = tid + i * NT;
+      if (s < CH * C::KSEG) {
+        const int r = s / C::KSEG, seg = s % C::KSEG;
+        if constexpr (BF) {
+          *reinterpret_cast<f32x4 *>(sK + r * C::LDK + seg * C::VEC) = pk[i];
+          if (WANT_O) *reinterpret_cast<f32x4 *>(sQ + r * C::LDK + seg * C::VEC) = pq[i];
         } else {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            sK[r * L::LDK + seg * VEC + e] = kv[e];
-            if (WANT_O) sQ[r * L::LDK + seg * VEC + e] = qv[e];
+          for (int e = 0; e < 4; ++e) {
+            sK[r * C::LDK + seg * 4 + e] = pk[i][e];
+            if (WANT_O) sQ[r * C::LDK + seg * 4 + e] = pq[i][e];
           }
         }
       }
-      if (!is_T) {
-        constexpr int VSEGS = RT / VEC;
-        for (int s = tid; s < CH * VSEGS; s += NT) {
-          const int r = s / VSEGS, seg = s % VSEGS;
-          f32x4 vraw = zero4();
-          if (r < Lc)
-            vraw = *reinterpret_cast<const f32x4 *>(gv + ((int64_t)(t0 + r) * H + h) * DV + row0 + seg * VEC);
-          const Tin *vv = reinterpret_cast<const Tin *>(&vraw);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) sVt[(seg * VEC + e) * L::LDVT + r] = vv[e];
-        }
-      }
-      if (tid < CH) {
-        float a = 1.f, b = 0.f;
-        if (tid < Lc) {
-          const int64_t gi = (int64_t)(t0 + tid) * H + h;
-          a = ld_in(ga, gi);
-          b = ld_in(gb, gi);
-        }
-        sRawA[tid] = a;
-        sRawB[tid] = b;
-      }
     }
-    __syncthreads();
-
-    // ---------------- phase 2: gates; clear Tau's upper blocks ----------------
     if (w == 0) {
-      const int r = l;
-      float g = (r < Lc) ? logf(sRawA[r]) : 0.f;
+      float g = (l < Lc) ? logf(pa) : 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(g, off);
-        if (r >= off) g += y;
+        if (l >= off) g += y;
       }
       const float gL = __shfl(g, Lc - 1);
-      const float bet = sRawB[r];
-      const float gam = expf(g);
-      sG[r] = g;
-      sBeta[r] = bet;
-      sBG[r] = bet * gam;
-      sGam[r] = gam;
-      sDec[r] = (r < Lc) ? expf(gL - g) : 0.f;
-      if (r == 0) sScal[0] = expf(gL);
-    } else {
-      // upper blocks (bi < bj) of Tau are read as zeros by the k-steps
-      for (int e = tid - 64; e < 6 * 256; e += NT - 64) {
-        const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-        sTau[(16 * bi + rr) * L::LDC + 16 * bj + cc] = 0.f;
+      sG[l] = g;
+      sBeta[l] = (l < Lc) ? pb : 0.f;
+      sGam[l] = __expf(g);
+      sDec[l] = (l < Lc) ? __expf(gL - g) : 0.f;
+      if (l == 0) sScal[0] = __expf(gL);
+    }
+#pragma unroll
+    for (int u = 0; u < C::SPW; ++u) {
+      const int ct = w + u * NW;
+      if (ct < C::NST) {
+        if constexpr (BF)
+          store_tile_planes(sSh, sSl, C::LDSP, 0, 16 * ct, sacc[u]);
+        else
+          store_tile(sSh, C::LDSP, 0, 16 * ct, sacc[u]);
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C::NTF; ++i) ctau[i] = ptau[i];
+    cvv = pvv;
+    if (t0 + CH < tend) prefetch(t0 + CH, min(CH, tend - t0 - CH), slot + 1);
+    lds_barrier();
 
-    // ---------------- phase 3: A = strictly-lower beta_r e^{g_r-g_s} K K^T ----------------
-    for (int t = w; t < 10; t += NW) {
-      const int bi = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
-      const int bj = t - (bi * (bi + 1)) / 2;
+    // ================= P1: Y -> R ; Z, P =================
+    {
       f32x4 c = zero4();
       if constexpr (BF)
-        mma<BF, 1, 1>(c, RowMajor<bf16>{(const bf16 *)sK, L::LDK}, RowMajor<bf16>{(const bf16 *)sK, L::LDK},
-                      16 * bi, 16 * bj, 0, DK);
+        mma_bf16<2, 1>(c, Planes{sSh, sSl, C::LDSP}, RowMajor<bf16>{sK, C::LDK}, 0, 16 * cb, 0, DK);
       else
-        mma<BF, 1, 1>(c, RowMajor<float>{(const float *)sK, L::LDK}, RowMajor<float>{(const float *)sK, L::LDK},
-                      16 * bi, 16 * bj, 0, DK);
-      const int col = 16 * bj + (l & 15);
+        mma_f32(c, RowMajor<float>{sSh, C::LDSP}, RowMajor<float>{sK, C::LDK}, 0, 16 * cb, 0, DK);
+      const int r = 16 * cb + (l & 15);
+      const float bet = sBeta[r], gam = sGam[r];
+      float vj[4];
+      if constexpr (BF) {
+        const bf16 *vb = reinterpret_cast<const bf16 *>(&cvv);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * bi + 4 * (l >> 4) + i;
-        sA[row * L::LDC + col] = (col < row) ? sBeta[row] * expf(sG[row] - sG[col]) * c[i] : 0.f;
+        for (int i = 0; i < 4; ++i) vj[i] = (float)vb[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vj[i] = cvv[i];
       }
+      f32x4 rv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rv[i] = bet * (vj[i] - gam * c[i]);
+      if constexpr (BF)
+        store_tile_planes(sRh, sRl, C::LDRP, 0, 16 * cb, rv);
+      else
+        store_tile(sRh, C::LDRP, 0, 16 * cb, rv);
     }
-    __syncthreads();
-
-    // ---------------- phase 4: Tau = (I + A)^{-1} ----------------
-    // diagonal 16x16 blocks by forward substitution, one column per lane
-    if (w == 0) {
-      const int b = l >> 4, j = l & 15;
-      float x[16];
+    f32x4 oacc = zero4();
+    if (WANT_O) {
+      if constexpr (BF)
+        mma_bf16<2, 1>(oacc, Planes{sSh, sSl, C::LDSP}, RowMajor<bf16>{sQ, C::LDK}, 0, 16 * cb, 0, DK);
+      else
+        mma_f32(oacc, RowMajor<float>{sSh, C::LDSP}, RowMajor<float>{sQ, C::LDK}, 0, 16 * cb, 0, DK);
+      const float gam = sGam[16 * cb + (l & 15)];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == j) ? 1.f : 0.f;
-        const float *arow = sA + (16 * b + r) * L::LDC + 16 * b;
+      for (int i = 0; i < 4; ++i) oacc[i] *= gam;
+      // P = M o Q K^T, lower 16x16 blocks (upper blocks are zeroed below)
+      for (int t = w; t < 16; t += NW) {
+        const int bi = t >> 2, bj = t & 3;
+        const int col = 16 * bj + (l & 15);
+        const int rb = 16 * bi + 4 * (l >> 4);
+        if (bj > bi) {
 #pragma unroll
-        for (int s = 0; s < r; ++s) acc -= arow[s] * x[s];
-        x[r] = acc;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sTau[(16 * b + r) * L::LDC + 16 * b + j] = x[r];
-    }
-    __syncthreads();
-    // off-diagonal blocks, by distance from the diagonal:
-    //   Tau_ij = -Tau_ii * sum_{m=j}^{i-1} A_im Tau_mj
-    for (int d = 1; d < 4; ++d) {
-      const int nb = 4 - d;
-      if (w < nb) {
-        const int i = d + w, j = w;
+          for (int i = 0; i < 4; ++i) sP[(rb + i) * C::LDC + col] = 0.f;
+          continue;
+        }
         f32x4 c = zero4();
-        mma_f32(c, RowMajor<float>{sA + 16 * i * L::LDC, L::LDC}, ColMajor<float>{sTau + 16 * j, L::LDC}, 0, 0,
-                16 * j, 16 * i);
-        store_tile(sX + w * 16 * L::LDX, L::LDX, 0, 0, c);
-      }
-      __syncthreads();
-      if (w < nb) {
-        const int i = d + w, j = w;
-        f32x4 c = zero4();
-        mma_f32(c, RowMajor<float>{sTau + 16 * i * L::LDC + 16 * i, L::LDC},
-                ColMajor<float>{sX + w * 16 * L::LDX, L::LDX}, 0, 0, 0, 16);
-        const int col = 16 * j + (l & 15);
+        if constexpr (BF)
+          mma_bf16<1, 1>(c, RowMajor<bf16>{sQ, C::LDK}, RowMajor<bf16>{sK, C::LDK}, 16 * bi, 16 * bj, 0, DK);
+        else
+          mma_f32(c, RowMajor<float>{sQ, C::LDK}, RowMajor<float>{sK, C::LDK}, 16 * bi, 16 * bj, 0, DK);
+        const float gc = sG[col];
+        const f32x4 gr = *reinterpret_cast<const f32x4 *>(sG + rb);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sTau[(16 * i + 4 * (l >> 4) + q) * L::LDC + col] = -c[q];
+        for (int i = 0; i < 4; ++i) sP[(rb + i) * C::LDC + col] = (col <= rb + i) ? __expf(gr[i] - gc) * c[i] : 0.f;
       }
-      __syncthreads();
     }
+    lds_barrier();
 
-    // ---------------- phase 5: W = Tau diag(beta e^g) K ; P = M o Q K^T ----------------
+    // ================= P2: D = R Tau^T =================
     {
-      constexpr int NWT = 4 * (DK / 16);
-      constexpr int NPT = WANT_O ? 10 : 0;
-      for (int t = w; t < NWT + NPT; t += NW) {
-        f32x4 c = zero4();
-        if (t < NWT) {
-          const int rb = t / (DK / 16), cb = t % (DK / 16);
-          const RowScaled ta{sTau + 16 * rb * L::LDC, L::LDC, sBG};
-          if constexpr (BF)
-            mma<BF, 2, 1>(c, ta, RowMajor<bf16>{sKt, L::LDKT}, 0, 16 * cb, 0, tri_kend<BF>(rb));
-          else
-            mma<BF, 2, 1>(c, ta, ColMajor<float>{(const float *)sK, L::LDK}, 0, 16 * cb, 0, tri_kend<BF>(rb));
-          store_tile(sW, L::LDW, 16 * rb, 16 * cb, c);
-        } else {
-          const int tt = t - NWT;
-          const int bi = tt < 1 ? 0 : (tt < 3 ? 1 : (tt < 6 ? 2 : 3));
-          const int bj = tt - (bi * (bi + 1)) / 2;
-          mma<BF, 1, 1>(c, RowMajor<Tin>{sQ, L::LDK}, RowMajor<Tin>{sK, L::LDK}, 16 * bi, 16 * bj, 0, DK);
-          const int col = 16 * bj + (l & 15);
+      f32x4 c = zero4();
+      if constexpr (BF) {
+        const int nks = (cb + 2) >> 1;
+        const int rr = l & 15, kq = 8 * (l >> 4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * bi + 4 * (l >> 4) + i;
-            sA[row * L::LDC + col] = (col <= row) ? expf(sG[row] - sG[col]) * c[i] : 0.f;
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks < nks) {
+            bf16x8 ah, al_, bh, bl;
+            load8<true>(Planes{sRh, sRl, C::LDRP}, rr, 32 * ks + kq, ah, al_);
+            const float xb[8] = {ctau[2 * ks][0], ctau[2 * ks][1], ctau[2 * ks][2], ctau[2 * ks][3],
+                                 ctau[2 * ks + 1][0], ctau[2 * ks + 1][1], ctau[2 * ks + 1][2], ctau[2 * ks + 1][3]};
+            split8(xb, bh, bl);
+            c = mfma_bf16(ah, bh, c);
+            c = mfma_bf16(ah, bl, c);
+            c = mfma_bf16(al_, bh, c);
           }
         }
-      }
-      if (WANT_O) {
-        // upper blocks of P are read as zeros by the PD product
-        for (int e = tid; e < 6 * 256; e += NT) {
-          const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-          const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-          const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-          sA[(16 * bi + rr) * L::LDC + 16 * bj + cc] = 0.f;
+      } else {
+        const int rr = l & 15, kk = l >> 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (i < 4 * (cb + 1)) c = mfma_f32(sRh[rr * C::LDRP + 4 * i + kk], ctau[i >> 2][i & 3], c);
         }
       }
-    }
-    __syncthreads();
-
-    // ---------------- phase 6: D^T = U^T - S W^T ; first half of O^T ----------------
-    f32x4 oacc = zero4();
-    if (w < 4) {
-      const int cb = w;
-      f32x4 c = zero4();
-      if (!is_T) {
-        const RowScaled tb{sTau, L::LDC, sBeta};
-        mma<BF, 1, 2>(c, RowMajor<Tin>{sVt, L::LDVT}, tb, 0, 16 * cb, 0, tri_kend<BF>(cb));
-      }
-      mma<BF, PRECISE_S ? 2 : 1, PRECISE_S ? 2 : 1>(c, RowNeg{sS, L::LDW}, RowMajor<float>{sW, L::LDW}, 0,
-                                                    16 * cb, 0, DK);
-      store_tile(sD, L::LDD, 0, 16 * cb, c);
       const float dec = sDec[16 * cb + (l & 15)];
       f32x4 cd;
 #pragma unroll
       for (int i = 0; i < 4; ++i) cd[i] = c[i] * dec;
-      store_tile(sDd, L::LDD, 0, 16 * cb, cd);
-    } else if (WANT_O) {
-      const int cb = w - 4;
-      mma<BF, 1, 1>(oacc, RowMajor<float>{sS, L::LDW}, RowMajor<Tin>{sQ, L::LDK}, 0, 16 * cb, 0, DK);
-      const float gam = sGam[16 * cb + (l & 15)];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[i] *= gam;
+      if constexpr (BF) {
+        if (WANT_O) store_tile_planes(sDh, sDl, C::LDRP, 0, 16 * cb, c);
+        store_tile_planes(sDdh, sDdl, C::LDRP, 0, 16 * cb, cd);
+      } else {
+        if (WANT_O) store_tile(sDh, C::LDRP, 0, 16 * cb, c);
+        store_tile(sDdh, C::LDRP, 0, 16 * cb, cd);
+      }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---------------- phase 7: O^T += D^T P^T, store o ; S update ----------------
-    if (WANT_O && w >= 4) {
-      const int cb = w - 4;
-      mma<BF, 2, 2>(oacc, RowMajor<float>{sD, L::LDD}, RowMajor<float>{sA, L::LDC}, 0, 16 * cb, 0,
-                    tri_kend<BF>(cb));
+    // ================= P3: outputs; state update =================
+    if (WANT_O) {
+      const int kend = BF ? 32 * ((cb + 2) >> 1) : 16 * (cb + 1);
+      if constexpr (BF)
+        mma_bf16<2, 2>(oacc, Planes{sDh, sDl, C::LDRP}, RowMajor<float>{sP, C::LDC}, 0, 16 * cb, 0, kend);
+      else
+        mma_f32(oacc, RowMajor<float>{sDh, C::LDRP}, RowMajor<float>{sP, C::LDC}, 0, 16 * cb, 0, kend);
       const int r = 16 * cb + (l & 15);
       if (r < Lc) {
         const int64_t base = ((int64_t)(t0 + r) * H + h) * DV + row0 + 4 * (l >> 4);
@@ -382,49 +386,55 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
         }
       }
     }
-    if (owns) {
+    {
       const float gl = sScal[0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sacc[i] *= gl;
-      if constexpr (BF)
-        mma<BF, 2, 1>(sacc, RowMajor<float>{sDd, L::LDD}, RowMajor<bf16>{sKt, L::LDKT}, 0, 16 * w, 0, CH);
-      else
-        mma<BF, 2, 1>(sacc, RowMajor<float>{sDd, L::LDD}, ColMajor<float>{(const float *)sK, L::LDK}, 0, 16 * w,
-                      0, CH);
+      for (int u = 0; u < C::SPW; ++u) {
+        const int ct = w + u * NW;
+        if (ct < C::NST) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[u][i] *= gl;
+          if constexpr (BF)
+            mma_bf16<2, 1>(sacc[u], Planes{sDdh, sDdl, C::LDRP}, ColMajor<bf16>{sK, C::LDK}, 0, 16 * ct, 0, CH);
+          else
+            mma_f32(sacc[u], RowMajor<float>{sDdh, C::LDRP}, ColMajor<float>{sK, C::LDK}, 0, 16 * ct, 0, CH);
+        }
+      }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---------------- epilogue: final rows ----------------
-  if (owns) {
+  {
     float *out = is_T ? p.T_out : p.S_out;
     const int nrows = is_T ? DK : DV;
-    const int col = 16 * w + (l & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = row0 + 4 * (l >> 4) + i;
-      out[(((int64_t)n * H + h) * nrows + r) * DK + col] = sacc[i];
+    for (int u = 0; u < C::SPW; ++u) {
+      const int ct = w + u * NW;
+      if (ct < C::NST) {
+        const int col = 16 * ct + (l & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = row0 + 4 * (l >> 4) + i;
+          out[(((int64_t)n * H + h) * nrows + r) * DK + col] = sacc[u][i];
+        }
+      }
     }
   }
 }
 
-template <class Tin, int DK, bool WANT_O, bool PRECISE_S>
+template <class Tin, int DK, bool WANT_O>
 hipError_t launch_t(const ChainLaunch &p, hipStream_t stream) {
   const int64_t items = (int64_t)p.n_seqs * p.H * (p.tiles_T + p.tiles_S);
   if (items <= 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((chain_kernel<Tin, DK, WANT_O, PRECISE_S>), dim3((unsigned)grid), dim3(NT), 0, stream, p,
-                     (int)items);
+  hipLaunchKernelGGL((chain_kernel<Tin, DK, WANT_O>), dim3((unsigned)grid), dim3(NT), 0, stream, p, (int)items);
   return hipGetLastError();
 }
 
 template <class Tin, int DK>
 hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
-  const bool want_o = p.o != nullptr;
-  if (p.precise_state) {
-    return want_o ? launch_t<Tin, DK, true, true>(p, stream) : launch_t<Tin, DK, false, true>(p, stream);
-  }
-  return want_o ? launch_t<Tin, DK, true, false>(p, stream) : launch_t<Tin, DK, false, false>(p, stream);
+  return p.o ? launch_t<Tin, DK, true>(p, stream) : launch_t<Tin, DK, false>(p, stream);
 }
 
 }  // namespace

@@ -7,6 +7,10 @@
 //     k = 8*(l >> 4) .. +7;  B[32 x 16]: lane l holds column (l & 15), the
 //     same 8 k;  C/D[16 x 16]: lane l holds column (l & 15), rows
 //     4*(l >> 4) .. +3.
+//   v_mfma_f32_16x16x16_bf16:  A: row (l & 15), k = 4*(l >> 4) .. +3;
+//     B: column (l & 15), the same 4 k;  C/D as above.  The C/D layout of a
+//     16 x 16 tile is therefore exactly its B-operand layout, which lets a
+//     product result feed the next product without leaving registers.
 //   v_mfma_f32_16x16x4_f32:    A: row (l & 15), k = l >> 4;  B: column
 //     (l & 15), k = l >> 4;  C/D as above.
 //
@@ -35,12 +39,22 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma_bf16_k16(const bf16x4 &a, const bf16x4 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+__device__ __forceinline__ float ld_in(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_in(const bf16 *p, int64_t i) { return (float)p[i]; }
+
+// Float offset of lower block row bi in a packed 64 x 64 Tau (block row bi
+// holds 16 rows x 16 (bi + 1) columns): 256 * bi (bi + 1) / 2.
+__device__ __forceinline__ int tau_off(int bi) { return 128 * bi * (bi + 1); }
 
 // ---------------------------------------------------------------------------
 // LDS operand views.  An operand of an MFMA tile is addressed as
@@ -125,12 +139,35 @@ __device__ __forceinline__ void load8(const RowMajor<bf16> &a, int row, int k, b
   (void)lo;
 }
 
+// A pre-split fp32 operand: hi = bf16(x), lo = bf16(x - hi), row-major planes.
+struct Planes {
+  const bf16 *hi;
+  const bf16 *lo;
+  int ld;
+};
+template <bool NEED_LO>
+__device__ __forceinline__ void load8(const Planes &a, int row, int k, bf16x8 &hi, bf16x8 &lo) {
+  hi = *reinterpret_cast<const bf16x8 *>(a.hi + row * a.ld + k);
+  if (NEED_LO) lo = *reinterpret_cast<const bf16x8 *>(a.lo + row * a.ld + k);
+}
+// Column access of exact bf16 data: element (row, k) = p[k * ld + row].
+template <bool NEED_LO>
+__device__ __forceinline__ void load8(const ColMajor<bf16> &a, int row, int k, bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) hi[e] = a.p[(k + e) * a.ld + row];
+  (void)lo;
+}
+
 template <class Op>
 struct IsExactBf16 {
   static constexpr bool value = false;
 };
 template <>
 struct IsExactBf16<RowMajor<bf16>> {
+  static constexpr bool value = true;
+};
+template <>
+struct IsExactBf16<ColMajor<bf16>> {
   static constexpr bool value = true;
 };
 
@@ -162,6 +199,51 @@ __device__ __forceinline__ void mma_f32(f32x4 &c, const OA &opA, const OB &opB, 
   const int l = lane_id();
   const int r = l & 15, kk = l >> 4;
   for (int k = k0; k < k1; k += 4) c = mfma_f32(opA.one(m0 + r, k + kk), opB.one(n0 + r, k + kk), c);
+}
+
+__device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bf16 h = (bf16)x[i];
+    hi[i] = h;
+    lo[i] = (bf16)(x[i] - (float)h);
+  }
+}
+
+// 3-pass split-bf16 product of 16 x 16 tiles, k = 16: A given as 4 fp32 per
+// lane in A layout, B as 4 fp32 per lane in B (= C) layout.
+__device__ __forceinline__ f32x4 mma16_split3(const f32x4 &a, const f32x4 &b, f32x4 c) {
+  bf16x4 ah, al, bh, bl;
+  split4(a, ah, al);
+  split4(b, bh, bl);
+  c = mfma_bf16_k16(ah, bh, c);
+  c = mfma_bf16_k16(ah, bl, c);
+  c = mfma_bf16_k16(al, bh, c);
+  return c;
+}
+
+// Store a C-layout tile into split planes (hi, lo) of a row-major bf16 array.
+__device__ __forceinline__ void store_tile_planes(bf16 *hi, bf16 *lo, int ld, int m0, int n0, const f32x4 &c) {
+  const int l = lane_id();
+  const int col = n0 + (l & 15), row = m0 + 4 * (l >> 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16 h = (bf16)c[i];
+    hi[(row + i) * ld + col] = h;
+    lo[(row + i) * ld + col] = (bf16)(c[i] - (float)h);
+  }
+}
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, not for its outstanding global loads (which stay in flight
+// across the barrier; their consumers wait for them as usual).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Make prior LDS writes of this wave visible to its later LDS reads.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 // Store a C-layout tile into a row-major fp32 LDS array (optionally scaled per column).

@@ -3,9 +3,39 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace gdn {
+
+// ---------------------------------------------------------------------------
+// Chunk slots.  Sequence n (tokens cu[n] .. cu[n+1]-1) is cut into 64-token
+// chunks; its chunk j lives in slot floor(cu[n] / 64) + n + j.  Slots of
+// different sequences never collide and all lie below
+// n_tokens / 64 + n_seqs + 1, so the host can size per-chunk storage
+// without reading cu (which lives on the device).
+// ---------------------------------------------------------------------------
+constexpr int kChunk = 64;
+// Tau = (I + A)^{-1} of one chunk, lower 16 x 16 block rows packed: block
+// row b holds 16 rows x 16 (b + 1) columns, row-major, at float offset
+// 256 * b (b + 1) / 2.
+constexpr int kTauFloats = 2560;
+
+inline int64_t slot_count(int64_t n_tokens, int32_t n_seqs) { return n_tokens / kChunk + n_seqs + 1; }
+
+inline size_t tau_workspace_bytes(int64_t n_tokens, int32_t n_seqs, int32_t n_heads) {
+  return (size_t)slot_count(n_tokens, n_seqs) * (size_t)n_heads * kTauFloats * sizeof(float);
+}
+
+// Per-chunk factor build: one workgroup per (slot, head).
+struct PrepLaunch {
+  const void *k, *alpha, *beta;
+  const int32_t *cu;
+  int32_t n_seqs, H, dk;
+  int in_bf16;
+  float *tau;        // [n_slots, H, kTauFloats]
+  int64_t n_slots;
+};
 
 // One launch of the chunked recurrence kernel.  A work item is one tile of
 // 16 rows of the state of one (sequence, head).  Row tiles come in two kinds:
@@ -18,6 +48,7 @@ struct ChainLaunch {
   const void *q, *k, *v, *alpha, *beta;
   const float *S0;          // [n_seqs, H, dv, dk] or null
   const int32_t *cu;        // [n_seqs + 1] (device)
+  const float *tau;         // per-chunk factors from the prep kernel
   int32_t n_seqs;
   int32_t H;
   int32_t dk, dv;
@@ -27,7 +58,6 @@ struct ChainLaunch {
   float *S_out;             // [n_seqs, H, dv, dk] (state tiles) or null
   float *T_out;             // [n_seqs, H, dk, dk] (transition tiles) or null
   int32_t tiles_T, tiles_S;
-  int precise_state;        // split the state operand of the state x W product
 };
 
 struct ComposeLaunch {
@@ -38,6 +68,7 @@ struct ComposeLaunch {
   float *S_out;             // [H, dv, dk]
 };
 
+hipError_t launch_prep(const PrepLaunch &p, hipStream_t stream);
 hipError_t launch_chain(const ChainLaunch &p, hipStream_t stream);
 hipError_t launch_compose(const ComposeLaunch &p, hipStream_t stream);
 

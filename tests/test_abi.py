@@ -93,6 +93,28 @@ def test_compose_argument_checks(lib):
 
 
 def test_workspace_queries(lib):
-    assert lib.gdn_replay_workspace_bytes(16, 30000, 32, 128, 128) == 0
-    assert lib.gdn_chunk_operator_workspace_bytes(64, 32768, 32, 128, 128) == 0
+    # one packed 64 x 64 lower-triangular factor (2560 floats) per chunk slot
+    # and head; slots = n_tokens / 64 + n_seqs + 1 (sequence n's chunk j sits
+    # in slot floor(cu[n] / 64) + n + j)
+    assert lib.gdn_replay_workspace_bytes(16, 30000, 32, 128, 128) == (30000 // 64 + 17) * 32 * 2560 * 4
+    assert lib.gdn_chunk_operator_workspace_bytes(64, 32768, 32, 128, 128) == (512 + 65) * 32 * 10240
     assert lib.gdn_compose_workspace_bytes(64, 32, 128, 128) == 0
+    # a missing workspace is reported before anything is launched
+    assert replay(lib) == WS
+    assert b"workspace" in lib.gdn_last_error()
+    assert lib.gdn_chunk_operator(P, P, P, P, P, 2, 10, 2, 64, 64, BF16, P, P, None, 0, None) == WS
+
+
+def test_chunk_slots_are_unique():
+    """The slot rule floor(cu[n]/64) + n + j never collides and stays below
+    n_tokens / 64 + n_seqs + 1 (checked exhaustively on random packings)."""
+    import numpy as np
+    rng = np.random.Generator(np.random.PCG64(3))
+    for _ in range(300):
+        lens = rng.integers(0, 300, size=rng.integers(1, 12))
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        slots = []
+        for n, L in enumerate(lens):
+            slots += [cu[n] // 64 + n + j for j in range(-(-L // 64))]
+        assert len(slots) == len(set(slots))
+        assert all(0 <= s < cu[-1] // 64 + len(lens) + 1 for s in slots)

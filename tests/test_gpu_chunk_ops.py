@@ -1,0 +1,115 @@
+"""GPU parity of gdn_chunk_operator and gdn_compose against the fp64 oracle.
+
+T_C / S_local are compared per chunk over the whole output tensors; the
+composed state is compared with the oracle's sequential replay over all the
+chunks' tokens (the composition adds no approximation of its own, so the
+two must agree to the kernels' rounding).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_helpers import dev, rel, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _gdn():
+    import torch
+    assert torch.cuda.is_available()
+    import gated_deltanet_state_amd as gdn
+    return gdn, torch
+
+
+def gpu_ops(inp, bounds, with_v=True):
+    gdn, torch = _gdn()
+    d = dev(inp)
+    cu = torch.from_numpy(np.asarray(bounds, np.int32)).cuda()
+    TC, SL = gdn.chunk_operator(d["k"], d["alpha"], d["beta"], cu, v=d["v"] if with_v else None)
+    torch.cuda.synchronize()
+    return TC, SL
+
+
+def tol(inp):
+    return 1e-5 if inp.dtype == "f32" else 3e-3
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128)])
+def test_chunk_operator_uneven_chunks(dtype, dk, dv):
+    bounds = np.cumsum([0, 1, 5, 64, 65, 130, 0, 200]).astype(np.int32)
+    inp = workloads.generate([int(bounds[-1])], H=2, dk=dk, dv=dv, dtype=dtype, seed=41,
+                             gate_scale=0.01)
+    TC, SL = gpu_ops(inp, bounds)
+    f = inp.f64
+    TC_ref, SL_ref = oracle.chunk_operator(f["k"], f["alpha"], f["beta"], bounds, v=f["v"])
+    eT, eS = rel(to_np(TC), TC_ref), rel(to_np(SL), SL_ref)
+    print("err_T %.3e err_Sloc %.3e" % (eT, eS), flush=True)
+    assert eT <= tol(inp) and eS <= tol(inp)
+    # the empty chunk is the identity with a zero local state
+    assert np.array_equal(to_np(TC)[5], np.broadcast_to(np.eye(dk), (2, dk, dk)))
+    assert not np.any(to_np(SL)[5])
+
+
+def test_transition_only():
+    bounds = np.array([0, 100, 300], np.int32)
+    inp = workloads.generate([300], H=2, dk=128, dv=128, dtype="bf16", seed=42, alpha_one=True)
+    TC, SL = gpu_ops(inp, bounds, with_v=False)
+    assert SL is None
+    TC2, _ = gpu_ops(inp, bounds, with_v=True)
+    assert np.array_equal(to_np(TC), to_np(TC2))
+    f = inp.f64
+    TC_ref, _ = oracle.chunk_operator(f["k"], f["alpha"], f["beta"], bounds)
+    assert rel(to_np(TC), TC_ref) <= 3e-3
+
+
+@pytest.mark.parametrize("gate", ["one", "slow", "workload"])
+def test_compose_matches_sequential_replay(gate):
+    kw = dict(alpha_one=True) if gate == "one" else (
+        dict(gate_scale=0.001) if gate == "slow" else {})
+    n_chunks, L = 6, 96
+    inp = workloads.generate([n_chunks * L], H=3, dk=128, dv=128, dtype="bf16", seed=43, **kw)
+    bounds = workloads.chunk_bounds(n_chunks * L, L)
+    gdn, torch = _gdn()
+    TC, SL = gpu_ops(inp, bounds)
+    rng = np.random.Generator(np.random.PCG64(9))
+    S_in = (rng.standard_normal((3, 128, 128)) * 0.2).astype(np.float32)
+    S_in_t = torch.from_numpy(S_in).cuda()
+    S = gdn.compose(TC, SL, S_in=S_in_t)
+    torch.cuda.synchronize()
+    f = inp.f64
+    _, S_seq = oracle.replay(None, f["k"], f["v"], f["alpha"], f["beta"], [0, n_chunks * L],
+                             S0=S_in[None].astype(np.float64), want_o=False)
+    e = rel(to_np(S), S_seq[0])
+    print("gate %s err_compose %.3e  ||T_C||/sqrt(d) %.3e" % (
+        gate, e, np.linalg.norm(to_np(TC)[0, 0]) / np.sqrt(128)), flush=True)
+    assert e <= 3e-3
+
+
+def test_compose_exact_operators_fp32():
+    """Compose alone, fed the oracle's own operators: fp32-level agreement."""
+    gdn, torch = _gdn()
+    rng = np.random.Generator(np.random.PCG64(10))
+    H, dk, dv, C = 2, 128, 64, 9
+    inp = workloads.generate([C * 40], H=H, dk=dk, dv=dv, dtype="f32", seed=44, gate_scale=0.01)
+    bounds = workloads.chunk_bounds(C * 40, 40)
+    f = inp.f64
+    TC_ref, SL_ref = oracle.chunk_operator(f["k"], f["alpha"], f["beta"], bounds, v=f["v"])
+    TC32, SL32 = TC_ref.astype(np.float32), SL_ref.astype(np.float32)
+    S_in = rng.standard_normal((H, dv, dk)).astype(np.float32)
+    ref = oracle.compose(TC32, SL32, S_in=S_in)
+    S = gdn.compose(torch.from_numpy(TC32).cuda(), torch.from_numpy(SL32).cuda(),
+                    S_in=torch.from_numpy(S_in).cuda())
+    torch.cuda.synchronize()
+    assert rel(to_np(S), ref) <= 1e-5
+    # zero chunks returns the incoming state; in place is allowed
+    S_in_t = torch.from_numpy(S_in).cuda()
+    S0 = gdn.compose(torch.from_numpy(TC32[:0]).cuda(), torch.from_numpy(SL32[:0]).cuda(),
+                     S_in=S_in_t)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(S0), S_in.astype(np.float64))
+    S_io = torch.from_numpy(S_in).cuda()
+    gdn.compose(torch.from_numpy(TC32).cuda(), torch.from_numpy(SL32).cuda(), S_in=S_io, out=S_io)
+    torch.cuda.synchronize()
+    assert torch.equal(S_io, S)

@@ -22,7 +22,7 @@ matched prefix, with r a fraction such as 5% or 10%.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from fractions import Fraction
 from typing import Optional
 
@@ -44,10 +44,9 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 
     Returns the uint16 bit patterns.  NaN is not expected in these inputs.
     """
-    f = f32_round(x)
-    u = f.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    u = (u + 0x7FFF + lsb) >> 16
+    u = f32_round(x).view(np.uint32)
+    # finite inputs only: the rounding increment cannot carry out of 32 bits
+    u = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
     return u.astype(np.uint16)
 
 
@@ -62,7 +61,7 @@ class Inputs:
 
     ``q``, ``k``, ``v``, ``alpha``, ``beta`` are numpy arrays in the input
     dtype's storage: float32, or uint16 bf16 bit patterns when dtype == 'bf16'.
-    ``f64`` holds the same values upcast exactly to float64.
+    ``f64`` gives the same values upcast exactly to float64.
     """
     dtype: str
     H: int
@@ -74,7 +73,15 @@ class Inputs:
     v: np.ndarray
     alpha: np.ndarray
     beta: np.ndarray
-    f64: dict = field(default_factory=dict)
+    _f64: Optional[dict] = None
+
+    @property
+    def f64(self) -> dict:
+        """The same values upcast exactly to float64 (computed on first use)."""
+        if self._f64 is None:
+            conv = bf16_to_f64 if self.dtype == "bf16" else (lambda a: a.astype(np.float64))
+            self._f64 = {n: conv(getattr(self, n)) for n in ("q", "k", "v", "alpha", "beta")}
+        return self._f64
 
     @property
     def n_tokens(self) -> int:
@@ -120,17 +127,9 @@ def generate(lengths, H: int, dk: int, dv: int, dtype: str = "bf16",
     beta = 1.0 / (1.0 + np.exp(-xb)) if beta_value is None else np.full((T, H), beta_value)
     alpha = np.ones((T, H)) if alpha_one else np.exp(-gate_scale * _softplus(xa))
     arrs = dict(q=q, k=k, v=v, alpha=alpha, beta=beta)
-    store, f64 = {}, {}
-    for name, a in arrs.items():
-        if dtype == "bf16":
-            bits = bf16_bits(a)
-            store[name] = bits
-            f64[name] = bf16_to_f64(bits)
-        else:
-            f = f32_round(a)
-            store[name] = f
-            f64[name] = f.astype(np.float64)
-    return Inputs(dtype=dtype, H=H, dk=dk, dv=dv, cu_seqlens=cu, f64=f64, **store)
+    rnd = bf16_bits if dtype == "bf16" else f32_round
+    store = {name: rnd(a) for name, a in arrs.items()}
+    return Inputs(dtype=dtype, H=H, dk=dk, dv=dv, cu_seqlens=cu, **store)
 
 
 # ---------------------------------------------------------------------------
