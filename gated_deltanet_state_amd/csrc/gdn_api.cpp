@@ -127,7 +127,7 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   p.T_out = nullptr;
   p.tiles_T = 0;
   p.tiles_S = dv / 16;
-  return launched(gdn::launch_chain(p, st), "gdn_replay launch");
+  return launched(p.in_bf16 ? gdn::launch_chain_bf16(p, st) : gdn::launch_chain(p, st), "gdn_replay launch");
 }
 
 gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, const void *beta,
@@ -186,7 +186,8 @@ gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, c
   p.T_out = T_C;
   p.tiles_T = dk / 16;
   p.tiles_S = v ? dv / 16 : 0;
-  return launched(gdn::launch_chain(p, st), "gdn_chunk_operator launch");
+  return launched(p.in_bf16 ? gdn::launch_chain_bf16(p, st) : gdn::launch_chain(p, st),
+                  "gdn_chunk_operator launch");
 }
 
 gdn_status gdn_compose(const float *S_in, const float *T_C, const float *S_local, int32_t n_chunks,

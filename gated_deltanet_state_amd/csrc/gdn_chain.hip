@@ -27,14 +27,15 @@
 // fp32 inputs use the fp32 MFMA.
 //
 // Four waves; wave w owns token block w (16 tokens) of every 16 x 64 tile
-// (Y, R, D, O) and state column tiles w, w + 4.  Per chunk, four phases
-// separated by LDS-only barriers (global loads of the next chunk stay in
-// flight across them):
-//   P0  store the prefetched keys (and queries) to LDS, gates, state planes;
-//       issue the next chunk's loads (keys, queries, V, gates, Tau rows)
+// (Y, R, D, O) and state column tiles w, w + 4.  Per chunk, three phases
+// separated by LDS-only barriers (each chunk's global loads are issued one
+// chunk period before they are staged and stay in flight across the
+// barriers); keys and gates are double-buffered in LDS:
 //   P1  Y = S K^T -> R;  [o] Z = e^g S Q^T,  P = M o Q K^T
 //   P2  D = R Tau^T (Tau rows straight from registers)
-//   P3  [o] O = Z + D P^T -> o;  S = e^{g_L} S + (e^{g_L - g} D)^T K
+//   P3  [o] O = Z + D P^T -> o;  S = e^{g_L} S + (e^{g_L - g} D)^T K; then
+//       state planes, the next chunk's keys / queries / gates to LDS, and
+//       the loads of the chunk after it
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -62,15 +63,17 @@ struct Cfg {
   static constexpr int NPL = BF ? 2 : 1;             // planes per split operand
 
   static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
-  static constexpr size_t oK = 0;
-  static constexpr size_t oQ = oK + al(sizeof(Tin) * CH * LDK);
+  static constexpr size_t KBYTES = al(sizeof(Tin) * CH * LDK);
+  static constexpr size_t oK = 0;                     // two buffers (chunk parity)
+  static constexpr size_t oQ = oK + 2 * KBYTES;
   static constexpr size_t oP = oQ + (WANT_O ? al(sizeof(Tin) * CH * LDK) : 0);
   static constexpr size_t oS = oP + (WANT_O ? al(4 * CH * LDC) : 0);
   static constexpr size_t oR = oS + NPL * al(sizeof(PT) * RT * LDSP);
   static constexpr size_t oD = oR + NPL * al(sizeof(PT) * RT * LDRP);
   static constexpr size_t oDd = oD + (WANT_O ? NPL * al(sizeof(PT) * RT * LDRP) : 0);
   static constexpr size_t oGate = oDd + NPL * al(sizeof(PT) * RT * LDRP);
-  static constexpr size_t TOTAL = oGate + al(4 * 5 * CH);
+  static constexpr size_t GBYTES = al(4 * 5 * CH);
+  static constexpr size_t TOTAL = oGate + 2 * GBYTES;  // two gate buffers
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 
   static constexpr int NST = DK / 16;          // state column tiles
@@ -91,7 +94,7 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
   constexpr bool BF = C::BF;
   using PT = typename C::PT;
   __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
-  Tin *sK = reinterpret_cast<Tin *>(smem + C::oK);
+  Tin *sK0 = reinterpret_cast<Tin *>(smem + C::oK);
   Tin *sQ = reinterpret_cast<Tin *>(smem + C::oQ);
   float *sP = reinterpret_cast<float *>(smem + C::oP);
   PT *sSh = reinterpret_cast<PT *>(smem + C::oS);
@@ -102,12 +105,9 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
   PT *sDl = sDh + (BF ? RT * C::LDRP : 0);
   PT *sDdh = reinterpret_cast<PT *>(smem + C::oDd);
   PT *sDdl = sDdh + (BF ? RT * C::LDRP : 0);
-  float *sGate = reinterpret_cast<float *>(smem + C::oGate);
-  float *sG = sGate;             // g_r
-  float *sBeta = sGate + CH;     // beta_r (0 past the chunk end)
-  float *sGam = sGate + 2 * CH;  // e^{g_r}
-  float *sDec = sGate + 3 * CH;  // e^{g_L - g_r} (0 past the end)
-  float *sScal = sGate + 4 * CH; // [0] = e^{g_L}
+  // gate buffer (per chunk parity): g_r | beta_r (0 past the chunk end) |
+  // e^{g_r} | e^{g_L - g_r} (0 past the end) | [0] = e^{g_L}
+  float *sGate0 = reinterpret_cast<float *>(smem + C::oGate);
 
   // ---- work item: XCD-aware order (block b runs on XCD b % 8; each XCD
   // takes a contiguous range of items so the row tiles of one head share
@@ -152,8 +152,12 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
   // ---- prefetch registers (next chunk) and current-chunk copies ----
   f32x4 pk[C::NKP], pq[C::NKP];
   f32x4 ptau[C::NTF], ctau[C::NTF];
-  f32x4 pvv, cvv;  // V[t0 + 16 cb + (l & 15)][row0 + 4 (l >> 4) .. + 3] (bf16: first half used)
-  float pa = 1.f, pb = 0.f;
+  // V[t0 + 16 cb + (l & 15)][row0 + 4 (l >> 4) .. + 3]
+  using VRaw = typename std::conditional<BF, uint2, f32x4>::type;
+  VRaw pvv, cvv;
+  // gates are carried as loaded (no conversion) so that issuing the next
+  // chunk's loads never waits for them
+  Tin pa = Tin(1.f), pb = Tin(0.f);
   const int tbeg = p.cu[n], tend = p.cu[n + 1];
   const int64_t slot0 = (int64_t)(tbeg / CH) + n;
 
@@ -191,67 +195,59 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
         ptau[i >> 2][i & 3] = (s < ncol) ? tau[s] : 0.f;
       }
     }
-    pvv = zero4();
+    pvv = VRaw{};
     const int r = 16 * cb + (l & 15);
     if (!is_T && r < Lc) {
       const Tin *src = gv + ((int64_t)(t0 + r) * H + h) * DV + row0 + 4 * (l >> 4);
-      if constexpr (BF) {
-        const uint2 u2 = *reinterpret_cast<const uint2 *>(src);
-        pvv[0] = __uint_as_float(u2.x);
-        pvv[1] = __uint_as_float(u2.y);
-      } else {
-        pvv = *reinterpret_cast<const f32x4 *>(src);
-      }
+      pvv = *reinterpret_cast<const VRaw *>(src);
     }
     if (w == 0) {
-      pa = 1.f;
-      pb = 0.f;
+      pa = Tin(1.f);
+      pb = Tin(0.f);
       if (l < Lc) {
         const int64_t gi = (int64_t)(t0 + l) * H + h;
-        pa = ld_in(ga, gi);
-        pb = ld_in(gb, gi);
+        pa = ga[gi];
+        pb = gb[gi];
       }
     }
   };
 
-  if (tbeg < tend) prefetch(tbeg, min(CH, tend - tbeg), slot0);
-
-  int64_t slot = slot0;
-  for (int t0 = tbeg; t0 < tend; t0 += CH, ++slot) {
-    const int Lc = min(CH, tend - t0);
-
-    // ================= P0 =================
+  // Store a prefetched chunk into K buffer `kb` (and Q), gates into gate
+  // buffer `kb`; move the per-wave fragments to their "current" copies.
+  auto stage = [&](int kb, int Lc) {
+    Tin *sKb = sK0 + kb * (C::KBYTES / sizeof(Tin));
 #pragma unroll
     for (int i = 0; i < C::NKP; ++i) {
       const int s = tid + i * NT;
       if (s < CH * C::KSEG) {
         const int r = s / C::KSEG, seg = s % C::KSEG;
         if constexpr (BF) {
-          *reinterpret_cast<f32x4 *>(sK + r * C::LDK + seg * C::VEC) = pk[i];
+          *reinterpret_cast<f32x4 *>(sKb + r * C::LDK + seg * C::VEC) = pk[i];
           if (WANT_O) *reinterpret_cast<f32x4 *>(sQ + r * C::LDK + seg * C::VEC) = pq[i];
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            sK[r * C::LDK + seg * 4 + e] = pk[i][e];
+            sKb[r * C::LDK + seg * 4 + e] = pk[i][e];
             if (WANT_O) sQ[r * C::LDK + seg * 4 + e] = pq[i][e];
           }
         }
       }
     }
     if (w == 0) {
-      float g = (l < Lc) ? logf(pa) : 0.f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(g, off);
-        if (l >= off) g += y;
-      }
-      const float gL = __shfl(g, Lc - 1);
-      sG[l] = g;
-      sBeta[l] = (l < Lc) ? pb : 0.f;
-      sGam[l] = __expf(g);
-      sDec[l] = (l < Lc) ? __expf(gL - g) : 0.f;
-      if (l == 0) sScal[0] = __expf(gL);
+      float *sGb = sGate0 + kb * (C::GBYTES / 4);
+      const float g = wave_inclusive_scan((l < Lc) ? logf(to_f32(pa)) : 0.f);
+      const float gL = lane_value(g, Lc - 1);
+      sGb[l] = g;
+      sGb[CH + l] = (l < Lc) ? to_f32(pb) : 0.f;
+      sGb[2 * CH + l] = __expf(g);
+      sGb[3 * CH + l] = (l < Lc) ? __expf(gL - g) : 0.f;
+      if (l == 0) sGb[4 * CH] = __expf(gL);
     }
+#pragma unroll
+    for (int i = 0; i < C::NTF; ++i) ctau[i] = ptau[i];
+    cvv = pvv;
+  };
+  auto store_state_planes = [&]() {
 #pragma unroll
     for (int u = 0; u < C::SPW; ++u) {
       const int ct = w + u * NW;
@@ -262,11 +258,23 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
           store_tile(sSh, C::LDSP, 0, 16 * ct, sacc[u]);
       }
     }
-#pragma unroll
-    for (int i = 0; i < C::NTF; ++i) ctau[i] = ptau[i];
-    cvv = pvv;
-    if (t0 + CH < tend) prefetch(t0 + CH, min(CH, tend - t0 - CH), slot + 1);
-    lds_barrier();
+  };
+
+  if (tbeg < tend) {
+    prefetch(tbeg, min(CH, tend - tbeg), slot0);
+    stage(0, min(CH, tend - tbeg));
+    store_state_planes();
+    if (tbeg + CH < tend) prefetch(tbeg + CH, min(CH, tend - tbeg - CH), slot0 + 1);
+  }
+  lds_barrier();
+
+  int64_t slot = slot0;
+  int kb = 0;
+  for (int t0 = tbeg; t0 < tend; t0 += CH, ++slot, kb ^= 1) {
+    const int Lc = min(CH, tend - t0);
+    const Tin *sK = sK0 + kb * (C::KBYTES / sizeof(Tin));
+    const float *sG = sGate0 + kb * (C::GBYTES / 4);
+    const float *sBeta = sG + CH, *sGam = sG + 2 * CH, *sDec = sG + 3 * CH;
 
     // ================= P1: Y -> R ; Z, P =================
     {
@@ -303,7 +311,7 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
       const float gam = sGam[16 * cb + (l & 15)];
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[i] *= gam;
-      // P = M o Q K^T, lower 16x16 blocks (upper blocks are zeroed below)
+      // P = M o Q K^T, lower 16x16 blocks (upper blocks written as zeros)
       for (int t = w; t < 16; t += NW) {
         const int bi = t >> 2, bj = t & 3;
         const int col = 16 * bj + (l & 15);
@@ -366,7 +374,7 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
     }
     lds_barrier();
 
-    // ================= P3: outputs; state update =================
+    // ================= P3: outputs; state update; stage the next chunk =================
     if (WANT_O) {
       const int kend = BF ? 32 * ((cb + 2) >> 1) : 16 * (cb + 1);
       if constexpr (BF)
@@ -387,7 +395,7 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
       }
     }
     {
-      const float gl = sScal[0];
+      const float gl = sG[4 * CH];
 #pragma unroll
       for (int u = 0; u < C::SPW; ++u) {
         const int ct = w + u * NW;
@@ -400,6 +408,13 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
             mma_f32(sacc[u], RowMajor<float>{sDdh, C::LDRP}, ColMajor<float>{sK, C::LDK}, 0, 16 * ct, 0, CH);
         }
       }
+    }
+    if (t0 + CH < tend) {
+      // the state planes and the other K / gate buffer are free: every read
+      // of them in this chunk happened before the P2 barrier
+      store_state_planes();
+      stage(kb ^ 1, min(CH, tend - t0 - CH));
+      if (t0 + 2 * CH < tend) prefetch(t0 + 2 * CH, min(CH, tend - t0 - 2 * CH), slot + 2);
     }
     lds_barrier();
   }

@@ -234,6 +234,81 @@ __device__ __forceinline__ void store_tile_planes(bf16 *hi, bf16 *lo, int ld, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wave-wide inclusive prefix sum over the 64 lanes with DPP: row_shr 1, 2,
+// 4, 8 scans each row of 16 lanes, then row_bcast:15 and row_bcast:31 carry
+// the row totals upward (GFX9 wave64 DPP controls).  Lanes with no source
+// keep the "old" operand, 0.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_src(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  x += dpp_src<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_src<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_src<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_src<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_src<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_src<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// ---------------------------------------------------------------------------
+// Fragments with a permuted contraction index.  A C-layout 16 x 16 result
+// (lane l holds rows 4 (l >> 4) .. + 3 of column l & 15) is used directly as
+// the B operand of a k = 32 MFMA by pairing two such tiles: lane group
+// g = l >> 4 then supplies the rows {4g .. 4g+3} of the first tile and
+// {4g .. 4g+3} of the second, i.e. the physical k indices
+// {4g + e, 16 + 4g + e} (e < 4) of the 32-wide step.  Any A operand of the
+// same product must be read with the same k order; a sum over k does not
+// depend on the order.
+// ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 cat_bf16x8(uint2 a, uint2 b) {
+  union { uint4 u; bf16x8 v; } x;
+  x.u = uint4{a.x, a.y, b.x, b.y};
+  return x.v;
+}
+
+// A fragment of a row-major bf16 matrix: row pointer rowp, step base kb.
+__device__ __forceinline__ bf16x8 a_frag_perm(const bf16 *rowp, int kb, int g) {
+  const uint2 x0 = *reinterpret_cast<const uint2 *>(rowp + kb + 4 * g);
+  const uint2 x1 = *reinterpret_cast<const uint2 *>(rowp + kb + 16 + 4 * g);
+  return cat_bf16x8(x0, x1);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16
+// lanes, output lane i element e is element (i mod 4) of the 8 bytes read by
+// source lane 4e + i/4.  Pointing source lane q of group g at
+// M[r0 + 4g + q/4][c0 + 4 (q mod 4)] of a row-major bf16 matrix M therefore
+// gives lane i the column c0 + i, rows r0 + 4g + e (e < 4): a k = 16 A
+// fragment of M^T.
+__device__ __forceinline__ uint2 ds_read_tr16(const bf16 *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+  union { s16x4 s; uint2 u; } x;
+  x.s = v;
+  return x.u;
+}
+
+// A fragment of M^T (rows = columns of M) for the permuted k = 32 step with
+// base row kb of M: columns c0 .. c0 + 15 of M, rows kb + {4g + e, 16 + 4g + e}.
+__device__ __forceinline__ bf16x8 a_frag_trans_perm(const bf16 *M, int ld, int kb, int c0, int l) {
+  const int g = l >> 4, q = l & 15;
+  const bf16 *p0 = M + (kb + 4 * g + (q >> 2)) * ld + c0 + 4 * (q & 3);
+  return cat_bf16x8(ds_read_tr16(p0), ds_read_tr16(p0 + 16 * ld));
+}
+
+// Split two C-layout tiles into a k = 32 B fragment (hi, lo).
+__device__ __forceinline__ void b_frag_split(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi, bf16x8 &lo) {
+  const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+  split8(x, hi, lo);
+}
+
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
 // operations, not for its outstanding global loads (which stay in flight
 // across the barrier; their consumers wait for them as usual).

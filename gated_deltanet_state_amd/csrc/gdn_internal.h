@@ -17,8 +17,9 @@ namespace gdn {
 // ---------------------------------------------------------------------------
 constexpr int kChunk = 64;
 // Tau = (I + A)^{-1} of one chunk, lower 16 x 16 block rows packed: block
-// row b holds 16 rows x 16 (b + 1) columns, row-major, at float offset
-// 256 * b (b + 1) / 2.
+// row b holds 16 rows x 16 (b + 1) columns, row-major, at element offset
+// 256 * b (b + 1) / 2 (2560 elements).  fp32 inputs: one fp32 array; bf16
+// inputs: split bf16 planes, hi then lo (same 10240 bytes).
 constexpr int kTauFloats = 2560;
 
 inline int64_t slot_count(int64_t n_tokens, int32_t n_seqs) { return n_tokens / kChunk + n_seqs + 1; }
@@ -69,7 +70,8 @@ struct ComposeLaunch {
 };
 
 hipError_t launch_prep(const PrepLaunch &p, hipStream_t stream);
-hipError_t launch_chain(const ChainLaunch &p, hipStream_t stream);
+hipError_t launch_chain(const ChainLaunch &p, hipStream_t stream);        // fp32 inputs
+hipError_t launch_chain_bf16(const ChainLaunch &p, hipStream_t stream);   // bf16 inputs
 hipError_t launch_compose(const ComposeLaunch &p, hipStream_t stream);
 
 }  // namespace gdn

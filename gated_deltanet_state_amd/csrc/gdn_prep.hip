@@ -18,7 +18,8 @@
 //   4. off-diagonal blocks Tau_ij = -Tau_ii sum_{m=j}^{i-1} A_im Tau_mj; a
 //      block column depends only on the diagonal blocks and the blocks above
 //      it, so one wave per block column, in registers (split-bf16 products)
-// The result is written packed (lower block rows only, fp32).
+// The result is written packed (lower block rows only): fp32 for fp32
+// inputs, split bf16 planes (hi, lo) for bf16 inputs.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -85,7 +86,18 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
   const int t0 = tbeg + (int)j * kChunk;
   const int Lc = min(kChunk, len - (int)j * kChunk);
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  // output: fp32 packed Tau, or (bf16 inputs) split hi / lo bf16 planes
   float *out = p.tau + (slot * H + h) * (int64_t)kTauFloats;
+  bf16 *outh = reinterpret_cast<bf16 *>(out), *outl = outh + kTauFloats;
+  auto put = [&](int idx, float x) {
+    if constexpr (BF) {
+      const bf16 hi = (bf16)x;
+      outh[idx] = hi;
+      outl[idx] = (bf16)(x - (float)hi);
+    } else {
+      out[idx] = x;
+    }
+  };
 
   // ---- 1. keys and gates ----
   const Tin *gk = reinterpret_cast<const Tin *>(p.k);
@@ -111,11 +123,7 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
       g = logf(ld_in(reinterpret_cast<const Tin *>(p.alpha), gi));
       b = ld_in(reinterpret_cast<const Tin *>(p.beta), gi);
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(g, off);
-      if (l >= off) g += y;
-    }
+    g = wave_inclusive_scan(g);
     sG[l] = g;
     sBeta[l] = b;
   }
@@ -158,11 +166,11 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
       }
       x[r] = acc0 + acc1;
     }
-    float *ob = out + tau_off(b) + 16 * b + jj;
+    const int ob = tau_off(b) + 16 * b + jj;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       sTau[(16 * b + r) * C::LDC + 16 * b + jj] = x[r];
-      ob[r * 16 * (b + 1)] = x[r];
+      put(ob + r * 16 * (b + 1), x[r]);
     }
   }
   lds_barrier();
@@ -197,9 +205,9 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) Y[q] = -Y[q];
         T[i] = Y;
-        float *ob = out + tau_off(i) + 16 * jc + (l & 15);
+        const int ob = tau_off(i) + 16 * jc + (l & 15);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) ob[(kq + q) * 16 * (i + 1)] = Y[q];
+        for (int q = 0; q < 4; ++q) put(ob + (kq + q) * 16 * (i + 1), Y[q]);
       }
     } else {
       float *xs = sX + w * 16 * C::LDX;
@@ -215,9 +223,9 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) Y[q] = -Y[q];
         store_tile(sTau, C::LDC, 16 * i, 16 * jc, Y);
-        float *ob = out + tau_off(i) + 16 * jc + (l & 15);
+        const int ob = tau_off(i) + 16 * jc + (l & 15);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) ob[(4 * (l >> 4) + q) * 16 * (i + 1)] = Y[q];
+        for (int q = 0; q < 4; ++q) put(ob + (4 * (l >> 4) + q) * 16 * (i + 1), Y[q]);
         wave_lds_fence();
       }
     }
