@@ -149,6 +149,8 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
     }
   }
 
+  wait_vmem();  // start-state loads land before the chunk loop (see the bf16 kernel)
+
   // ---- prefetch registers (next chunk) and current-chunk copies ----
   f32x4 pk[C::NKP], pq[C::NKP];
   f32x4 ptau[C::NTF], ctau[C::NTF];

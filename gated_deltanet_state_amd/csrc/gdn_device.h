@@ -309,6 +309,9 @@ __device__ __forceinline__ void b_frag_split(const f32x4 &t0, const f32x4 &t1, b
   split8(x, hi, lo);
 }
 
+// Wait for all outstanding vector-memory loads of this wave (vmcnt(0)).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
 // operations, not for its outstanding global loads (which stay in flight
 // across the barrier; their consumers wait for them as usual).
