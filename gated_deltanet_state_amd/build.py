@@ -24,6 +24,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA accumulators in ordinary VGPRs: the kernels post-process every
+          # product with vector ALU code, which AGPR accumulators would force
+          # through extra register moves
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-munsafe-fp-atomics"]
 
 

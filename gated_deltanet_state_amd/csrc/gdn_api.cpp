@@ -4,7 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -51,13 +53,54 @@ gdn_status launched(hipError_t e, const char *what) {
   return ok();
 }
 
+// Segments per sequence for a state-only replay with bf16 inputs.  A
+// sequence cut into P segments of whole chunks runs as P independent
+// recurrences (segment 0 from S0 with its state rows only, later segments as
+// affine operators with dk transition rows as well), composed afterwards.
+// The state-only chain kernel runs one wave per 16 rows, two waves per SIMD
+// (2048 slots on 256 compute units x 4 SIMDs); the time of a launch is
+// roughly (waves / 2048 rounded up) x (chunks per segment), plus about half
+// a chunk per composition step.  P = 1 unless splitting pays.
+// GDN_REPLAY_SEGMENTS=<n> overrides the choice (tuning and tests).
+int replay_segments(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv) {
+  if (const char *env = std::getenv("GDN_REPLAY_SEGMENTS")) {
+    const int v = std::atoi(env);
+    if (v >= 1) return v < 64 ? v : 64;
+  }
+  const double chunks = (double)n_tokens / gdn::kChunk / (n_seqs > 0 ? n_seqs : 1);
+  int pmax = (int)chunks;
+  if (pmax > 16) pmax = 16;
+  if (pmax < 1) pmax = 1;
+  const int64_t gS = (dv / 16 + 3) / 4, gA = ((dk + dv) / 16 + 3) / 4;
+  int best = 1;
+  double best_t = 0;
+  for (int P = 1; P <= pmax; ++P) {
+    const int64_t waves = (int64_t)n_seqs * n_heads * 4 * (gS + (int64_t)(P - 1) * gA);
+    if (waves > (int64_t(1) << 28)) break;
+    const double t = (double)((waves + 2047) / 2048) * std::ceil(chunks / P) + 0.5 * (P - 1);
+    if (P == 1 || t < best_t) {
+      best = P;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
+size_t seg_workspace_bytes(int32_t n_seqs, int32_t P, int32_t n_heads, int32_t dk, int32_t dv) {
+  if (P <= 1) return 0;
+  return (size_t)n_seqs * P * n_heads * ((size_t)dk * dk + (size_t)dv * dk) * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
 
-size_t gdn_replay_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t, int32_t) {
+size_t gdn_replay_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv) {
   if (n_seqs < 1 || n_tokens < 0 || n_heads < 1) return 0;
-  return gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads);
+  size_t seg = 0;
+  if (supported_dim(dk) && supported_dim(dv))
+    seg = seg_workspace_bytes(n_seqs, replay_segments(n_seqs, n_tokens, n_heads, dk, dv), n_heads, dk, dv);
+  return gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads) + seg;
 }
 
 size_t gdn_chunk_operator_workspace_bytes(int32_t n_chunks, int64_t n_tokens, int32_t n_heads, int32_t,
@@ -90,7 +133,10 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
       (s = check_align("cu_seqlens", cu_seqlens)) || (s = check_align("o", o)) ||
       (s = check_align("S_final", S_final)))
     return s;
-  const size_t need = gdn_replay_workspace_bytes(n_seqs, n_tokens, n_heads, dk, dv);
+  const bool bf = in_dtype == GDN_BF16;
+  const int32_t P = (!o && bf) ? replay_segments(n_seqs, n_tokens, n_heads, dk, dv) : 1;
+  const size_t tau_bytes = gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads);
+  const size_t need = tau_bytes + seg_workspace_bytes(n_seqs, P, n_heads, dk, dv);
   if (workspace_bytes < need || !workspace)
     return fail(GDN_ERR_WORKSPACE, "gdn_replay: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
   if ((s = check_align("workspace", workspace))) return s;
@@ -123,11 +169,35 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   p.in_bf16 = in_dtype == GDN_BF16;
   p.o = o;
   p.o_bf16 = o_dtype == GDN_BF16;
-  p.S_out = S_final;
-  p.T_out = nullptr;
-  p.tiles_T = 0;
+  p.n_segs = 1;
+  if (P == 1) {
+    p.S_out = S_final;
+    p.T_out = nullptr;
+    p.tiles_T = 0;
+    p.tiles_S = dv / 16;
+    return launched(bf ? gdn::launch_chain_bf16(p, st) : gdn::launch_chain(p, st), "gdn_replay launch");
+  }
+  // time split: segment operators, then their composition
+  float *Tseg = reinterpret_cast<float *>(static_cast<char *>(workspace) + tau_bytes);
+  float *Sseg = Tseg + (size_t)n_seqs * P * n_heads * dk * dk;
+  p.n_segs = P;
+  p.skip_T0 = 1;
+  p.T_transposed = 1;
+  p.tiles_T = dk / 16;
   p.tiles_S = dv / 16;
-  return launched(p.in_bf16 ? gdn::launch_chain_bf16(p, st) : gdn::launch_chain(p, st), "gdn_replay launch");
+  p.T_out = Tseg;
+  p.S_out = Sseg;
+  if ((s = launched(gdn::launch_chain_bf16(p, st), "gdn_replay segment launch"))) return s;
+  gdn::SegComposeLaunch c{};
+  c.S_seg = Sseg;
+  c.Tt_seg = Tseg;
+  c.n_seqs = n_seqs;
+  c.n_segs = P;
+  c.H = n_heads;
+  c.dk = dk;
+  c.dv = dv;
+  c.S_out = S_final;
+  return launched(gdn::launch_seg_compose(c, st), "gdn_replay segment compose launch");
 }
 
 gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, const void *beta,
@@ -184,6 +254,7 @@ gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, c
   p.in_bf16 = in_dtype == GDN_BF16;
   p.S_out = S_local;
   p.T_out = T_C;
+  p.n_segs = 1;
   p.tiles_T = dk / 16;
   p.tiles_S = v ? dv / 16 : 0;
   return launched(p.in_bf16 ? gdn::launch_chain_bf16(p, st) : gdn::launch_chain(p, st),

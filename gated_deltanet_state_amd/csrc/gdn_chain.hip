@@ -177,7 +177,7 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
       }
     }
     // Tau rows 16 cb + (l & 15) of this chunk
-    const float *tau = p.tau + (slot * H + h) * (int64_t)kTauFloats + tau_off(cb) + (l & 15) * 16 * (cb + 1);
+    const float *tau = p.tau + (slot * H + h) * (int64_t)kRecFloats + tau_off(cb) + (l & 15) * 16 * (cb + 1);
     const int ncol = 16 * (cb + 1);
     if constexpr (BF) {
 #pragma unroll

@@ -1,42 +1,50 @@
 // gdn_chain_bf16.hip -- chunkwise Gated DeltaNet recurrence for bf16 inputs
-// on gfx950: one workgroup of four waves per 16 state rows.
+// on gfx950: one wave per 16 state rows, all operands of a chunk in
+// registers.
 //
 // The recurrence (page "Tail-Replay: Escaping the Curse of Linear Attention
 // in Prefix Caching for Hybrid LLMs", section 2 Eq. (1); state S dv x dk):
 //     S_t = S_{t-1} alpha_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t.
 // Over a chunk of L <= 64 tokens with cumulative log-gates g and the
-// per-chunk factor Tau = (I + A)^{-1} (built by gdn_prep.hip), for the 16
-// state rows j owned by a wave (everything transposed: tokens x rows):
+// per-chunk factor Tau = (I + A)^{-1} (gdn_prep.hip), for the 16 state rows
+// owned by a wave (transposed: tokens x rows):
 //     Y = K S^T                        (64 x 16)
 //     R = diag(beta) (V - diag(e^g) Y)
 //     D = Tau R                        (per-token delta-rule corrections)
 //     O = diag(e^g) Q S^T + (M o Q K^T) D,   M_rs = e^{g_r - g_s}, s <= r
 //     S^T <- e^{g_L} S^T + K^T diag(e^{g_L - g}) D
-// S^T (dk x 16) stays in registers in MFMA C layout, split by dk blocks
-// over the four waves.  A C-layout result is used directly as the B operand
-// of the next product (k = 16 tiles, or paired tiles with a permuted k
-// order for k = 32, gdn_device.h).  Per chunk:
-//   1. each wave forms the partial Y (and Z = Q S^T) over its dk blocks and
-//      posts it to LDS                                         | barrier
-//   2. every wave sums the partials, forms R; wave w forms token block w
-//      of D = Tau R and posts D and diag(e^{g_L - g}) D          | barrier
-//   3. wave w writes the outputs of token block w and updates its dk
-//      blocks of S^T with K^T diag(e^{g_L - g}) D; the workgroup stages the
-//      next chunk (keys, queries, values, Tau, gates)          | barrier
+//
+// Register layout.  S^T (dk x 16) stays in registers as NSB C-layout 16 x 16
+// blocks whose rows are a fixed permutation of dk: block d, lane group
+// g = l >> 4, element e holds dk index 32 (d >> 1) + 8 g + 4 (d & 1) + e.
+// With that order the pair of blocks (2m, 2m + 1) is, element for element,
+// the B operand of the k = 32 MFMA over dk = 32m .. 32m + 31 in natural
+// order, so K S^T takes K's A fragments straight from row-major K (one
+// 16-byte read per fragment) and S^T never leaves the C layout.  Products
+// over the token index pair two C-layout token blocks into one B operand
+// with the permuted order {4g + e, 16 + 4g + e}; their A operands (Tau, and
+// M o Q K^T) are stored in that order, and K^T comes from the gfx950
+// transposing LDS read.
+//
+// Workgroup: NW waves = NW row tiles of one (sequence segment, head).  While
+// chunk c runs from one LDS buffer set, the operands of chunk c + 1 are
+// copied into the other one by load-to-LDS DMA (buffer_load ... lds; no
+// registers, no staging code): K and Q as MFMA A fragments, the per-chunk
+// record of gdn_prep.hip (Tau diag(beta) and K^T fragments), and the value
+// columns of the workgroup.  Every fragment read is then a conflict-free
+// 16-byte LDS read by lane.  One LDS barrier per chunk (two with outputs:
+// M o Q K^T of the next chunk is built once its keys and queries landed).
 //
 // The same kernel builds the affine chunk operator of the page "LinearKV:
 // One Cached State Suffices for Position-Independent Caching in Hybrid
 // LLMs" (affine chunk operator paragraph): rows of the transition product
-// T_C are rows of a "state" that starts as the identity and gets no value.
+// T_C are rows of a "state" that starts as the identity and gets no value
+// input.  Time-split replay runs the segments of a sequence as independent
+// operators of this kind (composed afterwards by gdn_compose.hip).
 //
-// Precision: K, Q, V are exact in bf16; S, R, D, Tau and M o QK^T are split
+// Precision: K, Q, V are exact in bf16; S, R, D, Tau and M o Q K^T are split
 // into bf16 hi + lo where they enter a product (split-bfloat16), which keeps
 // every product within a few fp32 ulps.
-//
-// Inputs are double-buffered in LDS by chunk parity; the global loads of a
-// chunk are issued one chunk period before it is staged.  With outputs,
-// M o QK^T of the next chunk is built after its keys and queries land (one
-// more barrier).  All barriers are LDS-only.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -45,218 +53,194 @@ namespace gdn {
 namespace {
 
 constexpr int CH = kChunk;
-// packed lower block-row matrix (Tau or M o QK^T) as split bf16 planes:
-// hi at [0, kPlane), lo at [kPlane, 2 kPlane)
-constexpr int kPlane = kTauFloats;
 
-template <int DK, bool WANT_O>
-struct BCfg {
-  static constexpr int NWV = 4;                       // waves per workgroup (one 16-row tile)
-  static constexpr int NT = NWV * 64;
-  static constexpr int LDK = DK + 8;                  // sK, sQ [CH][LDK] bf16
-  static constexpr int LDV = 16 + 8;                  // sV [CH][LDV] bf16 (the tile's 16 value columns)
-  static constexpr int NSB = DK / 16;                 // 16-row blocks of S^T
-  static constexpr int NOWN = NSB / NWV;              // blocks of S^T owned by a wave (1 or 2)
-  static constexpr int NX = WANT_O ? 8 : 4;           // exchanged partial tiles per wave (Y, Z)
-  static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
-  static constexpr size_t KBYTES = al(2 * CH * LDK);
-  static constexpr size_t VBYTES = al(2 * CH * LDV);
-  static constexpr size_t TBYTES = al(2 * kPlane * sizeof(bf16));    // hi + lo planes
-  static constexpr size_t GBYTES = al(4 * 5 * CH);
-  static constexpr size_t oK = 0;                                    // [2]
-  static constexpr size_t oQ = oK + 2 * KBYTES;                      // [2] (o)
-  static constexpr size_t oV = oQ + (WANT_O ? 2 * KBYTES : 0);       // [2]
-  static constexpr size_t oT = oV + 2 * VBYTES;                      // [2] Tau planes
-  static constexpr size_t oP = oT + 2 * TBYTES;                      // [1] P planes (o)
-  static constexpr size_t oG = oP + (WANT_O ? TBYTES : 0);           // [2] gates
-  static constexpr size_t oX = oG + 2 * GBYTES;                      // partial-sum exchange
-  static constexpr size_t oE = oX + (size_t)NWV * NX * 64 * 16;      // D / D'' exchange
-  static constexpr size_t TOTAL = oE + (size_t)NWV * 2 * 64 * 16;
+template <int DK, bool WANT_O, int NW>
+struct Cfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int NSB = DK / 16;          // 16-row blocks of S^T
+  static constexpr int NKS = DK / 32;          // k = 32 steps over dk
+  // LDS buffer set: 1 KiB blocks, one MFMA fragment (64 lanes x 16 bytes) each
+  static constexpr int NKA = 4 * NKS;          // K (and Q) A fragments (bt, m)
+  static constexpr int NKT = 2 * NSB;          // K^T fragments (d, m)
+  static constexpr int NTF = 2 * kTauFrags;    // Tau diag(beta) fragments, hi then lo
+  static constexpr int VU = 2 * NW;            // 16-byte units per staged value row
+  static constexpr int NVB = CH * VU / 64;     // value slab blocks
+  static constexpr int bKA = 0, bKT = NKA, bTF = bKT + NKT, bV = bTF + NTF, bQA = bV + NVB;
+  static constexpr int NBLK = bQA + (WANT_O ? NKA : 0);
+  static constexpr size_t BUF = (size_t)NBLK * 1024;
+  static constexpr int GN = 3 * CH + 4;        // gate floats per buffer set
+  static constexpr size_t oP = 2 * BUF;        // M o Q K^T fragments (outputs only)
+  static constexpr size_t oG = oP + (WANT_O ? 2 * kTauFragPlane * 2 : 0);
+  static constexpr size_t TOTAL = oG + 2 * GN * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
-  // staging: 16-byte segments
-  static constexpr int KSEG = DK / 8;
-  static constexpr int NKP = (CH * KSEG + NT - 1) / NT;
-  static constexpr int TSEG = (int)(2 * kPlane * sizeof(bf16) / 16);
-  static constexpr int NTP = (TSEG + NT - 1) / NT;
 };
 
-__device__ __forceinline__ bf16x4 u2_bf16x4(uint2 u) {
-  union { uint2 u; bf16x4 v; } x;
-  x.u = u;
-  return x.v;
+// Gate buffer: [0, 64) e^g, [64, 128) e^{g_L - g} (0 past the chunk),
+// [128, 192) g, [192] e^{g_L}.
+constexpr int G_EG = 0, G_DEC = 64, G_G = 128, G_EGL = 192;
+
+// Unit swizzle of the staged value slab: 16-byte unit u of row r sits at
+// unit u ^ vswz(r), so that the 8 rows x 4 quads of a half-wave's
+// transposing read fall in distinct banks.
+template <int NW>
+__device__ __forceinline__ int vswz(int r) {
+  return NW == 8 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
 }
 
-template <int DK, bool WANT_O>
-__global__ void __launch_bounds__(256) chain_bf16_kernel(ChainLaunch p, int n_items) {
-  using C = BCfg<DK, WANT_O>;
-  constexpr int NWV = C::NWV;
+template <int DK, bool WANT_O, int NW>
+__global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf16_kernel(ChainLaunch p, int n_items) {
+  using C = Cfg<DK, WANT_O, NW>;
   __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
-  bf16 *sK0 = reinterpret_cast<bf16 *>(smem + C::oK);
-  bf16 *sQ0 = reinterpret_cast<bf16 *>(smem + C::oQ);
-  bf16 *sV0 = reinterpret_cast<bf16 *>(smem + C::oV);
-  bf16 *sT0 = reinterpret_cast<bf16 *>(smem + C::oT);
   bf16 *sP = reinterpret_cast<bf16 *>(smem + C::oP);
   float *sG0 = reinterpret_cast<float *>(smem + C::oG);
-  f32x4 *sX = reinterpret_cast<f32x4 *>(smem + C::oX);
-  f32x4 *sE = reinterpret_cast<f32x4 *>(smem + C::oE);
-  constexpr int KE = C::KBYTES / 2, VE = C::VBYTES / 2, TE = C::TBYTES / 2, GE = C::GBYTES / 4;
 
-  // ---- work item (XCD-aware order): one 16-row tile of one (sequence, head) ----
+  // ---- work item (XCD-aware order: consecutive items share one XCD's L2) ----
   const int per = (int)(gridDim.x >> 3);
   const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (item >= n_items) return;
-  const int tiles = p.tiles_T + p.tiles_S;
-  const int unit = item / tiles, tile = item % tiles;
-  const int n = unit / p.H, h = unit % p.H;
+  const int tilesA = p.tiles_T + p.tiles_S;
+  const int tiles0 = p.skip_T0 ? p.tiles_S : tilesA;
+  const int grp0 = (tiles0 + NW - 1) / NW, grpA = (tilesA + NW - 1) / NW;
+  const int per_nh = grp0 + (p.n_segs - 1) * grpA;
+  const int nh = item / per_nh;
+  int rem = item % per_nh, seg = 0, grp = rem;
+  if (rem >= grp0) {
+    rem -= grp0;
+    seg = 1 + rem / grpA;
+    grp = rem % grpA;
+  }
+  const int n = nh / p.H, h = nh % p.H;
   const int H = p.H, DV = p.dv;
-  const bool is_T = tile < p.tiles_T;
-  const int row0 = is_T ? 16 * tile : 16 * (tile - p.tiles_T);
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int w = wave_id(), l = lane_id();
   const int g4 = l >> 4, jl = l & 15;
+  const int tT = (seg == 0 && p.skip_T0) ? 0 : p.tiles_T;
+  const int tile = grp * NW + w;
+  const bool active = tile < tT + p.tiles_S;
+  const bool is_T = active && tile < tT;
+  const int row0 = is_T ? 16 * tile : 16 * (tile - tT);
+  // tile counts are multiples of NW (launcher), so a workgroup holds either
+  // transition tiles only or state tiles only; state workgroups stage the
+  // value columns vcol0 .. vcol0 + 16 NW - 1
+  const bool grp_S = grp * NW >= tT;
+  const int vcol0 = 16 * (grp * NW - tT);
 
-  const bf16 *gq = reinterpret_cast<const bf16 *>(p.q);
+  // ---- this segment's token range ----
+  const int cbeg = p.cu[n], cend = p.cu[n + 1];
+  int64_t seg_len = cend - cbeg;
+  if (p.n_segs > 1) seg_len = ((seg_len + p.n_segs - 1) / p.n_segs + CH - 1) / CH * CH;
+  const int tbeg = (int)min((int64_t)cend, (int64_t)cbeg + seg * seg_len);
+  const int tend = (int)min((int64_t)cend, (int64_t)tbeg + seg_len);
+  const int64_t slot0 = (int64_t)(cbeg / CH) + n + (tbeg - cbeg) / CH;
+
   const bf16 *gk = reinterpret_cast<const bf16 *>(p.k);
+  const bf16 *gq = reinterpret_cast<const bf16 *>(p.q);
   const bf16 *gv = reinterpret_cast<const bf16 *>(p.v);
-  const bf16 *ga = reinterpret_cast<const bf16 *>(p.alpha);
-  const bf16 *gb = reinterpret_cast<const bf16 *>(p.beta);
-  const bf16 *gtau = reinterpret_cast<const bf16 *>(p.tau);
+  const unsigned short *ga = reinterpret_cast<const unsigned short *>(p.alpha);
+  const char *grec = reinterpret_cast<const char *>(p.tau);
 
-  // ---- owned blocks of S^T (C layout): st[u] holds S[row0 + jl][16 d + 4 g4 + i],
-  // d = w NOWN + u ----
-  f32x4 st[C::NOWN];
+  // ---- S^T in registers (dk order of the header comment) ----
+  f32x4 st[C::NSB];
 #pragma unroll
-  for (int u = 0; u < C::NOWN; ++u) {
-    const int d = w * C::NOWN + u;
-    st[u] = zero4();
-    if (is_T) {
+  for (int d = 0; d < C::NSB; ++d) {
+    const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1);
+    st[d] = zero4();
+    if (active) {
+      if (is_T) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[u][i] = (row0 + jl == 16 * d + 4 * g4 + i) ? 1.f : 0.f;
-    } else if (p.S0) {
-      st[u] = *reinterpret_cast<const f32x4 *>(p.S0 + (((int64_t)n * H + h) * DV + row0 + jl) * DK + 16 * d + 4 * g4);
+        for (int e = 0; e < 4; ++e) st[d][e] = (row0 + jl == c0 + e) ? 1.f : 0.f;
+      } else if (p.S0 && seg == 0) {
+        st[d] = *reinterpret_cast<const f32x4 *>(p.S0 + (((int64_t)n * H + h) * DV + row0 + jl) * DK + c0);
+      }
     }
   }
-  // Let the start-state loads land here: otherwise the compiler's wait
-  // bookkeeping keeps them pending into the chunk loop and waits for all
-  // global loads (including the prefetch) at the top of every iteration.
-  wait_vmem();
 
-  // ---- prefetch registers (one chunk ahead of staging) ----
-  f32x4 pk[C::NKP], pq[C::NKP], pt[C::NTP], pvv;
-  bf16 pa = bf16(1.f), pb = bf16(0.f);
-  const int tbeg = p.cu[n], tend = p.cu[n + 1];
-  const int64_t slot0 = (int64_t)(tbeg / CH) + n;
-
-  auto prefetch = [&](int t0, int Lc, int64_t slot) {
-    const bool full = Lc == CH;
-#pragma unroll
-    for (int i = 0; i < C::NKP; ++i) {
-      const int s = tid + i * C::NT;
-      const int r = s / C::KSEG, seg = s % C::KSEG;
-      const bool ok = (s < CH * C::KSEG) && (full || r < Lc);
-      const int64_t goff = ((int64_t)(t0 + r) * H + h) * DK + seg * 8;
-      pk[i] = ok ? *reinterpret_cast<const f32x4 *>(gk + goff) : zero4();
-      if (WANT_O) pq[i] = ok ? *reinterpret_cast<const f32x4 *>(gq + goff) : zero4();
-    }
-    const bf16 *tsrc = gtau + (slot * H + h) * (int64_t)(2 * kPlane);
-#pragma unroll
-    for (int i = 0; i < C::NTP; ++i) {
-      const int s = tid + i * C::NT;
-      if (s < C::TSEG) pt[i] = *reinterpret_cast<const f32x4 *>(tsrc + 8 * s);
-    }
-    {
-      // V rows t0 + r, columns row0 .. row0 + 15: 2 segments per token
-      const int r = tid >> 1, seg = tid & 1;
-      const bool ok = !is_T && tid < 2 * CH && (full || r < Lc);
-      pvv = ok ? *reinterpret_cast<const f32x4 *>(gv + ((int64_t)(t0 + r) * H + h) * DV + row0 + 8 * seg) : zero4();
-    }
-    if (w == 0) {
-      const bool ok = l < Lc;
-      const int64_t gi = (int64_t)(t0 + l) * H + h;
-      pa = ok ? ga[gi] : bf16(1.f);
-      pb = ok ? gb[gi] : bf16(0.f);
-    }
-  };
-
-  // stage the prefetched chunk into buffer set `b`
-  auto stage = [&](int b, int Lc) {
-    bf16 *sK = sK0 + b * KE;
-    bf16 *sQ = sQ0 + b * KE;
-    bf16 *sT = sT0 + b * TE;
-    bf16 *sV = sV0 + b * VE;
-#pragma unroll
-    for (int i = 0; i < C::NKP; ++i) {
-      const int s = tid + i * C::NT;
-      if (s < CH * C::KSEG) {
-        const int r = s / C::KSEG, seg = s % C::KSEG;
-        *reinterpret_cast<f32x4 *>(sK + r * C::LDK + seg * 8) = pk[i];
-        if (WANT_O) *reinterpret_cast<f32x4 *>(sQ + r * C::LDK + seg * 8) = pq[i];
+  // ---- DMA of one chunk's operands into buffer set b ----
+  // Rows past the chunk read as zero: each tensor's descriptor covers rows
+  // t0 .. t0 + Lc - 1 of head h only.
+  auto issue_dma = [&](int b, int t0, int Lc, int64_t slot) {
+    char *buf = smem + b * C::BUF;
+    const uint32_t krec = (uint32_t)(((Lc - 1) * (int64_t)H + 1) * DK * 2);
+    const uint32_t vrec = (uint32_t)(((Lc - 1) * (int64_t)H + 1) * DV * 2);
+    const bf16 *kbase = gk + ((int64_t)t0 * H + h) * DK;
+    const bf16 *qbase = gq + ((int64_t)t0 * H + h) * DK;
+    const bf16 *vbase = gv + ((int64_t)t0 * H + h) * DV;
+    const char *rec = grec + (slot * H + h) * (int64_t)(kRecFloats * 4);
+    for (int i = w; i < C::NBLK; i += NW) {
+      lds_void *dst = (lds_void *)(buf + i * 1024);
+      if (i < C::bKT || (WANT_O && i >= C::bQA)) {   // K or Q A fragment (bt, m)
+        const int f = i < C::bKT ? i : i - C::bQA;
+        const int bt = f / C::NKS, m = f % C::NKS;
+        const uint32_t off = (uint32_t)(((16 * bt + jl) * H) * DK + 32 * m + 8 * g4) * 2;
+        dma16_buffer(i < C::bKT ? (const void *)kbase : (const void *)qbase, krec, dst, off);
+      } else if (i < C::bTF) {                         // K^T fragments (record)
+        dma16_global(rec + kRecKtOffsetBytes + (i - C::bKT) * 1024 + 16 * l, dst);
+      } else if (i < C::bV) {                          // Tau diag(beta) fragments (record)
+        dma16_global(rec + (i - C::bTF) * 1024 + 16 * l, dst);
+      } else if (grp_S) {                              // value slab block
+        const int u_lds = (i - C::bV) * 64 + l;
+        const int r = u_lds / C::VU, u = (u_lds % C::VU) ^ vswz<NW>(r);
+        dma16_buffer(vbase, vrec, dst, (uint32_t)((r * H) * DV + vcol0 + 8 * u) * 2);
       }
     }
-#pragma unroll
-    for (int i = 0; i < C::NTP; ++i) {
-      const int s = tid + i * C::NT;
-      if (s < C::TSEG) *reinterpret_cast<f32x4 *>(sT + 8 * s) = pt[i];
-    }
-    if (tid < 2 * CH) *reinterpret_cast<f32x4 *>(sV + (tid >> 1) * C::LDV + 8 * (tid & 1)) = pvv;
-    if (w == 0) {
-      float *sG = sG0 + b * GE;
-      const float g = wave_inclusive_scan((l < Lc) ? logf((float)pa) : 0.f);
-      const float gL = lane_value(g, Lc - 1);
-      sG[l] = g;
-      sG[CH + l] = (l < Lc) ? (float)pb : 0.f;
-      sG[2 * CH + l] = __expf(g);
-      sG[3 * CH + l] = (l < Lc) ? __expf(gL - g) : 0.f;
-      if (l == 0) sG[4 * CH] = __expf(gL);
-    }
   };
 
-  // P = M o Q K^T of the chunk in buffer set `b`: packed lower block rows,
-  // split planes (upper blocks are never read)
+  unsigned short pa = 0x3f80;   // wave 0: alpha bits of token t0 + l (1.0 past the end)
+  auto load_alpha = [&](int t0, int Lc) {
+    pa = 0x3f80;
+    if (w == 0 && l < Lc) pa = ga[(int64_t)(t0 + l) * H + h];
+  };
+  auto gates = [&](int b, int Lc) {
+    if (w != 0) return;
+    float *sG = sG0 + b * C::GN;
+    const float g = wave_inclusive_scan((l < Lc) ? logf(__uint_as_float((unsigned)pa << 16)) : 0.f);
+    const float gL = lane_value(g, Lc - 1);
+    sG[G_EG + l] = __expf(g);
+    sG[G_DEC + l] = (l < Lc) ? __expf(gL - g) : 0.f;
+    sG[G_G + l] = g;
+    if (l == 0) sG[G_EGL] = __expf(gL);
+  };
+
+  // M o Q K^T of the chunk in buffer set b, as split-bf16 A fragments in the
+  // Tau fragment order (gdn_internal.h): tile (bi, bj) of 16 x 16 lands in
+  // fragment (bi, bj >> 1), lane (r & 15) + 16 (c' >> 2), element
+  // 4 (bj & 1) + (c' & 3) for row r, column 16 bj + c'.
   auto build_p = [&](int b) {
-    const bf16 *sK = sK0 + b * KE;
-    const bf16 *sQ = sQ0 + b * KE;
-    const float *sG = sG0 + b * GE;
-    for (int t = w; t < 10; t += NWV) {
-      const int bi = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
-      const int bj = t - (bi * (bi + 1)) / 2;
+    const char *buf = smem + b * C::BUF;
+    const float *sG = sG0 + b * C::GN;
+    for (int t = w; t < 2 * kTauFrags; t += NW) {
+      const int f = t >> 1, half = t & 1;
+      const int bi = f < 2 ? f : (f - 2) / 2 + 2;
+      const int bj = 2 * (f < 2 ? 0 : (f - 2) % 2) + half;
       f32x4 c = zero4();
-      mma_bf16<1, 1>(c, RowMajor<bf16>{sQ, C::LDK}, RowMajor<bf16>{sK, C::LDK}, 16 * bi, 16 * bj, 0, DK);
-      const int col = 16 * bj + jl;
-      const float gc = sG[col];
-      const int rb = 16 * bi + 4 * g4;
-      const f32x4 gr = *reinterpret_cast<const f32x4 *>(sG + rb);
-      bf16 *dst = sP + tau_off(bi) + 4 * g4 * 16 * (bi + 1) + col;
+      if (bj <= bi) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = (col <= rb + i) ? __expf(gr[i] - gc) * c[i] : 0.f;
+        for (int m = 0; m < C::NKS; ++m) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(buf + (C::bQA + bi * C::NKS + m) * 1024 + 16 * l);
+          const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(buf + (C::bKA + bj * C::NKS + m) * 1024 + 16 * l);
+          c = mfma_bf16(a, bb, c);
+        }
+      }
+      const int col = 16 * bj + jl;
+      const float gc = sG[G_G + col];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * bi + 4 * g4 + e;
+        const float x = (col <= r) ? __expf(sG[G_G + r] - gc) * c[e] : 0.f;
         const bf16 hi = (bf16)x;
-        dst[i * 16 * (bi + 1)] = hi;
-        dst[i * 16 * (bi + 1) + kPlane] = (bf16)(x - (float)hi);
+        const int idx = (f * 64 + (r & 15) + 16 * (jl >> 2)) * 8 + 4 * half + (jl & 3);
+        sP[idx] = hi;
+        sP[kTauFragPlane + idx] = (bf16)(x - (float)hi);
       }
     }
-  };
-
-  // A fragment (permuted k = 32 step m) of a packed lower block-row matrix,
-  // token block bt; columns past the stored block row are zero.
-  auto a_frag_packed = [&](const bf16 *M, int bt, int m, bf16x8 &hi, bf16x8 &lo) {
-    const int ncol = 16 * (bt + 1);
-    const bf16 *row = M + tau_off(bt) + jl * ncol;
-    const int c0 = 32 * m + 4 * g4, c1 = c0 + 16;
-    const uint2 z = uint2{0u, 0u};
-    const uint2 h0 = *reinterpret_cast<const uint2 *>(row + c0);
-    const uint2 l0 = *reinterpret_cast<const uint2 *>(row + kPlane + c0);
-    const bool has1 = c1 < ncol;
-    const uint2 h1 = has1 ? *reinterpret_cast<const uint2 *>(row + c1) : z;
-    const uint2 l1 = has1 ? *reinterpret_cast<const uint2 *>(row + kPlane + c1) : z;
-    hi = cat_bf16x8(h0, h1);
-    lo = cat_bf16x8(l0, l1);
   };
 
   if (tbeg < tend) {
-    prefetch(tbeg, min(CH, tend - tbeg), slot0);
-    stage(0, min(CH, tend - tbeg));
-    if (tbeg + CH < tend) prefetch(tbeg + CH, min(CH, tend - tbeg - CH), slot0 + 1);
+    const int L0 = min(CH, tend - tbeg);
+    issue_dma(0, tbeg, L0, slot0);
+    load_alpha(tbeg, L0);
+    gates(0, L0);
   }
+  wait_vmem();
   lds_barrier();
   if (WANT_O && tbeg < tend) {
     build_p(0);
@@ -267,240 +251,208 @@ __global__ void __launch_bounds__(256) chain_bf16_kernel(ChainLaunch p, int n_it
   int b = 0;
   for (int t0 = tbeg; t0 < tend; t0 += CH, ++slot, b ^= 1) {
     const int Lc = min(CH, tend - t0);
-    const bf16 *sK = sK0 + b * KE;
-    const bf16 *sQ = sQ0 + b * KE;
-    const bf16 *sV = sV0 + b * VE;
-    const bf16 *sT = sT0 + b * TE;
-    const float *sG = sG0 + b * GE;
-
-    // ---- 1. partial Y = K S^T (and Z = Q S^T) over the owned dk blocks ----
-    // (all fragment loads first, then the products on independent
-    // accumulators, then the stores)
-    {
-      f32x4 y[4], z[4];
-#pragma unroll
-      for (int bt = 0; bt < 4; ++bt) {
-        y[bt] = zero4();
-        z[bt] = zero4();
-      }
-      if constexpr (C::NOWN == 2) {
-        // the two owned blocks form one k = 32 step (permuted k order)
-        bf16x8 sh, sl;
-        b_frag_split(st[0], st[1], sh, sl);
-        bf16x8 ka[4], qa[4];
-#pragma unroll
-        for (int bt = 0; bt < 4; ++bt) {
-          ka[bt] = a_frag_perm(sK + (16 * bt + jl) * C::LDK, 32 * w, g4);
-          if (WANT_O) qa[bt] = a_frag_perm(sQ + (16 * bt + jl) * C::LDK, 32 * w, g4);
-        }
-#pragma unroll
-        for (int bt = 0; bt < 4; ++bt) y[bt] = mfma_bf16(ka[bt], sh, y[bt]);
-#pragma unroll
-        for (int bt = 0; bt < 4; ++bt) y[bt] = mfma_bf16(ka[bt], sl, y[bt]);
-        if (WANT_O) {
-#pragma unroll
-          for (int bt = 0; bt < 4; ++bt) z[bt] = mfma_bf16(qa[bt], sh, z[bt]);
-#pragma unroll
-          for (int bt = 0; bt < 4; ++bt) z[bt] = mfma_bf16(qa[bt], sl, z[bt]);
-        }
-      } else {
-        bf16x4 sh, sl;
-        split4(st[0], sh, sl);
-        uint2 ka[4], qa[4];
-#pragma unroll
-        for (int bt = 0; bt < 4; ++bt) {
-          const int off = (16 * bt + jl) * C::LDK + 16 * w + 4 * g4;
-          ka[bt] = *reinterpret_cast<const uint2 *>(sK + off);
-          if (WANT_O) qa[bt] = *reinterpret_cast<const uint2 *>(sQ + off);
-        }
-#pragma unroll
-        for (int bt = 0; bt < 4; ++bt) y[bt] = mfma_bf16_k16(u2_bf16x4(ka[bt]), sh, y[bt]);
-#pragma unroll
-        for (int bt = 0; bt < 4; ++bt) y[bt] = mfma_bf16_k16(u2_bf16x4(ka[bt]), sl, y[bt]);
-        if (WANT_O) {
-#pragma unroll
-          for (int bt = 0; bt < 4; ++bt) z[bt] = mfma_bf16_k16(u2_bf16x4(qa[bt]), sh, z[bt]);
-#pragma unroll
-          for (int bt = 0; bt < 4; ++bt) z[bt] = mfma_bf16_k16(u2_bf16x4(qa[bt]), sl, z[bt]);
-        }
-      }
-#pragma unroll
-      for (int bt = 0; bt < 4; ++bt) {
-        sX[(w * C::NX + bt) * 64 + l] = y[bt];
-        if (WANT_O) sX[(w * C::NX + 4 + bt) * 64 + l] = z[bt];
-      }
+    const bool more = t0 + CH < tend;
+    const int L1 = more ? min(CH, tend - t0 - CH) : 0;
+    // operands of the next chunk: in flight while this one runs
+    if (more) {
+      issue_dma(b ^ 1, t0 + CH, L1, slot + 1);
+      load_alpha(t0 + CH, L1);
     }
-    lds_barrier();
+    const char *buf = smem + b * C::BUF;
+    const float *sG = sG0 + b * C::GN;
+    auto frag = [&](int blk) { return *reinterpret_cast<const bf16x8 *>(buf + blk * 1024 + 16 * l); };
 
-    // ---- 2. Y (summed), R = beta (V - e^g Y); D_w = (Tau R)_w ----
-    {
-      f32x4 part[NWV][4];
-      uint2 vraw[4];
-      f32x4 bet[4], gam[4];
+    if (active) {
+      // ---- S^T as k = 32 B fragments ----
+      bf16x8 sh[C::NKS], sl[C::NKS];
 #pragma unroll
-      for (int bt = 0; bt < 4; ++bt) {
+      for (int m = 0; m < C::NKS; ++m) b_frag_split(st[2 * m], st[2 * m + 1], sh[m], sl[m]);
+
+      // ---- Y = K S^T ----
+      f32x4 y[4];
 #pragma unroll
-        for (int q = 0; q < NWV; ++q) part[q][bt] = sX[(q * C::NX + bt) * 64 + l];
-        // V[16 bt + 4 g4 + e][jl] via the transposing read of the row-major tile
-        vraw[bt] = ds_read_tr16(sV + (16 * bt + 4 * g4 + (jl >> 2)) * C::LDV + 4 * (jl & 3));
-        bet[bt] = *reinterpret_cast<const f32x4 *>(sG + CH + 16 * bt + 4 * g4);
-        gam[bt] = *reinterpret_cast<const f32x4 *>(sG + 2 * CH + 16 * bt + 4 * g4);
-      }
-      // Tau fragments of token block w (hi / lo planes, up to two k steps)
-      bf16x8 th[2], tl[2];
+      for (int bt = 0; bt < 4; ++bt) y[bt] = zero4();
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
-        if (m <= (w >> 1)) a_frag_packed(sT, w, m, th[m], tl[m]);
-      const f32x4 dec = *reinterpret_cast<const f32x4 *>(sG + 3 * CH + 16 * w + 4 * g4);
+      for (int m = 0; m < C::NKS; ++m)
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) {
+          const bf16x8 a = frag(C::bKA + bt * C::NKS + m);
+          y[bt] = mfma_bf16(a, sh[m], y[bt]);
+          y[bt] = mfma_bf16(a, sl[m], y[bt]);
+        }
+
+      // ---- R = V - e^g Y  (beta is folded into the Tau fragments) ----
       f32x4 rr[4];
 #pragma unroll
       for (int bt = 0; bt < 4; ++bt) {
-        const bf16x4 vv = u2_bf16x4(vraw[bt]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float y = part[0][bt][i];
-#pragma unroll
-          for (int q = 1; q < NWV; ++q) y += part[q][bt][i];
-          rr[bt][i] = bet[bt][i] * ((float)vv[i] - gam[bt][i] * y);
+        const f32x4 eg = *reinterpret_cast<const f32x4 *>(sG + G_EG + 16 * bt + 4 * g4);
+        float vv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (!is_T) {
+          const int rr0 = 16 * bt + 4 * g4 + (jl >> 2);
+          const int u = 2 * w + ((jl & 3) >> 1);
+          const uint2 x = ds_read_tr16(reinterpret_cast<const bf16 *>(
+              buf + C::bV * 1024 + rr0 * (C::VU * 16) + 16 * (u ^ vswz<NW>(rr0)) + 8 * (jl & 1)));
+          vv[0] = __uint_as_float(x.x << 16);
+          vv[1] = __uint_as_float(x.x & 0xffff0000u);
+          vv[2] = __uint_as_float(x.y << 16);
+          vv[3] = __uint_as_float(x.y & 0xffff0000u);
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rr[bt][e] = vv[e] - eg[e] * y[bt][e];
       }
       bf16x8 rh[2], rl[2];
       b_frag_split(rr[0], rr[1], rh[0], rl[0]);
       b_frag_split(rr[2], rr[3], rh[1], rl[1]);
-      // three independent accumulators (one per split product), summed at the end
-      f32x4 c0 = zero4(), c1 = zero4(), c2 = zero4();
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (m > (w >> 1)) continue;
-        c0 = mfma_bf16(th[m], rh[m], c0);
-        c1 = mfma_bf16(th[m], rl[m], c1);
-        c2 = mfma_bf16(tl[m], rh[m], c2);
-      }
-      f32x4 c, cd;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[i] = c0[i] + c1[i] + c2[i];
-        cd[i] = c[i] * dec[i];
-      }
-      sE[(w * 2 + 0) * 64 + l] = cd;
-      if (WANT_O) sE[(w * 2 + 1) * 64 + l] = c;
-    }
-    lds_barrier();
 
-    // ---- 3. outputs of token block w; update of the owned S^T blocks ----
-    {
-      // K^T fragments of the owned dk blocks, and D'' for all token blocks
-      bf16x8 kt[C::NOWN][2];
+      // ---- D = (Tau diag(beta)) R  (f: (bt, m) = (0,0),(1,0),(2,0),(2,1),(3,0),(3,1)) ----
+      f32x4 dd[4];
 #pragma unroll
-      for (int u = 0; u < C::NOWN; ++u)
+      for (int bt = 0; bt < 4; ++bt) dd[bt] = zero4();
 #pragma unroll
-        for (int m = 0; m < 2; ++m) kt[u][m] = a_frag_trans_perm(sK, C::LDK, 32 * m, 16 * (w * C::NOWN + u), l);
-      f32x4 e4[4];
-#pragma unroll
-      for (int bt = 0; bt < 4; ++bt) e4[bt] = sE[(bt * 2) * 64 + l];
-      const float gl = sG[4 * CH];
+      for (int f = 0; f < kTauFrags; ++f) {
+        const int bt = f < 2 ? f : (f - 2) / 2 + 2;
+        const int m = f < 2 ? 0 : (f - 2) % 2;
+        const bf16x8 th = frag(C::bTF + f), tl = frag(C::bTF + kTauFrags + f);
+        dd[bt] = mfma_bf16(th, rh[m], dd[bt]);
+        dd[bt] = mfma_bf16(th, rl[m], dd[bt]);
+        dd[bt] = mfma_bf16(tl, rh[m], dd[bt]);
+      }
 
+      // ---- O = e^g Q S^T + (M o Q K^T) D ----
       if (WANT_O) {
-        f32x4 zp[NWV], d4[4];
-#pragma unroll
-        for (int q = 0; q < NWV; ++q) zp[q] = sX[(q * C::NX + 4 + w) * 64 + l];
-#pragma unroll
-        for (int bt = 0; bt < 4; ++bt) d4[bt] = sE[(bt * 2 + 1) * 64 + l];
-        bf16x8 ph[2], pl[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-          if (m <= (w >> 1)) a_frag_packed(sP, w, m, ph[m], pl[m]);
-        const f32x4 gam = *reinterpret_cast<const f32x4 *>(sG + 2 * CH + 16 * w + 4 * g4);
         bf16x8 dh[2], dl[2];
-        b_frag_split(d4[0], d4[1], dh[0], dl[0]);
-        b_frag_split(d4[2], d4[3], dh[1], dl[1]);
-        f32x4 o0 = zero4(), o1 = zero4(), o2 = zero4();
+        b_frag_split(dd[0], dd[1], dh[0], dl[0]);
+        b_frag_split(dd[2], dd[3], dh[1], dl[1]);
+        f32x4 z[4];
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) z[bt] = zero4();
+#pragma unroll
+        for (int m = 0; m < C::NKS; ++m)
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) {
+            const bf16x8 a = frag(C::bQA + bt * C::NKS + m);
+            z[bt] = mfma_bf16(a, sh[m], z[bt]);
+            z[bt] = mfma_bf16(a, sl[m], z[bt]);
+          }
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) {
+          const f32x4 eg = *reinterpret_cast<const f32x4 *>(sG + G_EG + 16 * bt + 4 * g4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[bt][e] *= eg[e];
+        }
+#pragma unroll
+        for (int f = 0; f < kTauFrags; ++f) {
+          const int bt = f < 2 ? f : (f - 2) / 2 + 2;
+          const int m = f < 2 ? 0 : (f - 2) % 2;
+          const bf16x8 ph = *reinterpret_cast<const bf16x8 *>(sP + (f * 64 + l) * 8);
+          const bf16x8 pl = *reinterpret_cast<const bf16x8 *>(sP + kTauFragPlane + (f * 64 + l) * 8);
+          z[bt] = mfma_bf16(ph, dh[m], z[bt]);
+          z[bt] = mfma_bf16(ph, dl[m], z[bt]);
+          z[bt] = mfma_bf16(pl, dh[m], z[bt]);
+        }
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * bt + 4 * g4 + e;
+            if (r < Lc) {
+              const int64_t oi = ((int64_t)(t0 + r) * H + h) * DV + row0 + jl;
+              if (p.o_bf16)
+                reinterpret_cast<bf16 *>(p.o)[oi] = (bf16)z[bt][e];
+              else
+                reinterpret_cast<float *>(p.o)[oi] = z[bt][e];
+            }
+          }
+      }
+
+      // ---- S^T <- e^{g_L} S^T + K^T diag(e^{g_L - g}) D ----
+      bf16x8 eh[2], el[2];
+      {
+        f32x4 de[4];
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) {
+          const f32x4 dec = *reinterpret_cast<const f32x4 *>(sG + G_DEC + 16 * bt + 4 * g4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) de[bt][e] = dd[bt][e] * dec[e];
+        }
+        b_frag_split(de[0], de[1], eh[0], el[0]);
+        b_frag_split(de[2], de[3], eh[1], el[1]);
+      }
+      const float gl = sG[G_EGL];
+#pragma unroll
+      for (int d = 0; d < C::NSB; ++d) {
+        f32x4 c = st[d];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[e] *= gl;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          if (m > (w >> 1)) continue;
-          o0 = mfma_bf16(ph[m], dh[m], o0);
-          o1 = mfma_bf16(ph[m], dl[m], o1);
-          o2 = mfma_bf16(pl[m], dh[m], o2);
+          const bf16x8 a = frag(C::bKT + 2 * d + m);
+          c = mfma_bf16(a, eh[m], c);
+          c = mfma_bf16(a, el[m], c);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float zz = zp[0][i];
-#pragma unroll
-          for (int q = 1; q < NWV; ++q) zz += zp[q][i];
-          const float ov = gam[i] * zz + (o0[i] + o1[i] + o2[i]);
-          const int r = 16 * w + 4 * g4 + i;
-          if (r < Lc) {
-            const int64_t oi = ((int64_t)(t0 + r) * H + h) * DV + row0 + jl;
-            if (p.o_bf16)
-              reinterpret_cast<bf16 *>(p.o)[oi] = (bf16)ov;
-            else
-              reinterpret_cast<float *>(p.o)[oi] = ov;
-          }
-        }
+        st[d] = c;
       }
-
-      bf16x8 eh[2], el[2];
-      b_frag_split(e4[0], e4[1], eh[0], el[0]);
-      b_frag_split(e4[2], e4[3], eh[1], el[1]);
-      f32x4 a0[C::NOWN], a1[C::NOWN];
-#pragma unroll
-      for (int u = 0; u < C::NOWN; ++u) {
-        a0[u] = st[u];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a0[u][i] *= gl;
-        a1[u] = zero4();
-      }
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int u = 0; u < C::NOWN; ++u) a0[u] = mfma_bf16(kt[u][m], eh[m], a0[u]);
-#pragma unroll
-        for (int u = 0; u < C::NOWN; ++u) a1[u] = mfma_bf16(kt[u][m], el[m], a1[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < C::NOWN; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st[u][i] = a0[u][i] + a1[u][i];
     }
 
-    // ---- 4. stage the next chunk into the other buffer set ----
-    if (t0 + CH < tend) {
-      stage(b ^ 1, min(CH, tend - t0 - CH));
-      if (t0 + 2 * CH < tend) prefetch(t0 + 2 * CH, min(CH, tend - t0 - 2 * CH), slot + 2);
-    }
+    // ---- hand over to the next chunk ----
+    if (more) gates(b ^ 1, L1);
+    wait_vmem();
     lds_barrier();
-    if (WANT_O && t0 + CH < tend) {
+    if (WANT_O && more) {
       build_p(b ^ 1);
       lds_barrier();
     }
   }
 
-  // ---------------- epilogue: owned blocks of the final rows ----------------
-  {
-    float *out = is_T ? p.T_out : p.S_out;
-    const int nrows = is_T ? DK : DV;
+  // ---------------- epilogue: final rows ----------------
+  if (active) {
+    const int64_t unit = ((int64_t)n * p.n_segs + seg) * H + h;
 #pragma unroll
-    for (int u = 0; u < C::NOWN; ++u) {
-      const int d = w * C::NOWN + u;
-      *reinterpret_cast<f32x4 *>(out + (((int64_t)n * H + h) * nrows + row0 + jl) * DK + 16 * d + 4 * g4) = st[u];
+    for (int d = 0; d < C::NSB; ++d) {
+      const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1);
+      if (is_T) {
+        float *out = p.T_out + unit * DK * DK;
+        if (p.T_transposed) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[(int64_t)(c0 + e) * DK + row0 + jl] = st[d][e];
+        } else {
+          *reinterpret_cast<f32x4 *>(out + (int64_t)(row0 + jl) * DK + c0) = st[d];
+        }
+      } else {
+        *reinterpret_cast<f32x4 *>(p.S_out + unit * DV * DK + (int64_t)(row0 + jl) * DK + c0) = st[d];
+      }
     }
   }
 }
 
-template <int DK, bool WANT_O>
+template <int DK, bool WANT_O, int NW>
 hipError_t launch_b(const ChainLaunch &p, hipStream_t stream) {
-  const int64_t items = (int64_t)p.n_seqs * p.H * (p.tiles_T + p.tiles_S);
+  const int tilesA = p.tiles_T + p.tiles_S;
+  const int tiles0 = p.skip_T0 ? p.tiles_S : tilesA;
+  const int64_t per_nh = (tiles0 + NW - 1) / NW + (int64_t)(p.n_segs - 1) * ((tilesA + NW - 1) / NW);
+  const int64_t items = (int64_t)p.n_seqs * p.H * per_nh;
   if (items <= 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((chain_bf16_kernel<DK, WANT_O>), dim3((unsigned)grid), dim3(256), 0, stream, p, (int)items);
+  hipLaunchKernelGGL((chain_bf16_kernel<DK, WANT_O, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, p,
+                     (int)items);
   return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
+  // eight waves per workgroup when every tile count is a multiple of eight
+  // (the operands of a chunk are then shared by eight row tiles)
+  const bool eight = p.tiles_S % 8 == 0 && p.tiles_T % 8 == 0;
+  if (p.o) return launch_b<DK, true, 4>(p, stream);
+  return eight ? launch_b<DK, false, 8>(p, stream) : launch_b<DK, false, 4>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_chain_bf16(const ChainLaunch &p, hipStream_t stream) {
-  if (p.dk == 64) return p.o ? launch_b<64, true>(p, stream) : launch_b<64, false>(p, stream);
-  if (p.dk == 128) return p.o ? launch_b<128, true>(p, stream) : launch_b<128, false>(p, stream);
+  if (p.n_segs < 1 || p.tiles_S % 4 != 0 || p.tiles_T % 4 != 0) return hipErrorInvalidValue;
+  if (p.dk == 64) return launch_dk<64>(p, stream);
+  if (p.dk == 128) return launch_dk<128>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -82,7 +82,92 @@ hipError_t launch_c(const ComposeLaunch &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Composition of time-split segments (one sequence's segment operators, in
+// order): S = S_seg[0], then S <- S T_seg[s] + S_seg[s].  T_seg arrives
+// transposed (T^T row-major), so the A operand of S_new^T = T^T S^T comes
+// straight from global memory, 8 consecutive floats per lane.  Workgroup =
+// 4 waves on 16 rows of one (sequence, head); wave w owns dk blocks
+// w * NOB .. w * NOB + NOB - 1 of S^T (C layout, natural dk order) and the
+// full S^T operand is exchanged through LDS once per step.
+// ---------------------------------------------------------------------------
+constexpr int SNW = 4;
+
+template <int DK>
+__global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch p, int n_items) {
+  constexpr int LDS_ = DK + 4;
+  constexpr int NOB = DK / 16 / SNW;  // owned 16-row blocks of S^T per wave
+  constexpr int NKS = DK / 32;
+  __shared__ __attribute__((aligned(16))) float sS[16 * LDS_];
+
+  const int per = (int)(gridDim.x >> 3);
+  const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (item >= n_items) return;
+  const int tiles = p.dv / 16;
+  const int nh = item / tiles, row0 = 16 * (item % tiles);
+  const int n = nh / p.H, h = nh % p.H;
+  const int H = p.H, DV = p.dv, P = p.n_segs;
+  const int w = wave_id(), l = lane_id(), g4 = l >> 4, jl = l & 15;
+
+  auto seg_state = [&](int s) { return p.S_seg + (((int64_t)n * P + s) * H + h) * DV * DK; };
+  f32x4 acc[NOB];
+#pragma unroll
+  for (int i = 0; i < NOB; ++i)
+    acc[i] = *reinterpret_cast<const f32x4 *>(seg_state(0) + (int64_t)(row0 + jl) * DK + 16 * (w * NOB + i) + 4 * g4);
+
+  for (int s = 1; s < P; ++s) {
+#pragma unroll
+    for (int i = 0; i < NOB; ++i)
+      *reinterpret_cast<f32x4 *>(sS + jl * LDS_ + 16 * (w * NOB + i) + 4 * g4) = acc[i];
+    lds_barrier();
+    bf16x8 bh[NKS], bl[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4 *>(sS + jl * LDS_ + 32 * ks + 8 * g4);
+      const f32x4 x1 = *reinterpret_cast<const f32x4 *>(sS + jl * LDS_ + 32 * ks + 8 * g4 + 4);
+      b_frag_split(x0, x1, bh[ks], bl[ks]);
+    }
+    const float *Tt = p.Tt_seg + (((int64_t)n * P + s) * H + h) * DK * DK;
+    const float *Ls = seg_state(s);
+#pragma unroll
+    for (int i = 0; i < NOB; ++i) {
+      const int jb = w * NOB + i;
+      f32x4 c = *reinterpret_cast<const f32x4 *>(Ls + (int64_t)(row0 + jl) * DK + 16 * jb + 4 * g4);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const float *a = Tt + (int64_t)(16 * jb + jl) * DK + 32 * ks + 8 * g4;
+        bf16x8 ah, al;
+        b_frag_split(*reinterpret_cast<const f32x4 *>(a), *reinterpret_cast<const f32x4 *>(a + 4), ah, al);
+        c = mfma_bf16(ah, bh[ks], c);
+        c = mfma_bf16(ah, bl[ks], c);
+        c = mfma_bf16(al, bh[ks], c);
+      }
+      acc[i] = c;
+    }
+    lds_barrier();
+  }
+  float *out = p.S_out + ((int64_t)n * H + h) * DV * DK;
+#pragma unroll
+  for (int i = 0; i < NOB; ++i)
+    *reinterpret_cast<f32x4 *>(out + (int64_t)(row0 + jl) * DK + 16 * (w * NOB + i) + 4 * g4) = acc[i];
+}
+
+template <int DK>
+hipError_t launch_sc(const SegComposeLaunch &p, hipStream_t stream) {
+  const int64_t items = (int64_t)p.n_seqs * p.H * (p.dv / 16);
+  if (items <= 0) return hipSuccess;
+  const int64_t grid = (items + 7) / 8 * 8;
+  hipLaunchKernelGGL((seg_compose_kernel<DK>), dim3((unsigned)grid), dim3(SNW * 64), 0, stream, p, (int)items);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_seg_compose(const SegComposeLaunch &p, hipStream_t stream) {
+  if (p.dk == 64) return launch_sc<64>(p, stream);
+  if (p.dk == 128) return launch_sc<128>(p, stream);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_compose(const ComposeLaunch &p, hipStream_t stream) {
   if (p.dk == 64) return launch_c<64>(p, stream);

@@ -303,10 +303,51 @@ __device__ __forceinline__ bf16x8 a_frag_trans_perm(const bf16 *M, int ld, int k
   return cat_bf16x8(ds_read_tr16(p0), ds_read_tr16(p0 + 16 * ld));
 }
 
+// Two fp32 values as packed bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
+// Split-bf16 of a pair with one rounding per part: hi = bf16(x), read back
+// exactly by shifting the packed bits, lo = bf16(x - hi).
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(a, b);
+  const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
+  lo = pack_bf16x2(a - ha, b - hb);
+}
+
 // Split two C-layout tiles into a k = 32 B fragment (hi, lo).
 __device__ __forceinline__ void b_frag_split(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi, bf16x8 &lo) {
-  const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-  split8(x, hi, lo);
+  uint4 h, o;
+  split2(t0[0], t0[1], h.x, o.x);
+  split2(t0[2], t0[3], h.y, o.y);
+  split2(t1[0], t1[1], h.z, o.z);
+  split2(t1[2], t1[3], h.w, o.w);
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, o);
+}
+
+// ---------------------------------------------------------------------------
+// Load-to-LDS DMA (gfx950 buffer_load_dwordx4 ... lds / global_load_lds_dwordx4):
+// lane l of the wave copies 16 bytes from its own source address to
+// dst + 16 l; completion is counted by vmcnt.  The buffer form reads through
+// a raw descriptor covering nbytes from base: lanes past the range write
+// zeros.  (The builtins exist only for the device pass; the host pass of a
+// kernel template must not see them.)
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16_buffer(const void *base, uint32_t nbytes, lds_void *dst, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+#endif
+}
+__device__ __forceinline__ void dma16_global(const void *src, lds_void *dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+#endif
 }
 
 // Wait for all outstanding vector-memory loads of this wave (vmcnt(0)).

@@ -16,16 +16,28 @@ namespace gdn {
 // without reading cu (which lives on the device).
 // ---------------------------------------------------------------------------
 constexpr int kChunk = 64;
-// Tau = (I + A)^{-1} of one chunk, lower 16 x 16 block rows packed: block
-// row b holds 16 rows x 16 (b + 1) columns, row-major, at element offset
-// 256 * b (b + 1) / 2 (2560 elements).  fp32 inputs: one fp32 array; bf16
-// inputs: split bf16 planes, hi then lo (same 10240 bytes).
-constexpr int kTauFloats = 2560;
+// Per-chunk factor record, one per (slot, head), 28 KiB:
+//   * fp32 inputs: Tau = (I + A)^{-1}, lower 16 x 16 block rows packed, block
+//     row b holds 16 rows x 16 (b + 1) columns, row-major, at element offset
+//     256 * b (b + 1) / 2 (2560 floats);
+//   * bf16 inputs: bytes [0, 12 KiB): Tau diag(beta) as the six A operands of
+//     the k = 32 MFMAs that apply it to a 64 x 16 right-hand side given as
+//     C-layout tiles (see kTauFrags), split bf16 planes [hi/lo][fragment]
+//     [lane][8]; bytes [12 KiB, 28 KiB): K^T as the A operands of the state
+//     update (gdn_chain_bf16.hip), [fragment][lane][8] bf16.
+constexpr int kRecFloats = 7168;
+constexpr int kRecKtOffsetBytes = 12288;
+// Fragment f of Tau covers token block row bt and the pair of 16-column
+// blocks (2m, 2m + 1): f = 0: (0,0), 1: (1,0), 2: (2,0), 3: (2,1), 4: (3,0),
+// 5: (3,1).  Lane l holds row 16 bt + (l & 15), columns
+// 32 m + 4 (l >> 4) + {0..3} then 32 m + 16 + 4 (l >> 4) + {0..3}.
+constexpr int kTauFrags = 6;
+constexpr int kTauFragPlane = kTauFrags * 64 * 8;  // bf16 elements per plane
 
 inline int64_t slot_count(int64_t n_tokens, int32_t n_seqs) { return n_tokens / kChunk + n_seqs + 1; }
 
 inline size_t tau_workspace_bytes(int64_t n_tokens, int32_t n_seqs, int32_t n_heads) {
-  return (size_t)slot_count(n_tokens, n_seqs) * (size_t)n_heads * kTauFloats * sizeof(float);
+  return (size_t)slot_count(n_tokens, n_seqs) * (size_t)n_heads * kRecFloats * sizeof(float);
 }
 
 // Per-chunk factor build: one workgroup per (slot, head).
@@ -34,7 +46,7 @@ struct PrepLaunch {
   const int32_t *cu;
   int32_t n_seqs, H, dk;
   int in_bf16;
-  float *tau;        // [n_slots, H, kTauFloats]
+  float *tau;        // [n_slots, H, kRecFloats] per-chunk factor records
   int64_t n_slots;
 };
 
@@ -56,9 +68,15 @@ struct ChainLaunch {
   int in_bf16;              // inputs are bf16 (else fp32)
   void *o;                  // [T, H, dv] or null
   int o_bf16;
-  float *S_out;             // [n_seqs, H, dv, dk] (state tiles) or null
-  float *T_out;             // [n_seqs, H, dk, dk] (transition tiles) or null
+  float *S_out;             // [n_seqs, n_segs, H, dv, dk] (state tiles) or null
+  float *T_out;             // [n_seqs, n_segs, H, dk, dk] (transition tiles) or null
   int32_t tiles_T, tiles_S;
+  // Time split: each sequence is cut into n_segs segments of equal whole
+  // chunks; every segment runs independently (state tiles of segment 0 from
+  // S0, of later segments from zero; transition tiles from the identity).
+  int32_t n_segs;           // >= 1
+  int skip_T0;              // segment 0 has no transition tiles
+  int T_transposed;         // write T^T (row-major) instead of T
 };
 
 struct ComposeLaunch {
@@ -69,9 +87,20 @@ struct ComposeLaunch {
   float *S_out;             // [H, dv, dk]
 };
 
+// Composition of time-split segments: for each (sequence, head),
+//   S = S_seg[0];  S <- S T_seg[s] + S_seg[s] for s = 1 .. n_segs - 1,
+// with T_seg stored transposed.
+struct SegComposeLaunch {
+  const float *S_seg;       // [n_seqs, n_segs, H, dv, dk]
+  const float *Tt_seg;      // [n_seqs, n_segs, H, dk, dk] (T^T; segment 0 unused)
+  int32_t n_seqs, n_segs, H, dk, dv;
+  float *S_out;             // [n_seqs, H, dv, dk]
+};
+
 hipError_t launch_prep(const PrepLaunch &p, hipStream_t stream);
 hipError_t launch_chain(const ChainLaunch &p, hipStream_t stream);        // fp32 inputs
 hipError_t launch_chain_bf16(const ChainLaunch &p, hipStream_t stream);   // bf16 inputs
 hipError_t launch_compose(const ComposeLaunch &p, hipStream_t stream);
+hipError_t launch_seg_compose(const SegComposeLaunch &p, hipStream_t stream);
 
 }  // namespace gdn

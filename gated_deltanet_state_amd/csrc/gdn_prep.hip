@@ -18,8 +18,11 @@
 //   4. off-diagonal blocks Tau_ij = -Tau_ii sum_{m=j}^{i-1} A_im Tau_mj; a
 //      block column depends only on the diagonal blocks and the blocks above
 //      it, so one wave per block column, in registers (split-bf16 products)
-// The result is written packed (lower block rows only): fp32 for fp32
-// inputs, split bf16 planes (hi, lo) for bf16 inputs.
+// The result is written packed (lower block rows only) in fp32 for fp32
+// inputs.  For bf16 inputs the record holds what the recurrence kernel feeds
+// its k = 32 MFMAs, in their lane order (layout in gdn_internal.h), so that
+// it can copy the record straight into LDS: Tau diag(beta) as split-bf16 A
+// fragments, and K^T as the A fragments of its state update.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -86,17 +89,10 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
   const int t0 = tbeg + (int)j * kChunk;
   const int Lc = min(kChunk, len - (int)j * kChunk);
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  // output: fp32 packed Tau, or (bf16 inputs) split hi / lo bf16 planes
-  float *out = p.tau + (slot * H + h) * (int64_t)kTauFloats;
-  bf16 *outh = reinterpret_cast<bf16 *>(out), *outl = outh + kTauFloats;
+  // output: fp32 packed Tau (fp32 inputs); bf16 inputs: fragments, below
+  float *out = p.tau + (slot * H + h) * (int64_t)kRecFloats;
   auto put = [&](int idx, float x) {
-    if constexpr (BF) {
-      const bf16 hi = (bf16)x;
-      outh[idx] = hi;
-      outl[idx] = (bf16)(x - (float)hi);
-    } else {
-      out[idx] = x;
-    }
+    if constexpr (!BF) out[idx] = x;
   };
 
   // ---- 1. keys and gates ----
@@ -205,9 +201,8 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) Y[q] = -Y[q];
         T[i] = Y;
-        const int ob = tau_off(i) + 16 * jc + (l & 15);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) put(ob + (kq + q) * 16 * (i + 1), Y[q]);
+        for (int q = 0; q < 4; ++q) sTau[(16 * i + kq + q) * C::LDC + 16 * jc + rA] = Y[q];
       }
     } else {
       float *xs = sX + w * 16 * C::LDX;
@@ -228,6 +223,52 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
         for (int q = 0; q < 4; ++q) put(ob + (4 * (l >> 4) + q) * 16 * (i + 1), Y[q]);
         wave_lds_fence();
       }
+    }
+  }
+
+  // ---- 5. (bf16 inputs) Tau as split-bf16 MFMA A fragments ----
+  if constexpr (BF) {
+    lds_barrier();
+    bf16 *outh = reinterpret_cast<bf16 *>(out), *outl = outh + kTauFragPlane;
+    for (int s = tid; s < kTauFrags * 64; s += PNT) {
+      const int f = s >> 6, ln = s & 63;
+      const int bt = f < 2 ? f : (f - 2) / 2 + 2;
+      const int m = f < 2 ? 0 : (f - 2) % 2;
+      const int row = 16 * bt + (ln & 15);
+      float x[8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int c0 = 32 * m + 16 * half + 4 * (ln >> 4);
+        const bool live = (c0 >> 4) <= bt;  // blocks right of the diagonal are zero
+        const f32x4 v = live ? *reinterpret_cast<const f32x4 *>(sTau + row * C::LDC + c0) : zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * half + e] = v[e];
+      }
+      // fold beta into the columns: Tau R = (Tau diag(beta)) (V - e^g Y)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const f32x4 bc = *reinterpret_cast<const f32x4 *>(sBeta + 32 * m + 16 * half + 4 * (ln >> 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * half + e] *= bc[e];
+      }
+      bf16x8 hi, lo;
+      split8(x, hi, lo);
+      *reinterpret_cast<bf16x8 *>(outh + 8 * s) = hi;
+      *reinterpret_cast<bf16x8 *>(outl + 8 * s) = lo;
+    }
+    // K^T fragments of the state update S^T += K^T D': fragment (d, mm), lane
+    // (q, g) holds K[32 mm + 4 g + e (+16)][32 (d >> 1) + 8 (q >> 2) + 4 (d & 1) + (q & 3)],
+    // e < 4: the row order of the recurrence kernel's S^T blocks and the
+    // token order of its paired C-layout right-hand sides
+    bf16 *kt = reinterpret_cast<bf16 *>(reinterpret_cast<char *>(out) + kRecKtOffsetBytes);
+    for (int s = tid; s < 2 * (DK / 16) * 64; s += PNT) {
+      const int j = s >> 6, ln = s & 63;
+      const int d = j >> 1, mm = j & 1, q = ln & 15, g = ln >> 4;
+      const int col = 32 * (d >> 1) + 8 * (q >> 2) + 4 * (d & 1) + (q & 3);
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = sK[(32 * mm + 4 * g + (e & 3) + 16 * (e >> 2)) * C::LDK + col];
+      *reinterpret_cast<bf16x8 *>(kt + 8 * s) = v;
     }
   }
 }

@@ -92,12 +92,26 @@ def test_compose_argument_checks(lib):
     assert cp(Si=P + 4) == ALIGN
 
 
-def test_workspace_queries(lib):
-    # one packed 64 x 64 lower-triangular factor (2560 floats) per chunk slot
+def test_workspace_queries(lib, monkeypatch):
+    # one 28 KiB record of per-chunk factors ((I + A)^{-1} and K^T fragments) per chunk slot
     # and head; slots = n_tokens / 64 + n_seqs + 1 (sequence n's chunk j sits
     # in slot floor(cu[n] / 64) + n + j)
-    assert lib.gdn_replay_workspace_bytes(16, 30000, 32, 128, 128) == (30000 // 64 + 17) * 32 * 2560 * 4
-    assert lib.gdn_chunk_operator_workspace_bytes(64, 32768, 32, 128, 128) == (512 + 65) * 32 * 10240
+    monkeypatch.delenv("GDN_REPLAY_SEGMENTS", raising=False)
+    tau = lambda n_seqs, n_tokens, H: (n_tokens // 64 + n_seqs + 1) * H * 28672
+    # 16 sequences x 32 heads already fill the chip: no time split
+    assert lib.gdn_replay_workspace_bytes(16, 30000, 32, 128, 128) == tau(16, 30000, 32)
+    assert lib.gdn_chunk_operator_workspace_bytes(64, 32768, 32, 128, 128) == tau(64, 32768, 32)
+    # one long sequence: room for P segment operators (T_seg and S_seg per
+    # head), 1 < P <= 16
+    extra = lib.gdn_replay_workspace_bytes(1, 3277, 32, 128, 128) - tau(1, 3277, 32)
+    per_seg = 32 * (128 * 128 + 128 * 128) * 4
+    assert extra % per_seg == 0 and 2 <= extra // per_seg <= 16
+    # the override sets P directly
+    monkeypatch.setenv("GDN_REPLAY_SEGMENTS", "5")
+    assert lib.gdn_replay_workspace_bytes(2, 300, 4, 64, 128) == tau(2, 300, 4) + 2 * 5 * 4 * (64 * 64 + 128 * 64) * 4
+    monkeypatch.setenv("GDN_REPLAY_SEGMENTS", "1")
+    assert lib.gdn_replay_workspace_bytes(1, 3277, 32, 128, 128) == tau(1, 3277, 32)
+    monkeypatch.delenv("GDN_REPLAY_SEGMENTS")
     assert lib.gdn_compose_workspace_bytes(64, 32, 128, 128) == 0
     # a missing workspace is reported before anything is launched
     assert replay(lib) == WS
