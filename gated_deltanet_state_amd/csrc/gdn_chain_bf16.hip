@@ -155,23 +155,20 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
   }
 
   // ---- DMA of one chunk's operands into buffer set b ----
-  // Rows past the chunk read as zero: each tensor's descriptor covers rows
-  // t0 .. t0 + Lc - 1 of head h only.
+  // Rows past the chunk are copies of its last row: they only meet zero
+  // coefficients (beta = 0 in the Tau columns, zero K^T rows from the prep
+  // kernel, masked M o Q K^T), so any finite value serves.
   auto issue_dma = [&](int b, int t0, int Lc, int64_t slot) {
     char *buf = smem + b * C::BUF;
-    const uint32_t krec = (uint32_t)(((Lc - 1) * (int64_t)H + 1) * DK * 2);
-    const uint32_t vrec = (uint32_t)(((Lc - 1) * (int64_t)H + 1) * DV * 2);
-    const bf16 *kbase = gk + ((int64_t)t0 * H + h) * DK;
-    const bf16 *qbase = gq + ((int64_t)t0 * H + h) * DK;
-    const bf16 *vbase = gv + ((int64_t)t0 * H + h) * DV;
     const char *rec = grec + (slot * H + h) * (int64_t)(kRecFloats * 4);
     for (int i = w; i < C::NBLK; i += NW) {
       lds_void *dst = (lds_void *)(buf + i * 1024);
       if (i < C::bKT || (WANT_O && i >= C::bQA)) {   // K or Q A fragment (bt, m)
         const int f = i < C::bKT ? i : i - C::bQA;
         const int bt = f / C::NKS, m = f % C::NKS;
-        const uint32_t off = (uint32_t)(((16 * bt + jl) * H) * DK + 32 * m + 8 * g4) * 2;
-        dma16_buffer(i < C::bKT ? (const void *)kbase : (const void *)qbase, krec, dst, off);
+        const int r = min(16 * bt + jl, Lc - 1);
+        const bf16 *src = (i < C::bKT ? gk : gq) + ((int64_t)(t0 + r) * H + h) * DK + 32 * m + 8 * g4;
+        dma16_global(src, dst);
       } else if (i < C::bTF) {                         // K^T fragments (record)
         dma16_global(rec + kRecKtOffsetBytes + (i - C::bKT) * 1024 + 16 * l, dst);
       } else if (i < C::bV) {                          // Tau diag(beta) fragments (record)
@@ -179,7 +176,7 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
       } else if (grp_S) {                              // value slab block
         const int u_lds = (i - C::bV) * 64 + l;
         const int r = u_lds / C::VU, u = (u_lds % C::VU) ^ vswz<NW>(r);
-        dma16_buffer(vbase, vrec, dst, (uint32_t)((r * H) * DV + vcol0 + 8 * u) * 2);
+        dma16_global(gv + ((int64_t)(t0 + min(r, Lc - 1)) * H + h) * DV + vcol0 + 8 * u, dst);
       }
     }
   };

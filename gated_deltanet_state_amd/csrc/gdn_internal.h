@@ -97,7 +97,8 @@ struct SegComposeLaunch {
   float *S_out;             // [n_seqs, H, dv, dk]
 };
 
-hipError_t launch_prep(const PrepLaunch &p, hipStream_t stream);
+hipError_t launch_prep(const PrepLaunch &p, hipStream_t stream);        // dispatches bf16 inputs to launch_prep_bf16
+hipError_t launch_prep_bf16(const PrepLaunch &p, hipStream_t stream);
 hipError_t launch_chain(const ChainLaunch &p, hipStream_t stream);        // fp32 inputs
 hipError_t launch_chain_bf16(const ChainLaunch &p, hipStream_t stream);   // bf16 inputs
 hipError_t launch_compose(const ComposeLaunch &p, hipStream_t stream);

@@ -284,8 +284,7 @@ hipError_t launch_p(const PrepLaunch &p, hipStream_t stream) {
 
 hipError_t launch_prep(const PrepLaunch &p, hipStream_t stream) {
   if (p.in_bf16) {
-    if (p.dk == 64) return launch_p<bf16, 64>(p, stream);
-    if (p.dk == 128) return launch_p<bf16, 128>(p, stream);
+    return launch_prep_bf16(p, stream);
   } else {
     if (p.dk == 64) return launch_p<float, 64>(p, stream);
     if (p.dk == 128) return launch_p<float, 128>(p, stream);
