@@ -231,6 +231,30 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
     }
   };
 
+  // Value columns of the staged chunk in buffer set b, transposed to the
+  // C layout of R (lane: column row0 + jl, tokens 16 bt + 4 g4 + e).  The
+  // transposing read carries no alias information, so a read issued while
+  // a load-to-LDS copy is in flight would make the compiler wait for that
+  // copy; the values are therefore read right after each hand-over
+  // barrier, before the next copies are issued, and kept in registers.
+  // The read is issued by every wave with all lanes on: a transposing read
+  // under a partial or empty EXEC mask still writes its destination (the
+  // data of a lane comes from other lanes' addresses).  Transition tiles,
+  // whose workgroups stage no values, clear the result with a mask.
+  uint2 vt[4];
+  const uint32_t vmask = (active && !is_T) ? 0xffffffffu : 0u;
+  auto read_v = [&](int b) {
+    const char *buf = smem + b * C::BUF;
+#pragma unroll
+    for (int bt = 0; bt < 4; ++bt) {
+      const int rr0 = 16 * bt + 4 * g4 + (jl >> 2);
+      const int u = 2 * (w & (NW - 1)) + ((jl & 3) >> 1);
+      const uint2 x = ds_read_tr16(reinterpret_cast<const bf16 *>(
+          buf + C::bV * 1024 + rr0 * (C::VU * 16) + 16 * (u ^ vswz<NW>(rr0)) + 8 * (jl & 1)));
+      vt[bt] = uint2{x.x & vmask, x.y & vmask};
+    }
+  };
+
   if (tbeg < tend) {
     const int L0 = min(CH, tend - tbeg);
     issue_dma(0, tbeg, L0, slot0);
@@ -243,6 +267,28 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
     build_p(0);
     lds_barrier();
   }
+  read_v(0);
+
+  // Outputs of a chunk are stored at the start of the next one, so that
+  // the hand-over wait (which also counts stores) finds them complete.
+  f32x4 zp[4];
+  int tp = 0, Lp = 0;
+  auto store_o = [&]() {
+#pragma unroll
+    for (int bt = 0; bt < 4; ++bt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * bt + 4 * g4 + e;
+        if (r < Lp) {
+          const int64_t oi = ((int64_t)(tp + r) * H + h) * DV + row0 + jl;
+          if (p.o_bf16)
+            reinterpret_cast<bf16 *>(p.o)[oi] = (bf16)zp[bt][e];
+          else
+            reinterpret_cast<float *>(p.o)[oi] = zp[bt][e];
+        }
+      }
+    Lp = 0;
+  };
 
   int64_t slot = slot0;
   int b = 0;
@@ -250,6 +296,7 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
     const int Lc = min(CH, tend - t0);
     const bool more = t0 + CH < tend;
     const int L1 = more ? min(CH, tend - t0 - CH) : 0;
+    if (WANT_O && active && Lp > 0) store_o();
     // operands of the next chunk: in flight while this one runs
     if (more) {
       issue_dma(b ^ 1, t0 + CH, L1, slot + 1);
@@ -283,17 +330,8 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
 #pragma unroll
       for (int bt = 0; bt < 4; ++bt) {
         const f32x4 eg = *reinterpret_cast<const f32x4 *>(sG + G_EG + 16 * bt + 4 * g4);
-        float vv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (!is_T) {
-          const int rr0 = 16 * bt + 4 * g4 + (jl >> 2);
-          const int u = 2 * w + ((jl & 3) >> 1);
-          const uint2 x = ds_read_tr16(reinterpret_cast<const bf16 *>(
-              buf + C::bV * 1024 + rr0 * (C::VU * 16) + 16 * (u ^ vswz<NW>(rr0)) + 8 * (jl & 1)));
-          vv[0] = __uint_as_float(x.x << 16);
-          vv[1] = __uint_as_float(x.x & 0xffff0000u);
-          vv[2] = __uint_as_float(x.y << 16);
-          vv[3] = __uint_as_float(x.y & 0xffff0000u);
-        }
+        const float vv[4] = {__uint_as_float(vt[bt].x << 16), __uint_as_float(vt[bt].x & 0xffff0000u),
+                             __uint_as_float(vt[bt].y << 16), __uint_as_float(vt[bt].y & 0xffff0000u)};
 #pragma unroll
         for (int e = 0; e < 4; ++e) rr[bt][e] = vv[e] - eg[e] * y[bt][e];
       }
@@ -348,18 +386,9 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
           z[bt] = mfma_bf16(pl, dh[m], z[bt]);
         }
 #pragma unroll
-        for (int bt = 0; bt < 4; ++bt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * bt + 4 * g4 + e;
-            if (r < Lc) {
-              const int64_t oi = ((int64_t)(t0 + r) * H + h) * DV + row0 + jl;
-              if (p.o_bf16)
-                reinterpret_cast<bf16 *>(p.o)[oi] = (bf16)z[bt][e];
-              else
-                reinterpret_cast<float *>(p.o)[oi] = z[bt][e];
-            }
-          }
+        for (int bt = 0; bt < 4; ++bt) zp[bt] = z[bt];
+        tp = t0;
+        Lp = Lc;
       }
 
       // ---- S^T <- e^{g_L} S^T + K^T diag(e^{g_L - g}) D ----
@@ -399,9 +428,11 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
       build_p(b ^ 1);
       lds_barrier();
     }
+    if (more) read_v(b ^ 1);
   }
 
   // ---------------- epilogue: final rows ----------------
+  if (WANT_O && active && Lp > 0) store_o();
   if (active) {
     const int64_t unit = ((int64_t)n * p.n_segs + seg) * H + h;
 #pragma unroll

@@ -287,7 +287,10 @@ __device__ __forceinline__ bf16x8 a_frag_perm(const bf16 *rowp, int kb, int g) {
 // source lane 4e + i/4.  Pointing source lane q of group g at
 // M[r0 + 4g + q/4][c0 + 4 (q mod 4)] of a row-major bf16 matrix M therefore
 // gives lane i the column c0 + i, rows r0 + 4g + e (e < 4): a k = 16 A
-// fragment of M^T.
+// fragment of M^T.  Issue it with every lane of the wave on: under a partial
+// or empty EXEC mask the destination is still written, with unusable data.
+// It carries no alias information either, so while a load-to-LDS copy is in
+// flight the compiler makes it wait for that copy.
 __device__ __forceinline__ uint2 ds_read_tr16(const bf16 *p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
   union { s16x4 s; uint2 u; } x;
