@@ -42,6 +42,9 @@ bool valid_dtype(gdn_dtype t) { return t == GDN_F32 || t == GDN_BF16; }
 // Largest token count whose (token, head) indexing stays within the 32-bit
 // arithmetic of the chunk loop.
 constexpr int64_t kMaxTokens = (int64_t(1) << 31) - 64;
+// Largest head count whose in-chunk byte offsets (64 tokens x heads x 128
+// bf16) fit the kernels' 32-bit offsets.
+constexpr int32_t kMaxHeads = 65536;
 
 gdn_status check_align(const char *name, const void *p) {
   if (p && !aligned16(p)) return fail(GDN_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
@@ -57,28 +60,33 @@ gdn_status launched(hipError_t e, const char *what) {
 // sequence cut into P segments of whole chunks runs as P independent
 // recurrences (segment 0 from S0 with its state rows only, later segments as
 // affine operators with dk transition rows as well), composed afterwards.
-// The state-only chain kernel runs one wave per 16 rows, two waves per SIMD
-// (2048 slots on 256 compute units x 4 SIMDs); the time of a launch is
-// roughly (waves / 2048 rounded up) x (chunks per segment), plus about half
-// a chunk per composition step.  P = 1 unless splitting pays.
-// GDN_REPLAY_SEGMENTS=<n> overrides the choice (tuning and tests).
+// Cost model, in units of one chunk step of an eight-wave state workgroup
+// (one workgroup per compute unit, 256 compute units):
+//   P = 1:  (workgroups / 256 rounded up) x chunks per sequence
+//   P > 1:  one workgroup of transition + state tiles per (sequence, head,
+//           segment), each chunk step about 1.25 units, plus about 0.3 units
+//           per composition step.
+// P = 1 unless splitting pays.  GDN_REPLAY_SEGMENTS=<n> overrides the
+// choice (tuning and tests).
 int replay_segments(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv) {
   if (const char *env = std::getenv("GDN_REPLAY_SEGMENTS")) {
     const int v = std::atoi(env);
     if (v >= 1) return v < 64 ? v : 64;
   }
-  const double chunks = (double)n_tokens / gdn::kChunk / (n_seqs > 0 ? n_seqs : 1);
+  if ((dk + dv) / 16 > 16) return 1;
+  const double chunks = std::ceil((double)n_tokens / gdn::kChunk / (n_seqs > 0 ? n_seqs : 1));
   int pmax = (int)chunks;
   if (pmax > 16) pmax = 16;
   if (pmax < 1) pmax = 1;
-  const int64_t gS = (dv / 16 + 3) / 4, gA = ((dk + dv) / 16 + 3) / 4;
+  constexpr int64_t kCUs = 256;
+  const int64_t wg1 = (int64_t)n_seqs * n_heads * ((dv / 16 + 7) / 8);
   int best = 1;
-  double best_t = 0;
-  for (int P = 1; P <= pmax; ++P) {
-    const int64_t waves = (int64_t)n_seqs * n_heads * 4 * (gS + (int64_t)(P - 1) * gA);
-    if (waves > (int64_t(1) << 28)) break;
-    const double t = (double)((waves + 2047) / 2048) * std::ceil(chunks / P) + 0.5 * (P - 1);
-    if (P == 1 || t < best_t) {
+  double best_t = (double)((wg1 + kCUs - 1) / kCUs) * chunks;
+  for (int P = 2; P <= pmax; ++P) {
+    const int64_t wg = (int64_t)n_seqs * n_heads * P;
+    if (wg > (int64_t(1) << 28)) break;
+    const double t = (double)((wg + kCUs - 1) / kCUs) * std::ceil(chunks / P) * 1.25 + 0.3 * (P - 1);
+    if (t < best_t) {
       best = P;
       best_t = t;
     }
@@ -125,7 +133,7 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
     return fail(GDN_ERR_UNSUPPORTED, "gdn_replay: dk and dv must be 64 or 128 (got %d, %d)", dk, dv);
   if (!valid_dtype(in_dtype) || (o && !valid_dtype(o_dtype)))
     return fail(GDN_ERR_UNSUPPORTED, "gdn_replay: dtypes must be GDN_F32 or GDN_BF16");
-  if (n_tokens > kMaxTokens || (int64_t)n_seqs * n_heads * (dv / 16) > (int64_t(1) << 30))
+  if (n_tokens > kMaxTokens || n_heads > kMaxHeads || (int64_t)n_seqs * n_heads * (dv / 16) > (int64_t(1) << 30))
     return fail(GDN_ERR_UNSUPPORTED, "gdn_replay: problem too large for one call");
   gdn_status s;
   if ((s = check_align("q", q)) || (s = check_align("k", k)) || (s = check_align("v", v)) ||
@@ -214,7 +222,7 @@ gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, c
   if (!supported_dim(dk) || !supported_dim(dv))
     return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_operator: dk and dv must be 64 or 128 (got %d, %d)", dk, dv);
   if (!valid_dtype(in_dtype)) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_operator: bad dtype");
-  if (n_tokens > kMaxTokens || (int64_t)n_chunks * n_heads * ((dk + dv) / 16) > (int64_t(1) << 30))
+  if (n_tokens > kMaxTokens || n_heads > kMaxHeads || (int64_t)n_chunks * n_heads * ((dk + dv) / 16) > (int64_t(1) << 30))
     return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_operator: problem too large for one call");
   gdn_status s;
   if ((s = check_align("k", k)) || (s = check_align("v", v)) || (s = check_align("alpha", alpha)) ||

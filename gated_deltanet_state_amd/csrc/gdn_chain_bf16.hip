@@ -26,12 +26,15 @@
 // M o Q K^T) are stored in that order, and K^T comes from the gfx950
 // transposing LDS read.
 //
-// Workgroup: NW waves = NW row tiles of one (sequence segment, head).  While
+// Workgroup: NW waves, each owning RT (one or two) row tiles of one
+// (sequence segment, head); with two, every fragment read from LDS feeds
+// the products of both tiles.  While
 // chunk c runs from one LDS buffer set, the operands of chunk c + 1 are
 // copied into the other one by load-to-LDS DMA (buffer_load ... lds; no
 // registers, no staging code): K and Q as MFMA A fragments, the per-chunk
-// record of gdn_prep.hip (Tau diag(beta) and K^T fragments), and the value
-// columns of the workgroup.  Every fragment read is then a conflict-free
+// record of gdn_prep_bf16.hip (Tau diag(beta) fragments), and the value
+// columns of the workgroup; K^T fragments come from the staged keys by the
+// transposing LDS read.  Every fragment read is then a conflict-free
 // 16-byte LDS read by lane.  One LDS barrier per chunk (two with outputs:
 // M o Q K^T of the next chunk is built once its keys and queries landed).
 //
@@ -54,18 +57,19 @@ namespace {
 
 constexpr int CH = kChunk;
 
-template <int DK, bool WANT_O, int NW>
+template <int DK, bool WANT_O, int NW, int RT>
 struct Cfg {
   static constexpr int NT = NW * 64;
+  static constexpr int TW = NW * RT;           // row tiles per workgroup
   static constexpr int NSB = DK / 16;          // 16-row blocks of S^T
   static constexpr int NKS = DK / 32;          // k = 32 steps over dk
   // LDS buffer set: 1 KiB blocks, one MFMA fragment (64 lanes x 16 bytes) each
   static constexpr int NKA = 4 * NKS;          // K (and Q) A fragments (bt, m)
-  static constexpr int NKT = 2 * NSB;          // K^T fragments (d, m)
   static constexpr int NTF = 2 * kTauFrags;    // Tau diag(beta) fragments, hi then lo
-  static constexpr int VU = 2 * NW;            // 16-byte units per staged value row
+  static constexpr int NSV = TW < 8 ? TW : 8;  // state tiles a workgroup can hold (dv <= 128)
+  static constexpr int VU = 2 * NSV;           // 16-byte units per staged value row
   static constexpr int NVB = CH * VU / 64;     // value slab blocks
-  static constexpr int bKA = 0, bKT = NKA, bTF = bKT + NKT, bV = bTF + NTF, bQA = bV + NVB;
+  static constexpr int bKA = 0, bTF = NKA, bV = bTF + NTF, bQA = bV + NVB;
   static constexpr int NBLK = bQA + (WANT_O ? NKA : 0);
   static constexpr size_t BUF = (size_t)NBLK * 1024;
   static constexpr int GN = 3 * CH + 4;        // gate floats per buffer set
@@ -79,17 +83,57 @@ struct Cfg {
 // [128, 192) g, [192] e^{g_L}.
 constexpr int G_EG = 0, G_DEC = 64, G_G = 128, G_EGL = 192;
 
-// Unit swizzle of the staged value slab: 16-byte unit u of row r sits at
-// unit u ^ vswz(r), so that the 8 rows x 4 quads of a half-wave's
-// transposing read fall in distinct banks.
-template <int NW>
+// Unit swizzle of the staged value slab (VU 16-byte units per row): unit u
+// of row r sits at unit u ^ vswz(r), so that the 8 rows x 4 quads of a
+// half-wave's transposing read fall in distinct banks.
+template <int VU>
 __device__ __forceinline__ int vswz(int r) {
-  return NW == 8 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+  return VU == 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
 }
 
-template <int DK, bool WANT_O, int NW>
-__global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf16_kernel(ChainLaunch p, int n_items) {
-  using C = Cfg<DK, WANT_O, NW>;
+// K^T fragments of the state update S^T += K^T D' for token half m, all
+// NSB dk blocks d, read from the staged K A-fragments (fragment (bt, ks) at
+// (bt NKS + ks) KiB, lane (r & 15) + 16 ((c >> 3) & 3) holding key row r,
+// columns c .. c + 7 of its 32-column step) by the transposing LDS read:
+// fragment (d, m), lane (q, g) gets K[32 m + 4 g + e (+16)][32 (d >> 1) +
+// 8 (q >> 2) + 4 (d & 1) + (q & 3)], e < 4 -- the dk order of the S^T blocks
+// and the token order of the paired right-hand sides.  Inline assembly with
+// its own lgkmcnt wait: the transposing read carries no alias information,
+// and as a compiler builtin it would be made to wait for the load-to-LDS
+// copies of the next chunk that are in flight meanwhile.
+template <int NKS, int D>
+__device__ __forceinline__ void kt_pair(uint32_t addr, int m, bf16x8 &a0, bf16x8 &a1) {
+  // two dk blocks D, D + 1 of token half m: four 8-byte reads
+  constexpr int o0 = (D >> 1) * 1024 + 8 * (D & 1), o1 = ((D + 1) >> 1) * 1024 + 8 * ((D + 1) & 1);
+  uint2 r0, r1, r2, r3;
+  const uint32_t base = addr + (uint32_t)(2 * m * NKS * 1024);
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%c5\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%c6\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:%c7\n\t"
+      "ds_read_b64_tr_b16 %3, %4 offset:%c8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3)
+      : "v"(base), "i"(o0), "i"(o0 + NKS * 1024), "i"(o1), "i"(o1 + NKS * 1024));
+  a0 = cat_bf16x8(r0, r1);
+  a1 = cat_bf16x8(r2, r3);
+}
+template <int NKS, int NSB>
+__device__ __forceinline__ void kt_frags(int m, uint32_t addr, bf16x8 (&a)[NSB]) {
+  kt_pair<NKS, 0>(addr, m, a[0], a[1]);
+  kt_pair<NKS, 2>(addr, m, a[2], a[3]);
+  if constexpr (NSB > 4) {
+    kt_pair<NKS, 4>(addr, m, a[4], a[5]);
+    kt_pair<NKS, 6>(addr, m, a[6], a[7]);
+  }
+}
+
+template <int DK, bool WANT_O, int NW, int RT>
+__global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int n_items) {
+  static_assert(RT == 1 || RT == 2, "one or two row tiles per wave");
+  static_assert(!WANT_O || RT == 1, "outputs use one row tile per wave");
+  using C = Cfg<DK, WANT_O, NW, RT>;
+  constexpr int TW = C::TW;
   __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
   bf16 *sP = reinterpret_cast<bf16 *>(smem + C::oP);
   float *sG0 = reinterpret_cast<float *>(smem + C::oG);
@@ -100,7 +144,7 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
   if (item >= n_items) return;
   const int tilesA = p.tiles_T + p.tiles_S;
   const int tiles0 = p.skip_T0 ? p.tiles_S : tilesA;
-  const int grp0 = (tiles0 + NW - 1) / NW, grpA = (tilesA + NW - 1) / NW;
+  const int grp0 = (tiles0 + TW - 1) / TW, grpA = (tilesA + TW - 1) / TW;
   const int per_nh = grp0 + (p.n_segs - 1) * grpA;
   const int nh = item / per_nh;
   int rem = item % per_nh, seg = 0, grp = rem;
@@ -111,18 +155,23 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
   }
   const int n = nh / p.H, h = nh % p.H;
   const int H = p.H, DV = p.dv;
-  const int w = wave_id(), l = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
   const int g4 = l >> 4, jl = l & 15;
   const int tT = (seg == 0 && p.skip_T0) ? 0 : p.tiles_T;
-  const int tile = grp * NW + w;
+  // wave w owns row tiles tile .. tile + RT - 1, all of one kind (the
+  // launcher makes both tile counts multiples of RT)
+  const int tile = grp * TW + w * RT;
   const bool active = tile < tT + p.tiles_S;
   const bool is_T = active && tile < tT;
-  const int row0 = is_T ? 16 * tile : 16 * (tile - tT);
-  // tile counts are multiples of NW (launcher), so a workgroup holds either
-  // transition tiles only or state tiles only; state workgroups stage the
-  // value columns vcol0 .. vcol0 + 16 NW - 1
-  const bool grp_S = grp * NW >= tT;
-  const int vcol0 = 16 * (grp * NW - tT);
+  const int row0 = is_T ? 16 * tile : 16 * (tile - tT);  // first row; tile rt adds 16 rt
+  // state tiles of this workgroup: sfirst .. sfirst + nS - 1 (at most NSV;
+  // the launcher keeps transition and state tiles of a segment in one
+  // workgroup or makes tile counts multiples of NW); the workgroup stages
+  // the value columns vcol0 .. vcol0 + 16 nS - 1
+  const int s_lo = max(grp * TW, tT), s_hi = min(grp * TW + TW, tT + p.tiles_S);
+  const bool grp_S = s_hi > s_lo;
+  const int sfirst = s_lo - tT, nS = s_hi - s_lo;
+  const int vcol0 = 16 * sfirst;
 
   // ---- this segment's token range ----
   const int cbeg = p.cu[n], cend = p.cu[n + 1];
@@ -132,6 +181,11 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
   const int tend = (int)min((int64_t)cend, (int64_t)tbeg + seg_len);
   const int64_t slot0 = (int64_t)(cbeg / CH) + n + (tbeg - cbeg) / CH;
 
+  // LDS byte address (buffer set 0) of this lane's transposing reads of the
+  // staged keys: key row 4 g + (jl >> 2) of a 16-row block, 8-column group
+  // jl & 3 (see kt_frags)
+  const uint32_t kt_lds = (uint32_t)(uintptr_t)(lds_void *)(smem + C::bKA * 1024) +
+                          16u * (uint32_t)(4 * g4 + (jl >> 2) + 16 * (jl & 3));
   const bf16 *gk = reinterpret_cast<const bf16 *>(p.k);
   const bf16 *gq = reinterpret_cast<const bf16 *>(p.q);
   const bf16 *gv = reinterpret_cast<const bf16 *>(p.v);
@@ -139,44 +193,64 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
   const char *grec = reinterpret_cast<const char *>(p.tau);
 
   // ---- S^T in registers (dk order of the header comment) ----
-  f32x4 st[C::NSB];
+  f32x4 st[RT][C::NSB];
 #pragma unroll
-  for (int d = 0; d < C::NSB; ++d) {
-    const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1);
-    st[d] = zero4();
-    if (active) {
-      if (is_T) {
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st[d][e] = (row0 + jl == c0 + e) ? 1.f : 0.f;
-      } else if (p.S0 && seg == 0) {
-        st[d] = *reinterpret_cast<const f32x4 *>(p.S0 + (((int64_t)n * H + h) * DV + row0 + jl) * DK + c0);
+    for (int d = 0; d < C::NSB; ++d) {
+      const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1), r = row0 + 16 * rt + jl;
+      st[rt][d] = zero4();
+      if (active) {
+        if (is_T) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st[rt][d][e] = (r == c0 + e) ? 1.f : 0.f;
+        } else if (p.S0 && seg == 0) {
+          st[rt][d] = *reinterpret_cast<const f32x4 *>(p.S0 + (((int64_t)n * H + h) * DV + r) * DK + c0);
+        }
       }
     }
-  }
 
   // ---- DMA of one chunk's operands into buffer set b ----
   // Rows past the chunk are copies of its last row: they only meet zero
-  // coefficients (beta = 0 in the Tau columns, zero K^T rows from the prep
-  // kernel, masked M o Q K^T), so any finite value serves.
+  // coefficients (beta = 0 in the Tau columns, zero decayed corrections in
+  // the state update, masked M o Q K^T), so any finite value serves.
+  // Every wave issues whole 1 KiB blocks (one 16-byte copy per lane); the
+  // loops are unrolled over compile-time block ranges with the wave index
+  // uniform, so the issue is straight-line scalar-branch code.
+  const uint32_t tok_k = (uint32_t)H * DK * 2, tok_v = (uint32_t)H * DV * 2;  // bytes per token
   auto issue_dma = [&](int b, int t0, int Lc, int64_t slot) {
     char *buf = smem + b * C::BUF;
-    const char *rec = grec + (slot * H + h) * (int64_t)(kRecFloats * 4);
-    for (int i = w; i < C::NBLK; i += NW) {
-      lds_void *dst = (lds_void *)(buf + i * 1024);
-      if (i < C::bKT || (WANT_O && i >= C::bQA)) {   // K or Q A fragment (bt, m)
-        const int f = i < C::bKT ? i : i - C::bQA;
+    const int lm = Lc - 1;
+    const char *kb = reinterpret_cast<const char *>(gk + ((int64_t)t0 * H + h) * DK) + 16 * g4;
+    const char *qb = WANT_O ? reinterpret_cast<const char *>(gq + ((int64_t)t0 * H + h) * DK) + 16 * g4 : nullptr;
+    const char *rec = grec + (slot * H + h) * (int64_t)(kRecFloats * 4) + 16 * l;
+#pragma unroll
+    for (int j = 0; j < (C::NKA + NW - 1) / NW; ++j) {       // K (and Q) A fragments (bt, m)
+      const int f = j * NW + w;
+      if (C::NKA % NW == 0 || f < C::NKA) {
         const int bt = f / C::NKS, m = f % C::NKS;
-        const int r = min(16 * bt + jl, Lc - 1);
-        const bf16 *src = (i < C::bKT ? gk : gq) + ((int64_t)(t0 + r) * H + h) * DK + 32 * m + 8 * g4;
-        dma16_global(src, dst);
-      } else if (i < C::bTF) {                         // K^T fragments (record)
-        dma16_global(rec + kRecKtOffsetBytes + (i - C::bKT) * 1024 + 16 * l, dst);
-      } else if (i < C::bV) {                          // Tau diag(beta) fragments (record)
-        dma16_global(rec + (i - C::bTF) * 1024 + 16 * l, dst);
-      } else if (grp_S) {                              // value slab block
-        const int u_lds = (i - C::bV) * 64 + l;
-        const int r = u_lds / C::VU, u = (u_lds % C::VU) ^ vswz<NW>(r);
-        dma16_global(gv + ((int64_t)(t0 + min(r, Lc - 1)) * H + h) * DV + vcol0 + 8 * u, dst);
+        const uint32_t off = (uint32_t)min(16 * bt + jl, lm) * tok_k + 64 * m;
+        dma16_global(kb + off, (lds_void *)(buf + (C::bKA + f) * 1024));
+        if (WANT_O) dma16_global(qb + off, (lds_void *)(buf + (C::bQA + f) * 1024));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < (C::NTF + NW - 1) / NW; ++j) {         // Tau diag(beta) fragments (record)
+      const int f = j * NW + w;
+      if (C::NTF % NW == 0 || f < C::NTF) dma16_global(rec + f * 1024, (lds_void *)(buf + (C::bTF + f) * 1024));
+    }
+    if (grp_S) {                                               // value slab of the workgroup
+      const char *vb = reinterpret_cast<const char *>(gv + ((int64_t)t0 * H + h) * DV + vcol0);
+#pragma unroll
+      for (int j = 0; j < (C::NVB + NW - 1) / NW; ++j) {
+        const int f = j * NW + w;
+        if (C::NVB % NW == 0 || f < C::NVB) {
+          const int u_lds = f * 64 + l;
+          // logical unit u (8 columns) of row r; units past this
+          // workgroup's state columns re-read its last unit (never used)
+          const int r = u_lds / C::VU, u = min((u_lds % C::VU) ^ vswz<C::VU>(r), 2 * nS - 1);
+          dma16_global(vb + (uint32_t)min(r, lm) * tok_v + 16 * u, (lds_void *)(buf + (C::bV + f) * 1024));
+        }
       }
     }
   };
@@ -241,18 +315,21 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
   // under a partial or empty EXEC mask still writes its destination (the
   // data of a lane comes from other lanes' addresses).  Transition tiles,
   // whose workgroups stage no values, clear the result with a mask.
-  uint2 vt[4];
+  uint2 vt[RT][4];
   const uint32_t vmask = (active && !is_T) ? 0xffffffffu : 0u;
+  const int vtile = (active && !is_T) ? tile - tT - sfirst : 0;  // first staged state tile of the wave
   auto read_v = [&](int b) {
     const char *buf = smem + b * C::BUF;
 #pragma unroll
-    for (int bt = 0; bt < 4; ++bt) {
-      const int rr0 = 16 * bt + 4 * g4 + (jl >> 2);
-      const int u = 2 * (w & (NW - 1)) + ((jl & 3) >> 1);
-      const uint2 x = ds_read_tr16(reinterpret_cast<const bf16 *>(
-          buf + C::bV * 1024 + rr0 * (C::VU * 16) + 16 * (u ^ vswz<NW>(rr0)) + 8 * (jl & 1)));
-      vt[bt] = uint2{x.x & vmask, x.y & vmask};
-    }
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        const int rr0 = 16 * bt + 4 * g4 + (jl >> 2);
+        const int u = min(2 * (vtile + rt), C::VU - 2) + ((jl & 3) >> 1);
+        const uint2 x = ds_read_tr16(reinterpret_cast<const bf16 *>(
+            buf + C::bV * 1024 + rr0 * (C::VU * 16) + 16 * (u ^ vswz<C::VU>(rr0)) + 8 * (jl & 1)));
+        vt[rt][bt] = uint2{x.x & vmask, x.y & vmask};
+      }
   };
 
   if (tbeg < tend) {
@@ -274,19 +351,23 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
   f32x4 zp[4];
   int tp = 0, Lp = 0;
   auto store_o = [&]() {
+    const int64_t ob = ((int64_t)(tp + 4 * g4) * H + h) * DV + row0 + jl;
+    const int64_t tok = (int64_t)H * DV;
+    if (p.o_bf16) {
+      bf16 *o = reinterpret_cast<bf16 *>(p.o) + ob;
 #pragma unroll
-    for (int bt = 0; bt < 4; ++bt)
+      for (int bt = 0; bt < 4; ++bt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * bt + 4 * g4 + e;
-        if (r < Lp) {
-          const int64_t oi = ((int64_t)(tp + r) * H + h) * DV + row0 + jl;
-          if (p.o_bf16)
-            reinterpret_cast<bf16 *>(p.o)[oi] = (bf16)zp[bt][e];
-          else
-            reinterpret_cast<float *>(p.o)[oi] = zp[bt][e];
-        }
-      }
+        for (int e = 0; e < 4; ++e)
+          if (16 * bt + 4 * g4 + e < Lp) o[(16 * bt + e) * tok] = (bf16)zp[bt][e];
+    } else {
+      float *o = reinterpret_cast<float *>(p.o) + ob;
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (16 * bt + 4 * g4 + e < Lp) o[(16 * bt + e) * tok] = zp[bt][e];
+    }
     Lp = 0;
   };
 
@@ -308,82 +389,144 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
 
     if (active) {
       // ---- S^T as k = 32 B fragments ----
-      bf16x8 sh[C::NKS], sl[C::NKS];
+      bf16x8 sh[RT][C::NKS], sl[RT][C::NKS];
 #pragma unroll
-      for (int m = 0; m < C::NKS; ++m) b_frag_split(st[2 * m], st[2 * m + 1], sh[m], sl[m]);
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int m = 0; m < C::NKS; ++m) b_frag_split(st[rt][2 * m], st[rt][2 * m + 1], sh[rt][m], sl[rt][m]);
 
-      // ---- Y = K S^T ----
-      f32x4 y[4];
+      // ---- Y = K S^T (each K fragment read once for the wave's row tiles) ----
+      // A dependent MFMA (same accumulator) waits about three issue slots,
+      // so the hi and lo passes accumulate separately and every loop below
+      // rotates over at least four accumulators.
+      f32x4 y[RT][4];
+      {
+        f32x4 yl[RT][4];
 #pragma unroll
-      for (int bt = 0; bt < 4; ++bt) y[bt] = zero4();
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int m = 0; m < C::NKS; ++m)
+          for (int bt = 0; bt < 4; ++bt) y[rt][bt] = yl[rt][bt] = zero4();
 #pragma unroll
-        for (int bt = 0; bt < 4; ++bt) {
-          const bf16x8 a = frag(C::bKA + bt * C::NKS + m);
-          y[bt] = mfma_bf16(a, sh[m], y[bt]);
-          y[bt] = mfma_bf16(a, sl[m], y[bt]);
+        for (int m = 0; m < C::NKS; ++m) {
+          bf16x8 a[4];
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) a[bt] = frag(C::bKA + bt * C::NKS + m);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int bt = 0; bt < 4; ++bt) y[rt][bt] = mfma_bf16(a[bt], sh[rt][m], y[rt][bt]);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int bt = 0; bt < 4; ++bt) yl[rt][bt] = mfma_bf16(a[bt], sl[rt][m], yl[rt][bt]);
         }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) y[rt][bt] += yl[rt][bt];
+      }
 
       // ---- R = V - e^g Y  (beta is folded into the Tau fragments) ----
-      f32x4 rr[4];
+      bf16x8 rh[RT][2], rl[RT][2];
 #pragma unroll
-      for (int bt = 0; bt < 4; ++bt) {
-        const f32x4 eg = *reinterpret_cast<const f32x4 *>(sG + G_EG + 16 * bt + 4 * g4);
-        const float vv[4] = {__uint_as_float(vt[bt].x << 16), __uint_as_float(vt[bt].x & 0xffff0000u),
-                             __uint_as_float(vt[bt].y << 16), __uint_as_float(vt[bt].y & 0xffff0000u)};
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 rr[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rr[bt][e] = vv[e] - eg[e] * y[bt][e];
+        for (int bt = 0; bt < 4; ++bt) {
+          const f32x4 eg = *reinterpret_cast<const f32x4 *>(sG + G_EG + 16 * bt + 4 * g4);
+          const uint2 x = vt[rt][bt];
+          const float vv[4] = {__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                               __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rr[bt][e] = vv[e] - eg[e] * y[rt][bt][e];
+        }
+        b_frag_split(rr[0], rr[1], rh[rt][0], rl[rt][0]);
+        b_frag_split(rr[2], rr[3], rh[rt][1], rl[rt][1]);
       }
-      bf16x8 rh[2], rl[2];
-      b_frag_split(rr[0], rr[1], rh[0], rl[0]);
-      b_frag_split(rr[2], rr[3], rh[1], rl[1]);
 
       // ---- D = (Tau diag(beta)) R  (f: (bt, m) = (0,0),(1,0),(2,0),(2,1),(3,0),(3,1)) ----
-      f32x4 dd[4];
+      // fragments in the order 0, 2, 4, 1, 3, 5 (token blocks 0, 2, 3, 1, 2, 3)
+      // so that a block's two products are three issue slots apart; the
+      // hi-lo pass accumulates separately
+      f32x4 dd[RT][4];
+      {
+        f32x4 d2[RT][4];
 #pragma unroll
-      for (int bt = 0; bt < 4; ++bt) dd[bt] = zero4();
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int f = 0; f < kTauFrags; ++f) {
-        const int bt = f < 2 ? f : (f - 2) / 2 + 2;
-        const int m = f < 2 ? 0 : (f - 2) % 2;
-        const bf16x8 th = frag(C::bTF + f), tl = frag(C::bTF + kTauFrags + f);
-        dd[bt] = mfma_bf16(th, rh[m], dd[bt]);
-        dd[bt] = mfma_bf16(th, rl[m], dd[bt]);
-        dd[bt] = mfma_bf16(tl, rh[m], dd[bt]);
+          for (int bt = 0; bt < 4; ++bt) dd[rt][bt] = d2[rt][bt] = zero4();
+        constexpr int ford[kTauFrags] = {0, 2, 4, 1, 3, 5};
+        bf16x8 th[kTauFrags], tl[kTauFrags];
+#pragma unroll
+        for (int f = 0; f < kTauFrags; ++f) {
+          th[f] = frag(C::bTF + f);
+          tl[f] = frag(C::bTF + kTauFrags + f);
+        }
+#pragma unroll
+        for (int pass = 0; pass < 3; ++pass)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < kTauFrags; ++i) {
+              const int f = ford[i];
+              const int bt = f < 2 ? f : (f - 2) / 2 + 2;
+              const int m = f < 2 ? 0 : (f - 2) % 2;
+              if (pass == 0) dd[rt][bt] = mfma_bf16(th[f], rh[rt][m], dd[rt][bt]);
+              if (pass == 1) d2[rt][bt] = mfma_bf16(th[f], rl[rt][m], d2[rt][bt]);
+              if (pass == 2) dd[rt][bt] = mfma_bf16(tl[f], rh[rt][m], dd[rt][bt]);
+            }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) dd[rt][bt] += d2[rt][bt];
       }
 
-      // ---- O = e^g Q S^T + (M o Q K^T) D ----
+      // ---- O = e^g Q S^T + (M o Q K^T) D  (one row tile per wave) ----
       if (WANT_O) {
         bf16x8 dh[2], dl[2];
-        b_frag_split(dd[0], dd[1], dh[0], dl[0]);
-        b_frag_split(dd[2], dd[3], dh[1], dl[1]);
-        f32x4 z[4];
+        b_frag_split(dd[0][0], dd[0][1], dh[0], dl[0]);
+        b_frag_split(dd[0][2], dd[0][3], dh[1], dl[1]);
+        f32x4 z[4], z2[4];
 #pragma unroll
-        for (int bt = 0; bt < 4; ++bt) z[bt] = zero4();
+        for (int bt = 0; bt < 4; ++bt) z[bt] = z2[bt] = zero4();
 #pragma unroll
-        for (int m = 0; m < C::NKS; ++m)
+        for (int m = 0; m < C::NKS; ++m) {
+          bf16x8 a[4];
 #pragma unroll
-          for (int bt = 0; bt < 4; ++bt) {
-            const bf16x8 a = frag(C::bQA + bt * C::NKS + m);
-            z[bt] = mfma_bf16(a, sh[m], z[bt]);
-            z[bt] = mfma_bf16(a, sl[m], z[bt]);
-          }
+          for (int bt = 0; bt < 4; ++bt) a[bt] = frag(C::bQA + bt * C::NKS + m);
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) z[bt] = mfma_bf16(a[bt], sh[0][m], z[bt]);
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) z2[bt] = mfma_bf16(a[bt], sl[0][m], z2[bt]);
+        }
 #pragma unroll
         for (int bt = 0; bt < 4; ++bt) {
           const f32x4 eg = *reinterpret_cast<const f32x4 *>(sG + G_EG + 16 * bt + 4 * g4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) z[bt][e] *= eg[e];
+          for (int e = 0; e < 4; ++e) z[bt][e] = (z[bt][e] + z2[bt][e]) * eg[e];
+          z2[bt] = zero4();
         }
+        {
+          constexpr int ford[kTauFrags] = {0, 2, 4, 1, 3, 5};
+          bf16x8 ph[kTauFrags], pl[kTauFrags];
 #pragma unroll
-        for (int f = 0; f < kTauFrags; ++f) {
-          const int bt = f < 2 ? f : (f - 2) / 2 + 2;
-          const int m = f < 2 ? 0 : (f - 2) % 2;
-          const bf16x8 ph = *reinterpret_cast<const bf16x8 *>(sP + (f * 64 + l) * 8);
-          const bf16x8 pl = *reinterpret_cast<const bf16x8 *>(sP + kTauFragPlane + (f * 64 + l) * 8);
-          z[bt] = mfma_bf16(ph, dh[m], z[bt]);
-          z[bt] = mfma_bf16(ph, dl[m], z[bt]);
-          z[bt] = mfma_bf16(pl, dh[m], z[bt]);
+          for (int f = 0; f < kTauFrags; ++f) {
+            ph[f] = *reinterpret_cast<const bf16x8 *>(sP + (f * 64 + l) * 8);
+            pl[f] = *reinterpret_cast<const bf16x8 *>(sP + kTauFragPlane + (f * 64 + l) * 8);
+          }
+#pragma unroll
+          for (int pass = 0; pass < 3; ++pass)
+#pragma unroll
+            for (int i = 0; i < kTauFrags; ++i) {
+              const int f = ford[i];
+              const int bt = f < 2 ? f : (f - 2) / 2 + 2;
+              const int m = f < 2 ? 0 : (f - 2) % 2;
+              if (pass == 0) z[bt] = mfma_bf16(ph[f], dh[m], z[bt]);
+              if (pass == 1) z2[bt] = mfma_bf16(ph[f], dl[m], z2[bt]);
+              if (pass == 2) z[bt] = mfma_bf16(pl[f], dh[m], z[bt]);
+            }
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) z[bt] += z2[bt];
         }
 #pragma unroll
         for (int bt = 0; bt < 4; ++bt) zp[bt] = z[bt];
@@ -392,31 +535,41 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
       }
 
       // ---- S^T <- e^{g_L} S^T + K^T diag(e^{g_L - g}) D ----
-      bf16x8 eh[2], el[2];
-      {
+      bf16x8 eh[RT][2], el[RT][2];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
         f32x4 de[4];
 #pragma unroll
         for (int bt = 0; bt < 4; ++bt) {
           const f32x4 dec = *reinterpret_cast<const f32x4 *>(sG + G_DEC + 16 * bt + 4 * g4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) de[bt][e] = dd[bt][e] * dec[e];
+          for (int e = 0; e < 4; ++e) de[bt][e] = dd[rt][bt][e] * dec[e];
         }
-        b_frag_split(de[0], de[1], eh[0], el[0]);
-        b_frag_split(de[2], de[3], eh[1], el[1]);
+        b_frag_split(de[0], de[1], eh[rt][0], el[rt][0]);
+        b_frag_split(de[2], de[3], eh[rt][1], el[rt][1]);
       }
+      // K^T fragments of one token half m for all dk blocks, then the four
+      // (m, pass) sweeps over the dk blocks: each state block is touched
+      // once every NSB products
       const float gl = sG[G_EGL];
 #pragma unroll
-      for (int d = 0; d < C::NSB; ++d) {
-        f32x4 c = st[d];
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) c[e] *= gl;
+        for (int d = 0; d < C::NSB; ++d)
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const bf16x8 a = frag(C::bKT + 2 * d + m);
-          c = mfma_bf16(a, eh[m], c);
-          c = mfma_bf16(a, el[m], c);
-        }
-        st[d] = c;
+          for (int e = 0; e < 4; ++e) st[rt][d][e] *= gl;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        bf16x8 a[C::NSB];
+        kt_frags<C::NKS, C::NSB>(m, kt_lds + (uint32_t)(b * C::BUF), a);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int d = 0; d < C::NSB; ++d) st[rt][d] = mfma_bf16(a[d], eh[rt][m], st[rt][d]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int d = 0; d < C::NSB; ++d) st[rt][d] = mfma_bf16(a[d], el[rt][m], st[rt][d]);
       }
     }
 
@@ -436,43 +589,57 @@ __global__ void __launch_bounds__(NW * 64, (WANT_O || NW == 4) ? 1 : 1) chain_bf
   if (active) {
     const int64_t unit = ((int64_t)n * p.n_segs + seg) * H + h;
 #pragma unroll
-    for (int d = 0; d < C::NSB; ++d) {
-      const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1);
-      if (is_T) {
-        float *out = p.T_out + unit * DK * DK;
-        if (p.T_transposed) {
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) out[(int64_t)(c0 + e) * DK + row0 + jl] = st[d][e];
+      for (int d = 0; d < C::NSB; ++d) {
+        const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1), r = row0 + 16 * rt + jl;
+        if (is_T) {
+          float *out = p.T_out + unit * DK * DK;
+          if (p.T_transposed) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[(int64_t)(c0 + e) * DK + r] = st[rt][d][e];
+          } else {
+            *reinterpret_cast<f32x4 *>(out + (int64_t)r * DK + c0) = st[rt][d];
+          }
         } else {
-          *reinterpret_cast<f32x4 *>(out + (int64_t)(row0 + jl) * DK + c0) = st[d];
+          *reinterpret_cast<f32x4 *>(p.S_out + unit * DV * DK + (int64_t)r * DK + c0) = st[rt][d];
         }
-      } else {
-        *reinterpret_cast<f32x4 *>(p.S_out + unit * DV * DK + (int64_t)(row0 + jl) * DK + c0) = st[d];
       }
-    }
   }
 }
 
-template <int DK, bool WANT_O, int NW>
+template <int DK, bool WANT_O, int NW, int RT>
 hipError_t launch_b(const ChainLaunch &p, hipStream_t stream) {
+  constexpr int TW = NW * RT;
+  if (p.tiles_T % RT != 0 || p.tiles_S % RT != 0 || p.tiles_T > 8 || p.tiles_S > 8) return hipErrorInvalidValue;
   const int tilesA = p.tiles_T + p.tiles_S;
   const int tiles0 = p.skip_T0 ? p.tiles_S : tilesA;
-  const int64_t per_nh = (tiles0 + NW - 1) / NW + (int64_t)(p.n_segs - 1) * ((tilesA + NW - 1) / NW);
+  const int64_t per_nh = (tiles0 + TW - 1) / TW + (int64_t)(p.n_segs - 1) * ((tilesA + TW - 1) / TW);
   const int64_t items = (int64_t)p.n_seqs * p.H * per_nh;
   if (items <= 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((chain_bf16_kernel<DK, WANT_O, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, p,
+  hipLaunchKernelGGL((chain_bf16_kernel<DK, WANT_O, NW, RT>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, p,
                      (int)items);
   return hipGetLastError();
 }
 
 template <int DK>
 hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
-  // eight waves per workgroup when every tile count is a multiple of eight
-  // (the operands of a chunk are then shared by eight row tiles)
-  const bool eight = p.tiles_S % 8 == 0 && p.tiles_T % 8 == 0;
-  if (p.o) return launch_b<DK, true, 4>(p, stream);
-  return eight ? launch_b<DK, false, 8>(p, stream) : launch_b<DK, false, 4>(p, stream);
+  if (p.o) {
+    if (p.tiles_T != 0) return hipErrorInvalidValue;
+    return launch_b<DK, true, 4, 1>(p, stream);
+  }
+  // Transition and state tiles of a segment share one workgroup, two row
+  // tiles per wave: every fragment read from LDS then feeds two products,
+  // and one staged copy of the chunk operands serves all the tiles.
+  // State-only replays keep one row tile per wave (shorter chunk steps).
+  const int tilesA = p.tiles_T + p.tiles_S;
+  if (p.tiles_T > 0) {
+    if (tilesA <= 8) return launch_b<DK, false, 4, 2>(p, stream);
+    if (tilesA <= 16) return launch_b<DK, false, 8, 2>(p, stream);
+    return hipErrorInvalidValue;
+  }
+  return p.tiles_S % 8 == 0 ? launch_b<DK, false, 8, 1>(p, stream) : launch_b<DK, false, 4, 1>(p, stream);
 }
 
 }  // namespace

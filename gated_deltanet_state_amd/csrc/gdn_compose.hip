@@ -89,15 +89,25 @@ hipError_t launch_c(const ComposeLaunch &p, hipStream_t stream) {
 // straight from global memory, 8 consecutive floats per lane.  Workgroup =
 // 4 waves on 16 rows of one (sequence, head); wave w owns dk blocks
 // w * NOB .. w * NOB + NOB - 1 of S^T (C layout, natural dk order) and the
-// full S^T operand is exchanged through LDS once per step.
+// full S^T operand is exchanged through LDS once per step.  The operands of
+// step s + 1 (which do not depend on the running state) are loaded into
+// registers while step s computes.
 // ---------------------------------------------------------------------------
 constexpr int SNW = 4;
 
 template <int DK>
+struct SegOps {
+  static constexpr int NOB = DK / 16 / SNW;
+  static constexpr int NKS = DK / 32;
+  f32x4 t[NOB][NKS][2];  // rows 16 jb + (l & 15) of T^T, 8 floats per k = 32 step
+  f32x4 loc[NOB];        // S_seg rows
+};
+
+template <int DK>
 __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch p, int n_items) {
   constexpr int LDS_ = DK + 4;
-  constexpr int NOB = DK / 16 / SNW;  // owned 16-row blocks of S^T per wave
-  constexpr int NKS = DK / 32;
+  constexpr int NOB = SegOps<DK>::NOB;
+  constexpr int NKS = SegOps<DK>::NKS;
   __shared__ __attribute__((aligned(16))) float sS[16 * LDS_];
 
   const int per = (int)(gridDim.x >> 3);
@@ -107,15 +117,30 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
   const int nh = item / tiles, row0 = 16 * (item % tiles);
   const int n = nh / p.H, h = nh % p.H;
   const int H = p.H, DV = p.dv, P = p.n_segs;
-  const int w = wave_id(), l = lane_id(), g4 = l >> 4, jl = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), g4 = l >> 4, jl = l & 15;
 
   auto seg_state = [&](int s) { return p.S_seg + (((int64_t)n * P + s) * H + h) * DV * DK; };
+  auto load = [&](int s, SegOps<DK> &o) {
+    const float *Tt = p.Tt_seg + (((int64_t)n * P + s) * H + h) * DK * DK;
+    const float *Ls = seg_state(s);
+#pragma unroll
+    for (int i = 0; i < NOB; ++i) {
+      const int jb = w * NOB + i;
+      o.loc[i] = *reinterpret_cast<const f32x4 *>(Ls + (int64_t)(row0 + jl) * DK + 16 * jb + 4 * g4);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const float *a = Tt + (int64_t)(16 * jb + jl) * DK + 32 * ks + 8 * g4;
+        o.t[i][ks][0] = *reinterpret_cast<const f32x4 *>(a);
+        o.t[i][ks][1] = *reinterpret_cast<const f32x4 *>(a + 4);
+      }
+    }
+  };
   f32x4 acc[NOB];
 #pragma unroll
   for (int i = 0; i < NOB; ++i)
     acc[i] = *reinterpret_cast<const f32x4 *>(seg_state(0) + (int64_t)(row0 + jl) * DK + 16 * (w * NOB + i) + 4 * g4);
 
-  for (int s = 1; s < P; ++s) {
+  auto step = [&](const SegOps<DK> &o) {
 #pragma unroll
     for (int i = 0; i < NOB; ++i)
       *reinterpret_cast<f32x4 *>(sS + jl * LDS_ + 16 * (w * NOB + i) + 4 * g4) = acc[i];
@@ -127,24 +152,39 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
       const f32x4 x1 = *reinterpret_cast<const f32x4 *>(sS + jl * LDS_ + 32 * ks + 8 * g4 + 4);
       b_frag_split(x0, x1, bh[ks], bl[ks]);
     }
-    const float *Tt = p.Tt_seg + (((int64_t)n * P + s) * H + h) * DK * DK;
-    const float *Ls = seg_state(s);
+    // three accumulators per block (one per split pass), rotated so that no
+    // product waits on the one just issued
+    f32x4 c0[NOB], c1[NOB], c2[NOB];
 #pragma unroll
     for (int i = 0; i < NOB; ++i) {
-      const int jb = w * NOB + i;
-      f32x4 c = *reinterpret_cast<const f32x4 *>(Ls + (int64_t)(row0 + jl) * DK + 16 * jb + 4 * g4);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const float *a = Tt + (int64_t)(16 * jb + jl) * DK + 32 * ks + 8 * g4;
-        bf16x8 ah, al;
-        b_frag_split(*reinterpret_cast<const f32x4 *>(a), *reinterpret_cast<const f32x4 *>(a + 4), ah, al);
-        c = mfma_bf16(ah, bh[ks], c);
-        c = mfma_bf16(ah, bl[ks], c);
-        c = mfma_bf16(al, bh[ks], c);
-      }
-      acc[i] = c;
+      c0[i] = o.loc[i];
+      c1[i] = c2[i] = zero4();
     }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 ah[NOB], al[NOB];
+#pragma unroll
+      for (int i = 0; i < NOB; ++i) b_frag_split(o.t[i][ks][0], o.t[i][ks][1], ah[i], al[i]);
+#pragma unroll
+      for (int i = 0; i < NOB; ++i) c0[i] = mfma_bf16(ah[i], bh[ks], c0[i]);
+#pragma unroll
+      for (int i = 0; i < NOB; ++i) c1[i] = mfma_bf16(ah[i], bl[ks], c1[i]);
+#pragma unroll
+      for (int i = 0; i < NOB; ++i) c2[i] = mfma_bf16(al[i], bh[ks], c2[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NOB; ++i) acc[i] = c0[i] + c1[i] + c2[i];
     lds_barrier();
+  };
+
+  SegOps<DK> o0, o1;
+  if (P > 1) load(1, o0);
+  for (int s = 1; s < P; s += 2) {
+    if (s + 1 < P) load(s + 1, o1);
+    step(o0);
+    if (s + 1 >= P) break;
+    if (s + 2 < P) load(s + 2, o0);
+    step(o1);
   }
   float *out = p.S_out + ((int64_t)n * H + h) * DV * DK;
 #pragma unroll

@@ -12,17 +12,14 @@
 //
 // One workgroup (4 waves) per (chunk slot, head):
 //   1. keys of the chunk to LDS; cumulative log-gates by a wave-wide scan
-//   2. A = scaled K K^T on bf16 (or fp32) MFMA, 10 lower 16 x 16 blocks
+//   2. A = scaled K K^T on fp32 MFMA, 10 lower 16 x 16 blocks
 //   3. inverses of the four diagonal 16 x 16 blocks by forward substitution
 //      (one lane per column)
 //   4. off-diagonal blocks Tau_ij = -Tau_ii sum_{m=j}^{i-1} A_im Tau_mj; a
 //      block column depends only on the diagonal blocks and the blocks above
-//      it, so one wave per block column, in registers (split-bf16 products)
-// The result is written packed (lower block rows only) in fp32 for fp32
-// inputs.  For bf16 inputs the record holds what the recurrence kernel feeds
-// its k = 32 MFMAs, in their lane order (layout in gdn_internal.h), so that
-// it can copy the record straight into LDS: Tau diag(beta) as split-bf16 A
-// fragments, and K^T as the A fragments of its state update.
+//      it, so one wave per block column (fp32 MFMA)
+// The result is written packed (lower block rows only) in fp32.  This
+// kernel serves fp32 inputs; bf16 inputs have their own (gdn_prep_bf16.hip).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -89,7 +86,7 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
   const int t0 = tbeg + (int)j * kChunk;
   const int Lc = min(kChunk, len - (int)j * kChunk);
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  // output: fp32 packed Tau (fp32 inputs); bf16 inputs: fragments, below
+  // output: fp32 packed Tau
   float *out = p.tau + (slot * H + h) * (int64_t)kRecFloats;
   auto put = [&](int idx, float x) {
     if constexpr (!BF) out[idx] = x;
@@ -104,12 +101,8 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
       const int r = s / C::KSEG, seg = s % C::KSEG;
       f32x4 x = zero4();
       if (r < Lc) x = *reinterpret_cast<const f32x4 *>(gk + ((int64_t)(t0 + r) * H + h) * DK + seg * C::VEC);
-      if constexpr (BF) {
-        *reinterpret_cast<f32x4 *>(sK + r * C::LDK + seg * C::VEC) = x;
-      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sK[r * C::LDK + seg * 4 + e] = x[e];
-      }
+      for (int e = 0; e < 4; ++e) sK[r * C::LDK + seg * 4 + e] = x[e];
     }
   }
   if (w == 0) {
@@ -130,10 +123,7 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
     const int bi = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
     const int bj = t - (bi * (bi + 1)) / 2;
     f32x4 c = zero4();
-    if constexpr (BF)
-      mma_bf16<1, 1>(c, RowMajor<bf16>{sK, C::LDK}, RowMajor<bf16>{sK, C::LDK}, 16 * bi, 16 * bj, 0, DK);
-    else
-      mma_f32(c, RowMajor<float>{sK, C::LDK}, RowMajor<float>{sK, C::LDK}, 16 * bi, 16 * bj, 0, DK);
+    mma_f32(c, RowMajor<float>{sK, C::LDK}, RowMajor<float>{sK, C::LDK}, 16 * bi, 16 * bj, 0, DK);
     const int col = 16 * bj + (l & 15);
     const float gc = sG[col];
     const int row0 = 16 * bi + 4 * (l >> 4);
@@ -174,37 +164,7 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
   // ---- 4. off-diagonal blocks, one block column per wave ----
   if (w < 3) {
     const int jc = w;
-    if constexpr (BF) {
-      // a C-layout tile is its own B operand for the k = 16 MFMA
-      const int rA = l & 15, kq = 4 * (l >> 4);
-      f32x4 T[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) T[m] = zero4();
-#pragma unroll
-      for (int m = 0; m < 3; ++m)
-        if (m == jc) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) T[m][i] = sTau[(16 * m + kq + i) * C::LDC + 16 * m + rA];
-        }
-#pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        if (i <= jc) continue;
-        f32x4 X = zero4();
-#pragma unroll
-        for (int m = 0; m < 3; ++m) {
-          if (m < jc || m >= i) continue;
-          const f32x4 a = *reinterpret_cast<const f32x4 *>(sA + (16 * i + rA) * C::LDC + 16 * m + kq);
-          X = mma16_split3(a, T[m], X);
-        }
-        const f32x4 d = *reinterpret_cast<const f32x4 *>(sTau + (16 * i + rA) * C::LDC + 16 * i + kq);
-        f32x4 Y = mma16_split3(d, X, zero4());
-#pragma unroll
-        for (int q = 0; q < 4; ++q) Y[q] = -Y[q];
-        T[i] = Y;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sTau[(16 * i + kq + q) * C::LDC + 16 * jc + rA] = Y[q];
-      }
-    } else {
+    {
       float *xs = sX + w * 16 * C::LDX;
       for (int i = jc + 1; i < 4; ++i) {
         f32x4 X = zero4();
@@ -226,51 +186,6 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
     }
   }
 
-  // ---- 5. (bf16 inputs) Tau as split-bf16 MFMA A fragments ----
-  if constexpr (BF) {
-    lds_barrier();
-    bf16 *outh = reinterpret_cast<bf16 *>(out), *outl = outh + kTauFragPlane;
-    for (int s = tid; s < kTauFrags * 64; s += PNT) {
-      const int f = s >> 6, ln = s & 63;
-      const int bt = f < 2 ? f : (f - 2) / 2 + 2;
-      const int m = f < 2 ? 0 : (f - 2) % 2;
-      const int row = 16 * bt + (ln & 15);
-      float x[8];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int c0 = 32 * m + 16 * half + 4 * (ln >> 4);
-        const bool live = (c0 >> 4) <= bt;  // blocks right of the diagonal are zero
-        const f32x4 v = live ? *reinterpret_cast<const f32x4 *>(sTau + row * C::LDC + c0) : zero4();
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * half + e] = v[e];
-      }
-      // fold beta into the columns: Tau R = (Tau diag(beta)) (V - e^g Y)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const f32x4 bc = *reinterpret_cast<const f32x4 *>(sBeta + 32 * m + 16 * half + 4 * (ln >> 4));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * half + e] *= bc[e];
-      }
-      bf16x8 hi, lo;
-      split8(x, hi, lo);
-      *reinterpret_cast<bf16x8 *>(outh + 8 * s) = hi;
-      *reinterpret_cast<bf16x8 *>(outl + 8 * s) = lo;
-    }
-    // K^T fragments of the state update S^T += K^T D': fragment (d, mm), lane
-    // (q, g) holds K[32 mm + 4 g + e (+16)][32 (d >> 1) + 8 (q >> 2) + 4 (d & 1) + (q & 3)],
-    // e < 4: the row order of the recurrence kernel's S^T blocks and the
-    // token order of its paired C-layout right-hand sides
-    bf16 *kt = reinterpret_cast<bf16 *>(reinterpret_cast<char *>(out) + kRecKtOffsetBytes);
-    for (int s = tid; s < 2 * (DK / 16) * 64; s += PNT) {
-      const int j = s >> 6, ln = s & 63;
-      const int d = j >> 1, mm = j & 1, q = ln & 15, g = ln >> 4;
-      const int col = 32 * (d >> 1) + 8 * (q >> 2) + 4 * (d & 1) + (q & 3);
-      bf16x8 v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = sK[(32 * mm + 4 * g + (e & 3) + 16 * (e >> 2)) * C::LDK + col];
-      *reinterpret_cast<bf16x8 *>(kt + 8 * s) = v;
-    }
-  }
 }
 
 template <class Tin, int DK>

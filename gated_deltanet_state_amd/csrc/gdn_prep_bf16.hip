@@ -9,20 +9,18 @@
 // Tau = (I + A)^{-1} is built here once per (chunk, head), fully in
 // parallel, for every row tile of the recurrence kernel.
 //
-// One workgroup (4 waves) per (chunk slot, head):
+// One wave per (chunk slot, head), no workgroup barriers (a workgroup is a
+// single wave with its own LDS):
 //   1. keys to LDS by load-to-LDS DMA, in MFMA A-fragment order; cumulative
 //      log-gates by a wave-wide scan
-//   2. the 10 lower 16 x 16 blocks of A on bf16 MFMA (keys are exact in bf16)
-//   3. wave b inverts diagonal block b by forward substitution, one lane per
-//      column, from registers
-//   4. off-diagonal blocks Tau_ij = -Tau_ii sum_{m=j}^{i-1} A_im Tau_mj, one
-//      block column per wave, on split-bf16 k = 16 MFMAs in registers
-//   5. the record of gdn_internal.h: Tau diag(beta) as split-bf16 A fragments
-//      of the recurrence kernel's k = 32 products, and K^T as the A fragments
-//      of its state update (zero past the chunk), read from the staged keys
-//      with the transposing LDS read.
-// A and Tau live in LDS as packed 16 x 16 blocks (row pitch 20 floats), which
-// keeps the workgroup at about 36 KiB (four per compute unit).
+//   2. the 10 lower 16 x 16 blocks of A on bf16 MFMA (keys are exact in
+//      bf16), ten independent accumulators
+//   3. the four diagonal blocks inverted at once by forward substitution:
+//      lane (b, c) = (l >> 4, l & 15) computes column c of (I + A_bb)^{-1}
+//   4. off-diagonal blocks Tau_ij = -Tau_ii sum_{m=j}^{i-1} A_im Tau_mj on
+//      split-bf16 k = 16 MFMAs, in three dependency levels
+//   5. Tau diag(beta) as split-bf16 A fragments of the recurrence kernel's
+//      k = 32 products (record layout of gdn_internal.h).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -30,23 +28,7 @@ namespace gdn {
 
 namespace {
 
-constexpr int PW = 4;
-constexpr int PT = PW * 64;
-constexpr int LDB = 20;            // row pitch of a packed 16 x 16 block (floats)
-constexpr int BLK = 16 * LDB;      // floats per packed block
-
 __device__ __forceinline__ int blk(int i, int j) { return i * (i + 1) / 2 + j; }  // i >= j
-
-template <int DK>
-struct PB {
-  static constexpr int NKS = DK / 32;
-  static constexpr int NKA = 4 * NKS;               // 1 KiB key fragments (bt, m)
-  static constexpr size_t oK = 0;
-  static constexpr size_t oA = oK + NKA * 1024;
-  static constexpr size_t oT = oA + 10 * BLK * 4;
-  static constexpr size_t oG = oT + 10 * BLK * 4;
-  static constexpr size_t TOTAL = oG + 2 * 64 * 4;
-};
 
 // Largest n in [0, n_seqs) whose first chunk slot floor(cu[n]/64) + n is <= slot.
 __device__ __forceinline__ int find_seq_b(const int32_t *cu, int n_seqs, int64_t slot) {
@@ -61,23 +43,34 @@ __device__ __forceinline__ int find_seq_b(const int32_t *cu, int n_seqs, int64_t
   return lo;
 }
 
-// Byte offset of key row r, columns c .. c + 3 (c a multiple of 4) in the
-// fragment-ordered key buffer: fragment (r >> 4, c >> 5), lane
-// (r & 15) + 16 ((c >> 3) & 3), half (c >> 2) & 1.
-template <int DK>
-__device__ __forceinline__ int kfrag_off(int r, int c) {
-  return (((r >> 4) * PB<DK>::NKS + (c >> 5)) * 64 + (r & 15) + 16 * ((c >> 3) & 3)) * 16 + 8 * ((c >> 2) & 1);
+// x (4 fp32 in A layout) times y (4 fp32 in B layout), k = 16, as split bf16
+// with the three partial products in separate accumulators (no product
+// waits on the one before it).
+struct Acc3 {
+  f32x4 a, b, c;
+};
+__device__ __forceinline__ void acc_split3(Acc3 &acc, const f32x4 &x, const f32x4 &y) {
+  bf16x4 xh, xl, yh, yl;
+  split4(x, xh, xl);
+  split4(y, yh, yl);
+  acc.a = mfma_bf16_k16(xh, yh, acc.a);
+  acc.b = mfma_bf16_k16(xh, yl, acc.b);
+  acc.c = mfma_bf16_k16(xl, yh, acc.c);
 }
+__device__ __forceinline__ Acc3 acc3_zero() { return Acc3{zero4(), zero4(), zero4()}; }
+__device__ __forceinline__ f32x4 acc3_sum(const Acc3 &a) { return a.a + a.b + a.c; }
 
 template <int DK>
-__global__ void __launch_bounds__(PT) prep_bf16_kernel(PrepLaunch p) {
-  using C = PB<DK>;
-  __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
-  char *sK = smem + C::oK;
-  float *sA = reinterpret_cast<float *>(smem + C::oA);
-  float *sT = reinterpret_cast<float *>(smem + C::oT);
-  float *sG = reinterpret_cast<float *>(smem + C::oG);
-  float *sB = sG + 64;
+__global__ void __launch_bounds__(64) prep_bf16_kernel(PrepLaunch p) {
+  constexpr int NKS = DK / 32;
+  constexpr int NKA = 4 * NKS;                     // 1 KiB key fragments (bt, m)
+  // sK: keys, then (once the keys are no longer read) the row-major Tau
+  // blocks (10 KiB) and the transposed diagonal blocks (4 KiB)
+  __shared__ __attribute__((aligned(16))) char sK[NKA * 1024 > 14336 ? NKA * 1024 : 14336];
+  __shared__ __attribute__((aligned(16))) float sA[10 * 256];  // A blocks, 16 x 16 row-major
+  __shared__ __attribute__((aligned(16))) float sG[64], sB[64];
+  float *sT = reinterpret_cast<float *>(sK);       // Tau blocks, row-major, block blk(i, j)
+  float *sTT = sT + 10 * 256;                      // Tau_bb transposed, block b
 
   const int64_t slot = blockIdx.x;
   const int h = blockIdx.y, H = p.H;
@@ -87,67 +80,75 @@ __global__ void __launch_bounds__(PT) prep_bf16_kernel(PrepLaunch p) {
   if (j < 0 || j * kChunk >= len) return;  // slot past the end of its sequence
   const int t0 = tbeg + (int)j * kChunk;
   const int Lc = min(kChunk, len - (int)j * kChunk);
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  const int g4 = l >> 4, jl = l & 15;
+  const int l = lane_id(), g4 = l >> 4, jl = l & 15;
   char *rec = reinterpret_cast<char *>(p.tau + (slot * H + h) * (int64_t)kRecFloats);
 
-  // ---- 1. keys (rows past the chunk: copies of its last row; they only meet
+  // ---- 1. keys (rows past the chunk: copies of its last row; they meet
   // beta = 0 below) and gates ----
   const bf16 *gk = reinterpret_cast<const bf16 *>(p.k);
-  for (int f = w; f < C::NKA; f += PW) {
-    const int bt = f / C::NKS, m = f % C::NKS;
+#pragma unroll
+  for (int f = 0; f < NKA; ++f) {
+    const int bt = f / NKS, m = f % NKS;
     const int r = min(16 * bt + jl, Lc - 1);
     dma16_global(gk + ((int64_t)(t0 + r) * H + h) * DK + 32 * m + 8 * g4, (lds_void *)(sK + f * 1024));
   }
-  if (w == 0) {
+  {
     float g = 0.f, b = 0.f;
     if (l < Lc) {
       const int64_t gi = (int64_t)(t0 + l) * H + h;
       g = logf((float)reinterpret_cast<const bf16 *>(p.alpha)[gi]);
       b = (float)reinterpret_cast<const bf16 *>(p.beta)[gi];
     }
-    g = wave_inclusive_scan(g);
-    sG[l] = g;
+    sG[l] = wave_inclusive_scan(g);
     sB[l] = b;
   }
   wait_vmem();
-  lds_barrier();
+  wave_lds_fence();
 
-  // ---- 2. A = strictly-lower beta_r e^{g_r - g_s} K K^T, packed blocks ----
-  for (int t = w; t < 10; t += PW) {
-    const int bi = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
-    const int bj = t - (bi * (bi + 1)) / 2;
-    bf16x8 a[C::NKS], bb[C::NKS];
-#pragma unroll
-    for (int m = 0; m < C::NKS; ++m) {
-      a[m] = *reinterpret_cast<const bf16x8 *>(sK + (bi * C::NKS + m) * 1024 + 16 * l);
-      bb[m] = *reinterpret_cast<const bf16x8 *>(sK + (bj * C::NKS + m) * 1024 + 16 * l);
-    }
-    f32x4 c = zero4();
-#pragma unroll
-    for (int m = 0; m < C::NKS; ++m) c = mfma_bf16(a[m], bb[m], c);
-    const int col = 16 * bj + jl;
-    const float gc = sG[col];
-    const int row0 = 16 * bi + 4 * g4;
-    const f32x4 gr = *reinterpret_cast<const f32x4 *>(sG + row0);
-    const f32x4 br = *reinterpret_cast<const f32x4 *>(sB + row0);
-    float *dst = sA + blk(bi, bj) * BLK + 4 * g4 * LDB + jl;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e * LDB] = (col < row0 + e) ? br[e] * __expf(gr[e] - gc) * c[e] : 0.f;
-  }
-  lds_barrier();
-
-  // ---- 3. diagonal blocks: wave b solves (I + A_bb) x = e_jj, lane jj ----
+  // ---- 2. A = strictly-lower beta_r e^{g_r - g_s} K K^T, 10 blocks ----
   {
-    const int b = w;
-    const float *ab = sA + blk(b, b) * BLK;
+    f32x4 acc[10];
+#pragma unroll
+    for (int t = 0; t < 10; ++t) acc[t] = zero4();
+#pragma unroll
+    for (int m = 0; m < NKS; ++m) {
+      bf16x8 kf[4];
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) kf[bt] = *reinterpret_cast<const bf16x8 *>(sK + (bt * NKS + m) * 1024 + 16 * l);
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int bj = 0; bj <= bi; ++bj) acc[blk(bi, bj)] = mfma_bf16(kf[bi], kf[bj], acc[blk(bi, bj)]);
+    }
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int bj = 0; bj <= bi; ++bj) {
+        const int col = 16 * bj + jl, row0 = 16 * bi + 4 * g4;
+        const float gc = sG[col];
+        const f32x4 gr = *reinterpret_cast<const f32x4 *>(sG + row0);
+        const f32x4 br = *reinterpret_cast<const f32x4 *>(sB + row0);
+        float *dst = sA + blk(bi, bj) * 256 + 4 * g4 * 16 + jl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dst[e * 16] = (col < row0 + e) ? br[e] * __expf(gr[e] - gc) * acc[blk(bi, bj)][e] : 0.f;
+      }
+  }
+  // the key buffer is reused for Tau from here on (this wave's key reads
+  // above were consumed by the products before these writes)
+  wave_lds_fence();
+
+  // ---- 3. diagonal blocks: lane (b, c) solves (I + A_bb) x = e_c ----
+  {
+    const int b = g4, c = jl;
+    const float *ab = sA + blk(b, b) * 256;
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float acc0 = (r == jl) ? 1.f : 0.f, acc1 = 0.f;
+      float acc0 = (r == c) ? 1.f : 0.f, acc1 = 0.f;
 #pragma unroll
       for (int s4 = 0; s4 < (r + 3) / 4; ++s4) {
-        const f32x4 ar = *reinterpret_cast<const f32x4 *>(ab + r * LDB + 4 * s4);
+        const f32x4 ar = *reinterpret_cast<const f32x4 *>(ab + r * 16 + 4 * s4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int s = 4 * s4 + e;
@@ -161,107 +162,90 @@ __global__ void __launch_bounds__(PT) prep_bf16_kernel(PrepLaunch p) {
       }
       x[r] = acc0 + acc1;
     }
-    if (l < 16) {
-      float *tb = sT + blk(b, b) * BLK + jl;
+    float *tr = sT + blk(b, b) * 256 + c;           // row-major: Tau_bb[r][c]
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tb[r * LDB] = x[r];
-    }
+    for (int r = 0; r < 16; ++r) tr[r * 16] = x[r];
+    float *tt = sTT + b * 256 + c * 16;             // transposed: row c holds column c
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) *reinterpret_cast<f32x4 *>(tt + 4 * r4) = f32x4{x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]};
   }
-  lds_barrier();
+  wave_lds_fence();
 
-  // ---- 4. off-diagonal blocks, block column jc = w (a C-layout 16 x 16 tile
-  // is its own B operand for the k = 16 MFMA; A operands read by rows) ----
-  if (w < 3) {
-    const int jc = w;
-    f32x4 T[4], AL[4][3], TD[4];
+  // ---- 4. off-diagonal blocks (C layout: lane column jl, rows 4 g4 + e) ----
+  {
+    // operands: A_im and Tau_ii in A layout (row jl, columns 4 g4 ..), Tau_jj
+    // in B layout (column jl, rows 4 g4 ..) from the transposed copy
+    auto Aop = [&](int i, int m) { return *reinterpret_cast<const f32x4 *>(sA + blk(i, m) * 256 + jl * 16 + 4 * g4); };
+    auto Tii = [&](int i) { return *reinterpret_cast<const f32x4 *>(sT + blk(i, i) * 256 + jl * 16 + 4 * g4); };
+    auto Tjj = [&](int i) { return *reinterpret_cast<const f32x4 *>(sTT + i * 256 + jl * 16 + 4 * g4); };
+    auto neg_tau = [&](int i, const Acc3 &x) {       // -Tau_ii X
+      Acc3 y = acc3_zero();
+      acc_split3(y, Tii(i), acc3_sum(x));
+      return -acc3_sum(y);
+    };
+    const f32x4 T00 = Tjj(0), T11 = Tjj(1), T22 = Tjj(2);
+    // level 1: Tau_10, Tau_21, Tau_32
+    Acc3 x10 = acc3_zero(), x21 = acc3_zero(), x32 = acc3_zero();
+    acc_split3(x10, Aop(1, 0), T00);
+    acc_split3(x21, Aop(2, 1), T11);
+    acc_split3(x32, Aop(3, 2), T22);
+    const f32x4 T10 = neg_tau(1, x10), T21 = neg_tau(2, x21), T32 = neg_tau(3, x32);
+    // level 2: Tau_20, Tau_31
+    Acc3 x20 = acc3_zero(), x31 = acc3_zero();
+    acc_split3(x20, Aop(2, 0), T00);
+    acc_split3(x31, Aop(3, 1), T11);
+    acc_split3(x20, Aop(2, 1), T10);
+    acc_split3(x31, Aop(3, 2), T21);
+    const f32x4 T20 = neg_tau(2, x20), T31 = neg_tau(3, x31);
+    // level 3: Tau_30
+    Acc3 x30 = acc3_zero();
+    acc_split3(x30, Aop(3, 0), T00);
+    acc_split3(x30, Aop(3, 1), T10);
+    acc_split3(x30, Aop(3, 2), T20);
+    const f32x4 T30 = neg_tau(3, x30);
+    auto put = [&](int i, int jb, const f32x4 &t) {
+      float *dst = sT + blk(i, jb) * 256 + 4 * g4 * 16 + jl;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      T[i] = zero4();
-      TD[i] = zero4();
-#pragma unroll
-      for (int m = 0; m < 3; ++m) AL[i][m] = zero4();
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) T[jc][e] = sT[blk(jc, jc) * BLK + (4 * g4 + e) * LDB + jl];
-#pragma unroll
-    for (int i = 1; i < 4; ++i) {
-      if (i <= jc) continue;
-      TD[i] = *reinterpret_cast<const f32x4 *>(sT + blk(i, i) * BLK + jl * LDB + 4 * g4);
-#pragma unroll
-      for (int m = 0; m < 3; ++m)
-        if (m >= jc && m < i) AL[i][m] = *reinterpret_cast<const f32x4 *>(sA + blk(i, m) * BLK + jl * LDB + 4 * g4);
-    }
-#pragma unroll
-    for (int i = 1; i < 4; ++i) {
-      if (i <= jc) continue;
-      f32x4 X = zero4();
-#pragma unroll
-      for (int m = 0; m < 3; ++m)
-        if (m >= jc && m < i) X = mma16_split3(AL[i][m], T[m], X);
-      f32x4 Y = mma16_split3(TD[i], X, zero4());
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Y[e] = -Y[e];
-      T[i] = Y;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sT[blk(i, jc) * BLK + (4 * g4 + e) * LDB + jl] = Y[e];
-    }
+      for (int e = 0; e < 4; ++e) dst[e * 16] = t[e];
+    };
+    put(1, 0, T10);
+    put(2, 1, T21);
+    put(3, 2, T32);
+    put(2, 0, T20);
+    put(3, 1, T31);
+    put(3, 0, T30);
   }
-  lds_barrier();
+  wave_lds_fence();
 
-  // ---- 5a. Tau diag(beta) as split-bf16 A fragments ----
+  // ---- 5. Tau diag(beta) as split-bf16 A fragments: fragment f = (bt, m),
+  // lane (r, g) = (l & 15, l >> 4) holds row 16 bt + r, columns
+  // 32 m + 4 g + {0..3} then 32 m + 16 + 4 g + {0..3} ----
   bf16 *outh = reinterpret_cast<bf16 *>(rec), *outl = outh + kTauFragPlane;
-  for (int s = tid; s < kTauFrags * 64; s += PT) {
-    const int f = s >> 6, ln = s & 63;
+#pragma unroll
+  for (int f = 0; f < kTauFrags; ++f) {
     const int bt = f < 2 ? f : (f - 2) / 2 + 2;
     const int m = f < 2 ? 0 : (f - 2) % 2;
-    const int r = ln & 15;
     float x[8];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int c0 = 32 * m + 16 * half + 4 * (ln >> 4);
-      const int cb = c0 >> 4;
+      const int cb = 2 * m + half, c0 = 16 * cb + 4 * g4;
       f32x4 v = zero4();
-      if (cb <= bt) v = *reinterpret_cast<const f32x4 *>(sT + blk(bt, cb) * BLK + r * LDB + (c0 & 15));
+      if (cb <= bt) v = *reinterpret_cast<const f32x4 *>(sT + blk(bt, cb) * 256 + jl * 16 + 4 * g4);
       const f32x4 bc = *reinterpret_cast<const f32x4 *>(sB + c0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[4 * half + e] = v[e] * bc[e];
     }
     bf16x8 hi, lo;
     split8(x, hi, lo);
-    *reinterpret_cast<bf16x8 *>(outh + 8 * s) = hi;
-    *reinterpret_cast<bf16x8 *>(outl + 8 * s) = lo;
-  }
-
-  // ---- 5b. K^T fragments of the state update S^T += K^T D': fragment (d, mm),
-  // lane (q, g) holds K[32 mm + 4 g + e (+16)][32 (d >> 1) + 8 (q >> 2) + 4 (d & 1) + (q & 3)]
-  // for e < 4, zero past the chunk; each wave handles whole fragments, so the
-  // transposing read sees the lanes of one fragment ----
-  uint4 *kt = reinterpret_cast<uint4 *>(rec + kRecKtOffsetBytes);
-  for (int jf = w; jf < 2 * (DK / 16); jf += PW) {
-    const int d = jf >> 1, mm = jf & 1;
-    const int row = 32 * mm + 4 * g4 + (jl >> 2);
-    const int col = 32 * (d >> 1) + 8 * (jl & 3) + 4 * (d & 1);
-    uint2 lo4 = ds_read_tr16(reinterpret_cast<const bf16 *>(sK + kfrag_off<DK>(row, col)));
-    uint2 hi4 = ds_read_tr16(reinterpret_cast<const bf16 *>(sK + kfrag_off<DK>(row + 16, col)));
-    const int tk = 32 * mm + 4 * g4;  // tokens tk + e and tk + 16 + e
-    unsigned m0 = 0, m1 = 0;          // keep masks for the packed bf16 pairs
-    auto keep = [&](int t) { return t < Lc ? 0xffffu : 0u; };
-    m0 = keep(tk) | (keep(tk + 1) << 16);
-    m1 = keep(tk + 2) | (keep(tk + 3) << 16);
-    lo4.x &= m0;
-    lo4.y &= m1;
-    m0 = keep(tk + 16) | (keep(tk + 17) << 16);
-    m1 = keep(tk + 18) | (keep(tk + 19) << 16);
-    hi4.x &= m0;
-    hi4.y &= m1;
-    kt[jf * 64 + l] = uint4{lo4.x, lo4.y, hi4.x, hi4.y};
+    *reinterpret_cast<bf16x8 *>(outh + 8 * (f * 64 + l)) = hi;
+    *reinterpret_cast<bf16x8 *>(outl + 8 * (f * 64 + l)) = lo;
   }
 }
 
 template <int DK>
 hipError_t launch_pb(const PrepLaunch &p, hipStream_t stream) {
   if (p.n_slots <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prep_bf16_kernel<DK>), dim3((unsigned)p.n_slots, (unsigned)p.H), dim3(PT), 0, stream, p);
+  hipLaunchKernelGGL((prep_bf16_kernel<DK>), dim3((unsigned)p.n_slots, (unsigned)p.H), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 

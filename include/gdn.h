@@ -75,7 +75,7 @@ typedef void *gdn_stream_t;
  *          gdn_replay_workspace_bytes(...) bytes (may be NULL if that is 0)
  *
  * Supported: dk, dv in {64, 128}; in_dtype F32 or BF16 (q, k, v, alpha,
- * beta all of it); o_dtype F32 or BF16; n_seqs >= 1; n_heads >= 1.
+ * beta all of it); o_dtype F32 or BF16; n_seqs >= 1; 1 <= n_heads <= 65536.
  * Deterministic: equal inputs give bitwise-equal outputs.
  */
 gdn_status gdn_replay(const void *q, const void *k, const void *v,
@@ -104,6 +104,7 @@ size_t gdn_replay_workspace_bytes(int32_t n_seqs, int64_t n_tokens,
  *   S_local [n_chunks, H, dv, dk] fp32 out
  *   v and S_local may both be NULL: only T_C is built (T_C needs only the
  *   key / gate stream).
+ * Supported: dk, dv in {64, 128}; in_dtype F32 or BF16; 1 <= n_heads <= 65536.
  */
 gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha,
                               const void *beta, const int32_t *cu_chunks,

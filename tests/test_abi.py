@@ -64,6 +64,7 @@ def test_replay_argument_checks(lib):
     assert replay(lib, dt=7) == UNSUP
     assert replay(lib, odt=9) == UNSUP
     assert replay(lib, T=1 << 31) == UNSUP
+    assert replay(lib, H=65537) == UNSUP            # in-chunk offsets are 32-bit
     assert replay(lib, k=P + 2) == ALIGN
     assert b"k is not 16-byte aligned" in lib.gdn_last_error()
     assert replay(lib, S0=P + 8) == ALIGN
@@ -78,6 +79,7 @@ def test_chunk_operator_argument_checks(lib):
     assert co(SL=None) == NULLP
     assert co(C=-1) == SHAPE
     assert co(dk=100) == UNSUP
+    assert co(H=65537) == UNSUP
     assert co(b=P + 2) == ALIGN
     assert co(C=0) == OK                            # nothing to do, nothing launched
 
@@ -93,11 +95,11 @@ def test_compose_argument_checks(lib):
 
 
 def test_workspace_queries(lib, monkeypatch):
-    # one 28 KiB record of per-chunk factors ((I + A)^{-1} and K^T fragments) per chunk slot
+    # one 12 KiB record of per-chunk factors ((I + A)^{-1} diag(beta) fragments) per chunk slot
     # and head; slots = n_tokens / 64 + n_seqs + 1 (sequence n's chunk j sits
     # in slot floor(cu[n] / 64) + n + j)
     monkeypatch.delenv("GDN_REPLAY_SEGMENTS", raising=False)
-    tau = lambda n_seqs, n_tokens, H: (n_tokens // 64 + n_seqs + 1) * H * 28672
+    tau = lambda n_seqs, n_tokens, H: (n_tokens // 64 + n_seqs + 1) * H * 12288
     # 16 sequences x 32 heads already fill the chip: no time split
     assert lib.gdn_replay_workspace_bytes(16, 30000, 32, 128, 128) == tau(16, 30000, 32)
     assert lib.gdn_chunk_operator_workspace_bytes(64, 32768, 32, 128, 128) == tau(64, 32768, 32)

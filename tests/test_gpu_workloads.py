@@ -53,10 +53,15 @@ def test_full_size_with_outputs_sampled_heads(wid, heads):
     eS = rel(to_np(S[:, heads]), S_ref)
     print("workload %d heads %s err_o %.3e err_S %.3e" % (wid, heads, eo, eS), flush=True)
     assert eo <= 3e-3 and eS <= 3e-3
-    # every head's outputs are finite and the state path matches state-only
+    # every head's outputs are finite; the state-only replay (which may run
+    # time-split and composed, rounding differently) meets the same bar and
+    # stays within twice the bar's noise of the replay with outputs
     assert bool(o.isfinite().all())
     _, S2 = replay_all(inp, want_o=False)
-    assert bool((S2 == S).all())
+    eS2 = rel(to_np(S2[:, heads]), S_ref)
+    d = rel(to_np(S2), to_np(S).astype(np.float64))
+    print("state-only err_S %.3e, |S_state_only - S_with_o| / |S| %.3e" % (eS2, d), flush=True)
+    assert eS2 <= 3e-3 and d <= 1e-4
 
 
 def test_workload4_chunk_operators_and_composition():
