@@ -160,7 +160,10 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   pp.in_bf16 = in_dtype == GDN_BF16;
   pp.tau = static_cast<float *>(workspace);
   pp.n_slots = gdn::slot_count(n_tokens, n_seqs);
-  if ((s = launched(gdn::launch_prep(pp, st), "gdn_replay prep launch"))) return s;
+  // bf16 time-split replays build the per-chunk records inside the segment
+  // kernel; everything else runs the stand-alone prep kernel first
+  const bool fuse = bf && P > 1;
+  if (!fuse && (s = launched(gdn::launch_prep(pp, st), "gdn_replay prep launch"))) return s;
   gdn::ChainLaunch p{};
   p.tau = pp.tau;
   p.q = o ? q : nullptr;
@@ -189,6 +192,7 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   float *Tseg = reinterpret_cast<float *>(static_cast<char *>(workspace) + tau_bytes);
   float *Sseg = Tseg + (size_t)n_seqs * P * n_heads * dk * dk;
   p.n_segs = P;
+  p.fuse_prep = 1;
   p.skip_T0 = 1;
   p.T_transposed = 1;
   p.tiles_T = dk / 16;
@@ -247,7 +251,10 @@ gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, c
   pp.in_bf16 = in_dtype == GDN_BF16;
   pp.tau = static_cast<float *>(workspace);
   pp.n_slots = gdn::slot_count(n_tokens, n_chunks);
-  if ((s = launched(gdn::launch_prep(pp, st), "gdn_chunk_operator prep launch"))) return s;
+  // bf16: each chunk's workgroup builds the records of its own 64-token
+  // sub-chunks first (no separate prep launch)
+  const bool fuse = in_dtype == GDN_BF16;
+  if (!fuse && (s = launched(gdn::launch_prep(pp, st), "gdn_chunk_operator prep launch"))) return s;
   gdn::ChainLaunch p{};
   p.tau = pp.tau;
   p.k = k;
@@ -265,6 +272,7 @@ gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, c
   p.n_segs = 1;
   p.tiles_T = dk / 16;
   p.tiles_S = v ? dv / 16 : 0;
+  p.fuse_prep = fuse ? 1 : 0;
   return launched(p.in_bf16 ? gdn::launch_chain_bf16(p, st) : gdn::launch_chain(p, st),
                   "gdn_chunk_operator launch");
 }

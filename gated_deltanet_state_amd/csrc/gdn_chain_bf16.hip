@@ -50,6 +50,7 @@
 // every product within a few fp32 ulps.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_prep_wave.h"
 
 namespace gdn {
 
@@ -57,7 +58,7 @@ namespace {
 
 constexpr int CH = kChunk;
 
-template <int DK, bool WANT_O, int NW, int RT>
+template <int DK, bool WANT_O, int NW, int RT, bool FUSED>
 struct Cfg {
   static constexpr int NT = NW * 64;
   static constexpr int TW = NW * RT;           // row tiles per workgroup
@@ -76,7 +77,9 @@ struct Cfg {
   static constexpr size_t oP = 2 * BUF;        // M o Q K^T fragments (outputs only)
   static constexpr size_t oG = oP + (WANT_O ? 2 * kTauFragPlane * 2 : 0);
   static constexpr size_t TOTAL = oG + 2 * GN * 4;
-  static_assert(TOTAL <= 160 * 1024, "LDS budget");
+  // the prologue that builds the segment's records uses the same LDS first
+  static constexpr size_t SMEM = FUSED && (size_t)NW * kPrepWaveLds > TOTAL ? (size_t)NW * kPrepWaveLds : TOTAL;
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
 // Gate buffer: [0, 64) e^g, [64, 128) e^{g_L - g} (0 past the chunk),
@@ -128,13 +131,13 @@ __device__ __forceinline__ void kt_frags(int m, uint32_t addr, bf16x8 (&a)[NSB])
   }
 }
 
-template <int DK, bool WANT_O, int NW, int RT>
+template <int DK, bool WANT_O, int NW, int RT, bool FUSED>
 __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int n_items) {
   static_assert(RT == 1 || RT == 2, "one or two row tiles per wave");
   static_assert(!WANT_O || RT == 1, "outputs use one row tile per wave");
-  using C = Cfg<DK, WANT_O, NW, RT>;
+  using C = Cfg<DK, WANT_O, NW, RT, FUSED>;
   constexpr int TW = C::TW;
-  __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
+  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   bf16 *sP = reinterpret_cast<bf16 *>(smem + C::oP);
   float *sG0 = reinterpret_cast<float *>(smem + C::oG);
 
@@ -331,6 +334,22 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
         vt[rt][bt] = uint2{x.x & vmask, x.y & vmask};
       }
   };
+
+  // ---- prologue (fused mode): the workgroup builds the per-chunk records of
+  // its own segment, one chunk per wave at a time, before the recurrence
+  // reads them ----
+  if constexpr (FUSED) {
+    float *scr = reinterpret_cast<float *>(smem) + w * (kPrepWaveLds / 4);
+    const int nch = (tend - tbeg + CH - 1) / CH;
+    for (int c = w; c < nch; c += NW) {
+      const int tc = tbeg + c * CH;
+      prep_chunk_wave<DK>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta), H, h,
+                          tc, min(CH, tend - tc),
+                          const_cast<char *>(grec) + ((slot0 + c) * H + h) * (int64_t)(kRecFloats * 4), scr);
+    }
+    wait_vmem();
+    __syncthreads();
+  }
 
   if (tbeg < tend) {
     const int L0 = min(CH, tend - tbeg);
@@ -608,7 +627,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   }
 }
 
-template <int DK, bool WANT_O, int NW, int RT>
+template <int DK, bool WANT_O, int NW, int RT, bool FUSED = false>
 hipError_t launch_b(const ChainLaunch &p, hipStream_t stream) {
   constexpr int TW = NW * RT;
   if (p.tiles_T % RT != 0 || p.tiles_S % RT != 0 || p.tiles_T > 8 || p.tiles_S > 8) return hipErrorInvalidValue;
@@ -618,7 +637,7 @@ hipError_t launch_b(const ChainLaunch &p, hipStream_t stream) {
   const int64_t items = (int64_t)p.n_seqs * p.H * per_nh;
   if (items <= 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((chain_bf16_kernel<DK, WANT_O, NW, RT>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, p,
+  hipLaunchKernelGGL((chain_bf16_kernel<DK, WANT_O, NW, RT, FUSED>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, p,
                      (int)items);
   return hipGetLastError();
 }
@@ -626,7 +645,7 @@ hipError_t launch_b(const ChainLaunch &p, hipStream_t stream) {
 template <int DK>
 hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
   if (p.o) {
-    if (p.tiles_T != 0) return hipErrorInvalidValue;
+    if (p.tiles_T != 0 || p.fuse_prep) return hipErrorInvalidValue;
     return launch_b<DK, true, 4, 1>(p, stream);
   }
   // Transition and state tiles of a segment share one workgroup, two row
@@ -635,10 +654,15 @@ hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
   // State-only replays keep one row tile per wave (shorter chunk steps).
   const int tilesA = p.tiles_T + p.tiles_S;
   if (p.tiles_T > 0) {
-    if (tilesA <= 8) return launch_b<DK, false, 4, 2>(p, stream);
-    if (tilesA <= 16) return launch_b<DK, false, 8, 2>(p, stream);
+    // one workgroup per (sequence, segment, head): it may build its own
+    // segment's records first
+    if (tilesA <= 8)
+      return p.fuse_prep ? launch_b<DK, false, 4, 2, true>(p, stream) : launch_b<DK, false, 4, 2>(p, stream);
+    if (tilesA <= 16)
+      return p.fuse_prep ? launch_b<DK, false, 8, 2, true>(p, stream) : launch_b<DK, false, 8, 2>(p, stream);
     return hipErrorInvalidValue;
   }
+  if (p.fuse_prep) return hipErrorInvalidValue;
   return p.tiles_S % 8 == 0 ? launch_b<DK, false, 8, 1>(p, stream) : launch_b<DK, false, 4, 1>(p, stream);
 }
 

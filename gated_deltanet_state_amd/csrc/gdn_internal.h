@@ -74,6 +74,9 @@ struct ChainLaunch {
   int32_t n_segs;           // >= 1
   int skip_T0;              // segment 0 has no transition tiles
   int T_transposed;         // write T^T (row-major) instead of T
+  // bf16 inputs with transition tiles: every workgroup first builds the
+  // per-chunk records of its own segment (no separate prep launch)
+  int fuse_prep;
 };
 
 struct ComposeLaunch {
