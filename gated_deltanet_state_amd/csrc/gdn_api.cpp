@@ -194,7 +194,7 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   p.n_segs = P;
   p.fuse_prep = 1;
   p.skip_T0 = 1;
-  p.T_transposed = 1;
+  p.T_frags = 1;
   p.tiles_T = dk / 16;
   p.tiles_S = dv / 16;
   p.T_out = Tseg;
@@ -202,7 +202,7 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   if ((s = launched(gdn::launch_chain_bf16(p, st), "gdn_replay segment launch"))) return s;
   gdn::SegComposeLaunch c{};
   c.S_seg = Sseg;
-  c.Tt_seg = Tseg;
+  c.T_frag = Tseg;
   c.n_seqs = n_seqs;
   c.n_segs = P;
   c.H = n_heads;

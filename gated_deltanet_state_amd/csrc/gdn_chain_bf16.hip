@@ -605,24 +605,43 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 
   // ---------------- epilogue: final rows ----------------
   if (WANT_O && active && Lp > 0) store_o();
-  if (active) {
-    const int64_t unit = ((int64_t)n * p.n_segs + seg) * H + h;
+  const int64_t unit = ((int64_t)n * p.n_segs + seg) * H + h;
+  if (RT == 2 && is_T && p.T_frags) {
+    // Segment operator as composition fragments: this wave holds rows
+    // 32 ks .. 32 ks + 31 of T (ks = row0 / 32); they go through the wave's
+    // own LDS region (all waves passed the last hand-over barrier, so the
+    // chunk buffers are free) and come back as column slices.
+    constexpr int LDT = DK + 4;
+    float *sw = reinterpret_cast<float *>(smem) + w * (32 * LDT);
+    const int ks = row0 >> 5;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int d = 0; d < C::NSB; ++d) {
+        const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1);
+        *reinterpret_cast<f32x4 *>(sw + (16 * rt + jl) * LDT + c0) = st[rt][d];
+      }
+    wave_lds_fence();
+    bf16 *fh = reinterpret_cast<bf16 *>(p.T_out) + unit * DK * DK * 2, *fl = fh + DK * DK;
+#pragma unroll
+    for (int jb = 0; jb < C::NSB; ++jb) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = sw[(8 * g4 + i) * LDT + 16 * jb + jl];
+      bf16x8 hi, lo;
+      split8(x, hi, lo);
+      const int f = jb * C::NKS + ks;
+      *reinterpret_cast<bf16x8 *>(fh + (f * 64 + l) * 8) = hi;
+      *reinterpret_cast<bf16x8 *>(fl + (f * 64 + l) * 8) = lo;
+    }
+  } else if (active) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int d = 0; d < C::NSB; ++d) {
         const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1), r = row0 + 16 * rt + jl;
-        if (is_T) {
-          float *out = p.T_out + unit * DK * DK;
-          if (p.T_transposed) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[(int64_t)(c0 + e) * DK + r] = st[rt][d][e];
-          } else {
-            *reinterpret_cast<f32x4 *>(out + (int64_t)r * DK + c0) = st[rt][d];
-          }
-        } else {
-          *reinterpret_cast<f32x4 *>(p.S_out + unit * DV * DK + (int64_t)r * DK + c0) = st[rt][d];
-        }
+        float *out = is_T ? p.T_out + unit * DK * DK : p.S_out + unit * DV * DK;
+        *reinterpret_cast<f32x4 *>(out + (int64_t)r * DK + c0) = st[rt][d];
       }
   }
 }
@@ -653,6 +672,7 @@ hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
   // and one staged copy of the chunk operands serves all the tiles.
   // State-only replays keep one row tile per wave (shorter chunk steps).
   const int tilesA = p.tiles_T + p.tiles_S;
+  if (p.T_frags && (p.tiles_T * 16 != p.dk || p.tiles_T % 2 != 0)) return hipErrorInvalidValue;
   if (p.tiles_T > 0) {
     // one workgroup per (sequence, segment, head): it may build its own
     // segment's records first

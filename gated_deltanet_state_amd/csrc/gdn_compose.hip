@@ -84,117 +84,127 @@ hipError_t launch_c(const ComposeLaunch &p, hipStream_t stream) {
 
 // ---------------------------------------------------------------------------
 // Composition of time-split segments (one sequence's segment operators, in
-// order): S = S_seg[0], then S <- S T_seg[s] + S_seg[s].  T_seg arrives
-// transposed (T^T row-major), so the A operand of S_new^T = T^T S^T comes
-// straight from global memory, 8 consecutive floats per lane.  Workgroup =
-// 4 waves on 16 rows of one (sequence, head); wave w owns dk blocks
-// w * NOB .. w * NOB + NOB - 1 of S^T (C layout, natural dk order) and the
-// full S^T operand is exchanged through LDS once per step.  The operands of
-// step s + 1 (which do not depend on the running state) are loaded into
-// registers while step s computes.
+// order): S = S_seg[0], then S <- S T_seg[s] + S_seg[s], computed as
+// S_new^T = T^T S^T + S_seg^T.  The operators arrive as split-bf16 MFMA
+// fragments (gdn_internal.h), so a workgroup copies each step's operator
+// into LDS once (load-to-LDS DMA, one step ahead, two buffers) and its
+// waves read their A operands from there without converting anything.
+// Workgroup = 4 waves on 32 rows of one (sequence, head): wave w owns rows
+// 16 (w & 1) .. + 15 of the group and dk blocks (w >> 1) * NSB / 2 .. of
+// S^T (C layout); the two halves of a row tile meet in LDS once per step.
 // ---------------------------------------------------------------------------
 constexpr int SNW = 4;
 
 template <int DK>
-struct SegOps {
-  static constexpr int NOB = DK / 16 / SNW;
-  static constexpr int NKS = DK / 32;
-  f32x4 t[NOB][NKS][2];  // rows 16 jb + (l & 15) of T^T, 8 floats per k = 32 step
-  f32x4 loc[NOB];        // S_seg rows
+struct SegCfg {
+  static constexpr int NSB = DK / 16, NKS = DK / 32, HALF = NSB / 2;
+  static constexpr int NF = NSB * NKS;               // fragments per plane
+  static constexpr int OPB = 2 * NF * 1024;          // bytes of one operator (both planes)
+  static constexpr int LDS_ = DK + 4;                // sS row pitch (floats)
+  static constexpr size_t TOTAL = 2 * (size_t)OPB + 32 * LDS_ * 4;
+  static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
 template <int DK>
 __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch p, int n_items) {
-  constexpr int LDS_ = DK + 4;
-  constexpr int NOB = SegOps<DK>::NOB;
-  constexpr int NKS = SegOps<DK>::NKS;
-  __shared__ __attribute__((aligned(16))) float sS[16 * LDS_];
+  using C = SegCfg<DK>;
+  constexpr int NKS = C::NKS, HALF = C::HALF, NF = C::NF, LDS_ = C::LDS_;
+  __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
+  float *sS = reinterpret_cast<float *>(smem + 2 * C::OPB);
 
   const int per = (int)(gridDim.x >> 3);
   const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (item >= n_items) return;
-  const int tiles = p.dv / 16;
-  const int nh = item / tiles, row0 = 16 * (item % tiles);
+  const int groups = p.dv / 32;
+  const int nh = item / groups, rg = item % groups;
   const int n = nh / p.H, h = nh % p.H;
   const int H = p.H, DV = p.dv, P = p.n_segs;
   const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), g4 = l >> 4, jl = l & 15;
+  const int rsub = w & 1, jb0 = (w >> 1) * HALF;
+  const int row = 32 * rg + 16 * rsub + jl;   // this lane's S row (C-layout column)
 
   auto seg_state = [&](int s) { return p.S_seg + (((int64_t)n * P + s) * H + h) * DV * DK; };
-  auto load = [&](int s, SegOps<DK> &o) {
-    const float *Tt = p.Tt_seg + (((int64_t)n * P + s) * H + h) * DK * DK;
-    const float *Ls = seg_state(s);
+  auto seg_op = [&](int s) {
+    return reinterpret_cast<const char *>(p.T_frag) + (((int64_t)n * P + s) * H + h) * (int64_t)C::OPB;
+  };
+  // operator of step s into LDS buffer b: 2 NF blocks of 1 KiB, NF / 2 per wave
+  auto issue_op = [&](int s, int b) {
+    const char *src = seg_op(s) + 16 * l;
+    char *dst = smem + b * C::OPB;
 #pragma unroll
-    for (int i = 0; i < NOB; ++i) {
-      const int jb = w * NOB + i;
-      o.loc[i] = *reinterpret_cast<const f32x4 *>(Ls + (int64_t)(row0 + jl) * DK + 16 * jb + 4 * g4);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const float *a = Tt + (int64_t)(16 * jb + jl) * DK + 32 * ks + 8 * g4;
-        o.t[i][ks][0] = *reinterpret_cast<const f32x4 *>(a);
-        o.t[i][ks][1] = *reinterpret_cast<const f32x4 *>(a + 4);
-      }
+    for (int j = 0; j < 2 * NF / SNW; ++j) {
+      const int f = j * SNW + w;
+      dma16_global(src + f * 1024, (lds_void *)(dst + f * 1024));
     }
   };
-  f32x4 acc[NOB];
+  auto load_loc = [&](int s, f32x4 (&loc)[HALF]) {
+    const float *Ls = seg_state(s) + (int64_t)row * DK + 4 * g4;
 #pragma unroll
-  for (int i = 0; i < NOB; ++i)
-    acc[i] = *reinterpret_cast<const f32x4 *>(seg_state(0) + (int64_t)(row0 + jl) * DK + 16 * (w * NOB + i) + 4 * g4);
+    for (int i = 0; i < HALF; ++i) loc[i] = *reinterpret_cast<const f32x4 *>(Ls + 16 * (jb0 + i));
+  };
 
-  auto step = [&](const SegOps<DK> &o) {
+  f32x4 acc[HALF], loc[HALF];
+  load_loc(0, acc);
+  if (P > 1) {
+    issue_op(1, 0);
+    load_loc(1, loc);
+  }
+  for (int s = 1; s < P; ++s) {
+    const int b = (s - 1) & 1;
+    // this wave's half of its row tile to LDS; the operator of step s landed
 #pragma unroll
-    for (int i = 0; i < NOB; ++i)
-      *reinterpret_cast<f32x4 *>(sS + jl * LDS_ + 16 * (w * NOB + i) + 4 * g4) = acc[i];
-    lds_barrier();
-    bf16x8 bh[NKS], bl[NKS];
+    for (int i = 0; i < HALF; ++i)
+      *reinterpret_cast<f32x4 *>(sS + (16 * rsub + jl) * LDS_ + 16 * (jb0 + i) + 4 * g4) = acc[i];
+    f32x4 c0[HALF], c1[HALF], c2[HALF];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4 *>(sS + jl * LDS_ + 32 * ks + 8 * g4);
-      const f32x4 x1 = *reinterpret_cast<const f32x4 *>(sS + jl * LDS_ + 32 * ks + 8 * g4 + 4);
-      b_frag_split(x0, x1, bh[ks], bl[ks]);
-    }
-    // three accumulators per block (one per split pass), rotated so that no
-    // product waits on the one just issued
-    f32x4 c0[NOB], c1[NOB], c2[NOB];
-#pragma unroll
-    for (int i = 0; i < NOB; ++i) {
-      c0[i] = o.loc[i];
+    for (int i = 0; i < HALF; ++i) {
+      c0[i] = loc[i];
       c1[i] = c2[i] = zero4();
     }
+    wait_vmem();
+    lds_barrier();
+    // next step's operator and local state are in flight while this one runs
+    if (s + 1 < P) {
+      issue_op(s + 1, b ^ 1);
+      load_loc(s + 1, loc);
+    }
+    const char *op = smem + b * C::OPB;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 ah[NOB], al[NOB];
+      bf16x8 bh, bl;
+      {
+        const float *x = sS + (16 * rsub + jl) * LDS_ + 32 * ks + 8 * g4;
+        b_frag_split(*reinterpret_cast<const f32x4 *>(x), *reinterpret_cast<const f32x4 *>(x + 4), bh, bl);
+      }
+      bf16x8 ah[HALF], al[HALF];
 #pragma unroll
-      for (int i = 0; i < NOB; ++i) b_frag_split(o.t[i][ks][0], o.t[i][ks][1], ah[i], al[i]);
+      for (int i = 0; i < HALF; ++i) {
+        const int f = (jb0 + i) * NKS + ks;
+        ah[i] = *reinterpret_cast<const bf16x8 *>(op + f * 1024 + 16 * l);
+        al[i] = *reinterpret_cast<const bf16x8 *>(op + (NF + f) * 1024 + 16 * l);
+      }
+      // three accumulators per block (one per split pass), rotated so that
+      // no product waits on the one just issued
 #pragma unroll
-      for (int i = 0; i < NOB; ++i) c0[i] = mfma_bf16(ah[i], bh[ks], c0[i]);
+      for (int i = 0; i < HALF; ++i) c0[i] = mfma_bf16(ah[i], bh, c0[i]);
 #pragma unroll
-      for (int i = 0; i < NOB; ++i) c1[i] = mfma_bf16(ah[i], bl[ks], c1[i]);
+      for (int i = 0; i < HALF; ++i) c1[i] = mfma_bf16(ah[i], bl, c1[i]);
 #pragma unroll
-      for (int i = 0; i < NOB; ++i) c2[i] = mfma_bf16(al[i], bh[ks], c2[i]);
+      for (int i = 0; i < HALF; ++i) c2[i] = mfma_bf16(al[i], bh, c2[i]);
     }
 #pragma unroll
-    for (int i = 0; i < NOB; ++i) acc[i] = c0[i] + c1[i] + c2[i];
+    for (int i = 0; i < HALF; ++i) acc[i] = c0[i] + c1[i] + c2[i];
     lds_barrier();
-  };
-
-  SegOps<DK> o0, o1;
-  if (P > 1) load(1, o0);
-  for (int s = 1; s < P; s += 2) {
-    if (s + 1 < P) load(s + 1, o1);
-    step(o0);
-    if (s + 1 >= P) break;
-    if (s + 2 < P) load(s + 2, o0);
-    step(o1);
   }
-  float *out = p.S_out + ((int64_t)n * H + h) * DV * DK;
+  float *out = p.S_out + ((int64_t)n * H + h) * DV * DK + (int64_t)row * DK + 4 * g4;
 #pragma unroll
-  for (int i = 0; i < NOB; ++i)
-    *reinterpret_cast<f32x4 *>(out + (int64_t)(row0 + jl) * DK + 16 * (w * NOB + i) + 4 * g4) = acc[i];
+  for (int i = 0; i < HALF; ++i) *reinterpret_cast<f32x4 *>(out + 16 * (jb0 + i)) = acc[i];
 }
 
 template <int DK>
 hipError_t launch_sc(const SegComposeLaunch &p, hipStream_t stream) {
-  const int64_t items = (int64_t)p.n_seqs * p.H * (p.dv / 16);
+  if (p.dv % 32 != 0) return hipErrorInvalidValue;
+  const int64_t items = (int64_t)p.n_seqs * p.H * (p.dv / 32);
   if (items <= 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
   hipLaunchKernelGGL((seg_compose_kernel<DK>), dim3((unsigned)grid), dim3(SNW * 64), 0, stream, p, (int)items);

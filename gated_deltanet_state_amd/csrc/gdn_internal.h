@@ -73,7 +73,9 @@ struct ChainLaunch {
   // S0, of later segments from zero; transition tiles from the identity).
   int32_t n_segs;           // >= 1
   int skip_T0;              // segment 0 has no transition tiles
-  int T_transposed;         // write T^T (row-major) instead of T
+  // write each segment's T as composition fragments (kSegOpFragments)
+  // instead of row-major fp32
+  int T_frags;
   // bf16 inputs with transition tiles: every workgroup first builds the
   // per-chunk records of its own segment (no separate prep launch)
   int fuse_prep;
@@ -87,12 +89,18 @@ struct ComposeLaunch {
   float *S_out;             // [H, dv, dk]
 };
 
+// Segment operator fragments (time-split replay): per (sequence, segment,
+// head), dk * dk * 4 bytes holding T as split-bf16 MFMA operands of the
+// composition S_new^T = T^T S^T + S_seg^T: fragment f = jb * (dk / 32) + ks
+// (jb < dk / 16, ks < dk / 32), lane (q, g) = (l & 15, l >> 4) holds
+// T[32 ks + 8 g + i][16 jb + q], i < 8; hi plane [f][lane][8] bf16, then
+// the lo plane.
+//
 // Composition of time-split segments: for each (sequence, head),
-//   S = S_seg[0];  S <- S T_seg[s] + S_seg[s] for s = 1 .. n_segs - 1,
-// with T_seg stored transposed.
+//   S = S_seg[0];  S <- S T_seg[s] + S_seg[s] for s = 1 .. n_segs - 1.
 struct SegComposeLaunch {
   const float *S_seg;       // [n_seqs, n_segs, H, dv, dk]
-  const float *Tt_seg;      // [n_seqs, n_segs, H, dk, dk] (T^T; segment 0 unused)
+  const void *T_frag;       // [n_seqs, n_segs, H] operators as fragments (segment 0 unused)
   int32_t n_seqs, n_segs, H, dk, dv;
   float *S_out;             // [n_seqs, H, dv, dk]
 };
