@@ -65,20 +65,102 @@ def to_dev(inp, torch, np):
 def measured_traffic(workload_name):
     """HBM bytes per call from the committed counter summary for this
     workload, or None when the kernel sources changed since it was taken."""
-    import glob
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic_tail_replay_T3277_H32_d128_bf16.json")
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload_name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if rec.get("workload") != workload_name or rec.get("sources_sha256") != sources_sha256():
+        return None
+    return int(rec["hbm_bytes_per_call"])
+
+
+def sources_sha256():
+    import glob
+    import hashlib
     h = hashlib.sha256()
     for src in sorted(glob.glob(os.path.join(ROOT, "gated_deltanet_state_amd", "csrc", "*"))):
         with open(src, "rb") as f:
             h.update(f.read())
-    if rec.get("workload") != workload_name or rec.get("sources_sha256") != h.hexdigest():
-        return None
-    return int(rec["hbm_bytes_per_call"])
+    return h.hexdigest()
+
+
+def _csv_rows(folder, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit("no *%s under %s" % (suffix, folder))
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    name = name.replace("void ", "").replace("gdn::(anonymous namespace)::", "")
+    return name.split("(")[0]
+
+
+def _counter_kib(folder, counter):
+    """Mean counter value per dispatch of each kernel (KiB for FETCH_SIZE and
+    WRITE_SIZE), summed over the counter's instances within a dispatch."""
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for r in _csv_rows(folder, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        per[_short(r["Kernel_Name"])][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def summarize_counters(wid, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, command=""):
+    """profiles/<workload>.md and profiles/traffic_<workload>.json from
+    rocprofv3 runs of this script: a --kernel-trace --stats run, one --pmc
+    FETCH_SIZE run, one --pmc WRITE_SIZE run, and the same two counters on a
+    --calibrate-copy run (bytes = counter x 1024 / (counter bytes per byte
+    copied))."""
+    import workloads
+    wname = workloads.WORKLOADS[wid]["name"]
+    stats = [r for r in _csv_rows(stats_dir, "kernel_stats.csv") if "rocclr" not in r["Name"]]
+    fetch, write = _counter_kib(fetch_dir, "FETCH_SIZE"), _counter_kib(write_dir, "WRITE_SIZE")
+    cf, cw = _counter_kib(cal_fetch_dir, "FETCH_SIZE"), _counter_kib(cal_write_dir, "WRITE_SIZE")
+    copy_kib = {k: v for k, v in cf.items() if "copy" in k.lower()}
+    copy_wkib = {k: v for k, v in cw.items() if "copy" in k.lower()}
+    if not copy_kib or not copy_wkib:
+        raise SystemExit("no copy kernel in the calibration runs")
+    cal_mib = 256
+    ff = list(copy_kib.values())[0] / (cal_mib * 1024.0)
+    wf = list(copy_wkib.values())[0] / (cal_mib * 1024.0)
+    kernels, total = {}, 0.0
+    for k in sorted((set(fetch) | set(write)) - {k for k in set(fetch) | set(write) if "rocclr" in k}):
+        fb, wb = fetch.get(k, 0.0) * 1024 / ff, write.get(k, 0.0) * 1024 / wf
+        kernels[k] = dict(fetch_kib=fetch.get(k, 0.0), write_kib=write.get(k, 0.0), fetch_bytes=fb, write_bytes=wb)
+        total += fb + wb
+    rec = dict(workload=wname, sources_sha256=sources_sha256(),
+               calibration=dict(copy_mib=cal_mib, fetch_factor=round(ff, 4), write_factor=round(wf, 4)),
+               kernels=kernels, hbm_bytes_per_call=int(total))
+    with open(os.path.join(ROOT, "profiles", "traffic_%s.json" % wname), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = ["# %s: kernel times and HBM traffic" % wname, "",
+             "Kernel trace (rocprofv3 `--kernel-trace --stats`):", "", "```", command or "(command not recorded)",
+             "```", "", "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    tot_avg = 0.0
+    for r in stats:
+        avg = float(r["AverageNs"]) / 1e3
+        tot_avg += avg
+        lines.append("| %s | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
+            _short(r["Name"]), r["Calls"], avg, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["Percentage"])))
+    lines += ["", "Sum of the kernel averages: %.1f us per call." % tot_avg, "",
+              "HBM traffic per dispatch (one `--pmc` counter per run; a %d MiB device copy reads %.3f KiB of "
+              "FETCH_SIZE and writes %.3f KiB of WRITE_SIZE per KiB moved):" % (cal_mib, ff, wf), "",
+              "| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (MB) | written (MB) |", "|---|---|---|---|---|"]
+    for k, v in kernels.items():
+        lines.append("| %s | %.0f | %.0f | %.1f | %.1f |" % (k, v["fetch_kib"], v["write_kib"], v["fetch_bytes"] / 1e6,
+                                                           v["write_bytes"] / 1e6))
+    lines += ["", "HBM bytes per call: %.1f MB." % (total / 1e6), ""]
+    with open(os.path.join(ROOT, "profiles", "%s.md" % wname), "w") as f:
+        f.write("\n".join(lines))
+    print("wrote profiles/%s.md and profiles/traffic_%s.json" % (wname, wname))
 
 
 def cpu_baseline(inp, want_o, wid, min_seconds=3.0):
@@ -120,7 +202,13 @@ def main():
     ap.add_argument("--o-bf16", action="store_true", help="write o in bf16 (workloads 2, 3)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (HBM counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=5, metavar=("STATS", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="write profiles/ summaries from rocprofv3 output folders (no GPU needed)")
+    ap.add_argument("--command", default="", help="with --summarize-counters: the command line profiled")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.workload, *args.summarize_counters, command=args.command)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the replay path is a single-GPU kernel library "
               "(heads and requests shard across GPUs without any exchange); run with --gpus 1.",
@@ -210,7 +298,7 @@ def main():
     achieved = byt / (avg_kern / 1e3) / 1e9
     roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(wdef["name"]),
-                kernel="replay call (per-chunk factor kernel + chunk recurrence kernel)",
+                kernel=("chunk-operator call" if wid == 4 else "replay call (all kernels of one gdn_replay)"),
                 algorithmic_bytes=byt, kernel_ms_avg=round(avg_kern, 5),
                 kernel_ms_median=round(med_kern, 5), kernel_ms_min=round(min(kern_ms), 5),
                 mfma_frac=round(fl / (avg_kern / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
