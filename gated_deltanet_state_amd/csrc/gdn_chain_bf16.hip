@@ -77,8 +77,13 @@ struct Cfg {
   static constexpr size_t oP = 2 * BUF;        // M o Q K^T fragments (outputs only)
   static constexpr size_t oG = oP + (WANT_O ? 2 * kTauFragPlane * 2 : 0);
   static constexpr size_t TOTAL = oG + 2 * GN * 4;
-  // the prologue that builds the segment's records uses the same LDS first
-  static constexpr size_t SMEM = FUSED && (size_t)NW * kPrepWaveLds > TOTAL ? (size_t)NW * kPrepWaveLds : TOTAL;
+  // the prologue that builds the segment's records (on at most eight
+  // waves) uses the LDS above buffer set 0, whose first chunk is in flight
+  // meanwhile
+  static constexpr int NPW = NW < 8 ? NW : 8;
+  static constexpr size_t PSCR = BUF;
+  static constexpr size_t SMEM =
+      FUSED && PSCR + (size_t)NPW * kPrepWaveLds > TOTAL ? PSCR + (size_t)NPW * kPrepWaveLds : TOTAL;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
@@ -221,7 +226,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   // loops are unrolled over compile-time block ranges with the wave index
   // uniform, so the issue is straight-line scalar-branch code.
   const uint32_t tok_k = (uint32_t)H * DK * 2, tok_v = (uint32_t)H * DV * 2;  // bytes per token
-  auto issue_dma = [&](int b, int t0, int Lc, int64_t slot) {
+  auto issue_dma = [&](int b, int t0, int Lc, int64_t slot, bool with_rec = true) {
     char *buf = smem + b * C::BUF;
     const int lm = Lc - 1;
     const char *kb = reinterpret_cast<const char *>(gk + ((int64_t)t0 * H + h) * DK) + 16 * g4;
@@ -240,7 +245,8 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 #pragma unroll
     for (int j = 0; j < (C::NTF + NW - 1) / NW; ++j) {         // Tau diag(beta) fragments (record)
       const int f = j * NW + w;
-      if (C::NTF % NW == 0 || f < C::NTF) dma16_global(rec + f * 1024, (lds_void *)(buf + (C::bTF + f) * 1024));
+      if (with_rec && (C::NTF % NW == 0 || f < C::NTF))
+        dma16_global(rec + f * 1024, (lds_void *)(buf + (C::bTF + f) * 1024));
     }
     if (grp_S) {                                               // value slab of the workgroup
       const char *vb = reinterpret_cast<const char *>(gv + ((int64_t)t0 * H + h) * DV + vcol0);
@@ -338,20 +344,27 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   // ---- prologue (fused mode): the workgroup builds the per-chunk records of
   // its own segment, one chunk per wave at a time, before the recurrence
   // reads them ----
+  // The first chunk's keys and values are copied meanwhile; its record
+  // goes straight into buffer set 0 as well.
   if constexpr (FUSED) {
-    float *scr = reinterpret_cast<float *>(smem) + w * (kPrepWaveLds / 4);
+    if (tbeg < tend) {
+      const int L0 = min(CH, tend - tbeg);
+      issue_dma(0, tbeg, L0, slot0, false);
+      load_alpha(tbeg, L0);
+    }
+    float *scr = reinterpret_cast<float *>(smem + C::PSCR) + (w % C::NPW) * (kPrepWaveLds / 4);
     const int nch = (tend - tbeg + CH - 1) / CH;
-    for (int c = w; c < nch; c += NW) {
+    for (int c = w; c < nch && w < C::NPW; c += C::NPW) {
       const int tc = tbeg + c * CH;
       prep_chunk_wave<DK>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta), H, h,
                           tc, min(CH, tend - tc),
-                          const_cast<char *>(grec) + ((slot0 + c) * H + h) * (int64_t)(kRecFloats * 4), scr);
+                          const_cast<char *>(grec) + ((slot0 + c) * H + h) * (int64_t)(kRecFloats * 4), scr,
+                          c == 0 ? smem + C::bTF * 1024 : nullptr);
     }
     wait_vmem();
     __syncthreads();
-  }
-
-  if (tbeg < tend) {
+    if (tbeg < tend) gates(0, min(CH, tend - tbeg));
+  } else if (tbeg < tend) {
     const int L0 = min(CH, tend - tbeg);
     issue_dma(0, tbeg, L0, slot0);
     load_alpha(tbeg, L0);
@@ -406,7 +419,127 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     const float *sG = sG0 + b * C::GN;
     auto frag = [&](int blk) { return *reinterpret_cast<const bf16x8 *>(buf + blk * 1024 + 16 * l); };
 
-    if (active) {
+    if constexpr (RT == 2) {
+      // ---- two row tiles, skewed by one stage: tile 1's vector-ALU work
+      // (fragment splits, residuals) sits next to tile 0's MFMAs and the
+      // other way round, so the two can overlap.  The fragments both tiles
+      // read (K, Tau, K^T) stay in registers across the skewed pair ----
+      if (active) {
+        constexpr int NKS = C::NKS, NSB = C::NSB;
+        auto split_s = [&](const f32x4 (&sv)[NSB], bf16x8 (&hh)[NKS], bf16x8 (&ll)[NKS]) {
+#pragma unroll
+          for (int m = 0; m < NKS; ++m) b_frag_split(sv[2 * m], sv[2 * m + 1], hh[m], ll[m]);
+        };
+        // Y = K S^T: each accumulator is touched once every four products
+        auto y_mfma = [&](const bf16x8 (&ka)[4][NKS], const bf16x8 (&hh)[NKS], const bf16x8 (&ll)[NKS],
+                          f32x4 (&yy)[4]) {
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) yy[bt] = zero4();
+#pragma unroll
+          for (int m = 0; m < NKS; ++m) {
+#pragma unroll
+            for (int bt = 0; bt < 4; ++bt) yy[bt] = mfma_bf16(ka[bt][m], hh[m], yy[bt]);
+#pragma unroll
+            for (int bt = 0; bt < 4; ++bt) yy[bt] = mfma_bf16(ka[bt][m], ll[m], yy[bt]);
+          }
+        };
+        // R = V - e^g Y, split into B fragments (beta is in the Tau fragments)
+        auto r_valu = [&](const uint2 (&vv4)[4], const f32x4 (&yy)[4], bf16x8 (&rh)[2], bf16x8 (&rl)[2]) {
+          f32x4 rr[4];
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) {
+            const f32x4 eg = *reinterpret_cast<const f32x4 *>(sG + G_EG + 16 * bt + 4 * g4);
+            const uint2 x = vv4[bt];
+            const float vv[4] = {__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                                 __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rr[bt][e] = vv[e] - eg[e] * yy[bt][e];
+          }
+          b_frag_split(rr[0], rr[1], rh[0], rl[0]);
+          b_frag_split(rr[2], rr[3], rh[1], rl[1]);
+        };
+        // D = (Tau diag(beta)) R, fragments in the order 0, 2, 4, 1, 3, 5
+        auto d_mfma = [&](const bf16x8 (&th)[kTauFrags], const bf16x8 (&tl)[kTauFrags], const bf16x8 (&rh)[2],
+                          const bf16x8 (&rl)[2], f32x4 (&dd)[4]) {
+          constexpr int ford[kTauFrags] = {0, 2, 4, 1, 3, 5};
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) dd[bt] = zero4();
+#pragma unroll
+          for (int pass = 0; pass < 3; ++pass)
+#pragma unroll
+            for (int i = 0; i < kTauFrags; ++i) {
+              const int f = ford[i];
+              const int bt = f < 2 ? f : (f - 2) / 2 + 2;
+              const int m = f < 2 ? 0 : (f - 2) % 2;
+              dd[bt] = mfma_bf16(pass == 2 ? tl[f] : th[f], pass == 1 ? rl[m] : rh[m], dd[bt]);
+            }
+        };
+        // e^{g_L} S^T, and the decayed corrections as B fragments
+        auto de_valu = [&](const f32x4 (&dd)[4], f32x4 (&sv)[NSB], bf16x8 (&eh)[2], bf16x8 (&el)[2]) {
+          f32x4 de[4];
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) {
+            const f32x4 dec = *reinterpret_cast<const f32x4 *>(sG + G_DEC + 16 * bt + 4 * g4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) de[bt][e] = dd[bt][e] * dec[e];
+          }
+          b_frag_split(de[0], de[1], eh[0], el[0]);
+          b_frag_split(de[2], de[3], eh[1], el[1]);
+          const float gl = sG[G_EGL];
+#pragma unroll
+          for (int d = 0; d < NSB; ++d)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[d][e] *= gl;
+        };
+        // S^T += K^T D': each state block is touched once every NSB products
+        auto upd_mfma = [&](const bf16x8 (&kt)[2][NSB], const bf16x8 (&eh)[2], const bf16x8 (&el)[2],
+                            f32x4 (&sv)[NSB]) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int d = 0; d < NSB; ++d) sv[d] = mfma_bf16(kt[m][d], eh[m], sv[d]);
+#pragma unroll
+            for (int d = 0; d < NSB; ++d) sv[d] = mfma_bf16(kt[m][d], el[m], sv[d]);
+          }
+        };
+
+        bf16x8 sh0[NKS], sl0[NKS], sh1[NKS], sl1[NKS];
+        f32x4 y0[4], y1[4], d0[4], d1[4];
+        bf16x8 rh0[2], rl0[2], rh1[2], rl1[2], eh0[2], el0[2], eh1[2], el1[2];
+        {
+          bf16x8 ka[4][NKS];
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt)
+#pragma unroll
+            for (int m = 0; m < NKS; ++m) ka[bt][m] = frag(C::bKA + bt * NKS + m);
+          split_s(st[0], sh0, sl0);
+          y_mfma(ka, sh0, sl0, y0);
+          split_s(st[1], sh1, sl1);
+          r_valu(vt[0], y0, rh0, rl0);
+          y_mfma(ka, sh1, sl1, y1);
+        }
+        {
+          bf16x8 th[kTauFrags], tl[kTauFrags];
+#pragma unroll
+          for (int f = 0; f < kTauFrags; ++f) {
+            th[f] = frag(C::bTF + f);
+            tl[f] = frag(C::bTF + kTauFrags + f);
+          }
+          d_mfma(th, tl, rh0, rl0, d0);
+          r_valu(vt[1], y1, rh1, rl1);
+          de_valu(d0, st[0], eh0, el0);
+          d_mfma(th, tl, rh1, rl1, d1);
+        }
+        {
+          bf16x8 kt[2][NSB];
+          kt_frags<NKS, NSB>(0, kt_lds + (uint32_t)(b * C::BUF), kt[0]);
+          kt_frags<NKS, NSB>(1, kt_lds + (uint32_t)(b * C::BUF), kt[1]);
+          upd_mfma(kt, eh0, el0, st[0]);
+          de_valu(d1, st[1], eh1, el1);
+          upd_mfma(kt, eh1, el1, st[1]);
+        }
+      }
+    } else if (active) {
       // ---- S^T as k = 32 B fragments ----
       bf16x8 sh[RT][C::NKS], sl[RT][C::NKS];
 #pragma unroll
@@ -606,35 +739,40 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   // ---------------- epilogue: final rows ----------------
   if (WANT_O && active && Lp > 0) store_o();
   const int64_t unit = ((int64_t)n * p.n_segs + seg) * H + h;
-  if (RT == 2 && is_T && p.T_frags) {
-    // Segment operator as composition fragments: this wave holds rows
-    // 32 ks .. 32 ks + 31 of T (ks = row0 / 32); they go through the wave's
-    // own LDS region (all waves passed the last hand-over barrier, so the
-    // chunk buffers are free) and come back as column slices.
+  if (p.T_frags) {
+    // Segment operator as composition fragments: the transition rows go to
+    // LDS (all waves passed the last hand-over barrier, so the chunk
+    // buffers are free) and come back as column slices, split into bf16
+    // hi and lo.  The barrier is workgroup-uniform (T_frags is a launch
+    // argument).
     constexpr int LDT = DK + 4;
-    float *sw = reinterpret_cast<float *>(smem) + w * (32 * LDT);
-    const int ks = row0 >> 5;
+    float *sw = reinterpret_cast<float *>(smem);
+    if (is_T) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int d = 0; d < C::NSB; ++d) {
-        const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1);
-        *reinterpret_cast<f32x4 *>(sw + (16 * rt + jl) * LDT + c0) = st[rt][d];
-      }
-    wave_lds_fence();
-    bf16 *fh = reinterpret_cast<bf16 *>(p.T_out) + unit * DK * DK * 2, *fl = fh + DK * DK;
-#pragma unroll
-    for (int jb = 0; jb < C::NSB; ++jb) {
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = sw[(8 * g4 + i) * LDT + 16 * jb + jl];
-      bf16x8 hi, lo;
-      split8(x, hi, lo);
-      const int f = jb * C::NKS + ks;
-      *reinterpret_cast<bf16x8 *>(fh + (f * 64 + l) * 8) = hi;
-      *reinterpret_cast<bf16x8 *>(fl + (f * 64 + l) * 8) = lo;
+        for (int d = 0; d < C::NSB; ++d) {
+          const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1);
+          *reinterpret_cast<f32x4 *>(sw + (row0 + 16 * rt + jl) * LDT + c0) = st[rt][d];
+        }
     }
-  } else if (active) {
+    __syncthreads();
+    if (is_T) {
+      const int n_tw = tT / RT, tw = row0 / (16 * RT);
+      bf16 *fh = reinterpret_cast<bf16 *>(p.T_out) + unit * DK * DK * 2, *fl = fh + DK * DK;
+      for (int f = tw; f < C::NSB * C::NKS; f += n_tw) {
+        const int jb = f / C::NKS, ks = f % C::NKS;
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = sw[(32 * ks + 8 * g4 + i) * LDT + 16 * jb + jl];
+        bf16x8 hi, lo;
+        split8(x, hi, lo);
+        *reinterpret_cast<bf16x8 *>(fh + (f * 64 + l) * 8) = hi;
+        *reinterpret_cast<bf16x8 *>(fl + (f * 64 + l) * 8) = lo;
+      }
+    }
+  }
+  if (active && !(p.T_frags && is_T)) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -672,7 +810,7 @@ hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
   // and one staged copy of the chunk operands serves all the tiles.
   // State-only replays keep one row tile per wave (shorter chunk steps).
   const int tilesA = p.tiles_T + p.tiles_S;
-  if (p.T_frags && (p.tiles_T * 16 != p.dk || p.tiles_T % 2 != 0)) return hipErrorInvalidValue;
+  if (p.T_frags && p.tiles_T * 16 != p.dk) return hipErrorInvalidValue;
   if (p.tiles_T > 0) {
     // one workgroup per (sequence, segment, head): it may build its own
     // segment's records first

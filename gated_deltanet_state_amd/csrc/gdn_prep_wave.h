@@ -58,10 +58,11 @@ __device__ __forceinline__ f32x4 acc3_sum(const Acc3 &a) { return a.a + a.b + a.
 
 // Record of one (chunk, head): tokens t0 .. t0 + Lc - 1 (1 <= Lc <= 64) of
 // head h, keys k [T, H, DK], gates alpha / beta [T, H] (bf16); rec receives
-// kRecFloats * 4 bytes; scratch is this wave's kPrepWaveLds bytes of LDS.
+// kRecFloats * 4 bytes; scratch is this wave's kPrepWaveLds bytes of LDS;
+// lds_rec (may be null) receives a second copy of the record in LDS.
 template <int DK>
 __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha, const bf16 *beta, int H, int h,
-                                                int t0, int Lc, char *rec, float *scratch) {
+                                                int t0, int Lc, char *rec, float *scratch, char *lds_rec = nullptr) {
   using namespace prep_detail;
   constexpr int NKS = DK / 32;
   float *sA = scratch;             // 10 blocks 16 x 16 row-major: A, then Tau
@@ -221,6 +222,11 @@ __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha
     split8(x, hi, lo);
     *reinterpret_cast<bf16x8 *>(outh + 8 * (f * 64 + l)) = hi;
     *reinterpret_cast<bf16x8 *>(outl + 8 * (f * 64 + l)) = lo;
+    if (lds_rec) {
+      bf16 *lh = reinterpret_cast<bf16 *>(lds_rec), *ll = lh + kTauFragPlane;
+      *reinterpret_cast<bf16x8 *>(lh + 8 * (f * 64 + l)) = hi;
+      *reinterpret_cast<bf16x8 *>(ll + 8 * (f * 64 + l)) = lo;
+    }
   }
 }
 
