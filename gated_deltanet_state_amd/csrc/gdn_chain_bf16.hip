@@ -183,10 +183,21 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 
   // ---- this segment's token range ----
   const int cbeg = p.cu[n], cend = p.cu[n + 1];
-  int64_t seg_len = cend - cbeg;
-  if (p.n_segs > 1) seg_len = ((seg_len + p.n_segs - 1) / p.n_segs + CH - 1) / CH * CH;
-  const int tbeg = (int)min((int64_t)cend, (int64_t)cbeg + seg * seg_len);
-  const int tend = (int)min((int64_t)cend, (int64_t)tbeg + seg_len);
+  int tbeg = cbeg, tend = cend;
+  if (p.n_segs > 1) {
+    // Segments of whole chunks.  Segment 0 carries state rows only (no
+    // transition rows) and steps about 1.6 times faster, so it takes a
+    // larger share: e = round(chunks / (P - 1 + 1.6)) chunks for each later
+    // segment, the rest for segment 0.  Segments past the end are empty.
+    const int P = p.n_segs, nch = (cend - cbeg + CH - 1) / CH;
+    const int den = 5 * (P - 1) + 8;
+    const int e = max(1, (5 * nch + den / 2) / den);
+    const int c0 = max(0, nch - (P - 1) * e);
+    const int64_t off = seg == 0 ? 0 : (int64_t)(c0 + (seg - 1) * e) * CH;
+    const int64_t len = (int64_t)(seg == 0 ? c0 : e) * CH;
+    tbeg = (int)min((int64_t)cend, (int64_t)cbeg + off);
+    tend = (int)min((int64_t)cend, (int64_t)tbeg + len);
+  }
   const int64_t slot0 = (int64_t)(cbeg / CH) + n + (tbeg - cbeg) / CH;
 
   // LDS byte address (buffer set 0) of this lane's transposing reads of the

@@ -91,15 +91,8 @@ struct RowNeg {  // -p[row * ld + k], fp32
   __device__ float one(int row, int k) const { return -p[row * ld + k]; }
 };
 
-// 8 consecutive k of one row as split bf16 (hi, lo).
-__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    bf16 h = (bf16)x[i];
-    hi[i] = h;
-    lo[i] = (bf16)(x[i] - (float)h);
-  }
-}
+// 8 consecutive k of one row as split bf16 (hi, lo); defined below split2.
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo);
 
 template <bool NEED_LO>
 __device__ __forceinline__ void load8f(const float *src, const float *scale, float sign, bf16x8 &hi,
@@ -201,14 +194,7 @@ __device__ __forceinline__ void mma_f32(f32x4 &c, const OA &opA, const OB &opB, 
   for (int k = k0; k < k1; k += 4) c = mfma_f32(opA.one(m0 + r, k + kk), opB.one(n0 + r, k + kk), c);
 }
 
-__device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bf16 h = (bf16)x[i];
-    hi[i] = h;
-    lo[i] = (bf16)(x[i] - (float)h);
-  }
-}
+__device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo);  // defined below split2
 
 // 3-pass split-bf16 product of 16 x 16 tiles, k = 16: A given as 4 fp32 per
 // lane in A layout, B as 4 fp32 per lane in B (= C) layout.
@@ -329,6 +315,24 @@ __device__ __forceinline__ void b_frag_split(const f32x4 &t0, const f32x4 &t1, b
   split2(t1[2], t1[3], h.w, o.w);
   hi = __builtin_bit_cast(bf16x8, h);
   lo = __builtin_bit_cast(bf16x8, o);
+}
+
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+  uint4 h, o;
+  split2(x[0], x[1], h.x, o.x);
+  split2(x[2], x[3], h.y, o.y);
+  split2(x[4], x[5], h.z, o.z);
+  split2(x[6], x[7], h.w, o.w);
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, o);
+}
+
+__device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
+  uint2 h, o;
+  split2(x[0], x[1], h.x, o.x);
+  split2(x[2], x[3], h.y, o.y);
+  hi = __builtin_bit_cast(bf16x4, h);
+  lo = __builtin_bit_cast(bf16x4, o);
 }
 
 // ---------------------------------------------------------------------------
