@@ -151,6 +151,7 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   gdn::PrepLaunch pp{};
   pp.k = k;
+  pp.q = (o && bf) ? q : nullptr;
   pp.alpha = alpha;
   pp.beta = beta;
   pp.cu = cu_seqlens;

@@ -32,11 +32,11 @@
 // chunk c runs from one LDS buffer set, the operands of chunk c + 1 are
 // copied into the other one by load-to-LDS DMA (buffer_load ... lds; no
 // registers, no staging code): K and Q as MFMA A fragments, the per-chunk
-// record of gdn_prep_bf16.hip (Tau diag(beta) fragments), and the value
+// record of gdn_prep_wave.h (Tau diag(beta) and, with outputs, M o Q K^T
+// fragments), and the value
 // columns of the workgroup; K^T fragments come from the staged keys by the
 // transposing LDS read.  Every fragment read is then a conflict-free
-// 16-byte LDS read by lane.  One LDS barrier per chunk (two with outputs:
-// M o Q K^T of the next chunk is built once its keys and queries landed).
+// 16-byte LDS read by lane.  One LDS barrier per chunk.
 //
 // The same kernel builds the affine chunk operator of the page "LinearKV:
 // One Cached State Suffices for Position-Independent Caching in Hybrid
@@ -71,11 +71,11 @@ struct Cfg {
   static constexpr int VU = 2 * NSV;           // 16-byte units per staged value row
   static constexpr int NVB = CH * VU / 64;     // value slab blocks
   static constexpr int bKA = 0, bTF = NKA, bV = bTF + NTF, bQA = bV + NVB;
-  static constexpr int NBLK = bQA + (WANT_O ? NKA : 0);
+  static constexpr int bPF = bQA + (WANT_O ? NKA : 0);   // M o Q K^T fragments (outputs only)
+  static constexpr int NBLK = bPF + (WANT_O ? NTF : 0);
   static constexpr size_t BUF = (size_t)NBLK * 1024;
   static constexpr int GN = 3 * CH + 4;        // gate floats per buffer set
-  static constexpr size_t oP = 2 * BUF;        // M o Q K^T fragments (outputs only)
-  static constexpr size_t oG = oP + (WANT_O ? 2 * kTauFragPlane * 2 : 0);
+  static constexpr size_t oG = 2 * BUF;
   static constexpr size_t TOTAL = oG + 2 * GN * 4;
   // the prologue that builds the segment's records (on at most eight
   // waves) uses the LDS above buffer set 0, whose first chunk is in flight
@@ -143,7 +143,6 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   using C = Cfg<DK, WANT_O, NW, RT, FUSED>;
   constexpr int TW = C::TW;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-  bf16 *sP = reinterpret_cast<bf16 *>(smem + C::oP);
   float *sG0 = reinterpret_cast<float *>(smem + C::oG);
 
   // ---- work item (XCD-aware order: consecutive items share one XCD's L2) ----
@@ -256,8 +255,11 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 #pragma unroll
     for (int j = 0; j < (C::NTF + NW - 1) / NW; ++j) {         // Tau diag(beta) fragments (record)
       const int f = j * NW + w;
-      if (with_rec && (C::NTF % NW == 0 || f < C::NTF))
+      if (with_rec && (C::NTF % NW == 0 || f < C::NTF)) {
         dma16_global(rec + f * 1024, (lds_void *)(buf + (C::bTF + f) * 1024));
+        if (WANT_O)                                            // M o Q K^T fragments (record)
+          dma16_global(rec + kRecPOffsetBytes + f * 1024, (lds_void *)(buf + (C::bPF + f) * 1024));
+      }
     }
     if (grp_S) {                                               // value slab of the workgroup
       const char *vb = reinterpret_cast<const char *>(gv + ((int64_t)t0 * H + h) * DV + vcol0);
@@ -289,40 +291,6 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     sG[G_DEC + l] = (l < Lc) ? __expf(gL - g) : 0.f;
     sG[G_G + l] = g;
     if (l == 0) sG[G_EGL] = __expf(gL);
-  };
-
-  // M o Q K^T of the chunk in buffer set b, as split-bf16 A fragments in the
-  // Tau fragment order (gdn_internal.h): tile (bi, bj) of 16 x 16 lands in
-  // fragment (bi, bj >> 1), lane (r & 15) + 16 (c' >> 2), element
-  // 4 (bj & 1) + (c' & 3) for row r, column 16 bj + c'.
-  auto build_p = [&](int b) {
-    const char *buf = smem + b * C::BUF;
-    const float *sG = sG0 + b * C::GN;
-    for (int t = w; t < 2 * kTauFrags; t += NW) {
-      const int f = t >> 1, half = t & 1;
-      const int bi = f < 2 ? f : (f - 2) / 2 + 2;
-      const int bj = 2 * (f < 2 ? 0 : (f - 2) % 2) + half;
-      f32x4 c = zero4();
-      if (bj <= bi) {
-#pragma unroll
-        for (int m = 0; m < C::NKS; ++m) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(buf + (C::bQA + bi * C::NKS + m) * 1024 + 16 * l);
-          const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(buf + (C::bKA + bj * C::NKS + m) * 1024 + 16 * l);
-          c = mfma_bf16(a, bb, c);
-        }
-      }
-      const int col = 16 * bj + jl;
-      const float gc = sG[G_G + col];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * bi + 4 * g4 + e;
-        const float x = (col <= r) ? __expf(sG[G_G + r] - gc) * c[e] : 0.f;
-        const bf16 hi = (bf16)x;
-        const int idx = (f * 64 + (r & 15) + 16 * (jl >> 2)) * 8 + 4 * half + (jl & 3);
-        sP[idx] = hi;
-        sP[kTauFragPlane + idx] = (bf16)(x - (float)hi);
-      }
-    }
   };
 
   // Value columns of the staged chunk in buffer set b, transposed to the
@@ -383,10 +351,6 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   }
   wait_vmem();
   lds_barrier();
-  if (WANT_O && tbeg < tend) {
-    build_p(0);
-    lds_barrier();
-  }
   read_v(0);
 
   // Outputs of a chunk are stored at the start of the next one, so that
@@ -674,8 +638,8 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
           bf16x8 ph[kTauFrags], pl[kTauFrags];
 #pragma unroll
           for (int f = 0; f < kTauFrags; ++f) {
-            ph[f] = *reinterpret_cast<const bf16x8 *>(sP + (f * 64 + l) * 8);
-            pl[f] = *reinterpret_cast<const bf16x8 *>(sP + kTauFragPlane + (f * 64 + l) * 8);
+            ph[f] = frag(C::bPF + f);
+            pl[f] = frag(C::bPF + kTauFrags + f);
           }
 #pragma unroll
           for (int pass = 0; pass < 3; ++pass)
@@ -740,10 +704,6 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     if (more) gates(b ^ 1, L1);
     wait_vmem();
     lds_barrier();
-    if (WANT_O && more) {
-      build_p(b ^ 1);
-      lds_barrier();
-    }
     if (more) read_v(b ^ 1);
   }
 

@@ -16,14 +16,18 @@ namespace gdn {
 // without reading cu (which lives on the device).
 // ---------------------------------------------------------------------------
 constexpr int kChunk = 64;
-// Per-chunk factor record, one per (slot, head), 12 KiB:
+// Per-chunk factor record, one per (slot, head), 24 KiB:
 //   * fp32 inputs: Tau = (I + A)^{-1}, lower 16 x 16 block rows packed, block
 //     row b holds 16 rows x 16 (b + 1) columns, row-major, at element offset
 //     256 * b (b + 1) / 2 (2560 floats);
-//   * bf16 inputs: Tau diag(beta) as the six A operands of the k = 32 MFMAs
-//     that apply it to a 64 x 16 right-hand side given as C-layout tiles (see
-//     kTauFrags), split bf16 planes [hi/lo][fragment][lane][8].
-constexpr int kRecFloats = 3072;
+//   * bf16 inputs: bytes [0, 12 KiB): Tau diag(beta) as the six A operands of
+//     the k = 32 MFMAs that apply it to a 64 x 16 right-hand side given as
+//     C-layout tiles (see kTauFrags), split bf16 planes [hi/lo][fragment]
+//     [lane][8]; bytes [12 KiB, 24 KiB), replays with outputs only: the
+//     decay-masked M o Q K^T (M_rs = e^{g_r - g_s}, s <= r) in the same
+//     fragment layout.
+constexpr int kRecFloats = 6144;
+constexpr int kRecPOffsetBytes = 12288;
 // Fragment f of Tau covers token block row bt and the pair of 16-column
 // blocks (2m, 2m + 1): f = 0: (0,0), 1: (1,0), 2: (2,0), 3: (2,1), 4: (3,0),
 // 5: (3,1).  Lane l holds row 16 bt + (l & 15), columns
@@ -40,6 +44,7 @@ inline size_t tau_workspace_bytes(int64_t n_tokens, int32_t n_seqs, int32_t n_he
 // Per-chunk factor build: one workgroup per (slot, head).
 struct PrepLaunch {
   const void *k, *alpha, *beta;
+  const void *q;     // bf16 replays with outputs: also build M o Q K^T (else null)
   const int32_t *cu;
   int32_t n_seqs, H, dk;
   int in_bf16;

@@ -21,7 +21,9 @@
 //   4. off-diagonal blocks Tau_ij = -Tau_ii sum_{m=j}^{i-1} A_im Tau_mj on
 //      split-bf16 k = 16 MFMAs, in three dependency levels
 //   5. Tau diag(beta) as split-bf16 A fragments of the recurrence kernel's
-//      k = 32 products (record layout of gdn_internal.h).
+//      k = 32 products (record layout of gdn_internal.h)
+//   6. (replays with outputs) the decay-masked M o Q K^T in the same
+//      fragment layout, for the intra-chunk part of the outputs.
 // LDS per wave: kPrepWaveLds bytes (A blocks, overwritten in place by the
 // Tau blocks; a transposed copy of the diagonal Tau blocks; gates).
 #pragma once
@@ -59,10 +61,12 @@ __device__ __forceinline__ f32x4 acc3_sum(const Acc3 &a) { return a.a + a.b + a.
 // Record of one (chunk, head): tokens t0 .. t0 + Lc - 1 (1 <= Lc <= 64) of
 // head h, keys k [T, H, DK], gates alpha / beta [T, H] (bf16); rec receives
 // kRecFloats * 4 bytes; scratch is this wave's kPrepWaveLds bytes of LDS;
-// lds_rec (may be null) receives a second copy of the record in LDS.
+// lds_rec (may be null) receives a second copy of the Tau fragments in LDS;
+// q (may be null) requests the M o Q K^T fragments as well.
 template <int DK>
 __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha, const bf16 *beta, int H, int h,
-                                                int t0, int Lc, char *rec, float *scratch, char *lds_rec = nullptr) {
+                                                int t0, int Lc, char *rec, float *scratch, char *lds_rec = nullptr,
+                                                const bf16 *q = nullptr) {
   using namespace prep_detail;
   constexpr int NKS = DK / 32;
   float *sA = scratch;             // 10 blocks 16 x 16 row-major: A, then Tau
@@ -202,31 +206,71 @@ __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha
 
   // ---- 5. Tau diag(beta) as split-bf16 A fragments: fragment f = (bt, m),
   // lane (r, g) = (l & 15, l >> 4) holds row 16 bt + r, columns
-  // 32 m + 4 g + {0..3} then 32 m + 16 + 4 g + {0..3} ----
-  bf16 *outh = reinterpret_cast<bf16 *>(rec), *outl = outh + kTauFragPlane;
+  // 32 m + 4 g + {0..3} then 32 m + 16 + 4 g + {0..3} (column scale: beta,
+  // or none) ----
+  auto write_frags = [&](char *dst, char *lds_dst, bool scale_beta) {
+    bf16 *outh = reinterpret_cast<bf16 *>(dst), *outl = outh + kTauFragPlane;
 #pragma unroll
-  for (int f = 0; f < kTauFrags; ++f) {
-    const int bt = f < 2 ? f : (f - 2) / 2 + 2;
-    const int m = f < 2 ? 0 : (f - 2) % 2;
-    float x[8];
+    for (int f = 0; f < kTauFrags; ++f) {
+      const int bt = f < 2 ? f : (f - 2) / 2 + 2;
+      const int m = f < 2 ? 0 : (f - 2) % 2;
+      float x[8];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int cb = 2 * m + half, c0 = 16 * cb + 4 * g4;
-      f32x4 v = zero4();
-      if (cb <= bt) v = *reinterpret_cast<const f32x4 *>(sA + blk(bt, cb) * 256 + jl * 16 + 4 * g4);
-      const f32x4 bc = *reinterpret_cast<const f32x4 *>(sB + c0);
+      for (int half = 0; half < 2; ++half) {
+        const int cb = 2 * m + half, c0 = 16 * cb + 4 * g4;
+        f32x4 v = zero4();
+        if (cb <= bt) v = *reinterpret_cast<const f32x4 *>(sA + blk(bt, cb) * 256 + jl * 16 + 4 * g4);
+        if (scale_beta) {
+          const f32x4 bc = *reinterpret_cast<const f32x4 *>(sB + c0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * half + e] = v[e] * bc[e];
+          for (int e = 0; e < 4; ++e) v[e] *= bc[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * half + e] = v[e];
+      }
+      bf16x8 hi, lo;
+      split8(x, hi, lo);
+      *reinterpret_cast<bf16x8 *>(outh + 8 * (f * 64 + l)) = hi;
+      *reinterpret_cast<bf16x8 *>(outl + 8 * (f * 64 + l)) = lo;
+      if (lds_dst) {
+        bf16 *lh = reinterpret_cast<bf16 *>(lds_dst), *ll = lh + kTauFragPlane;
+        *reinterpret_cast<bf16x8 *>(lh + 8 * (f * 64 + l)) = hi;
+        *reinterpret_cast<bf16x8 *>(ll + 8 * (f * 64 + l)) = lo;
+      }
     }
-    bf16x8 hi, lo;
-    split8(x, hi, lo);
-    *reinterpret_cast<bf16x8 *>(outh + 8 * (f * 64 + l)) = hi;
-    *reinterpret_cast<bf16x8 *>(outl + 8 * (f * 64 + l)) = lo;
-    if (lds_rec) {
-      bf16 *lh = reinterpret_cast<bf16 *>(lds_rec), *ll = lh + kTauFragPlane;
-      *reinterpret_cast<bf16x8 *>(lh + 8 * (f * 64 + l)) = hi;
-      *reinterpret_cast<bf16x8 *>(ll + 8 * (f * 64 + l)) = lo;
+  };
+  write_frags(rec, lds_rec, true);
+
+  // ---- 6. M o Q K^T (s <= r) into the block slots, then its fragments ----
+  if (q) {
+    f32x4 acc[10];
+#pragma unroll
+    for (int t = 0; t < 10; ++t) acc[t] = zero4();
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      const int r = min(16 * bi + jl, Lc - 1);
+      const bf16 *src = q + ((int64_t)(t0 + r) * H + h) * DK + 8 * g4;
+#pragma unroll
+      for (int m = 0; m < NKS; ++m) {
+        const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(src + 32 * m);
+#pragma unroll
+        for (int bj = 0; bj <= bi; ++bj) acc[blk(bi, bj)] = mfma_bf16(qf, kf[bj][m], acc[blk(bi, bj)]);
+      }
     }
+    wave_lds_fence();   // the Tau fragments above have been read
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int bj = 0; bj <= bi; ++bj) {
+        const int col = 16 * bj + jl, row0 = 16 * bi + 4 * g4;
+        const float gc = sG[col];
+        const f32x4 gr = *reinterpret_cast<const f32x4 *>(sG + row0);
+        float *dst = sA + blk(bi, bj) * 256 + 4 * g4 * 16 + jl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e * 16] = (col <= row0 + e) ? __expf(gr[e] - gc) * acc[blk(bi, bj)][e] : 0.f;
+      }
+    wave_lds_fence();
+    write_frags(rec + kRecPOffsetBytes, nullptr, false);
   }
 }
 
