@@ -94,9 +94,32 @@ int replay_segments(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t d
   return best;
 }
 
-size_t seg_workspace_bytes(int32_t n_seqs, int32_t P, int32_t n_heads, int32_t dk, int32_t dv) {
+// Segments per sequence for a bf16 replay with outputs.  A split runs three
+// passes: the state-only segment operators, their composition (which also
+// yields every segment's true start state), and every segment again with
+// outputs from that start state.  Worth it when the (sequence, head) pairs
+// alone leave compute units idle: P fills 256 compute units with one
+// workgroup per (sequence, head, segment), with at least 8 chunks per
+// segment.  GDN_REPLAY_SEGMENTS=<n> overrides the choice.
+int replay_segments_o(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv) {
+  if (const char *env = std::getenv("GDN_REPLAY_SEGMENTS")) {
+    const int v = std::atoi(env);
+    if (v >= 1) return v < 64 ? v : 64;
+  }
+  if ((dk + dv) / 16 > 16) return 1;
+  const int64_t chunks = (n_tokens / gdn::kChunk) / (n_seqs > 0 ? n_seqs : 1);
+  const int64_t units = (int64_t)n_seqs * n_heads;
+  int64_t P = 256 / (units > 0 ? units : 1);
+  if (P > chunks / 8) P = chunks / 8;
+  if (P > 8) P = 8;
+  return P < 2 ? 1 : (int)P;
+}
+
+// Segment operators and states: [n_seqs, P, H] x (dk x dk + dv x dk) fp32;
+// with outputs also the start states [n_seqs, P, H, dv, dk].
+size_t seg_workspace_bytes(int32_t n_seqs, int32_t P, int32_t n_heads, int32_t dk, int32_t dv, bool prefix = false) {
   if (P <= 1) return 0;
-  return (size_t)n_seqs * P * n_heads * ((size_t)dk * dk + (size_t)dv * dk) * sizeof(float);
+  return (size_t)n_seqs * P * n_heads * ((size_t)dk * dk + (size_t)dv * dk * (prefix ? 2 : 1)) * sizeof(float);
 }
 
 }  // namespace
@@ -106,8 +129,13 @@ extern "C" {
 size_t gdn_replay_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv) {
   if (n_seqs < 1 || n_tokens < 0 || n_heads < 1) return 0;
   size_t seg = 0;
-  if (supported_dim(dk) && supported_dim(dv))
-    seg = seg_workspace_bytes(n_seqs, replay_segments(n_seqs, n_tokens, n_heads, dk, dv), n_heads, dk, dv);
+  if (supported_dim(dk) && supported_dim(dv)) {
+    // enough for either use: state only, or with outputs
+    const size_t s1 = seg_workspace_bytes(n_seqs, replay_segments(n_seqs, n_tokens, n_heads, dk, dv), n_heads, dk, dv);
+    const size_t s2 =
+        seg_workspace_bytes(n_seqs, replay_segments_o(n_seqs, n_tokens, n_heads, dk, dv), n_heads, dk, dv, true);
+    seg = s1 > s2 ? s1 : s2;
+  }
   return gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads) + seg;
 }
 
@@ -142,9 +170,10 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
       (s = check_align("S_final", S_final)))
     return s;
   const bool bf = in_dtype == GDN_BF16;
-  const int32_t P = (!o && bf) ? replay_segments(n_seqs, n_tokens, n_heads, dk, dv) : 1;
+  const int32_t P = !bf ? 1 : (o ? replay_segments_o(n_seqs, n_tokens, n_heads, dk, dv)
+                                 : replay_segments(n_seqs, n_tokens, n_heads, dk, dv));
   const size_t tau_bytes = gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads);
-  const size_t need = tau_bytes + seg_workspace_bytes(n_seqs, P, n_heads, dk, dv);
+  const size_t need = tau_bytes + seg_workspace_bytes(n_seqs, P, n_heads, dk, dv, o != nullptr);
   if (workspace_bytes < need || !workspace)
     return fail(GDN_ERR_WORKSPACE, "gdn_replay: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
   if ((s = check_align("workspace", workspace))) return s;
@@ -163,7 +192,7 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   pp.n_slots = gdn::slot_count(n_tokens, n_seqs);
   // bf16 time-split replays build the per-chunk records inside the segment
   // kernel; everything else runs the stand-alone prep kernel first
-  const bool fuse = bf && P > 1;
+  const bool fuse = bf && P > 1;   // (records built inside the segment launch)
   if (!fuse && (s = launched(gdn::launch_prep(pp, st), "gdn_replay prep launch"))) return s;
   gdn::ChainLaunch p{};
   p.tau = pp.tau;
@@ -192,14 +221,18 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   // time split: segment operators, then their composition
   float *Tseg = reinterpret_cast<float *>(static_cast<char *>(workspace) + tau_bytes);
   float *Sseg = Tseg + (size_t)n_seqs * P * n_heads * dk * dk;
+  float *Spre = Sseg + (size_t)n_seqs * P * n_heads * dv * dk;   // start states (with outputs)
   p.n_segs = P;
+  p.seg_uniform = o ? 1 : 0;
   p.fuse_prep = 1;
+  p.q_rec = o ? q : nullptr;
   p.skip_T0 = 1;
   p.T_frags = 1;
   p.tiles_T = dk / 16;
   p.tiles_S = dv / 16;
   p.T_out = Tseg;
   p.S_out = Sseg;
+  p.o = nullptr;
   if ((s = launched(gdn::launch_chain_bf16(p, st), "gdn_replay segment launch"))) return s;
   gdn::SegComposeLaunch c{};
   c.S_seg = Sseg;
@@ -210,7 +243,23 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   c.dk = dk;
   c.dv = dv;
   c.S_out = S_final;
-  return launched(gdn::launch_seg_compose(c, st), "gdn_replay segment compose launch");
+  c.S_prefix = o ? Spre : nullptr;
+  c.S0 = S0;
+  if ((s = launched(gdn::launch_seg_compose(c, st), "gdn_replay segment compose launch"))) return s;
+  if (!o) return ok();
+  // outputs: every segment again from its start state, with the records
+  // (Tau and M o Q K^T) the segment launch built
+  gdn::ChainLaunch r = p;
+  r.o = o;
+  r.S0 = nullptr;
+  r.S0_seg = Spre;
+  r.S_out = nullptr;
+  r.T_out = nullptr;
+  r.tiles_T = 0;
+  r.T_frags = 0;
+  r.fuse_prep = 0;
+  r.q_rec = nullptr;
+  return launched(gdn::launch_chain_bf16(r, st), "gdn_replay segment output launch");
 }
 
 gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, const void *beta,

@@ -187,11 +187,12 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     // Segments of whole chunks.  Segment 0 carries state rows only (no
     // transition rows) and steps about 1.6 times faster, so it takes a
     // larger share: e = round(chunks / (P - 1 + 1.6)) chunks for each later
-    // segment, the rest for segment 0.  Segments past the end are empty.
+    // segment, the rest for segment 0 (with seg_uniform: ceil(chunks / P)
+    // each).  Segments past the end are empty.
     const int P = p.n_segs, nch = (cend - cbeg + CH - 1) / CH;
     const int den = 5 * (P - 1) + 8;
-    const int e = max(1, (5 * nch + den / 2) / den);
-    const int c0 = max(0, nch - (P - 1) * e);
+    const int e = p.seg_uniform ? (nch + P - 1) / P : max(1, (5 * nch + den / 2) / den);
+    const int c0 = p.seg_uniform ? e : max(0, nch - (P - 1) * e);
     const int64_t off = seg == 0 ? 0 : (int64_t)(c0 + (seg - 1) * e) * CH;
     const int64_t len = (int64_t)(seg == 0 ? c0 : e) * CH;
     tbeg = (int)min((int64_t)cend, (int64_t)cbeg + off);
@@ -222,6 +223,9 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
         if (is_T) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) st[rt][d][e] = (r == c0 + e) ? 1.f : 0.f;
+        } else if (p.S0_seg) {
+          st[rt][d] = *reinterpret_cast<const f32x4 *>(
+              p.S0_seg + ((((int64_t)n * p.n_segs + seg) * H + h) * DV + r) * DK + c0);
         } else if (p.S0 && seg == 0) {
           st[rt][d] = *reinterpret_cast<const f32x4 *>(p.S0 + (((int64_t)n * H + h) * DV + r) * DK + c0);
         }
@@ -338,7 +342,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       prep_chunk_wave<DK>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta), H, h,
                           tc, min(CH, tend - tc),
                           const_cast<char *>(grec) + ((slot0 + c) * H + h) * (int64_t)(kRecFloats * 4), scr,
-                          c == 0 ? smem + C::bTF * 1024 : nullptr);
+                          c == 0 ? smem + C::bTF * 1024 : nullptr, reinterpret_cast<const bf16 *>(p.q_rec));
     }
     wait_vmem();
     __syncthreads();
@@ -743,7 +747,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       }
     }
   }
-  if (active && !(p.T_frags && is_T)) {
+  if (active && !(p.T_frags && is_T) && (is_T || p.S_out)) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -774,6 +778,8 @@ template <int DK>
 hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
   if (p.o) {
     if (p.tiles_T != 0 || p.fuse_prep) return hipErrorInvalidValue;
+    // segments of a time split: one eight-wave workgroup per (segment, head)
+    if (p.n_segs > 1 && p.tiles_S % 8 == 0) return launch_b<DK, true, 8, 1>(p, stream);
     return launch_b<DK, true, 4, 1>(p, stream);
   }
   // Transition and state tiles of a segment share one workgroup, two row

@@ -144,6 +144,13 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
   };
 
   f32x4 acc[HALF], loc[HALF];
+  if (p.S_prefix) {   // the state entering segment 0 (S0 may alias S_out: read it here, first)
+    float *pre = p.S_prefix + ((int64_t)n * P * H + h) * DV * DK + (int64_t)row * DK + 4 * g4;
+    const float *s0 = p.S0 ? p.S0 + ((int64_t)n * H + h) * DV * DK + (int64_t)row * DK + 4 * g4 : nullptr;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i)
+      *reinterpret_cast<f32x4 *>(pre + 16 * (jb0 + i)) = s0 ? *reinterpret_cast<const f32x4 *>(s0 + 16 * (jb0 + i)) : zero4();
+  }
   load_loc(0, acc);
   if (P > 1) {
     issue_op(1, 0);
@@ -151,6 +158,11 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
   }
   for (int s = 1; s < P; ++s) {
     const int b = (s - 1) & 1;
+    if (p.S_prefix) {   // the state entering segment s
+      float *pre = p.S_prefix + (((int64_t)n * P + s) * H + h) * DV * DK + (int64_t)row * DK + 4 * g4;
+#pragma unroll
+      for (int i = 0; i < HALF; ++i) *reinterpret_cast<f32x4 *>(pre + 16 * (jb0 + i)) = acc[i];
+    }
     // this wave's half of its row tile to LDS; the operator of step s landed
 #pragma unroll
     for (int i = 0; i < HALF; ++i)

@@ -73,10 +73,12 @@ struct ChainLaunch {
   float *S_out;             // [n_seqs, n_segs, H, dv, dk] (state tiles) or null
   float *T_out;             // [n_seqs, n_segs, H, dk, dk] (transition tiles) or null
   int32_t tiles_T, tiles_S;
-  // Time split: each sequence is cut into n_segs segments of equal whole
-  // chunks; every segment runs independently (state tiles of segment 0 from
-  // S0, of later segments from zero; transition tiles from the identity).
+  // Time split: each sequence is cut into n_segs segments of whole chunks;
+  // every segment runs independently (state tiles of segment 0 from S0, of
+  // later segments from S0_seg or zero; transition tiles from the identity).
   int32_t n_segs;           // >= 1
+  int seg_uniform;          // equal segments (else segment 0 takes a larger share)
+  const float *S0_seg;      // [n_seqs, n_segs, H, dv, dk]: start of every segment (replaces S0), or null
   int skip_T0;              // segment 0 has no transition tiles
   // write each segment's T as composition fragments (kSegOpFragments)
   // instead of row-major fp32
@@ -84,6 +86,7 @@ struct ChainLaunch {
   // bf16 inputs with transition tiles: every workgroup first builds the
   // per-chunk records of its own segment (no separate prep launch)
   int fuse_prep;
+  const void *q_rec;        // fused prologue: also build M o Q K^T from these queries (or null)
 };
 
 struct ComposeLaunch {
@@ -106,6 +109,8 @@ struct ComposeLaunch {
 struct SegComposeLaunch {
   const float *S_seg;       // [n_seqs, n_segs, H, dv, dk]
   const void *T_frag;       // [n_seqs, n_segs, H] operators as fragments (segment 0 unused)
+  float *S_prefix;          // [n_seqs, n_segs, H, dv, dk]: state entering each segment, or null
+  const float *S0;          // [n_seqs, H, dv, dk] start of segment 0 (copied to S_prefix), or null = zero
   int32_t n_seqs, n_segs, H, dk, dv;
   float *S_out;             // [n_seqs, H, dv, dk]
 };

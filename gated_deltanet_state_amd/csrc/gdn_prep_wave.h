@@ -243,6 +243,16 @@ __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha
 
   // ---- 6. M o Q K^T (s <= r) into the block slots, then its fragments ----
   if (q) {
+    // keys again (cache hits): keeping the fragments of step 1 alive all
+    // the way here would cost registers in every caller
+    bf16x8 kg[4][NKS];
+#pragma unroll
+    for (int bt = 0; bt < 4; ++bt) {
+      const int r = min(16 * bt + jl, Lc - 1);
+      const bf16 *src = k + ((int64_t)(t0 + r) * H + h) * DK + 8 * g4;
+#pragma unroll
+      for (int m = 0; m < NKS; ++m) kg[bt][m] = *reinterpret_cast<const bf16x8 *>(src + 32 * m);
+    }
     f32x4 acc[10];
 #pragma unroll
     for (int t = 0; t < 10; ++t) acc[t] = zero4();
@@ -254,7 +264,7 @@ __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha
       for (int m = 0; m < NKS; ++m) {
         const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(src + 32 * m);
 #pragma unroll
-        for (int bj = 0; bj <= bi; ++bj) acc[blk(bi, bj)] = mfma_bf16(qf, kf[bj][m], acc[blk(bi, bj)]);
+        for (int bj = 0; bj <= bi; ++bj) acc[blk(bi, bj)] = mfma_bf16(qf, kg[bj][m], acc[blk(bi, bj)]);
       }
     }
     wave_lds_fence();   // the Tau fragments above have been read

@@ -110,7 +110,8 @@ def test_workspace_queries(lib, monkeypatch):
     assert extra % per_seg == 0 and 2 <= extra // per_seg <= 16
     # the override sets P directly
     monkeypatch.setenv("GDN_REPLAY_SEGMENTS", "5")
-    assert lib.gdn_replay_workspace_bytes(2, 300, 4, 64, 128) == tau(2, 300, 4) + 2 * 5 * 4 * (64 * 64 + 128 * 64) * 4
+    # (room for the replay with outputs: segment operators, states and start states)
+    assert lib.gdn_replay_workspace_bytes(2, 300, 4, 64, 128) == tau(2, 300, 4) + 2 * 5 * 4 * (64 * 64 + 2 * 128 * 64) * 4
     monkeypatch.setenv("GDN_REPLAY_SEGMENTS", "1")
     assert lib.gdn_replay_workspace_bytes(1, 3277, 32, 128, 128) == tau(1, 3277, 32)
     monkeypatch.delenv("GDN_REPLAY_SEGMENTS")

@@ -94,3 +94,66 @@ def test_default_choice_splits_a_single_long_tail(monkeypatch):
     e = rel(S[:, heads], S_ref)
     print("default split err_S %.3e" % e, flush=True)
     assert e <= TOL_BF16
+
+
+# ---- time split with outputs: segment operators, their composition (which
+# also gives every segment's start state), then each segment again with
+# outputs from that start state ----
+
+def with_outputs(inp, S0=None):
+    gdn, torch = _gdn()
+    d = dev(inp)
+    S0_t = None if S0 is None else torch.from_numpy(np.asarray(S0, np.float32)).cuda()
+    o, S = gdn.replay(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu"], S0=S0_t, want_o=True)
+    torch.cuda.synchronize()
+    return to_np(o), to_np(S)
+
+
+def check_o(inp, S0=None, tol=TOL_BF16):
+    o, S = with_outputs(inp, S0=S0)
+    o_ref, S_ref = oracle_replay(inp, S0=S0, want_o=True)
+    eo, eS = rel(o, o_ref), rel(S, S_ref)
+    print("P-split with outputs err_o %.3e err_S %.3e (tol %.1e)" % (eo, eS, tol), flush=True)
+    assert eo <= tol and eS <= tol
+    return o, S
+
+
+@pytest.mark.parametrize("P", [2, 3, 5])
+def test_split_with_outputs_ragged(P, monkeypatch):
+    monkeypatch.setenv("GDN_REPLAY_SEGMENTS", str(P))
+    lengths = [1, 63, 64, 65, 0, 200, 330]
+    inp = workloads.generate(lengths, H=3, dk=128, dv=128, dtype="bf16", seed=51)
+    check_o(inp)
+    check_o(inp, S0=start_state(len(lengths), 3, 128, 128, 52))
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+def test_split_with_outputs_shapes(dk, dv, monkeypatch):
+    monkeypatch.setenv("GDN_REPLAY_SEGMENTS", "4")
+    inp = workloads.generate([500, 77], H=2, dk=dk, dv=dv, dtype="bf16", seed=53)
+    check_o(inp, S0=start_state(2, 2, dv, dk, 54))
+
+
+def test_split_with_outputs_alpha_one_matches_unsplit(monkeypatch):
+    # alpha = 1: every segment's start state carries real weight
+    inp = workloads.generate([1500], H=4, dk=128, dv=128, dtype="bf16", seed=55, alpha_one=True)
+    monkeypatch.setenv("GDN_REPLAY_SEGMENTS", "1")
+    o1, S1 = check_o(inp)
+    monkeypatch.setenv("GDN_REPLAY_SEGMENTS", "6")
+    o6, S6 = check_o(inp)
+    assert rel(o6, o1) <= TOL_BF16 and rel(S6, S1) <= TOL_BF16
+
+
+def test_split_with_outputs_start_state_aliases_final(monkeypatch):
+    # S_final may alias S0: the start state of segment 0 is read before the
+    # composed final state is written
+    monkeypatch.setenv("GDN_REPLAY_SEGMENTS", "3")
+    gdn, torch = _gdn()
+    inp = workloads.generate([400], H=2, dk=128, dv=128, dtype="bf16", seed=57)
+    S0 = start_state(1, 2, 128, 128, 58)
+    d = dev(inp)
+    buf = torch.from_numpy(np.asarray(S0, np.float32)).cuda()
+    o, S = gdn.replay(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu"], S0=buf, want_o=True, S_out=buf)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_replay(inp, S0=S0, want_o=True)
+    assert rel(to_np(o), o_ref) <= TOL_BF16 and rel(to_np(buf), S_ref) <= TOL_BF16
