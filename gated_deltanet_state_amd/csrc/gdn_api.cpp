@@ -94,6 +94,18 @@ int replay_segments(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t d
   return best;
 }
 
+// State-only bf16 replays can also run one workgroup per row tile whose
+// waves split the key dimension (gdn_chain_dks.hip): no time split, no
+// composition, but one chunk step per ~1.6 us, bound by staging a chunk's
+// keys and record into every tile's compute unit.  On one 3277-token tail
+// over 32 heads that is slower than the time split, so it runs only on
+// request: GDN_REPLAY_KEYSPLIT=1 (with at most 256 row tiles in all).
+bool replay_dks(int32_t n_seqs, int32_t n_heads, int32_t dv) {
+  const char *env = std::getenv("GDN_REPLAY_KEYSPLIT");
+  if (!env || std::atoi(env) != 1) return false;
+  return (int64_t)n_seqs * n_heads * (dv / 16) <= 256;
+}
+
 // Segments per sequence for a bf16 replay with outputs.  A split runs three
 // passes: the state-only segment operators, their composition (which also
 // yields every segment's true start state), and every segment again with
@@ -170,8 +182,10 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
       (s = check_align("S_final", S_final)))
     return s;
   const bool bf = in_dtype == GDN_BF16;
-  const int32_t P = !bf ? 1 : (o ? replay_segments_o(n_seqs, n_tokens, n_heads, dk, dv)
-                                 : replay_segments(n_seqs, n_tokens, n_heads, dk, dv));
+  const bool dks = bf && !o && replay_dks(n_seqs, n_heads, dv);
+  const int32_t P = (!bf || dks) ? 1
+                                 : (o ? replay_segments_o(n_seqs, n_tokens, n_heads, dk, dv)
+                                      : replay_segments(n_seqs, n_tokens, n_heads, dk, dv));
   const size_t tau_bytes = gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads);
   const size_t need = tau_bytes + seg_workspace_bytes(n_seqs, P, n_heads, dk, dv, o != nullptr);
   if (workspace_bytes < need || !workspace)
@@ -216,6 +230,7 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
     p.T_out = nullptr;
     p.tiles_T = 0;
     p.tiles_S = dv / 16;
+    if (dks) return launched(gdn::launch_chain_dks(p, st), "gdn_replay launch");
     return launched(bf ? gdn::launch_chain_bf16(p, st) : gdn::launch_chain(p, st), "gdn_replay launch");
   }
   // time split: segment operators, then their composition

@@ -16,7 +16,7 @@ namespace gdn {
 // without reading cu (which lives on the device).
 // ---------------------------------------------------------------------------
 constexpr int kChunk = 64;
-// Per-chunk factor record, one per (slot, head), 24 KiB:
+// Per-chunk factor record, one per (slot, head), 25 KiB:
 //   * fp32 inputs: Tau = (I + A)^{-1}, lower 16 x 16 block rows packed, block
 //     row b holds 16 rows x 16 (b + 1) columns, row-major, at element offset
 //     256 * b (b + 1) / 2 (2560 floats);
@@ -25,9 +25,12 @@ constexpr int kChunk = 64;
 //     C-layout tiles (see kTauFrags), split bf16 planes [hi/lo][fragment]
 //     [lane][8]; bytes [12 KiB, 24 KiB), replays with outputs only: the
 //     decay-masked M o Q K^T (M_rs = e^{g_r - g_s}, s <= r) in the same
-//     fragment layout.
-constexpr int kRecFloats = 6144;
+//     fragment layout; bytes [24 KiB, 25 KiB): the chunk's gates as fp32,
+//     [0, 64) e^{g_t}, [64, 128) e^{g_L - g_t} (0 past the chunk),
+//     [128] e^{g_L}, with g the cumulative log-gate and L the chunk length.
+constexpr int kRecFloats = 6400;
 constexpr int kRecPOffsetBytes = 12288;
+constexpr int kRecGateOffsetBytes = 24576;
 // Fragment f of Tau covers token block row bt and the pair of 16-column
 // blocks (2m, 2m + 1): f = 0: (0,0), 1: (1,0), 2: (2,0), 3: (2,1), 4: (3,0),
 // 5: (3,1).  Lane l holds row 16 bt + (l & 15), columns
@@ -119,6 +122,7 @@ hipError_t launch_prep(const PrepLaunch &p, hipStream_t stream);        // dispa
 hipError_t launch_prep_bf16(const PrepLaunch &p, hipStream_t stream);
 hipError_t launch_chain(const ChainLaunch &p, hipStream_t stream);        // fp32 inputs
 hipError_t launch_chain_bf16(const ChainLaunch &p, hipStream_t stream);   // bf16 inputs
+hipError_t launch_chain_dks(const ChainLaunch &p, hipStream_t stream);    // bf16, state only, few row tiles
 hipError_t launch_compose(const ComposeLaunch &p, hipStream_t stream);
 hipError_t launch_seg_compose(const SegComposeLaunch &p, hipStream_t stream);
 
