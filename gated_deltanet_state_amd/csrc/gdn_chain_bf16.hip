@@ -188,11 +188,19 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     // transition rows) and steps about 1.6 times faster, so it takes a
     // larger share: e = round(chunks / (P - 1 + 1.6)) chunks for each later
     // segment, the rest for segment 0 (with seg_uniform: ceil(chunks / P)
-    // each).  Segments past the end are empty.
+    // each).  When the workgroup builds its own records first, segment 0
+    // keeps to one record per prologue wave (a second round of the
+    // prologue costs more than a chunk step elsewhere) and the later
+    // segments take ceil(rest / (P - 1)) each.  Segments past the end are
+    // empty.
     const int P = p.n_segs, nch = (cend - cbeg + CH - 1) / CH;
     const int den = 5 * (P - 1) + 8;
-    const int e = p.seg_uniform ? (nch + P - 1) / P : max(1, (5 * nch + den / 2) / den);
-    const int c0 = p.seg_uniform ? e : max(0, nch - (P - 1) * e);
+    int e = p.seg_uniform ? (nch + P - 1) / P : max(1, (5 * nch + den / 2) / den);
+    int c0 = p.seg_uniform ? e : max(0, nch - (P - 1) * e);
+    if (FUSED && !p.seg_uniform && c0 > C::NPW) {
+      c0 = C::NPW;
+      e = (nch - c0 + P - 2) / (P - 1);
+    }
     const int64_t off = seg == 0 ? 0 : (int64_t)(c0 + (seg - 1) * e) * CH;
     const int64_t len = (int64_t)(seg == 0 ? c0 : e) * CH;
     tbeg = (int)min((int64_t)cend, (int64_t)cbeg + off);
