@@ -139,7 +139,6 @@ __device__ __forceinline__ void kt_frags(int m, uint32_t addr, bf16x8 (&a)[NSB])
 template <int DK, bool WANT_O, int NW, int RT, bool FUSED>
 __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int n_items) {
   static_assert(RT == 1 || RT == 2, "one or two row tiles per wave");
-  static_assert(!WANT_O || RT == 1, "outputs use one row tile per wave");
   using C = Cfg<DK, WANT_O, NW, RT, FUSED>;
   constexpr int TW = C::TW;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -367,25 +366,28 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 
   // Outputs of a chunk are stored at the start of the next one, so that
   // the hand-over wait (which also counts stores) finds them complete.
-  f32x4 zp[4];
+  f32x4 zp[RT][4];
   int tp = 0, Lp = 0;
   auto store_o = [&]() {
-    const int64_t ob = ((int64_t)(tp + 4 * g4) * H + h) * DV + row0 + jl;
     const int64_t tok = (int64_t)H * DV;
-    if (p.o_bf16) {
-      bf16 *o = reinterpret_cast<bf16 *>(p.o) + ob;
 #pragma unroll
-      for (int bt = 0; bt < 4; ++bt)
+    for (int rt = 0; rt < RT; ++rt) {
+      const int64_t ob = ((int64_t)(tp + 4 * g4) * H + h) * DV + row0 + 16 * rt + jl;
+      if (p.o_bf16) {
+        bf16 *o = reinterpret_cast<bf16 *>(p.o) + ob;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (16 * bt + 4 * g4 + e < Lp) o[(16 * bt + e) * tok] = (bf16)zp[bt][e];
-    } else {
-      float *o = reinterpret_cast<float *>(p.o) + ob;
+        for (int bt = 0; bt < 4; ++bt)
 #pragma unroll
-      for (int bt = 0; bt < 4; ++bt)
+          for (int e = 0; e < 4; ++e)
+            if (16 * bt + 4 * g4 + e < Lp) o[(16 * bt + e) * tok] = (bf16)zp[rt][bt][e];
+      } else {
+        float *o = reinterpret_cast<float *>(p.o) + ob;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (16 * bt + 4 * g4 + e < Lp) o[(16 * bt + e) * tok] = zp[bt][e];
+        for (int bt = 0; bt < 4; ++bt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (16 * bt + 4 * g4 + e < Lp) o[(16 * bt + e) * tok] = zp[rt][bt][e];
+      }
     }
     Lp = 0;
   };
@@ -406,7 +408,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     const float *sG = sG0 + b * C::GN;
     auto frag = [&](int blk) { return *reinterpret_cast<const bf16x8 *>(buf + blk * 1024 + 16 * l); };
 
-    if constexpr (RT == 2) {
+    if constexpr (RT == 2 && !WANT_O) {
       // ---- two row tiles, skewed by one stage: tile 1's vector-ALU work
       // (fragment splits, residuals) sits next to tile 0's MFMAs and the
       // other way round, so the two can overlap.  The fragments both tiles
@@ -620,30 +622,43 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
           for (int bt = 0; bt < 4; ++bt) dd[rt][bt] += d2[rt][bt];
       }
 
-      // ---- O = e^g Q S^T + (M o Q K^T) D  (one row tile per wave) ----
+      // ---- O = e^g Q S^T + (M o Q K^T) D  (every Q and M o Q K^T fragment
+      // read once for the wave's row tiles) ----
       if (WANT_O) {
-        bf16x8 dh[2], dl[2];
-        b_frag_split(dd[0][0], dd[0][1], dh[0], dl[0]);
-        b_frag_split(dd[0][2], dd[0][3], dh[1], dl[1]);
-        f32x4 z[4], z2[4];
+        bf16x8 dh[RT][2], dl[RT][2];
 #pragma unroll
-        for (int bt = 0; bt < 4; ++bt) z[bt] = z2[bt] = zero4();
+        for (int rt = 0; rt < RT; ++rt) {
+          b_frag_split(dd[rt][0], dd[rt][1], dh[rt][0], dl[rt][0]);
+          b_frag_split(dd[rt][2], dd[rt][3], dh[rt][1], dl[rt][1]);
+        }
+        f32x4 z[RT][4], z2[RT][4];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) z[rt][bt] = z2[rt][bt] = zero4();
 #pragma unroll
         for (int m = 0; m < C::NKS; ++m) {
           bf16x8 a[4];
 #pragma unroll
           for (int bt = 0; bt < 4; ++bt) a[bt] = frag(C::bQA + bt * C::NKS + m);
 #pragma unroll
-          for (int bt = 0; bt < 4; ++bt) z[bt] = mfma_bf16(a[bt], sh[0][m], z[bt]);
+          for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int bt = 0; bt < 4; ++bt) z2[bt] = mfma_bf16(a[bt], sl[0][m], z2[bt]);
+            for (int bt = 0; bt < 4; ++bt) z[rt][bt] = mfma_bf16(a[bt], sh[rt][m], z[rt][bt]);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int bt = 0; bt < 4; ++bt) z2[rt][bt] = mfma_bf16(a[bt], sl[rt][m], z2[rt][bt]);
         }
 #pragma unroll
         for (int bt = 0; bt < 4; ++bt) {
           const f32x4 eg = *reinterpret_cast<const f32x4 *>(sG + G_EG + 16 * bt + 4 * g4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) z[bt][e] = (z[bt][e] + z2[bt][e]) * eg[e];
-          z2[bt] = zero4();
+          for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[rt][bt][e] = (z[rt][bt][e] + z2[rt][bt][e]) * eg[e];
+            z2[rt][bt] = zero4();
+          }
         }
         {
           constexpr int ford[kTauFrags] = {0, 2, 4, 1, 3, 5};
@@ -656,19 +671,25 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 #pragma unroll
           for (int pass = 0; pass < 3; ++pass)
 #pragma unroll
-            for (int i = 0; i < kTauFrags; ++i) {
-              const int f = ford[i];
-              const int bt = f < 2 ? f : (f - 2) / 2 + 2;
-              const int m = f < 2 ? 0 : (f - 2) % 2;
-              if (pass == 0) z[bt] = mfma_bf16(ph[f], dh[m], z[bt]);
-              if (pass == 1) z2[bt] = mfma_bf16(ph[f], dl[m], z2[bt]);
-              if (pass == 2) z[bt] = mfma_bf16(pl[f], dh[m], z[bt]);
-            }
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int bt = 0; bt < 4; ++bt) z[bt] += z2[bt];
+              for (int i = 0; i < kTauFrags; ++i) {
+                const int f = ford[i];
+                const int bt = f < 2 ? f : (f - 2) / 2 + 2;
+                const int m = f < 2 ? 0 : (f - 2) % 2;
+                if (pass == 0) z[rt][bt] = mfma_bf16(ph[f], dh[rt][m], z[rt][bt]);
+                if (pass == 1) z2[rt][bt] = mfma_bf16(ph[f], dl[rt][m], z2[rt][bt]);
+                if (pass == 2) z[rt][bt] = mfma_bf16(pl[f], dh[rt][m], z[rt][bt]);
+              }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int bt = 0; bt < 4; ++bt) z[rt][bt] += z2[rt][bt];
         }
 #pragma unroll
-        for (int bt = 0; bt < 4; ++bt) zp[bt] = z[bt];
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int bt = 0; bt < 4; ++bt) zp[rt][bt] = z[rt][bt];
         tp = t0;
         Lp = Lc;
       }
@@ -786,8 +807,11 @@ template <int DK>
 hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
   if (p.o) {
     if (p.tiles_T != 0 || p.fuse_prep) return hipErrorInvalidValue;
-    // segments of a time split: one eight-wave workgroup per (segment, head)
-    if (p.n_segs > 1 && p.tiles_S % 8 == 0) return launch_b<DK, true, 8, 1>(p, stream);
+    // one eight-wave workgroup per (sequence, segment, head): two waves per
+    // SIMD interleave their work (measured on 16 packed tails: 668 us
+    // against 933 us for two four-wave workgroups per head and 826 us for
+    // four waves with two row tiles each)
+    if (p.tiles_S % 8 == 0) return launch_b<DK, true, 8, 1>(p, stream);
     return launch_b<DK, true, 4, 1>(p, stream);
   }
   // Transition and state tiles of a segment share one workgroup, two row
