@@ -194,7 +194,6 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   gdn::PrepLaunch pp{};
   pp.k = k;
-  pp.q = (o && bf) ? q : nullptr;
   pp.alpha = alpha;
   pp.beta = beta;
   pp.cu = cu_seqlens;
@@ -240,7 +239,6 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   p.n_segs = P;
   p.seg_uniform = o ? 1 : 0;
   p.fuse_prep = 1;
-  p.q_rec = o ? q : nullptr;
   p.skip_T0 = 1;
   p.T_frags = 1;
   p.tiles_T = dk / 16;
@@ -273,7 +271,6 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   r.tiles_T = 0;
   r.T_frags = 0;
   r.fuse_prep = 0;
-  r.q_rec = nullptr;
   return launched(gdn::launch_chain_bf16(r, st), "gdn_replay segment output launch");
 }
 

@@ -31,12 +31,13 @@
 // the products of both tiles.  While
 // chunk c runs from one LDS buffer set, the operands of chunk c + 1 are
 // copied into the other one by load-to-LDS DMA (buffer_load ... lds; no
-// registers, no staging code): K and Q as MFMA A fragments, the per-chunk
-// record of gdn_prep_wave.h (Tau diag(beta) and, with outputs, M o Q K^T
-// fragments), and the value
-// columns of the workgroup; K^T fragments come from the staged keys by the
-// transposing LDS read.  Every fragment read is then a conflict-free
-// 16-byte LDS read by lane.  One LDS barrier per chunk.
+// registers, no staging code): K and Q as MFMA A fragments, the Tau
+// diag(beta) fragments of the per-chunk record of gdn_prep_wave.h, and the
+// value columns of the workgroup; K^T fragments come from the staged keys
+// by the transposing LDS read.  Every fragment read is then a
+// conflict-free 16-byte LDS read by lane.  With outputs, the waves also
+// build the chunk's M o Q K^T from the staged Q and K.  One LDS barrier per
+// chunk.
 //
 // The same kernel builds the affine chunk operator of the page "LinearKV:
 // One Cached State Suffices for Position-Independent Caching in Hybrid
@@ -71,12 +72,14 @@ struct Cfg {
   static constexpr int VU = 2 * NSV;           // 16-byte units per staged value row
   static constexpr int NVB = CH * VU / 64;     // value slab blocks
   static constexpr int bKA = 0, bTF = NKA, bV = bTF + NTF, bQA = bV + NVB;
-  static constexpr int bPF = bQA + (WANT_O ? NKA : 0);   // M o Q K^T fragments (outputs only)
-  static constexpr int NBLK = bPF + (WANT_O ? NTF : 0);
+  static constexpr int NBLK = bQA + (WANT_O ? NKA : 0);
   static constexpr size_t BUF = (size_t)NBLK * 1024;
   static constexpr int GN = 3 * CH + 4;        // gate floats per buffer set
   static constexpr size_t oG = 2 * BUF;
-  static constexpr size_t TOTAL = oG + 2 * GN * 4;
+  // outputs: M o Q K^T of two chunks as split-bf16 fragments (hi, lo planes)
+  static constexpr size_t PSET = (size_t)2 * kTauFragPlane * 2;
+  static constexpr size_t oP = oG + 2 * GN * 4;
+  static constexpr size_t TOTAL = oP + (WANT_O ? 2 * PSET : 0);
   // the prologue that builds the segment's records (on at most eight
   // waves) uses the LDS above buffer set 0, whose first chunk is in flight
   // meanwhile
@@ -242,7 +245,8 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   // ---- DMA of one chunk's operands into buffer set b ----
   // Rows past the chunk are copies of its last row: they only meet zero
   // coefficients (beta = 0 in the Tau columns, zero decayed corrections in
-  // the state update, masked M o Q K^T), so any finite value serves.
+  // the state update, outputs past the chunk not stored), so any finite
+  // value serves.
   // Every wave issues whole 1 KiB blocks (one 16-byte copy per lane); the
   // loops are unrolled over compile-time block ranges with the wave index
   // uniform, so the issue is straight-line scalar-branch code.
@@ -268,8 +272,6 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       const int f = j * NW + w;
       if (with_rec && (C::NTF % NW == 0 || f < C::NTF)) {
         dma16_global(rec + f * 1024, (lds_void *)(buf + (C::bTF + f) * 1024));
-        if (WANT_O)                                            // M o Q K^T fragments (record)
-          dma16_global(rec + kRecPOffsetBytes + f * 1024, (lds_void *)(buf + (C::bPF + f) * 1024));
       }
     }
     if (grp_S) {                                               // value slab of the workgroup
@@ -349,7 +351,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       prep_chunk_wave<DK>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta), H, h,
                           tc, min(CH, tend - tc),
                           const_cast<char *>(grec) + ((slot0 + c) * H + h) * (int64_t)(kRecFloats * 4), scr,
-                          c == 0 ? smem + C::bTF * 1024 : nullptr, reinterpret_cast<const bf16 *>(p.q_rec));
+                          c == 0 ? smem + C::bTF * 1024 : nullptr);
     }
     wait_vmem();
     __syncthreads();
@@ -364,10 +366,84 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   lds_barrier();
   read_v(0);
 
-  // Outputs of a chunk are stored at the start of the next one, so that
-  // the hand-over wait (which also counts stores) finds them complete.
+  // Outputs.  O = diag(e^g) Q S^T + (M o Q K^T) D: the first part is
+  // formed in the chunk itself; M o Q K^T of the chunk is built during the
+  // chunk (split between the waves, into one of two LDS sets) and becomes
+  // visible to every wave at the chunk's hand-over barrier, so the second
+  // part and the store of a chunk's outputs follow in the next chunk (or
+  // after the last one).  zp holds the pending outputs, dph / dpl the
+  // pending D as split-bf16 B fragments, tp / Lp its token range.
   f32x4 zp[RT][4];
+  bf16x8 dph[RT][2], dpl[RT][2];
   int tp = 0, Lp = 0;
+  // M o Q K^T (M_rs = e^{g_r - g_s}, s <= r) of the chunk in buffer set b
+  // into set b of the M o Q K^T fragments: the twelve 16 x 16 halves of
+  // the six fragments (gdn_internal.h order) round-robin over the waves;
+  // tile (bi, bj) lands in fragment (bi, bj >> 1), lane (r & 15) +
+  // 16 (c >> 2), element 4 (bj & 1) + (c & 3) for row r, column 16 bj + c
+  auto build_p = [&](int b) {
+    const char *buf = smem + b * C::BUF;
+    const float *sG = sG0 + b * C::GN;
+    bf16 *sP = reinterpret_cast<bf16 *>(smem + C::oP + b * C::PSET);
+    for (int t = w; t < 2 * kTauFrags; t += NW) {
+      const int f = t >> 1, half = t & 1;
+      const int bi = f < 2 ? f : (f - 2) / 2 + 2;
+      const int bj = 2 * (f < 2 ? 0 : (f - 2) % 2) + half;
+      f32x4 c = zero4();
+      if (bj <= bi) {
+#pragma unroll
+        for (int m = 0; m < C::NKS; ++m) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(buf + (C::bQA + bi * C::NKS + m) * 1024 + 16 * l);
+          const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(buf + (C::bKA + bj * C::NKS + m) * 1024 + 16 * l);
+          c = mfma_bf16(a, bb, c);
+        }
+      }
+      const int col = 16 * bj + jl;
+      const float gc = sG[G_G + col];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * bi + 4 * g4 + e;
+        const float x = (col <= r) ? __expf(sG[G_G + r] - gc) * c[e] : 0.f;
+        const bf16 hi = (bf16)x;
+        const int idx = (f * 64 + (r & 15) + 16 * (jl >> 2)) * 8 + 4 * half + (jl & 3);
+        sP[idx] = hi;
+        sP[kTauFragPlane + idx] = (bf16)(x - (float)hi);
+      }
+    }
+  };
+  // the pending outputs: add (M o Q K^T) D from set b, then store
+  auto finish_o = [&](int b) {
+    const bf16 *sP = reinterpret_cast<const bf16 *>(smem + C::oP + b * C::PSET);
+    constexpr int ford[kTauFrags] = {0, 2, 4, 1, 3, 5};
+    bf16x8 ph[kTauFrags], pl[kTauFrags];
+#pragma unroll
+    for (int f = 0; f < kTauFrags; ++f) {
+      ph[f] = *reinterpret_cast<const bf16x8 *>(sP + (f * 64 + l) * 8);
+      pl[f] = *reinterpret_cast<const bf16x8 *>(sP + kTauFragPlane + (f * 64 + l) * 8);
+    }
+    f32x4 z2[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) z2[rt][bt] = zero4();
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < kTauFrags; ++i) {
+          const int f = ford[i];
+          const int bt = f < 2 ? f : (f - 2) / 2 + 2;
+          const int m = f < 2 ? 0 : (f - 2) % 2;
+          if (pass == 0) zp[rt][bt] = mfma_bf16(ph[f], dph[rt][m], zp[rt][bt]);
+          if (pass == 1) z2[rt][bt] = mfma_bf16(ph[f], dpl[rt][m], z2[rt][bt]);
+          if (pass == 2) zp[rt][bt] = mfma_bf16(pl[f], dph[rt][m], zp[rt][bt]);
+        }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) zp[rt][bt] += z2[rt][bt];
+  };
   auto store_o = [&]() {
     const int64_t tok = (int64_t)H * DV;
 #pragma unroll
@@ -398,7 +474,6 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     const int Lc = min(CH, tend - t0);
     const bool more = t0 + CH < tend;
     const int L1 = more ? min(CH, tend - t0 - CH) : 0;
-    if (WANT_O && active && Lp > 0) store_o();
     // operands of the next chunk: in flight while this one runs
     if (more) {
       issue_dma(b ^ 1, t0 + CH, L1, slot + 1);
@@ -622,20 +697,24 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
           for (int bt = 0; bt < 4; ++bt) dd[rt][bt] += d2[rt][bt];
       }
 
-      // ---- O = e^g Q S^T + (M o Q K^T) D  (every Q and M o Q K^T fragment
-      // read once for the wave's row tiles) ----
+      // ---- outputs: the previous chunk's finished and stored; this one's
+      // e^g Q S^T (every Q fragment read once for the wave's row tiles) and
+      // its D, pending ----
       if (WANT_O) {
-        bf16x8 dh[RT][2], dl[RT][2];
+        if (Lp > 0) {
+          finish_o(b ^ 1);
+          store_o();
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          b_frag_split(dd[rt][0], dd[rt][1], dh[rt][0], dl[rt][0]);
-          b_frag_split(dd[rt][2], dd[rt][3], dh[rt][1], dl[rt][1]);
+          b_frag_split(dd[rt][0], dd[rt][1], dph[rt][0], dpl[rt][0]);
+          b_frag_split(dd[rt][2], dd[rt][3], dph[rt][1], dpl[rt][1]);
         }
-        f32x4 z[RT][4], z2[RT][4];
+        f32x4 z2[RT][4];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int bt = 0; bt < 4; ++bt) z[rt][bt] = z2[rt][bt] = zero4();
+          for (int bt = 0; bt < 4; ++bt) zp[rt][bt] = z2[rt][bt] = zero4();
 #pragma unroll
         for (int m = 0; m < C::NKS; ++m) {
           bf16x8 a[4];
@@ -644,7 +723,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int bt = 0; bt < 4; ++bt) z[rt][bt] = mfma_bf16(a[bt], sh[rt][m], z[rt][bt]);
+            for (int bt = 0; bt < 4; ++bt) zp[rt][bt] = mfma_bf16(a[bt], sh[rt][m], zp[rt][bt]);
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -654,42 +733,10 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
         for (int bt = 0; bt < 4; ++bt) {
           const f32x4 eg = *reinterpret_cast<const f32x4 *>(sG + G_EG + 16 * bt + 4 * g4);
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[rt][bt][e] = (z[rt][bt][e] + z2[rt][bt][e]) * eg[e];
-            z2[rt][bt] = zero4();
-          }
-        }
-        {
-          constexpr int ford[kTauFrags] = {0, 2, 4, 1, 3, 5};
-          bf16x8 ph[kTauFrags], pl[kTauFrags];
-#pragma unroll
-          for (int f = 0; f < kTauFrags; ++f) {
-            ph[f] = frag(C::bPF + f);
-            pl[f] = frag(C::bPF + kTauFrags + f);
-          }
-#pragma unroll
-          for (int pass = 0; pass < 3; ++pass)
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-              for (int i = 0; i < kTauFrags; ++i) {
-                const int f = ford[i];
-                const int bt = f < 2 ? f : (f - 2) / 2 + 2;
-                const int m = f < 2 ? 0 : (f - 2) % 2;
-                if (pass == 0) z[rt][bt] = mfma_bf16(ph[f], dh[rt][m], z[rt][bt]);
-                if (pass == 1) z2[rt][bt] = mfma_bf16(ph[f], dl[rt][m], z2[rt][bt]);
-                if (pass == 2) z[rt][bt] = mfma_bf16(pl[f], dh[rt][m], z[rt][bt]);
-              }
-#pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int bt = 0; bt < 4; ++bt) z[rt][bt] += z2[rt][bt];
+            for (int e = 0; e < 4; ++e) zp[rt][bt][e] = (zp[rt][bt][e] + z2[rt][bt][e]) * eg[e];
         }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int bt = 0; bt < 4; ++bt) zp[rt][bt] = z[rt][bt];
         tp = t0;
         Lp = Lc;
       }
@@ -733,6 +780,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       }
     }
 
+    if (WANT_O) build_p(b);
     // ---- hand over to the next chunk ----
     if (more) gates(b ^ 1, L1);
     wait_vmem();
@@ -741,7 +789,10 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   }
 
   // ---------------- epilogue: final rows ----------------
-  if (WANT_O && active && Lp > 0) store_o();
+  if (WANT_O && active && Lp > 0) {
+    finish_o(b ^ 1);   // the last chunk's set (b has moved past it)
+    store_o();
+  }
   const int64_t unit = ((int64_t)n * p.n_segs + seg) * H + h;
   if (p.T_frags) {
     // Segment operator as composition fragments: the transition rows go to

@@ -16,21 +16,18 @@ namespace gdn {
 // without reading cu (which lives on the device).
 // ---------------------------------------------------------------------------
 constexpr int kChunk = 64;
-// Per-chunk factor record, one per (slot, head), 25 KiB:
+// Per-chunk factor record, one per (slot, head), 13 KiB:
 //   * fp32 inputs: Tau = (I + A)^{-1}, lower 16 x 16 block rows packed, block
 //     row b holds 16 rows x 16 (b + 1) columns, row-major, at element offset
 //     256 * b (b + 1) / 2 (2560 floats);
 //   * bf16 inputs: bytes [0, 12 KiB): Tau diag(beta) as the six A operands of
 //     the k = 32 MFMAs that apply it to a 64 x 16 right-hand side given as
 //     C-layout tiles (see kTauFrags), split bf16 planes [hi/lo][fragment]
-//     [lane][8]; bytes [12 KiB, 24 KiB), replays with outputs only: the
-//     decay-masked M o Q K^T (M_rs = e^{g_r - g_s}, s <= r) in the same
-//     fragment layout; bytes [24 KiB, 25 KiB): the chunk's gates as fp32,
+//     [lane][8]; bytes [12 KiB, 13 KiB): the chunk's gates as fp32,
 //     [0, 64) e^{g_t}, [64, 128) e^{g_L - g_t} (0 past the chunk),
 //     [128] e^{g_L}, with g the cumulative log-gate and L the chunk length.
-constexpr int kRecFloats = 6400;
-constexpr int kRecPOffsetBytes = 12288;
-constexpr int kRecGateOffsetBytes = 24576;
+constexpr int kRecFloats = 3328;
+constexpr int kRecGateOffsetBytes = 12288;
 // Fragment f of Tau covers token block row bt and the pair of 16-column
 // blocks (2m, 2m + 1): f = 0: (0,0), 1: (1,0), 2: (2,0), 3: (2,1), 4: (3,0),
 // 5: (3,1).  Lane l holds row 16 bt + (l & 15), columns
@@ -47,7 +44,6 @@ inline size_t tau_workspace_bytes(int64_t n_tokens, int32_t n_seqs, int32_t n_he
 // Per-chunk factor build: one workgroup per (slot, head).
 struct PrepLaunch {
   const void *k, *alpha, *beta;
-  const void *q;     // bf16 replays with outputs: also build M o Q K^T (else null)
   const int32_t *cu;
   int32_t n_seqs, H, dk;
   int in_bf16;
@@ -89,7 +85,6 @@ struct ChainLaunch {
   // bf16 inputs with transition tiles: every workgroup first builds the
   // per-chunk records of its own segment (no separate prep launch)
   int fuse_prep;
-  const void *q_rec;        // fused prologue: also build M o Q K^T from these queries (or null)
 };
 
 struct ComposeLaunch {

@@ -41,8 +41,7 @@ __global__ void __launch_bounds__(PW * 64) prep_bf16_kernel(PrepLaunch p) {
   const int Lc = min(kChunk, len - (int)j * kChunk);
   char *rec = reinterpret_cast<char *>(p.tau + (slot * H + h) * (int64_t)kRecFloats);
   prep_chunk_wave<DK>(reinterpret_cast<const bf16 *>(p.k), reinterpret_cast<const bf16 *>(p.alpha),
-                      reinterpret_cast<const bf16 *>(p.beta), H, h, t0, Lc, rec, scratch[w], nullptr,
-                      reinterpret_cast<const bf16 *>(p.q));
+                      reinterpret_cast<const bf16 *>(p.beta), H, h, t0, Lc, rec, scratch[w], nullptr);
 }
 
 template <int DK>

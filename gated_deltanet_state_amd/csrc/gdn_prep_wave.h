@@ -22,9 +22,7 @@
 //   4. off-diagonal blocks Tau_ij = -Tau_ii sum_{m=j}^{i-1} A_im Tau_mj on
 //      split-bf16 k = 16 MFMAs, in three dependency levels
 //   5. Tau diag(beta) as split-bf16 A fragments of the recurrence kernel's
-//      k = 32 products (record layout of gdn_internal.h)
-//   6. (replays with outputs) the decay-masked M o Q K^T in the same
-//      fragment layout, for the intra-chunk part of the outputs.
+//      k = 32 products (record layout of gdn_internal.h).
 // LDS per wave: kPrepWaveLds bytes (A blocks, overwritten in place by the
 // Tau blocks; a transposed copy of the diagonal Tau blocks; gates).
 #pragma once
@@ -62,12 +60,10 @@ __device__ __forceinline__ f32x4 acc3_sum(const Acc3 &a) { return a.a + a.b + a.
 // Record of one (chunk, head): tokens t0 .. t0 + Lc - 1 (1 <= Lc <= 64) of
 // head h, keys k [T, H, DK], gates alpha / beta [T, H] (bf16); rec receives
 // kRecFloats * 4 bytes; scratch is this wave's kPrepWaveLds bytes of LDS;
-// lds_rec (may be null) receives a second copy of the Tau fragments in LDS;
-// q (may be null) requests the M o Q K^T fragments as well.
+// lds_rec (may be null) receives a second copy of the Tau fragments in LDS.
 template <int DK>
 __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha, const bf16 *beta, int H, int h,
-                                                int t0, int Lc, char *rec, float *scratch, char *lds_rec = nullptr,
-                                                const bf16 *q = nullptr) {
+                                                int t0, int Lc, char *rec, float *scratch, char *lds_rec = nullptr) {
   using namespace prep_detail;
   constexpr int NKS = DK / 32;
   float *sA = scratch;             // 10 blocks 16 x 16 row-major: A, then Tau
@@ -249,47 +245,6 @@ __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha
   };
   write_frags(rec, lds_rec, true);
 
-  // ---- 6. M o Q K^T (s <= r) into the block slots, then its fragments ----
-  if (q) {
-    // keys again (cache hits): keeping the fragments of step 1 alive all
-    // the way here would cost registers in every caller
-    bf16x8 kg[4][NKS];
-#pragma unroll
-    for (int bt = 0; bt < 4; ++bt) {
-      const int r = min(16 * bt + jl, Lc - 1);
-      const bf16 *src = k + ((int64_t)(t0 + r) * H + h) * DK + 8 * g4;
-#pragma unroll
-      for (int m = 0; m < NKS; ++m) kg[bt][m] = *reinterpret_cast<const bf16x8 *>(src + 32 * m);
-    }
-    f32x4 acc[10];
-#pragma unroll
-    for (int t = 0; t < 10; ++t) acc[t] = zero4();
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-      const int r = min(16 * bi + jl, Lc - 1);
-      const bf16 *src = q + ((int64_t)(t0 + r) * H + h) * DK + 8 * g4;
-#pragma unroll
-      for (int m = 0; m < NKS; ++m) {
-        const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(src + 32 * m);
-#pragma unroll
-        for (int bj = 0; bj <= bi; ++bj) acc[blk(bi, bj)] = mfma_bf16(qf, kg[bj][m], acc[blk(bi, bj)]);
-      }
-    }
-    wave_lds_fence();   // the Tau fragments above have been read
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int bj = 0; bj <= bi; ++bj) {
-        const int col = 16 * bj + jl, row0 = 16 * bi + 4 * g4;
-        const float gc = sG[col];
-        const f32x4 gr = *reinterpret_cast<const f32x4 *>(sG + row0);
-        float *dst = sA + blk(bi, bj) * 256 + 4 * g4 * 16 + jl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e * 16] = (col <= row0 + e) ? __expf(gr[e] - gc) * acc[blk(bi, bj)][e] : 0.f;
-      }
-    wave_lds_fence();
-    write_frags(rec + kRecPOffsetBytes, nullptr, false);
-  }
 }
 
 }  // namespace gdn

@@ -99,7 +99,7 @@ def test_workspace_queries(lib, monkeypatch):
     # and head; slots = n_tokens / 64 + n_seqs + 1 (sequence n's chunk j sits
     # in slot floor(cu[n] / 64) + n + j)
     monkeypatch.delenv("GDN_REPLAY_SEGMENTS", raising=False)
-    tau = lambda n_seqs, n_tokens, H: (n_tokens // 64 + n_seqs + 1) * H * 25600
+    tau = lambda n_seqs, n_tokens, H: (n_tokens // 64 + n_seqs + 1) * H * 13312
     # 16 sequences x 32 heads already fill the chip: no time split
     assert lib.gdn_replay_workspace_bytes(16, 30000, 32, 128, 128) == tau(16, 30000, 32)
     assert lib.gdn_chunk_operator_workspace_bytes(64, 32768, 32, 128, 128) == tau(64, 32768, 32)

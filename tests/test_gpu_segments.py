@@ -85,7 +85,7 @@ def test_default_choice_splits_a_single_long_tail(monkeypatch):
     monkeypatch.delenv("GDN_REPLAY_SEGMENTS", raising=False)
     gdn, torch = _gdn()
     lib = gdn.library()
-    tau = (3277 // 64 + 2) * 32 * 25600
+    tau = (3277 // 64 + 2) * 32 * 13312
     assert lib.gdn_replay_workspace_bytes(1, 3277, 32, 128, 128) > tau
     inp = workloads.generate([3277], H=32, dk=128, dv=128, dtype="bf16", seed=46)
     S = state_only(inp)
