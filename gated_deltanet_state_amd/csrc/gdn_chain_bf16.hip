@@ -111,7 +111,10 @@ __device__ __forceinline__ int vswz(int r) {
 // and the token order of the paired right-hand sides.  Inline assembly with
 // its own lgkmcnt wait: the transposing read carries no alias information,
 // and as a compiler builtin it would be made to wait for the load-to-LDS
-// copies of the next chunk that are in flight meanwhile.
+// copies of the next chunk that are in flight meanwhile.  The results are
+// early-clobber operands: a read's data may land before the next read of
+// the group has taken its address, so no result may share a register with
+// the address.
 template <int NKS, int D>
 __device__ __forceinline__ void kt_pair(uint32_t addr, int m, bf16x8 &a0, bf16x8 &a1) {
   // two dk blocks D, D + 1 of token half m: four 8-byte reads
@@ -124,7 +127,7 @@ __device__ __forceinline__ void kt_pair(uint32_t addr, int m, bf16x8 &a0, bf16x8
       "ds_read_b64_tr_b16 %2, %4 offset:%c7\n\t"
       "ds_read_b64_tr_b16 %3, %4 offset:%c8\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3)
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
       : "v"(base), "i"(o0), "i"(o0 + NKS * 1024), "i"(o1), "i"(o1 + NKS * 1024));
   a0 = cat_bf16x8(r0, r1);
   a1 = cat_bf16x8(r2, r3);
@@ -474,6 +477,12 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     const int Lc = min(CH, tend - t0);
     const bool more = t0 + CH < tend;
     const int L1 = more ? min(CH, tend - t0 - CH) : 0;
+    // the previous chunk's outputs: its M o Q K^T became visible at the
+    // hand-over barrier just passed
+    if (WANT_O && active && Lp > 0) {
+      finish_o(b ^ 1);
+      store_o();
+    }
     // operands of the next chunk: in flight while this one runs
     if (more) {
       issue_dma(b ^ 1, t0 + CH, L1, slot + 1);
@@ -701,10 +710,6 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       // e^g Q S^T (every Q fragment read once for the wave's row tiles) and
       // its D, pending ----
       if (WANT_O) {
-        if (Lp > 0) {
-          finish_o(b ^ 1);
-          store_o();
-        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           b_frag_split(dd[rt][0], dd[rt][1], dph[rt][0], dpl[rt][0]);

@@ -176,7 +176,9 @@ __global__ void __launch_bounds__(DK / 32 * 64) chain_dks_kernel(ChainLaunch p, 
   };
   // operand reads from buffer set b; the transposing reads are waited for
   // by tr_wait (they are older than any LDS read the compiler issues after
-  // them, so its own counted waits stay valid)
+  // them, so its own counted waits stay valid); within a group of reads the
+  // results are early-clobber operands, since a read's data may land before
+  // a later read of the group has taken its address
   auto load_ops = [&](int b, Ops &o) {
     const char *buf = smem + b * C::BUF;
     const uint32_t boff = (uint32_t)(b * C::BUF);
@@ -191,7 +193,7 @@ __global__ void __launch_bounds__(DK / 32 * 64) chain_dks_kernel(ChainLaunch p, 
           "ds_read_b64_tr_b16 %1, %5\n\t"
           "ds_read_b64_tr_b16 %2, %4 offset:8\n\t"
           "ds_read_b64_tr_b16 %3, %5 offset:8"
-          : "=v"(o.kr[0][m][0]), "=v"(o.kr[0][m][1]), "=v"(o.kr[1][m][0]), "=v"(o.kr[1][m][1])
+          : "=&v"(o.kr[0][m][0]), "=&v"(o.kr[0][m][1]), "=&v"(o.kr[1][m][0]), "=&v"(o.kr[1][m][1])
           : "v"(a0), "v"(a1));
     }
 #pragma unroll
