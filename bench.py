@@ -11,6 +11,10 @@ section 3, Eq. (2)).  Other workloads: 2 = 16 packed tails of 410..3277
 tokens with outputs; 3 = a 32768-token prefill with outputs; 4 = 64
 chunk operators of 512 tokens and their composition; 0 = one fp32 head.
 
+``--tail-curve`` instead reports the tail-replay state error against the
+replayed fraction (the latest k tokens of a 32768-token prefix replayed
+from zero, against the full replay) next to the stored fp64 oracle curve.
+
 Prints ONE JSON line.  ``value`` is replayed tokens x heads per second;
 ``roofline`` compares the dominant kernel's algorithmic HBM bytes per launch
 over its average launch time (HIP events on the launch stream) against the
@@ -192,6 +196,43 @@ def cpu_baseline(inp, want_o, wid, min_seconds=3.0):
                 seconds=el)
 
 
+def tail_curve_gpu(law, gdn, torch, np):
+    """Relative state error ||S_tail - S_full|| / ||S_full|| of replaying only
+    the latest k tokens of the 32768-token prefix from zero (Tail-Replay,
+    section 3), for every k of workloads.TAIL_CURVE_KS, with gdn_replay: one
+    call for the full prefix, one packed call for all the tails."""
+    import workloads
+    inp = workloads.tail_curve_inputs(law)
+    d = to_dev(inp, torch, np)
+    m, ks = workloads.TAIL_CURVE_M, workloads.TAIL_CURVE_KS
+    _, S_full = gdn.replay(None, d["k"], d["v"], d["alpha"], d["beta"], d["cu"], want_o=False)
+    idx = torch.cat([torch.arange(m - kk, m, device="cuda") for kk in ks])
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(ks)]).astype(np.int32)).cuda()
+    sel = {n: d[n][idx].contiguous() for n in ("k", "v", "alpha", "beta")}
+    _, S_tail = gdn.replay(None, sel["k"], sel["v"], sel["alpha"], sel["beta"], cu, want_o=False)
+    torch.cuda.synchronize()
+    S_full = S_full.double().cpu().numpy()
+    S_tail = S_tail.double().cpu().numpy()
+    return [float(np.linalg.norm(S_tail[i] - S_full[0]) / np.linalg.norm(S_full)) for i in range(len(ks))]
+
+
+def tail_curve_report(gdn, torch, np):
+    """One JSON line: the GPU tail-error curve next to the stored fp64 oracle
+    curve and its bound (tests/golden/tail_curve.json)."""
+    import workloads
+    with open(os.path.join(ROOT, "tests", "golden", "tail_curve.json")) as fh:
+        ref = json.load(fh)
+    out = dict(metric="tail-replay relative state error ||S_tail - S_full|| / ||S_full||",
+               m=workloads.TAIL_CURVE_M, k=workloads.TAIL_CURVE_KS,
+               fraction=[round(kk / workloads.TAIL_CURVE_M, 6) for kk in workloads.TAIL_CURVE_KS], laws={})
+    for law in workloads.TAIL_CURVE_LAWS:
+        gpu = tail_curve_gpu(law, gdn, torch, np)
+        out["laws"][law] = dict(gate_scale=workloads.TAIL_CURVE_LAWS[law], gpu=[float("%.3e" % x) for x in gpu],
+                                oracle=[float("%.3e" % x) for x in ref["laws"][law]["err"]],
+                                bound=[float("%.3e" % x) for x in ref["laws"][law]["bound"]])
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +246,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs=5, metavar=("STATS", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="write profiles/ summaries from rocprofv3 output folders (no GPU needed)")
     ap.add_argument("--command", default="", help="with --summarize-counters: the command line profiled")
+    ap.add_argument("--tail-curve", action="store_true",
+                    help="only report the tail-replay state error against the replayed fraction")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.workload, *args.summarize_counters, command=args.command)
@@ -231,6 +274,10 @@ def main():
 
     import gated_deltanet_state_amd as gdn
     import workloads
+
+    if args.tail_curve:
+        tail_curve_report(gdn, torch, np)
+        return
 
     wid = args.workload
     wdef = workloads.WORKLOADS[wid]

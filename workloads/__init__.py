@@ -44,10 +44,20 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 
     Returns the uint16 bit patterns.  NaN is not expected in these inputs.
     """
-    u = f32_round(x).view(np.uint32)
-    # finite inputs only: the rounding increment cannot carry out of 32 bits
-    u = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
-    return u.astype(np.uint16)
+    x = np.asarray(x)
+    out = np.empty(x.shape, np.uint16)
+    src, dst = x.reshape(-1), out.reshape(-1)
+    step = 1 << 22   # elementwise, in cache-sized pieces
+    for s in range(0, src.size, step):
+        u = f32_round(src[s:s + step]).view(np.uint32)
+        # finite inputs only: the rounding increment cannot carry out of 32 bits
+        r = u >> np.uint32(16)
+        r &= np.uint32(1)
+        r += np.uint32(0x7FFF)
+        u += r
+        u >>= np.uint32(16)
+        dst[s:s + step] = u
+    return out
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -100,6 +110,16 @@ def _softplus(x):
     return np.logaddexp(0.0, x)
 
 
+def _unit_rows(x):
+    """x / ||x|| along the last axis, in pieces along the first (same values)."""
+    out = np.empty_like(x)
+    step = max(1, (1 << 22) // max(1, x[0].size)) if x.shape[0] else 1
+    for s in range(0, x.shape[0], step):
+        xs = x[s:s + step]
+        np.divide(xs, np.linalg.norm(xs, axis=-1, keepdims=True), out=out[s:s + step])
+    return out
+
+
 def generate(lengths, H: int, dk: int, dv: int, dtype: str = "bf16",
              seed: int = 0, gate_scale: float = 0.1, rng=None,
              alpha_one: bool = False, beta_value: Optional[float] = None) -> Inputs:
@@ -122,8 +142,7 @@ def generate(lengths, H: int, dk: int, dv: int, dtype: str = "bf16",
     v = rng.standard_normal((T, H, dv))
     xb = rng.standard_normal((T, H))
     xa = rng.standard_normal((T, H))
-    q = q / np.linalg.norm(q, axis=-1, keepdims=True)
-    k = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    q, k = _unit_rows(q), _unit_rows(k)
     beta = 1.0 / (1.0 + np.exp(-xb)) if beta_value is None else np.full((T, H), beta_value)
     alpha = np.ones((T, H)) if alpha_one else np.exp(-gate_scale * _softplus(xa))
     arrs = dict(q=q, k=k, v=v, alpha=alpha, beta=beta)
@@ -172,6 +191,22 @@ def make_workload(cfg_id: int, seed: Optional[int] = None, H: Optional[int] = No
     lengths = workload_lengths(cfg_id, rng)
     return generate(lengths, H=w["H"] if H is None else H, dk=w["d"], dv=w["d"],
                     dtype=w["dtype"], rng=rng)
+
+
+# Tail-error curve: the latest k tokens of the 32768-token prefill inputs
+# replayed from zero, k = 8 .. 256 tokens and ceil(r * 32768) for r = 1.25%,
+# 2.5%, 5% and 10%, under the workload gate law and, as a supplement, the
+# slow law (gate_scale 0.001).
+TAIL_CURVE_M = 32768
+TAIL_CURVE_KS = [8, 16, 32, 64, 128, 256] + [tail_length(32768, r) for r in ("0.0125", "0.025", "0.05", "0.1")]
+TAIL_CURVE_LAWS = {"workload": 0.1, "slow": 0.001}
+
+
+def tail_curve_inputs(law: str) -> Inputs:
+    """The prefix of the tail-error curve: workload 3's draw (seed 3, H = 32,
+    d = 128, bf16) with the named gate law."""
+    return generate([TAIL_CURVE_M], H=32, dk=128, dv=128, dtype="bf16", seed=3,
+                    gate_scale=TAIL_CURVE_LAWS[law])
 
 
 def chunk_bounds(n_tokens: int, chunk: int) -> np.ndarray:
