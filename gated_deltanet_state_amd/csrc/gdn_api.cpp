@@ -147,6 +147,8 @@ size_t gdn_replay_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t n_he
     const size_t s2 =
         seg_workspace_bytes(n_seqs, replay_segments_o(n_seqs, n_tokens, n_heads, dk, dv), n_heads, dk, dv, true);
     seg = s1 > s2 ? s1 : s2;
+    const size_t s3 = gdn::order_workspace_bytes(n_seqs);   // (replays without a time split)
+    seg = seg > s3 ? seg : s3;
   }
   return gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads) + seg;
 }
@@ -187,7 +189,10 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
                                  : (o ? replay_segments_o(n_seqs, n_tokens, n_heads, dk, dv)
                                       : replay_segments(n_seqs, n_tokens, n_heads, dk, dv));
   const size_t tau_bytes = gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads);
-  const size_t need = tau_bytes + seg_workspace_bytes(n_seqs, P, n_heads, dk, dv, o != nullptr);
+  // longest-first sequence order (bf16 replays without a time split, built by the prep kernel)
+  const bool ordered = bf && !dks && P == 1 && gdn::order_workspace_bytes(n_seqs) > 0;
+  const size_t need = tau_bytes + (P > 1 ? seg_workspace_bytes(n_seqs, P, n_heads, dk, dv, o != nullptr)
+                                         : (ordered ? gdn::order_workspace_bytes(n_seqs) : 0));
   if (workspace_bytes < need || !workspace)
     return fail(GDN_ERR_WORKSPACE, "gdn_replay: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
   if ((s = check_align("workspace", workspace))) return s;
@@ -203,6 +208,8 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   pp.in_bf16 = in_dtype == GDN_BF16;
   pp.tau = static_cast<float *>(workspace);
   pp.n_slots = gdn::slot_count(n_tokens, n_seqs);
+  int32_t *order = ordered ? reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + tau_bytes) : nullptr;
+  pp.order = order;
   // bf16 time-split replays build the per-chunk records inside the segment
   // kernel; everything else runs the stand-alone prep kernel first
   const bool fuse = bf && P > 1;   // (records built inside the segment launch)
@@ -225,6 +232,7 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   p.o_bf16 = o_dtype == GDN_BF16;
   p.n_segs = 1;
   if (P == 1) {
+    p.order = order;
     p.S_out = S_final;
     p.T_out = nullptr;
     p.tiles_T = 0;

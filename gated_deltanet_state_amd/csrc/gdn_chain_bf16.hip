@@ -150,14 +150,20 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   float *sG0 = reinterpret_cast<float *>(smem + C::oG);
 
-  // ---- work item (XCD-aware order: consecutive items share one XCD's L2) ----
-  const int per = (int)(gridDim.x >> 3);
-  const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  if (item >= n_items) return;
+  // ---- work item ----
   const int tilesA = p.tiles_T + p.tiles_S;
   const int tiles0 = p.skip_T0 ? p.tiles_S : tilesA;
   const int grp0 = (tiles0 + TW - 1) / TW, grpA = (tilesA + TW - 1) / TW;
   const int per_nh = grp0 + (p.n_segs - 1) * grpA;
+  // One workgroup per (sequence, head) with a longest-first sequence order:
+  // items in block order (the dispatcher deals blocks round-robin over the
+  // XCDs, so the longest items start first everywhere).  Otherwise
+  // XCD-aware: consecutive items (workgroups of one sequence and head,
+  // which stage the same operands) share one XCD's L2.
+  const bool ordered = p.order != nullptr && per_nh == 1;
+  const int per = (int)(gridDim.x >> 3);
+  const int item = ordered ? (int)blockIdx.x : (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (item >= n_items) return;
   const int nh = item / per_nh;
   int rem = item % per_nh, seg = 0, grp = rem;
   if (rem >= grp0) {
@@ -165,7 +171,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     seg = 1 + rem / grpA;
     grp = rem % grpA;
   }
-  const int n = nh / p.H, h = nh % p.H;
+  const int n = ordered ? p.order[nh / p.H] : nh / p.H, h = nh % p.H;
   const int H = p.H, DV = p.dv;
   const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
   const int g4 = l >> 4, jl = l & 15;

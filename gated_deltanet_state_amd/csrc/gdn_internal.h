@@ -41,6 +41,17 @@ inline size_t tau_workspace_bytes(int64_t n_tokens, int32_t n_seqs, int32_t n_he
   return (size_t)slot_count(n_tokens, n_seqs) * (size_t)n_heads * kRecFloats * sizeof(float);
 }
 
+// Longest-first order of the sequences of a packed replay that runs without
+// a time split: order[r] is the sequence with the r-th most chunks (ties by
+// index).  The recurrence then starts the longest (sequence, head) items
+// first, which shortens the tail of the launch when the items outnumber the
+// compute units.  Built by the bf16 prep kernel for 2 .. kMaxOrderedSeqs
+// sequences (a quadratic rank count by one wave); above that, sequence order.
+constexpr int32_t kMaxOrderedSeqs = 256;
+inline size_t order_workspace_bytes(int32_t n_seqs) {
+  return (n_seqs > 1 && n_seqs <= kMaxOrderedSeqs) ? ((size_t)n_seqs * 4 + 255) / 256 * 256 : 0;
+}
+
 // Per-chunk factor build: one workgroup per (slot, head).
 struct PrepLaunch {
   const void *k, *alpha, *beta;
@@ -49,6 +60,7 @@ struct PrepLaunch {
   int in_bf16;
   float *tau;        // [n_slots, H, kRecFloats] per-chunk factor records
   int64_t n_slots;
+  int32_t *order;    // [n_seqs] longest-first sequence order to build, or null (bf16 only)
 };
 
 // One launch of the chunked recurrence kernel.  A work item is one tile of
@@ -85,6 +97,9 @@ struct ChainLaunch {
   // bf16 inputs with transition tiles: every workgroup first builds the
   // per-chunk records of its own segment (no separate prep launch)
   int fuse_prep;
+  // [n_seqs] longest-first sequence order (PrepLaunch::order), or null;
+  // used by the bf16 recurrence when each (sequence, head) is one workgroup
+  const int32_t *order;
 };
 
 struct ComposeLaunch {

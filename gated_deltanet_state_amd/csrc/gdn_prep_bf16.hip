@@ -26,10 +26,27 @@ __device__ __forceinline__ int find_seq_b(const int32_t *cu, int n_seqs, int64_t
   return lo;
 }
 
+// Longest-first order of the sequences by chunk count (ties by index): each
+// lane ranks its sequences against all others (the inner loop is uniform, so
+// cu comes through scalar loads); ranks are distinct, so order is a
+// permutation.
+__device__ __forceinline__ void rank_sequences(const int32_t *cu, int n_seqs, int32_t *order) {
+  for (int i = lane_id(); i < n_seqs; i += 64) {
+    const int ci = (cu[i + 1] - cu[i] + kChunk - 1) / kChunk;
+    int r = 0;
+    for (int j = 0; j < n_seqs; ++j) {
+      const int cj = (cu[j + 1] - cu[j] + kChunk - 1) / kChunk;
+      r += (cj > ci || (cj == ci && j < i)) ? 1 : 0;
+    }
+    order[r] = i;
+  }
+}
+
 template <int DK>
 __global__ void __launch_bounds__(PW * 64) prep_bf16_kernel(PrepLaunch p) {
   __shared__ __attribute__((aligned(16))) float scratch[PW][kPrepWaveLds / 4];
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  if (p.order && blockIdx.x == 0 && blockIdx.y == 0 && w == 0) rank_sequences(p.cu, p.n_seqs, p.order);
   const int64_t slot = (int64_t)blockIdx.x * PW + w;
   if (slot >= p.n_slots) return;
   const int h = blockIdx.y, H = p.H;

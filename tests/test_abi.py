@@ -95,13 +95,14 @@ def test_compose_argument_checks(lib):
 
 
 def test_workspace_queries(lib, monkeypatch):
-    # one 24 KiB record of per-chunk factors ((I + A)^{-1} diag(beta) and M o Q K^T fragments) per chunk slot
-    # and head; slots = n_tokens / 64 + n_seqs + 1 (sequence n's chunk j sits
+    # one 13 KiB record of per-chunk factors ((I + A)^{-1} diag(beta) fragments and the gates) per chunk
+    # slot and head; slots = n_tokens / 64 + n_seqs + 1 (sequence n's chunk j sits
     # in slot floor(cu[n] / 64) + n + j)
     monkeypatch.delenv("GDN_REPLAY_SEGMENTS", raising=False)
     tau = lambda n_seqs, n_tokens, H: (n_tokens // 64 + n_seqs + 1) * H * 13312
-    # 16 sequences x 32 heads already fill the chip: no time split
-    assert lib.gdn_replay_workspace_bytes(16, 30000, 32, 128, 128) == tau(16, 30000, 32)
+    # 16 sequences x 32 heads already fill the chip: no time split, and room
+    # for the longest-first order of the 16 sequences (256 bytes)
+    assert lib.gdn_replay_workspace_bytes(16, 30000, 32, 128, 128) == tau(16, 30000, 32) + 256
     assert lib.gdn_chunk_operator_workspace_bytes(64, 32768, 32, 128, 128) == tau(64, 32768, 32)
     # one long sequence: room for P segment operators (T_seg and S_seg per
     # head), 1 < P <= 16

@@ -148,6 +148,16 @@ def test_repeated_calls_stay_bitwise_identical():
                 assert np.array_equal(o, first[i][0]) and np.array_equal(S, first[i][1]), "case %d" % i
 
 
+@pytest.mark.parametrize("n_seqs", [200, 300])
+def test_many_sequences(n_seqs):
+    # packed batches below and above the longest-first ordering limit (256
+    # sequences): lengths 0 .. 200, duplicates and empties included
+    rng = np.random.Generator(np.random.PCG64(n_seqs))
+    lengths = [int(x) for x in rng.integers(0, 200, size=n_seqs, endpoint=True)]
+    inp = workloads.generate(lengths, H=2, dk=64, dv=64, dtype="bf16", seed=n_seqs + 1)
+    check(inp)
+
+
 def test_varlen_equals_per_sequence_calls():
     inp = workloads.generate([90, 0, 257, 64], H=3, dk=128, dv=128, dtype="bf16", seed=29)
     o, S = run(inp)
