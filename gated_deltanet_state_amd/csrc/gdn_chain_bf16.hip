@@ -380,16 +380,24 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   // chunk (split between the waves, into one of two LDS sets) and becomes
   // visible to every wave at the chunk's hand-over barrier, so the second
   // part and the store of a chunk's outputs follow in the next chunk (or
-  // after the last one).  zp holds the pending outputs, dph / dpl the
-  // pending D as split-bf16 B fragments, tp / Lp its token range.
+  // after the last one).  Both parts are formed transposed, O^T = e^g S Q^T
+  // + D^T (M o Q K^T)^T: the split state and D fragments serve as A operands
+  // and the Q and M o Q K^T fragments as B operands with the registers they
+  // have in the other role, and a lane of the result holds four consecutive
+  // value columns of one token.  zp holds the pending outputs (block bt:
+  // tokens 16 bt + lane column), dph / dpl the pending D as split-bf16
+  // fragments, tp / Lp its token range.
   f32x4 zp[RT][4];
   bf16x8 dph[RT][2], dpl[RT][2];
   int tp = 0, Lp = 0;
   // M o Q K^T (M_rs = e^{g_r - g_s}, s <= r) of the chunk in buffer set b
   // into set b of the M o Q K^T fragments: the twelve 16 x 16 halves of
-  // the six fragments (gdn_internal.h order) round-robin over the waves;
-  // tile (bi, bj) lands in fragment (bi, bj >> 1), lane (r & 15) +
-  // 16 (c >> 2), element 4 (bj & 1) + (c & 3) for row r, column 16 bj + c
+  // the six fragments (gdn_internal.h order) round-robin over the waves.
+  // Half (bi, bj) (rows r of block bi, columns s of block bj) is formed
+  // transposed, K Q^T, so that lane (q, g) holds the four consecutive
+  // columns s = 16 bj + 4 g + e of row r = 16 bi + q: exactly elements
+  // 4 (bj & 1) .. + 3 of that lane's slot in fragment (bi, bj >> 1), one
+  // 8-byte LDS write per plane.
   auto build_p = [&](int b) {
     const char *buf = smem + b * C::BUF;
     const float *sG = sG0 + b * C::GN;
@@ -402,22 +410,21 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       if (bj <= bi) {
 #pragma unroll
         for (int m = 0; m < C::NKS; ++m) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(buf + (C::bQA + bi * C::NKS + m) * 1024 + 16 * l);
-          const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(buf + (C::bKA + bj * C::NKS + m) * 1024 + 16 * l);
-          c = mfma_bf16(a, bb, c);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(buf + (C::bKA + bj * C::NKS + m) * 1024 + 16 * l);
+          const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(buf + (C::bQA + bi * C::NKS + m) * 1024 + 16 * l);
+          c = mfma_bf16(ka, qb, c);
         }
       }
-      const int col = 16 * bj + jl;
-      const float gc = sG[G_G + col];
+      const int r = 16 * bi + jl, s0 = 16 * bj + 4 * g4;
+      const float gr = sG[G_G + r];
+      const f32x4 gs = *reinterpret_cast<const f32x4 *>(sG + G_G + s0);
+      f32x4 x;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * bi + 4 * g4 + e;
-        const float x = (col <= r) ? __expf(sG[G_G + r] - gc) * c[e] : 0.f;
-        const bf16 hi = (bf16)x;
-        const int idx = (f * 64 + (r & 15) + 16 * (jl >> 2)) * 8 + 4 * half + (jl & 3);
-        sP[idx] = hi;
-        sP[kTauFragPlane + idx] = (bf16)(x - (float)hi);
-      }
+      for (int e = 0; e < 4; ++e) x[e] = (s0 + e <= r) ? __expf(gr - gs[e]) * c[e] : 0.f;
+      bf16x4 hi, lo;
+      split4(x, hi, lo);
+      *reinterpret_cast<bf16x4 *>(sP + (f * 64 + l) * 8 + 4 * half) = hi;
+      *reinterpret_cast<bf16x4 *>(sP + kTauFragPlane + (f * 64 + l) * 8 + 4 * half) = lo;
     }
   };
   // the pending outputs: add (M o Q K^T) D from set b, then store
@@ -444,9 +451,9 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
           const int f = ford[i];
           const int bt = f < 2 ? f : (f - 2) / 2 + 2;
           const int m = f < 2 ? 0 : (f - 2) % 2;
-          if (pass == 0) zp[rt][bt] = mfma_bf16(ph[f], dph[rt][m], zp[rt][bt]);
-          if (pass == 1) z2[rt][bt] = mfma_bf16(ph[f], dpl[rt][m], z2[rt][bt]);
-          if (pass == 2) zp[rt][bt] = mfma_bf16(pl[f], dph[rt][m], zp[rt][bt]);
+          if (pass == 0) zp[rt][bt] = mfma_bf16(dph[rt][m], ph[f], zp[rt][bt]);
+          if (pass == 1) z2[rt][bt] = mfma_bf16(dpl[rt][m], ph[f], z2[rt][bt]);
+          if (pass == 2) zp[rt][bt] = mfma_bf16(dph[rt][m], pl[f], zp[rt][bt]);
         }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -454,24 +461,22 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       for (int bt = 0; bt < 4; ++bt) zp[rt][bt] += z2[rt][bt];
   };
   auto store_o = [&]() {
+    // lane (q, g) of block bt holds token tp + 16 bt + q, value columns
+    // row0 + 16 rt + 4 g .. + 3: one 16-byte (8-byte in bf16) store each
     const int64_t tok = (int64_t)H * DV;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const int64_t ob = ((int64_t)(tp + 4 * g4) * H + h) * DV + row0 + 16 * rt + jl;
-      if (p.o_bf16) {
-        bf16 *o = reinterpret_cast<bf16 *>(p.o) + ob;
+      const int64_t ob = ((int64_t)(tp + jl) * H + h) * DV + row0 + 16 * rt + 4 * g4;
 #pragma unroll
-        for (int bt = 0; bt < 4; ++bt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (16 * bt + 4 * g4 + e < Lp) o[(16 * bt + e) * tok] = (bf16)zp[rt][bt][e];
-      } else {
-        float *o = reinterpret_cast<float *>(p.o) + ob;
-#pragma unroll
-        for (int bt = 0; bt < 4; ++bt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (16 * bt + 4 * g4 + e < Lp) o[(16 * bt + e) * tok] = zp[rt][bt][e];
+      for (int bt = 0; bt < 4; ++bt) {
+        if (16 * bt + jl < Lp) {
+          if (p.o_bf16) {
+            *reinterpret_cast<uint2 *>(reinterpret_cast<bf16 *>(p.o) + ob + 16 * bt * tok) =
+                uint2{pack_bf16x2(zp[rt][bt][0], zp[rt][bt][1]), pack_bf16x2(zp[rt][bt][2], zp[rt][bt][3])};
+          } else {
+            *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.o) + ob + 16 * bt * tok) = zp[rt][bt];
+          }
+        }
       }
     }
     Lp = 0;
@@ -734,19 +739,19 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int bt = 0; bt < 4; ++bt) zp[rt][bt] = mfma_bf16(a[bt], sh[rt][m], zp[rt][bt]);
+            for (int bt = 0; bt < 4; ++bt) zp[rt][bt] = mfma_bf16(sh[rt][m], a[bt], zp[rt][bt]);
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int bt = 0; bt < 4; ++bt) z2[rt][bt] = mfma_bf16(a[bt], sl[rt][m], z2[rt][bt]);
+            for (int bt = 0; bt < 4; ++bt) z2[rt][bt] = mfma_bf16(sl[rt][m], a[bt], z2[rt][bt]);
         }
 #pragma unroll
         for (int bt = 0; bt < 4; ++bt) {
-          const f32x4 eg = *reinterpret_cast<const f32x4 *>(sG + G_EG + 16 * bt + 4 * g4);
+          const float eg = sG[G_EG + 16 * bt + jl];
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) zp[rt][bt][e] = (zp[rt][bt][e] + z2[rt][bt][e]) * eg[e];
+            for (int e = 0; e < 4; ++e) zp[rt][bt][e] = (zp[rt][bt][e] + z2[rt][bt][e]) * eg;
         }
         tp = t0;
         Lp = Lc;

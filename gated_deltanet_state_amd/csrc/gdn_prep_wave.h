@@ -57,13 +57,31 @@ __device__ __forceinline__ f32x4 acc3_sum(const Acc3 &a) { return a.a + a.b + a.
 
 }  // namespace prep_detail
 
-// Record of one (chunk, head): tokens t0 .. t0 + Lc - 1 (1 <= Lc <= 64) of
-// head h, keys k [T, H, DK], gates alpha / beta [T, H] (bf16); rec receives
-// kRecFloats * 4 bytes; scratch is this wave's kPrepWaveLds bytes of LDS;
-// lds_rec (may be null) receives a second copy of the Tau fragments in LDS.
+// The chunk's keys as MFMA fragments: kf[bt][m], lane (r, g) = (l & 15,
+// l >> 4) holds key row 16 bt + r (rows past the chunk repeat its last row;
+// they meet beta = 0 below), columns 32 m + 8 g .. + 7.  Plain loads, so a
+// caller may issue them for its next chunk before working on this one.
 template <int DK>
-__device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha, const bf16 *beta, int H, int h,
-                                                int t0, int Lc, char *rec, float *scratch, char *lds_rec = nullptr) {
+__device__ __forceinline__ void prep_load_keys(const bf16 *k, int H, int h, int t0, int Lc, bf16x8 (&kf)[4][DK / 32]) {
+  const int l = lane_id(), g4 = l >> 4, jl = l & 15;
+#pragma unroll
+  for (int bt = 0; bt < 4; ++bt) {
+    const int r = min(16 * bt + jl, Lc - 1);
+    const bf16 *src = k + ((int64_t)(t0 + r) * H + h) * DK + 8 * g4;
+#pragma unroll
+    for (int m = 0; m < DK / 32; ++m) kf[bt][m] = *reinterpret_cast<const bf16x8 *>(src + 32 * m);
+  }
+}
+
+// Record of one (chunk, head) from its keys kf (prep_load_keys): tokens
+// t0 .. t0 + Lc - 1 (1 <= Lc <= 64) of head h, gates alpha / beta [T, H]
+// (bf16); rec receives kRecFloats * 4 bytes; scratch is this wave's
+// kPrepWaveLds bytes of LDS; lds_rec (may be null) receives a second copy of
+// the Tau fragments in LDS.
+template <int DK>
+__device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 32], const bf16 *alpha,
+                                                     const bf16 *beta, int H, int h, int t0, int Lc, char *rec,
+                                                     float *scratch, char *lds_rec = nullptr) {
   using namespace prep_detail;
   constexpr int NKS = DK / 32;
   float *sA = scratch;             // 10 blocks 16 x 16 row-major: A, then Tau
@@ -71,15 +89,7 @@ __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha
   float *sG = sTT + 4 * 256, *sB = sG + 64;
   const int l = lane_id(), g4 = l >> 4, jl = l & 15;
 
-  // ---- 1. keys and gates ----
-  bf16x8 kf[4][NKS];
-#pragma unroll
-  for (int bt = 0; bt < 4; ++bt) {
-    const int r = min(16 * bt + jl, Lc - 1);
-    const bf16 *src = k + ((int64_t)(t0 + r) * H + h) * DK + 8 * g4;
-#pragma unroll
-    for (int m = 0; m < NKS; ++m) kf[bt][m] = *reinterpret_cast<const bf16x8 *>(src + 32 * m);
-  }
+  // ---- 1. gates (the keys are in kf) ----
   {
     float g = 0.f, b = 0.f;
     if (l < Lc) {
@@ -244,7 +254,15 @@ __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha
     }
   };
   write_frags(rec, lds_rec, true);
+}
 
+// Record of one (chunk, head), keys loaded here (see prep_chunk_wave_keys).
+template <int DK>
+__device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha, const bf16 *beta, int H, int h,
+                                                int t0, int Lc, char *rec, float *scratch, char *lds_rec = nullptr) {
+  bf16x8 kf[4][DK / 32];
+  prep_load_keys<DK>(k, H, h, t0, Lc, kf);
+  prep_chunk_wave_keys<DK>(kf, alpha, beta, H, h, t0, Lc, rec, scratch, lds_rec);
 }
 
 }  // namespace gdn
