@@ -252,49 +252,63 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     }
 
   // ---- DMA of one chunk's operands into buffer set b ----
-  // Rows past the chunk are copies of its last row: they only meet zero
-  // coefficients (beta = 0 in the Tau columns, zero decayed corrections in
-  // the state update, outputs past the chunk not stored), so any finite
-  // value serves.
   // Every wave issues whole 1 KiB blocks (one 16-byte copy per lane); the
   // loops are unrolled over compile-time block ranges with the wave index
-  // uniform, so the issue is straight-line scalar-branch code.
+  // uniform, so the issue is straight-line scalar-branch code.  The copies
+  // go through buffer descriptors whose base is the chunk's first token (a
+  // uniform address, rebuilt per chunk by scalar code) and whose range ends
+  // with the tensor, so each lane's byte offset is fixed for the whole
+  // sequence.  Rows past a short chunk read the tokens that follow it, or
+  // zeros past the end of the tensor: they only meet zero coefficients
+  // (beta = 0 in the Tau columns, zero decayed corrections in the state
+  // update, masked M o Q K^T entries, outputs past the chunk not stored),
+  // so any finite value serves.
   const uint32_t tok_k = (uint32_t)H * DK * 2, tok_v = (uint32_t)H * DV * 2;  // bytes per token
-  auto issue_dma = [&](int b, int t0, int Lc, int64_t slot, bool with_rec = true) {
-    char *buf = smem + b * C::BUF;
-    const int lm = Lc - 1;
-    const char *kb = reinterpret_cast<const char *>(gk + ((int64_t)t0 * H + h) * DK) + 16 * g4;
-    const char *qb = WANT_O ? reinterpret_cast<const char *>(gq + ((int64_t)t0 * H + h) * DK) + 16 * g4 : nullptr;
-    const char *rec = grec + (slot * H + h) * (int64_t)(kRecFloats * 4) + 16 * l;
+  const int64_t T_all = p.cu[p.n_seqs];
+  constexpr int JK = (C::NKA + NW - 1) / NW, JT = (C::NTF + NW - 1) / NW, JV = (C::NVB + NW - 1) / NW;
+  uint32_t off_kq[JK], off_v[JV];
 #pragma unroll
-    for (int j = 0; j < (C::NKA + NW - 1) / NW; ++j) {       // K (and Q) A fragments (bt, m)
+  for (int j = 0; j < JK; ++j) {                 // K (and Q) A fragment (bt, m): key row 16 bt + jl
+    const int f = j * NW + w, bt = f / C::NKS, m = f % C::NKS;
+    off_kq[j] = (uint32_t)(16 * bt + jl) * tok_k + 64 * m + 16 * g4;
+  }
+#pragma unroll
+  for (int j = 0; j < JV; ++j) {                 // value slab: logical unit u (8 columns) of row r
+    const int u_lds = (j * NW + w) * 64 + l;
+    // units past this workgroup's state columns re-read its last unit (never used)
+    const int r = u_lds / C::VU, u = min((u_lds % C::VU) ^ vswz<C::VU>(r), 2 * max(nS, 1) - 1);
+    off_v[j] = (uint32_t)r * tok_v + 16 * u;
+  }
+  auto issue_dma = [&](int b, int t0, int64_t slot, bool with_rec = true) {
+    char *buf = smem + b * C::BUF;
+    const int64_t left = T_all - t0;   // tokens from the chunk's first to the end of the tensor
+    const int64_t lim = 0xFFFFFFFFll;
+    const char *kb = reinterpret_cast<const char *>(gk + ((int64_t)t0 * H + h) * DK);
+    const uint32_t nk = (uint32_t)min(left * tok_k - (int64_t)h * DK * 2, lim);
+    const char *qb = WANT_O ? reinterpret_cast<const char *>(gq + ((int64_t)t0 * H + h) * DK) : nullptr;
+    const char *rec = grec + (slot * H + h) * (int64_t)(kRecFloats * 4);
+#pragma unroll
+    for (int j = 0; j < JK; ++j) {                           // K (and Q) A fragments
       const int f = j * NW + w;
       if (C::NKA % NW == 0 || f < C::NKA) {
-        const int bt = f / C::NKS, m = f % C::NKS;
-        const uint32_t off = (uint32_t)min(16 * bt + jl, lm) * tok_k + 64 * m;
-        dma16_global(kb + off, (lds_void *)(buf + (C::bKA + f) * 1024));
-        if (WANT_O) dma16_global(qb + off, (lds_void *)(buf + (C::bQA + f) * 1024));
+        dma16_buffer(kb, nk, (lds_void *)(buf + (C::bKA + f) * 1024), off_kq[j]);
+        if (WANT_O) dma16_buffer(qb, nk, (lds_void *)(buf + (C::bQA + f) * 1024), off_kq[j]);
       }
     }
 #pragma unroll
-    for (int j = 0; j < (C::NTF + NW - 1) / NW; ++j) {         // Tau diag(beta) fragments (record)
+    for (int j = 0; j < JT; ++j) {                           // Tau diag(beta) fragments (record)
       const int f = j * NW + w;
       if (with_rec && (C::NTF % NW == 0 || f < C::NTF)) {
-        dma16_global(rec + f * 1024, (lds_void *)(buf + (C::bTF + f) * 1024));
+        dma16_buffer(rec, kRecFloats * 4, (lds_void *)(buf + (C::bTF + f) * 1024), 16 * l, f * 1024);
       }
     }
-    if (grp_S) {                                               // value slab of the workgroup
+    if (grp_S) {                                             // value slab of the workgroup
       const char *vb = reinterpret_cast<const char *>(gv + ((int64_t)t0 * H + h) * DV + vcol0);
+      const uint32_t nv = (uint32_t)min(left * tok_v - ((int64_t)h * DV + vcol0) * 2, lim);
 #pragma unroll
-      for (int j = 0; j < (C::NVB + NW - 1) / NW; ++j) {
+      for (int j = 0; j < JV; ++j) {
         const int f = j * NW + w;
-        if (C::NVB % NW == 0 || f < C::NVB) {
-          const int u_lds = f * 64 + l;
-          // logical unit u (8 columns) of row r; units past this
-          // workgroup's state columns re-read its last unit (never used)
-          const int r = u_lds / C::VU, u = min((u_lds % C::VU) ^ vswz<C::VU>(r), 2 * nS - 1);
-          dma16_global(vb + (uint32_t)min(r, lm) * tok_v + 16 * u, (lds_void *)(buf + (C::bV + f) * 1024));
-        }
+        if (C::NVB % NW == 0 || f < C::NVB) dma16_buffer(vb, nv, (lds_void *)(buf + (C::bV + f) * 1024), off_v[j]);
       }
     }
   };
@@ -350,7 +364,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   if constexpr (FUSED) {
     if (tbeg < tend) {
       const int L0 = min(CH, tend - tbeg);
-      issue_dma(0, tbeg, L0, slot0, false);
+      issue_dma(0, tbeg, slot0, false);
       load_alpha(tbeg, L0);
     }
     float *scr = reinterpret_cast<float *>(smem + C::PSCR) + (w % C::NPW) * (kPrepWaveLds / 4);
@@ -367,7 +381,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     if (tbeg < tend) gates(0, min(CH, tend - tbeg));
   } else if (tbeg < tend) {
     const int L0 = min(CH, tend - tbeg);
-    issue_dma(0, tbeg, L0, slot0);
+    issue_dma(0, tbeg, slot0);
     load_alpha(tbeg, L0);
     gates(0, L0);
   }
@@ -496,7 +510,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     }
     // operands of the next chunk: in flight while this one runs
     if (more) {
-      issue_dma(b ^ 1, t0 + CH, L1, slot + 1);
+      issue_dma(b ^ 1, t0 + CH, slot + 1);
       load_alpha(t0 + CH, L1);
     }
     const char *buf = smem + b * C::BUF;

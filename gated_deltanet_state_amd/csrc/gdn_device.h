@@ -345,10 +345,11 @@ __device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo) {
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void dma16_buffer(const void *base, uint32_t nbytes, lds_void *dst, uint32_t voff) {
+__device__ __forceinline__ void dma16_buffer(const void *base, uint32_t nbytes, lds_void *dst, uint32_t voff,
+                                             uint32_t soff = 0) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nbytes, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 #endif
 }
 __device__ __forceinline__ void dma16_global(const void *src, lds_void *dst) {
