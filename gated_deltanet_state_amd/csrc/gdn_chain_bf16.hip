@@ -646,34 +646,28 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
         for (int m = 0; m < C::NKS; ++m) b_frag_split(st[rt][2 * m], st[rt][2 * m + 1], sh[rt][m], sl[rt][m]);
 
       // ---- Y = K S^T (each K fragment read once for the wave's row tiles) ----
-      // A dependent MFMA (same accumulator) waits about three issue slots,
-      // so the hi and lo passes accumulate separately and every loop below
-      // rotates over at least four accumulators.
+      // A dependent MFMA (same accumulator) waits about three issue slots:
+      // every loop below rotates over at least four accumulators (the hi
+      // and lo passes of a product share them where four or more rotate,
+      // and accumulate separately where fewer would).
       f32x4 y[RT][4];
-      {
-        f32x4 yl[RT][4];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) y[rt][bt] = zero4();
+#pragma unroll
+      for (int m = 0; m < C::NKS; ++m) {
+        bf16x8 a[4];
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) a[bt] = frag(C::bKA + bt * C::NKS + m);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int bt = 0; bt < 4; ++bt) y[rt][bt] = yl[rt][bt] = zero4();
-#pragma unroll
-        for (int m = 0; m < C::NKS; ++m) {
-          bf16x8 a[4];
-#pragma unroll
-          for (int bt = 0; bt < 4; ++bt) a[bt] = frag(C::bKA + bt * C::NKS + m);
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int bt = 0; bt < 4; ++bt) y[rt][bt] = mfma_bf16(a[bt], sh[rt][m], y[rt][bt]);
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int bt = 0; bt < 4; ++bt) yl[rt][bt] = mfma_bf16(a[bt], sl[rt][m], yl[rt][bt]);
-        }
+          for (int bt = 0; bt < 4; ++bt) y[rt][bt] = mfma_bf16(a[bt], sh[rt][m], y[rt][bt]);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int bt = 0; bt < 4; ++bt) y[rt][bt] += yl[rt][bt];
+          for (int bt = 0; bt < 4; ++bt) y[rt][bt] = mfma_bf16(a[bt], sl[rt][m], y[rt][bt]);
       }
 
       // ---- R = V - e^g Y  (beta is folded into the Tau fragments) ----
@@ -740,11 +734,10 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
           b_frag_split(dd[rt][0], dd[rt][1], dph[rt][0], dpl[rt][0]);
           b_frag_split(dd[rt][2], dd[rt][3], dph[rt][1], dpl[rt][1]);
         }
-        f32x4 z2[RT][4];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int bt = 0; bt < 4; ++bt) zp[rt][bt] = z2[rt][bt] = zero4();
+          for (int bt = 0; bt < 4; ++bt) zp[rt][bt] = zero4();
 #pragma unroll
         for (int m = 0; m < C::NKS; ++m) {
           bf16x8 a[4];
@@ -757,7 +750,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int bt = 0; bt < 4; ++bt) z2[rt][bt] = mfma_bf16(sl[rt][m], a[bt], z2[rt][bt]);
+            for (int bt = 0; bt < 4; ++bt) zp[rt][bt] = mfma_bf16(sl[rt][m], a[bt], zp[rt][bt]);
         }
 #pragma unroll
         for (int bt = 0; bt < 4; ++bt) {
@@ -765,7 +758,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) zp[rt][bt][e] = (zp[rt][bt][e] + z2[rt][bt][e]) * eg;
+            for (int e = 0; e < 4; ++e) zp[rt][bt][e] *= eg;
         }
         tp = t0;
         Lp = Lc;
