@@ -38,19 +38,26 @@ namespace prep_detail {
 
 __device__ __forceinline__ constexpr int blk(int i, int j) { return i * (i + 1) / 2 + j; }  // i >= j
 
-// x (4 fp32 in A layout) times y (4 fp32 in B layout), k = 16, as split bf16
-// with the three partial products in separate accumulators (no product
-// waits on the one before it).
+// A 4-value operand of a k = 16 MFMA as split bf16 (hi, lo).
+struct Split4 {
+  bf16x4 h, l;
+};
+__device__ __forceinline__ Split4 split_op(const f32x4 &x) {
+  Split4 r;
+  split4(x, r.h, r.l);
+  return r;
+}
+// x (A layout) times y (B layout), k = 16, as split bf16 with the three
+// partial products in separate accumulators (no product waits on the one
+// before it).  Operands are split once and reused by every product they
+// enter.
 struct Acc3 {
   f32x4 a, b, c;
 };
-__device__ __forceinline__ void acc_split3(Acc3 &acc, const f32x4 &x, const f32x4 &y) {
-  bf16x4 xh, xl, yh, yl;
-  split4(x, xh, xl);
-  split4(y, yh, yl);
-  acc.a = mfma_bf16_k16(xh, yh, acc.a);
-  acc.b = mfma_bf16_k16(xh, yl, acc.b);
-  acc.c = mfma_bf16_k16(xl, yh, acc.c);
+__device__ __forceinline__ void acc_split3(Acc3 &acc, const Split4 &x, const Split4 &y) {
+  acc.a = mfma_bf16_k16(x.h, y.h, acc.a);
+  acc.b = mfma_bf16_k16(x.h, y.l, acc.b);
+  acc.c = mfma_bf16_k16(x.l, y.h, acc.c);
 }
 __device__ __forceinline__ Acc3 acc3_zero() { return Acc3{zero4(), zero4(), zero4()}; }
 __device__ __forceinline__ f32x4 acc3_sum(const Acc3 &a) { return a.a + a.b + a.c; }
@@ -175,33 +182,39 @@ __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 
   {
     // operands: A_im and Tau_ii in A layout (row jl, columns 4 g4 ..), Tau_jj
     // in B layout (column jl, rows 4 g4 ..) from the transposed copy
-    auto Aop = [&](int i, int m) { return *reinterpret_cast<const f32x4 *>(sA + blk(i, m) * 256 + jl * 16 + 4 * g4); };
-    auto Tjj = [&](int i) { return *reinterpret_cast<const f32x4 *>(sTT + i * 256 + jl * 16 + 4 * g4); };
-    auto neg_tau = [&](int i, const Acc3 &x) {       // -Tau_ii X
+    auto Aop = [&](int i, int m) {
+      return split_op(*reinterpret_cast<const f32x4 *>(sA + blk(i, m) * 256 + jl * 16 + 4 * g4));
+    };
+    auto Tjj = [&](int i) { return split_op(*reinterpret_cast<const f32x4 *>(sTT + i * 256 + jl * 16 + 4 * g4)); };
+    auto neg_tau = [&](const Split4 &tii, const Acc3 &x) {       // -Tau_ii X
       Acc3 y = acc3_zero();
-      acc_split3(y, Aop(i, i), acc3_sum(x));
+      acc_split3(y, tii, split_op(acc3_sum(x)));
       return -acc3_sum(y);
     };
-    const f32x4 T00 = Tjj(0), T11 = Tjj(1), T22 = Tjj(2);
+    // every operand split once: Tau_jj (B layout), Tau_ii (A layout), A_im
+    const Split4 T00 = Tjj(0), T11 = Tjj(1), T22 = Tjj(2);
+    const Split4 D11 = Aop(1, 1), D22 = Aop(2, 2), D33 = Aop(3, 3);
+    const Split4 A10 = Aop(1, 0), A21 = Aop(2, 1), A32 = Aop(3, 2), A20 = Aop(2, 0), A31 = Aop(3, 1), A30 = Aop(3, 0);
     // level 1: Tau_10, Tau_21, Tau_32
     Acc3 x10 = acc3_zero(), x21 = acc3_zero(), x32 = acc3_zero();
-    acc_split3(x10, Aop(1, 0), T00);
-    acc_split3(x21, Aop(2, 1), T11);
-    acc_split3(x32, Aop(3, 2), T22);
-    const f32x4 T10 = neg_tau(1, x10), T21 = neg_tau(2, x21), T32 = neg_tau(3, x32);
+    acc_split3(x10, A10, T00);
+    acc_split3(x21, A21, T11);
+    acc_split3(x32, A32, T22);
+    const f32x4 T10 = neg_tau(D11, x10), T21 = neg_tau(D22, x21), T32 = neg_tau(D33, x32);
+    const Split4 T10s = split_op(T10), T21s = split_op(T21);
     // level 2: Tau_20, Tau_31
     Acc3 x20 = acc3_zero(), x31 = acc3_zero();
-    acc_split3(x20, Aop(2, 0), T00);
-    acc_split3(x31, Aop(3, 1), T11);
-    acc_split3(x20, Aop(2, 1), T10);
-    acc_split3(x31, Aop(3, 2), T21);
-    const f32x4 T20 = neg_tau(2, x20), T31 = neg_tau(3, x31);
+    acc_split3(x20, A20, T00);
+    acc_split3(x31, A31, T11);
+    acc_split3(x20, A21, T10s);
+    acc_split3(x31, A32, T21s);
+    const f32x4 T20 = neg_tau(D22, x20), T31 = neg_tau(D33, x31);
     // level 3: Tau_30
     Acc3 x30 = acc3_zero();
-    acc_split3(x30, Aop(3, 0), T00);
-    acc_split3(x30, Aop(3, 1), T10);
-    acc_split3(x30, Aop(3, 2), T20);
-    const f32x4 T30 = neg_tau(3, x30);
+    acc_split3(x30, A30, T00);
+    acc_split3(x30, A31, T10s);
+    acc_split3(x30, A32, split_op(T20));
+    const f32x4 T30 = neg_tau(D33, x30);
     // every A block has been read: the off-diagonal Tau blocks take their place
     wave_lds_fence();
     auto put = [&](int i, int jb, const f32x4 &t) {
