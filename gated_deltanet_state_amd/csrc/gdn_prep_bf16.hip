@@ -1,7 +1,8 @@
 // gdn_prep_bf16.hip -- per-chunk UT transform for bf16 inputs on gfx950:
 // one wave per (chunk slot, head) running prep_chunk_wave (gdn_prep_wave.h),
-// four independent waves (consecutive slots of one head) per workgroup, no
-// barriers, each wave with its own LDS scratch.  The factor
+// each in a workgroup of its own with its LDS scratch (no barriers), so that
+// the scratch and register use alone set how many waves share a compute
+// unit.  The factor
 // Tau = (I + A)^{-1} follows from the page "Tail-Replay: Escaping the Curse
 // of Linear Attention in Prefix Caching for Hybrid LLMs", section 2
 // Eq. (1), unrolled over a chunk.
@@ -11,7 +12,7 @@ namespace gdn {
 
 namespace {
 
-constexpr int PW = 4;
+constexpr int PW = 1;   // waves per workgroup
 
 // Largest n in [0, n_seqs) whose first chunk slot floor(cu[n]/64) + n is <= slot.
 __device__ __forceinline__ int find_seq_b(const int32_t *cu, int n_seqs, int64_t slot) {

@@ -24,7 +24,7 @@
 //   5. Tau diag(beta) as split-bf16 A fragments of the recurrence kernel's
 //      k = 32 products (record layout of gdn_internal.h).
 // LDS per wave: kPrepWaveLds bytes (A blocks, overwritten in place by the
-// Tau blocks; a transposed copy of the diagonal Tau blocks; gates).
+// Tau blocks; gates).
 #pragma once
 
 #include "gdn_device.h"
@@ -32,7 +32,7 @@
 
 namespace gdn {
 
-constexpr int kPrepWaveLds = (10 * 256 + 4 * 256 + 2 * 64) * 4;
+constexpr int kPrepWaveLds = (10 * 256 + 2 * 64) * 4;
 
 namespace prep_detail {
 
@@ -92,8 +92,7 @@ __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 
   using namespace prep_detail;
   constexpr int NKS = DK / 32;
   float *sA = scratch;             // 10 blocks 16 x 16 row-major: A, then Tau
-  float *sTT = sA + 10 * 256;      // Tau_bb transposed
-  float *sG = sTT + 4 * 256, *sB = sG + 64;
+  float *sG = sA + 10 * 256, *sB = sG + 64;
   const int l = lane_id(), g4 = l >> 4, jl = l & 15;
 
   // ---- 1. gates (the keys are in kf) ----
@@ -171,21 +170,20 @@ __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 
     wave_lds_fence();
 #pragma unroll
     for (int r = 0; r < 16; ++r) ab[r * 16 + c] = x[r];      // row-major: Tau_bb[r][c]
-    float *tt = sTT + b * 256 + c * 16;                       // transposed: row c holds column c
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      *reinterpret_cast<f32x4 *>(tt + 4 * r4) = f32x4{x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]};
   }
   wave_lds_fence();
 
   // ---- 4. off-diagonal blocks (C layout: lane column jl, rows 4 g4 + e) ----
   {
     // operands: A_im and Tau_ii in A layout (row jl, columns 4 g4 ..), Tau_jj
-    // in B layout (column jl, rows 4 g4 ..) from the transposed copy
+    // in B layout (column jl, rows 4 g4 ..: four reads down a column)
     auto Aop = [&](int i, int m) {
       return split_op(*reinterpret_cast<const f32x4 *>(sA + blk(i, m) * 256 + jl * 16 + 4 * g4));
     };
-    auto Tjj = [&](int i) { return split_op(*reinterpret_cast<const f32x4 *>(sTT + i * 256 + jl * 16 + 4 * g4)); };
+    auto Tjj = [&](int i) {
+      const float *t = sA + blk(i, i) * 256 + 4 * g4 * 16 + jl;
+      return split_op(f32x4{t[0], t[16], t[32], t[48]});
+    };
     auto neg_tau = [&](const Split4 &tii, const Acc3 &x) {       // -Tau_ii X
       Acc3 y = acc3_zero();
       acc_split3(y, tii, split_op(acc3_sum(x)));
