@@ -159,7 +159,11 @@ size_t gdn_chunk_operator_workspace_bytes(int32_t n_chunks, int64_t n_tokens, in
   return gdn::tau_workspace_bytes(n_tokens, n_chunks, n_heads);
 }
 
-size_t gdn_compose_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t gdn_compose_workspace_bytes(int32_t n_chunks, int32_t n_heads, int32_t dk, int32_t) {
+  // the operators as composition fragments: as many bytes as T_C
+  if (n_chunks < 1 || n_heads < 1 || dk < 1) return 0;
+  return (size_t)n_chunks * n_heads * dk * dk * sizeof(float);
+}
 
 gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *alpha, const void *beta,
                       const float *S0, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
@@ -360,19 +364,28 @@ gdn_status gdn_compose(const float *S_in, const float *T_C, const float *S_local
   if ((s = check_align("S_in", S_in)) || (s = check_align("T_C", T_C)) || (s = check_align("S_local", S_local)) ||
       (s = check_align("S_out", S_out)))
     return s;
-  if (workspace_bytes < gdn_compose_workspace_bytes(n_chunks, n_heads, dk, dv))
-    return fail(GDN_ERR_WORKSPACE, "gdn_compose: workspace too small");
-  (void)workspace;
-  gdn::ComposeLaunch p{};
-  p.S_in = S_in;
-  p.T_C = T_C;
-  p.S_local = S_local;
-  p.n_chunks = n_chunks;
-  p.H = n_heads;
-  p.dk = dk;
-  p.dv = dv;
-  p.S_out = S_out;
-  return launched(gdn::launch_compose(p, reinterpret_cast<hipStream_t>(stream)), "gdn_compose launch");
+  const size_t need = gdn_compose_workspace_bytes(n_chunks, n_heads, dk, dv);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(GDN_ERR_WORKSPACE, "gdn_compose: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  if ((s = check_align("workspace", workspace))) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // operators into fragments (all at once), then the chain per (head, 32 rows)
+  if (n_chunks > 0 && (s = launched(gdn::launch_op_frags(T_C, (int64_t)n_chunks * n_heads, dk, workspace, st),
+                                    "gdn_compose operator launch")))
+    return s;
+  gdn::SegComposeLaunch c{};
+  c.S_seg = S_local;
+  c.T_frag = workspace;
+  c.S_prefix = nullptr;
+  c.S0 = S_in;
+  c.n_seqs = 1;
+  c.n_segs = n_chunks;
+  c.H = n_heads;
+  c.dk = dk;
+  c.dv = dv;
+  c.S_out = S_out;
+  c.from_start = 1;
+  return launched(gdn::launch_seg_compose(c, st), "gdn_compose launch");
 }
 
 const char *gdn_status_string(gdn_status status) {

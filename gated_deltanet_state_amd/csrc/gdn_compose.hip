@@ -5,11 +5,13 @@
 // c+1's input, S <- S T_C[c] + S_local[c], in context order.
 //
 // Per head this is a chain of dv x dk x dk products.  Rows of S are
-// independent, so a workgroup owns 16 rows of one head and walks the chunks;
-// the dk x dk operator of each step is staged transposed in LDS (all row
-// tiles of a head read the same operator, on the same XCD, through L2).
-// Both operands are fp32 and carried as split bf16 (three products), which
-// keeps the product within a few fp32 ulps of the fp32 result.
+// independent, so a workgroup owns 32 rows of one head and walks the
+// operators; each operator enters the products as split-bf16 MFMA
+// fragments (three products per step keep the result within a few fp32
+// ulps of the fp32 product).  Operators that arrive as fp32 matrices
+// (gdn_compose) are first converted to that fragment form by a fully
+// parallel pass; the time-split replay writes its segment operators in that
+// form directly.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -17,75 +19,52 @@ namespace gdn {
 
 namespace {
 
-constexpr int CNW = 8;
-constexpr int CNT = CNW * 64;
+// ---------------------------------------------------------------------------
+// fp32 operators [n, dk, dk] (row-major) -> composition fragments (the
+// layout of gdn_internal.h: fragment f = jb * (dk / 32) + ks, lane (q, g)
+// holds T[32 ks + 8 g + i][16 jb + q], i < 8, hi plane then lo plane).  One
+// workgroup per operator: coalesced reads into LDS, then every wave reads
+// its fragments' columns and writes them split, 1 KiB per fragment.
+// ---------------------------------------------------------------------------
+constexpr int FNW = 4;
 
 template <int DK>
-__global__ void __launch_bounds__(CNT) compose_kernel(ComposeLaunch p, int n_items) {
-  constexpr int LDT = DK + 4;  // sTt [DK][LDT]: sTt[j][m] = T_C[m][j]
-  constexpr int LDS_ = DK + 4; // sS  [16][LDS_]
-  __shared__ __attribute__((aligned(16))) float sTt[DK * LDT];
-  __shared__ __attribute__((aligned(16))) float sS[16 * LDS_];
-
-  const int per = (int)(gridDim.x >> 3);
-  const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  if (item >= n_items) return;
-  const int tiles = p.dv / 16;
-  const int h = item / tiles, row0 = 16 * (item % tiles);
-  const int H = p.H, DV = p.dv;
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  constexpr int NST = DK / 16;
-  const bool owns = w < NST;
-  const int col = 16 * w + (l & 15);
-
-  f32x4 sacc = zero4();
-  if (owns && p.S_in) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sacc[i] = p.S_in[((int64_t)h * DV + row0 + 4 * (l >> 4) + i) * DK + col];
+__global__ void __launch_bounds__(FNW * 64) op_frag_kernel(const float *T, char *frag) {
+  constexpr int LD = DK + 4, NKS = DK / 32, NF = (DK / 16) * NKS;
+  __shared__ __attribute__((aligned(16))) float sT[DK * LD];
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, jl = l & 15;
+  const float *src = T + (int64_t)blockIdx.x * DK * DK;
+  char *dst = frag + (int64_t)blockIdx.x * (2 * NF * 1024);
+  for (int i = tid; i < DK * DK / 4; i += FNW * 64) {
+    const int m = i / (DK / 4), j4 = (i % (DK / 4)) * 4;
+    *reinterpret_cast<f32x4 *>(sT + m * LD + j4) = *reinterpret_cast<const f32x4 *>(src + (int64_t)m * DK + j4);
   }
-  for (int c = 0; c < p.n_chunks; ++c) {
-    if (owns) store_tile(sS, LDS_, 0, 16 * w, sacc);
-    const float *T = p.T_C + ((int64_t)c * H + h) * DK * DK;
-    for (int s = tid; s < DK * DK / 4; s += CNT) {
-      const int m = s / (DK / 4), j4 = (s % (DK / 4)) * 4;
-      const f32x4 x = *reinterpret_cast<const f32x4 *>(T + m * DK + j4);
+  __syncthreads();
+  for (int f = w; f < NF; f += FNW) {
+    const int jb = f / NKS, ks = f % NKS;
+    float x[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sTt[(j4 + e) * LDT + m] = x[e];
-    }
-    f32x4 loc = zero4();
-    if (owns) {
-      const float *Lp = p.S_local + ((int64_t)c * H + h) * DV * DK;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) loc[i] = Lp[(int64_t)(row0 + 4 * (l >> 4) + i) * DK + col];
-    }
-    __syncthreads();
-    if (owns) {
-      f32x4 acc = loc;
-      mma_bf16<2, 2>(acc, RowMajor<float>{sS, LDS_}, RowMajor<float>{sTt, LDT}, 0, 16 * w, 0, DK);
-      sacc = acc;
-    }
-    __syncthreads();
-  }
-  if (owns) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p.S_out[((int64_t)h * DV + row0 + 4 * (l >> 4) + i) * DK + col] = sacc[i];
+    for (int t = 0; t < 8; ++t) x[t] = sT[(32 * ks + 8 * g4 + t) * LD + 16 * jb + jl];
+    bf16x8 hi, lo;
+    split8(x, hi, lo);
+    *reinterpret_cast<bf16x8 *>(dst + f * 1024 + 16 * l) = hi;
+    *reinterpret_cast<bf16x8 *>(dst + (NF + f) * 1024 + 16 * l) = lo;
   }
 }
 
 template <int DK>
-hipError_t launch_c(const ComposeLaunch &p, hipStream_t stream) {
-  const int64_t items = (int64_t)p.H * (p.dv / 16);
-  if (items <= 0) return hipSuccess;
-  const int64_t grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((compose_kernel<DK>), dim3((unsigned)grid), dim3(CNT), 0, stream, p, (int)items);
+hipError_t launch_of(const float *T, int64_t n_ops, void *frag, hipStream_t stream) {
+  if (n_ops <= 0) return hipSuccess;
+  hipLaunchKernelGGL((op_frag_kernel<DK>), dim3((unsigned)n_ops), dim3(FNW * 64), 0, stream, T,
+                     static_cast<char *>(frag));
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Composition of time-split segments (one sequence's segment operators, in
-// order): S = S_seg[0], then S <- S T_seg[s] + S_seg[s], computed as
-// S_new^T = T^T S^T + S_seg^T.  The operators arrive as split-bf16 MFMA
+// Composition of one sequence's operators in order: S = S_seg[0] (time
+// split: segment 0 already started from S0), or S = S0 with every operator
+// applied (from_start: gdn_compose), then S <- S T_seg[s] + S_seg[s],
+// computed as S_new^T = T^T S^T + S_seg^T.  The operators arrive as split-bf16 MFMA
 // fragments (gdn_internal.h), so a workgroup copies each step's operator
 // into LDS once (load-to-LDS DMA, one step ahead, two buffers) and its
 // waves read their A operands from there without converting anything.
@@ -151,13 +130,20 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
     for (int i = 0; i < HALF; ++i)
       *reinterpret_cast<f32x4 *>(pre + 16 * (jb0 + i)) = s0 ? *reinterpret_cast<const f32x4 *>(s0 + 16 * (jb0 + i)) : zero4();
   }
-  load_loc(0, acc);
-  if (P > 1) {
-    issue_op(1, 0);
-    load_loc(1, loc);
+  const int s0 = p.from_start ? 0 : 1;   // first operator applied
+  if (p.from_start) {   // (S0 may alias S_out: every workgroup reads its own rows here, first)
+    const float *s0p = p.S0 ? p.S0 + ((int64_t)n * H + h) * DV * DK + (int64_t)row * DK + 4 * g4 : nullptr;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) acc[i] = s0p ? *reinterpret_cast<const f32x4 *>(s0p + 16 * (jb0 + i)) : zero4();
+  } else {
+    load_loc(0, acc);
   }
-  for (int s = 1; s < P; ++s) {
-    const int b = (s - 1) & 1;
+  if (s0 < P) {
+    issue_op(s0, 0);
+    load_loc(s0, loc);
+  }
+  for (int s = s0; s < P; ++s) {
+    const int b = (s - s0) & 1;
     if (p.S_prefix) {   // the state entering segment s
       float *pre = p.S_prefix + (((int64_t)n * P + s) * H + h) * DV * DK + (int64_t)row * DK + 4 * g4;
 #pragma unroll
@@ -231,9 +217,9 @@ hipError_t launch_seg_compose(const SegComposeLaunch &p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_compose(const ComposeLaunch &p, hipStream_t stream) {
-  if (p.dk == 64) return launch_c<64>(p, stream);
-  if (p.dk == 128) return launch_c<128>(p, stream);
+hipError_t launch_op_frags(const float *T, int64_t n_ops, int32_t dk, void *frag, hipStream_t stream) {
+  if (dk == 64) return launch_of<64>(T, n_ops, frag, stream);
+  if (dk == 128) return launch_of<128>(T, n_ops, frag, stream);
   return hipErrorInvalidValue;
 }
 

@@ -102,13 +102,6 @@ struct ChainLaunch {
   const int32_t *order;
 };
 
-struct ComposeLaunch {
-  const float *S_in;        // [H, dv, dk] or null
-  const float *T_C;         // [n, H, dk, dk]
-  const float *S_local;     // [n, H, dv, dk]
-  int32_t n_chunks, H, dk, dv;
-  float *S_out;             // [H, dv, dk]
-};
 
 // Segment operator fragments (time-split replay): per (sequence, segment,
 // head), dk * dk * 4 bytes holding T as split-bf16 MFMA operands of the
@@ -126,6 +119,9 @@ struct SegComposeLaunch {
   const float *S0;          // [n_seqs, H, dv, dk] start of segment 0 (copied to S_prefix), or null = zero
   int32_t n_seqs, n_segs, H, dk, dv;
   float *S_out;             // [n_seqs, H, dv, dk]
+  // start from S0 and apply every operator, segment 0's included (else
+  // S_seg[0] is the state after segment 0 and T_frag[0] is unused)
+  int from_start;
 };
 
 hipError_t launch_prep(const PrepLaunch &p, hipStream_t stream);        // dispatches bf16 inputs to launch_prep_bf16
@@ -133,7 +129,8 @@ hipError_t launch_prep_bf16(const PrepLaunch &p, hipStream_t stream);
 hipError_t launch_chain(const ChainLaunch &p, hipStream_t stream);        // fp32 inputs
 hipError_t launch_chain_bf16(const ChainLaunch &p, hipStream_t stream);   // bf16 inputs
 hipError_t launch_chain_dks(const ChainLaunch &p, hipStream_t stream);    // bf16, state only, few row tiles
-hipError_t launch_compose(const ComposeLaunch &p, hipStream_t stream);
+// fp32 operators [n_ops, dk, dk] into composition fragments (n_ops * dk * dk * 4 bytes)
+hipError_t launch_op_frags(const float *T, int64_t n_ops, int32_t dk, void *frag, hipStream_t stream);
 hipError_t launch_seg_compose(const SegComposeLaunch &p, hipStream_t stream);
 
 }  // namespace gdn

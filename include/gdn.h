@@ -127,6 +127,9 @@ size_t gdn_chunk_operator_workspace_bytes(int32_t n_chunks, int64_t n_tokens,
  *   S_in    [H, dv, dk] fp32 or NULL (zero)
  *   T_C     [n_chunks, H, dk, dk] fp32,  S_local [n_chunks, H, dv, dk] fp32
  *   S_out   [H, dv, dk] fp32 (may alias S_in)
+ *   workspace: gdn_compose_workspace_bytes(...) bytes (n_chunks * H * dk * dk
+ *          * 4: the operators converted to the products' split-bf16 form),
+ *          16-byte aligned; may be NULL when that is 0
  * n_chunks may be 0 (S_out = S_in, or zero).
  */
 gdn_status gdn_compose(const float *S_in, const float *T_C,

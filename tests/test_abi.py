@@ -116,7 +116,9 @@ def test_workspace_queries(lib, monkeypatch):
     monkeypatch.setenv("GDN_REPLAY_SEGMENTS", "1")
     assert lib.gdn_replay_workspace_bytes(1, 3277, 32, 128, 128) == tau(1, 3277, 32)
     monkeypatch.delenv("GDN_REPLAY_SEGMENTS")
-    assert lib.gdn_compose_workspace_bytes(64, 32, 128, 128) == 0
+    # gdn_compose: the operators converted to fragments, as many bytes as T_C
+    assert lib.gdn_compose_workspace_bytes(64, 32, 128, 128) == 64 * 32 * 128 * 128 * 4
+    assert lib.gdn_compose_workspace_bytes(0, 32, 128, 128) == 0
     # a missing workspace is reported before anything is launched
     assert replay(lib) == WS
     assert b"workspace" in lib.gdn_last_error()
