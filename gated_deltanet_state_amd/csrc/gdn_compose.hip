@@ -23,28 +23,32 @@ namespace {
 // fp32 operators [n, dk, dk] (row-major) -> composition fragments (the
 // layout of gdn_internal.h: fragment f = jb * (dk / 32) + ks, lane (q, g)
 // holds T[32 ks + 8 g + i][16 jb + q], i < 8, hi plane then lo plane).  One
-// workgroup per operator: coalesced reads into LDS, then every wave reads
-// its fragments' columns and writes them split, 1 KiB per fragment.
+// workgroup per (operator, 32-row step ks): coalesced reads of its 32 rows
+// into LDS, then every wave reads the columns of its fragments and writes
+// them split, 1 KiB per fragment.  (16 KiB of LDS per workgroup, so many
+// workgroups share a compute unit and hide each other's load latency.)
 // ---------------------------------------------------------------------------
 constexpr int FNW = 4;
 
 template <int DK>
 __global__ void __launch_bounds__(FNW * 64) op_frag_kernel(const float *T, char *frag) {
-  constexpr int LD = DK + 4, NKS = DK / 32, NF = (DK / 16) * NKS;
-  __shared__ __attribute__((aligned(16))) float sT[DK * LD];
+  constexpr int LD = DK + 4, NKS = DK / 32, NSB = DK / 16, NF = NSB * NKS;
+  __shared__ __attribute__((aligned(16))) float sT[32 * LD];
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, jl = l & 15;
-  const float *src = T + (int64_t)blockIdx.x * DK * DK;
-  char *dst = frag + (int64_t)blockIdx.x * (2 * NF * 1024);
-  for (int i = tid; i < DK * DK / 4; i += FNW * 64) {
+  const int64_t op = blockIdx.x / NKS;
+  const int ks = (int)(blockIdx.x % NKS);
+  const float *src = T + op * DK * DK + (int64_t)32 * ks * DK;
+  char *dst = frag + op * (2 * NF * 1024);
+  for (int i = tid; i < 32 * DK / 4; i += FNW * 64) {
     const int m = i / (DK / 4), j4 = (i % (DK / 4)) * 4;
     *reinterpret_cast<f32x4 *>(sT + m * LD + j4) = *reinterpret_cast<const f32x4 *>(src + (int64_t)m * DK + j4);
   }
   __syncthreads();
-  for (int f = w; f < NF; f += FNW) {
-    const int jb = f / NKS, ks = f % NKS;
+  for (int jb = w; jb < NSB; jb += FNW) {
+    const int f = jb * NKS + ks;
     float x[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) x[t] = sT[(32 * ks + 8 * g4 + t) * LD + 16 * jb + jl];
+    for (int t = 0; t < 8; ++t) x[t] = sT[(8 * g4 + t) * LD + 16 * jb + jl];
     bf16x8 hi, lo;
     split8(x, hi, lo);
     *reinterpret_cast<bf16x8 *>(dst + f * 1024 + 16 * l) = hi;
@@ -55,7 +59,7 @@ __global__ void __launch_bounds__(FNW * 64) op_frag_kernel(const float *T, char 
 template <int DK>
 hipError_t launch_of(const float *T, int64_t n_ops, void *frag, hipStream_t stream) {
   if (n_ops <= 0) return hipSuccess;
-  hipLaunchKernelGGL((op_frag_kernel<DK>), dim3((unsigned)n_ops), dim3(FNW * 64), 0, stream, T,
+  hipLaunchKernelGGL((op_frag_kernel<DK>), dim3((unsigned)(n_ops * (DK / 32))), dim3(FNW * 64), 0, stream, T,
                      static_cast<char *>(frag));
   return hipGetLastError();
 }
