@@ -68,32 +68,41 @@ hipError_t launch_of(const float *T, int64_t n_ops, void *frag, hipStream_t stre
 // Composition of one sequence's operators in order: S = S_seg[0] (time
 // split: segment 0 already started from S0), or S = S0 with every operator
 // applied (from_start: gdn_compose), then S <- S T_seg[s] + S_seg[s],
-// computed as S_new^T = T^T S^T + S_seg^T.  The operators arrive as split-bf16 MFMA
-// fragments (gdn_internal.h), so a workgroup copies each step's operator
-// into LDS once (load-to-LDS DMA, one step ahead, two buffers) and its
-// waves read their A operands from there without converting anything.
-// Workgroup = 4 waves on 32 rows of one (sequence, head): wave w owns rows
-// 16 (w & 1) .. + 15 of the group and dk blocks (w >> 1) * NSB / 2 .. of
-// S^T (C layout); the two halves of a row tile meet in LDS once per step.
+// computed as S_new^T = T^T S^T + S_seg^T.  The operators arrive as
+// split-bf16 MFMA fragments (gdn_internal.h).
+// Workgroup = 4 waves on 32 rows of one (sequence, head); wave w owns dk
+// blocks JBW w .. JBW w + JBW - 1 of S^T (C layout) for both 16-row tiles,
+// so it needs only its own fragments of each operator: those, and its rows
+// of each local state, are loaded straight into registers two steps ahead
+// (three register sets in rotation), which hides the load latency of the
+// serial chain.  Per step the waves exchange the new S rows through LDS,
+// already split into bf16 hi and lo planes.
 // ---------------------------------------------------------------------------
 constexpr int SNW = 4;
 
 template <int DK>
 struct SegCfg {
-  static constexpr int NSB = DK / 16, NKS = DK / 32, HALF = NSB / 2;
+  static constexpr int NSB = DK / 16, NKS = DK / 32;
+  static constexpr int JBW = NSB / SNW;              // dk blocks per wave
   static constexpr int NF = NSB * NKS;               // fragments per plane
   static constexpr int OPB = 2 * NF * 1024;          // bytes of one operator (both planes)
-  static constexpr int LDS_ = DK + 4;                // sS row pitch (floats)
-  static constexpr size_t TOTAL = 2 * (size_t)OPB + 32 * LDS_ * 4;
-  static_assert(TOTAL <= 160 * 1024, "LDS budget");
+  static constexpr int LDB = DK + 8;                 // row pitch of the split S planes (bf16)
+};
+
+// One step's operands of a wave: its operator fragments (hi, lo) and its
+// rows of the local state.
+template <int DK>
+struct StepRegs {
+  bf16x8 h[SegCfg<DK>::JBW][SegCfg<DK>::NKS], l[SegCfg<DK>::JBW][SegCfg<DK>::NKS];
+  f32x4 loc[2][SegCfg<DK>::JBW];
 };
 
 template <int DK>
 __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch p, int n_items) {
   using C = SegCfg<DK>;
-  constexpr int NKS = C::NKS, HALF = C::HALF, NF = C::NF, LDS_ = C::LDS_;
-  __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
-  float *sS = reinterpret_cast<float *>(smem + 2 * C::OPB);
+  constexpr int NKS = C::NKS, JBW = C::JBW, NF = C::NF, LDB = C::LDB;
+  __shared__ __attribute__((aligned(16))) bf16 sSh[32 * LDB];
+  __shared__ __attribute__((aligned(16))) bf16 sSl[32 * LDB];
 
   const int per = (int)(gridDim.x >> 3);
   const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
@@ -103,104 +112,127 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
   const int n = nh / p.H, h = nh % p.H;
   const int H = p.H, DV = p.dv, P = p.n_segs;
   const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), g4 = l >> 4, jl = l & 15;
-  const int rsub = w & 1, jb0 = (w >> 1) * HALF;
-  const int row = 32 * rg + 16 * rsub + jl;   // this lane's S row (C-layout column)
+  const int jb0 = JBW * w;
+  // lane's element offset of row tile rt, dk block jb0 + i: row 32 rg + 16 rt + jl, columns 16 jb + 4 g4 ..
+  auto eoff = [&](int rt, int i) { return (int64_t)(32 * rg + 16 * rt + jl) * DK + 16 * (jb0 + i) + 4 * g4; };
+  const int64_t head = ((int64_t)n * H + h) * DV * DK;
 
-  auto seg_state = [&](int s) { return p.S_seg + (((int64_t)n * P + s) * H + h) * DV * DK; };
-  auto seg_op = [&](int s) {
-    return reinterpret_cast<const char *>(p.T_frag) + (((int64_t)n * P + s) * H + h) * (int64_t)C::OPB;
-  };
-  // operator of step s into LDS buffer b: 2 NF blocks of 1 KiB, NF / 2 per wave
-  auto issue_op = [&](int s, int b) {
-    const char *src = seg_op(s) + 16 * l;
-    char *dst = smem + b * C::OPB;
+  auto load = [&](int s, StepRegs<DK> &R) {
+    const char *op = reinterpret_cast<const char *>(p.T_frag) + (((int64_t)n * P + s) * H + h) * (int64_t)C::OPB + 16 * l;
 #pragma unroll
-    for (int j = 0; j < 2 * NF / SNW; ++j) {
-      const int f = j * SNW + w;
-      dma16_global(src + f * 1024, (lds_void *)(dst + f * 1024));
-    }
-  };
-  auto load_loc = [&](int s, f32x4 (&loc)[HALF]) {
-    const float *Ls = seg_state(s) + (int64_t)row * DK + 4 * g4;
+    for (int i = 0; i < JBW; ++i)
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) loc[i] = *reinterpret_cast<const f32x4 *>(Ls + 16 * (jb0 + i));
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int f = (jb0 + i) * NKS + ks;
+        R.h[i][ks] = *reinterpret_cast<const bf16x8 *>(op + f * 1024);
+        R.l[i][ks] = *reinterpret_cast<const bf16x8 *>(op + (NF + f) * 1024);
+      }
+    const float *Ls = p.S_seg + (((int64_t)n * P + s) * H + h) * DV * DK;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < JBW; ++i) R.loc[rt][i] = *reinterpret_cast<const f32x4 *>(Ls + eoff(rt, i));
   };
 
-  f32x4 acc[HALF], loc[HALF];
-  if (p.S_prefix) {   // the state entering segment 0 (S0 may alias S_out: read it here, first)
-    float *pre = p.S_prefix + ((int64_t)n * P * H + h) * DV * DK + (int64_t)row * DK + 4 * g4;
-    const float *s0 = p.S0 ? p.S0 + ((int64_t)n * H + h) * DV * DK + (int64_t)row * DK + 4 * g4 : nullptr;
-#pragma unroll
-    for (int i = 0; i < HALF; ++i)
-      *reinterpret_cast<f32x4 *>(pre + 16 * (jb0 + i)) = s0 ? *reinterpret_cast<const f32x4 *>(s0 + 16 * (jb0 + i)) : zero4();
-  }
+  f32x4 acc[2][JBW];
   const int s0 = p.from_start ? 0 : 1;   // first operator applied
-  if (p.from_start) {   // (S0 may alias S_out: every workgroup reads its own rows here, first)
-    const float *s0p = p.S0 ? p.S0 + ((int64_t)n * H + h) * DV * DK + (int64_t)row * DK + 4 * g4 : nullptr;
+  {
+    // the state entering the chain: S0 (or zero), or segment 0's own state
+    // (S0 may alias S_out: every workgroup reads its own rows here, first)
+    const float *src = (p.from_start || p.S_prefix) ? (p.S0 ? p.S0 + head : nullptr) : nullptr;
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) acc[i] = s0p ? *reinterpret_cast<const f32x4 *>(s0p + 16 * (jb0 + i)) : zero4();
-  } else {
-    load_loc(0, acc);
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < JBW; ++i) acc[rt][i] = src ? *reinterpret_cast<const f32x4 *>(src + eoff(rt, i)) : zero4();
+    if (p.S_prefix) {   // the state entering segment 0
+      float *pre = p.S_prefix + ((int64_t)n * P * H + h) * DV * DK;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < JBW; ++i) *reinterpret_cast<f32x4 *>(pre + eoff(rt, i)) = acc[rt][i];
+    }
+    if (!p.from_start) {
+      const float *L0 = p.S_seg + ((int64_t)n * P * H + h) * DV * DK;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < JBW; ++i) acc[rt][i] = *reinterpret_cast<const f32x4 *>(L0 + eoff(rt, i));
+    }
   }
-  if (s0 < P) {
-    issue_op(s0, 0);
-    load_loc(s0, loc);
-  }
-  for (int s = s0; s < P; ++s) {
-    const int b = (s - s0) & 1;
+
+  auto step = [&](int s, const StepRegs<DK> &R) {
     if (p.S_prefix) {   // the state entering segment s
-      float *pre = p.S_prefix + (((int64_t)n * P + s) * H + h) * DV * DK + (int64_t)row * DK + 4 * g4;
+      float *pre = p.S_prefix + (((int64_t)n * P + s) * H + h) * DV * DK;
 #pragma unroll
-      for (int i = 0; i < HALF; ++i) *reinterpret_cast<f32x4 *>(pre + 16 * (jb0 + i)) = acc[i];
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < JBW; ++i) *reinterpret_cast<f32x4 *>(pre + eoff(rt, i)) = acc[rt][i];
     }
-    // this wave's half of its row tile to LDS; the operator of step s landed
+    // this wave's columns of both row tiles, split, to LDS
 #pragma unroll
-    for (int i = 0; i < HALF; ++i)
-      *reinterpret_cast<f32x4 *>(sS + (16 * rsub + jl) * LDS_ + 16 * (jb0 + i) + 4 * g4) = acc[i];
-    f32x4 c0[HALF], c1[HALF], c2[HALF];
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) {
-      c0[i] = loc[i];
-      c1[i] = c2[i] = zero4();
-    }
-    wait_vmem();
+      for (int i = 0; i < JBW; ++i) {
+        bf16x4 hi, lo;
+        split4(acc[rt][i], hi, lo);
+        const int o = (16 * rt + jl) * LDB + 16 * (jb0 + i) + 4 * g4;
+        *reinterpret_cast<bf16x4 *>(sSh + o) = hi;
+        *reinterpret_cast<bf16x4 *>(sSl + o) = lo;
+      }
     lds_barrier();
-    // next step's operator and local state are in flight while this one runs
-    if (s + 1 < P) {
-      issue_op(s + 1, b ^ 1);
-      load_loc(s + 1, loc);
-    }
-    const char *op = smem + b * C::OPB;
+    f32x4 c[2][JBW];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < JBW; ++i) c[rt][i] = R.loc[rt][i];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 bh, bl;
-      {
-        const float *x = sS + (16 * rsub + jl) * LDS_ + 32 * ks + 8 * g4;
-        b_frag_split(*reinterpret_cast<const f32x4 *>(x), *reinterpret_cast<const f32x4 *>(x + 4), bh, bl);
+      bf16x8 bh[2], bl[2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int o = (16 * rt + jl) * LDB + 32 * ks + 8 * g4;
+        bh[rt] = *reinterpret_cast<const bf16x8 *>(sSh + o);
+        bl[rt] = *reinterpret_cast<const bf16x8 *>(sSl + o);
       }
-      bf16x8 ah[HALF], al[HALF];
+      // the three split passes share each accumulator; 2 JBW of them rotate
 #pragma unroll
-      for (int i = 0; i < HALF; ++i) {
-        const int f = (jb0 + i) * NKS + ks;
-        ah[i] = *reinterpret_cast<const bf16x8 *>(op + f * 1024 + 16 * l);
-        al[i] = *reinterpret_cast<const bf16x8 *>(op + (NF + f) * 1024 + 16 * l);
-      }
-      // three accumulators per block (one per split pass), rotated so that
-      // no product waits on the one just issued
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int i = 0; i < HALF; ++i) c0[i] = mfma_bf16(ah[i], bh, c0[i]);
+        for (int i = 0; i < JBW; ++i) c[rt][i] = mfma_bf16(R.h[i][ks], bh[rt], c[rt][i]);
 #pragma unroll
-      for (int i = 0; i < HALF; ++i) c1[i] = mfma_bf16(ah[i], bl, c1[i]);
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int i = 0; i < HALF; ++i) c2[i] = mfma_bf16(al[i], bh, c2[i]);
+        for (int i = 0; i < JBW; ++i) c[rt][i] = mfma_bf16(R.h[i][ks], bl[rt], c[rt][i]);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < JBW; ++i) c[rt][i] = mfma_bf16(R.l[i][ks], bh[rt], c[rt][i]);
     }
+    lds_barrier();   // every wave has read the planes before the next step rewrites them
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) acc[i] = c0[i] + c1[i] + c2[i];
-    lds_barrier();
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < JBW; ++i) acc[rt][i] = c[rt][i];
+  };
+
+  StepRegs<DK> R0, R1, R2;
+  if (s0 < P) load(s0, R0);
+  if (s0 + 1 < P) load(s0 + 1, R1);
+  for (int s = s0; s < P; s += 3) {
+    if (s + 2 < P) load(s + 2, R2);
+    step(s, R0);
+    if (s + 1 >= P) break;
+    if (s + 3 < P) load(s + 3, R0);
+    step(s + 1, R1);
+    if (s + 2 >= P) break;
+    if (s + 4 < P) load(s + 4, R1);
+    step(s + 2, R2);
   }
-  float *out = p.S_out + ((int64_t)n * H + h) * DV * DK + (int64_t)row * DK + 4 * g4;
+  float *out = p.S_out + head;
 #pragma unroll
-  for (int i = 0; i < HALF; ++i) *reinterpret_cast<f32x4 *>(out + 16 * (jb0 + i)) = acc[i];
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int i = 0; i < JBW; ++i) *reinterpret_cast<f32x4 *>(out + eoff(rt, i)) = acc[rt][i];
 }
 
 template <int DK>
