@@ -196,18 +196,6 @@ __device__ __forceinline__ void mma_f32(f32x4 &c, const OA &opA, const OB &opB, 
 
 __device__ __forceinline__ void split4(const f32x4 &x, bf16x4 &hi, bf16x4 &lo);  // defined below split2
 
-// 3-pass split-bf16 product of 16 x 16 tiles, k = 16: A given as 4 fp32 per
-// lane in A layout, B as 4 fp32 per lane in B (= C) layout.
-__device__ __forceinline__ f32x4 mma16_split3(const f32x4 &a, const f32x4 &b, f32x4 c) {
-  bf16x4 ah, al, bh, bl;
-  split4(a, ah, al);
-  split4(b, bh, bl);
-  c = mfma_bf16_k16(ah, bh, c);
-  c = mfma_bf16_k16(ah, bl, c);
-  c = mfma_bf16_k16(al, bh, c);
-  return c;
-}
-
 // Store a C-layout tile into split planes (hi, lo) of a row-major bf16 array.
 __device__ __forceinline__ void store_tile_planes(bf16 *hi, bf16 *lo, int ld, int m0, int n0, const f32x4 &c) {
   const int l = lane_id();
@@ -261,13 +249,6 @@ __device__ __forceinline__ bf16x8 cat_bf16x8(uint2 a, uint2 b) {
   return x.v;
 }
 
-// A fragment of a row-major bf16 matrix: row pointer rowp, step base kb.
-__device__ __forceinline__ bf16x8 a_frag_perm(const bf16 *rowp, int kb, int g) {
-  const uint2 x0 = *reinterpret_cast<const uint2 *>(rowp + kb + 4 * g);
-  const uint2 x1 = *reinterpret_cast<const uint2 *>(rowp + kb + 16 + 4 * g);
-  return cat_bf16x8(x0, x1);
-}
-
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16
 // lanes, output lane i element e is element (i mod 4) of the 8 bytes read by
 // source lane 4e + i/4.  Pointing source lane q of group g at
@@ -282,14 +263,6 @@ __device__ __forceinline__ uint2 ds_read_tr16(const bf16 *p) {
   union { s16x4 s; uint2 u; } x;
   x.s = v;
   return x.u;
-}
-
-// A fragment of M^T (rows = columns of M) for the permuted k = 32 step with
-// base row kb of M: columns c0 .. c0 + 15 of M, rows kb + {4g + e, 16 + 4g + e}.
-__device__ __forceinline__ bf16x8 a_frag_trans_perm(const bf16 *M, int ld, int kb, int c0, int l) {
-  const int g = l >> 4, q = l & 15;
-  const bf16 *p0 = M + (kb + 4 * g + (q >> 2)) * ld + c0 + 4 * (q & 3);
-  return cat_bf16x8(ds_read_tr16(p0), ds_read_tr16(p0 + 16 * ld));
 }
 
 // Two fp32 values as packed bf16 (round to nearest even, v_cvt_pk_bf16_f32).
