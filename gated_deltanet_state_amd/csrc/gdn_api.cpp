@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
@@ -360,6 +361,9 @@ gdn_status gdn_compose(const float *S_in, const float *T_C, const float *S_local
     return fail(GDN_ERR_BAD_SHAPE, "gdn_compose: bad sizes (n_chunks %d, n_heads %d)", n_chunks, n_heads);
   if (!supported_dim(dk) || !supported_dim(dv))
     return fail(GDN_ERR_UNSUPPORTED, "gdn_compose: dk and dv must be 64 or 128 (got %d, %d)", dk, dv);
+  if ((int64_t)n_chunks * n_heads * (dk / 32) > INT32_MAX)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_compose: too many operators for one call (%d chunks x %d heads)", n_chunks,
+                n_heads);
   gdn_status s;
   if ((s = check_align("S_in", S_in)) || (s = check_align("T_C", T_C)) || (s = check_align("S_local", S_local)) ||
       (s = check_align("S_out", S_out)))

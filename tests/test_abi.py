@@ -91,7 +91,9 @@ def test_compose_argument_checks(lib):
     assert cp(TC=None) == NULLP
     assert cp(C=-2) == SHAPE
     assert cp(dv=48) == UNSUP
+    assert cp(C=1 << 30, H=4) == UNSUP           # operator-conversion grid beyond 32 bits
     assert cp(Si=P + 4) == ALIGN
+    assert cp() == WS                             # the converted operators need a workspace
 
 
 def test_workspace_queries(lib, monkeypatch):
