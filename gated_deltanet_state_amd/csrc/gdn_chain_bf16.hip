@@ -451,11 +451,6 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       ph[f] = *reinterpret_cast<const bf16x8 *>(sP + (f * 64 + l) * 8);
       pl[f] = *reinterpret_cast<const bf16x8 *>(sP + kTauFragPlane + (f * 64 + l) * 8);
     }
-    f32x4 z2[RT][4];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int bt = 0; bt < 4; ++bt) z2[rt][bt] = zero4();
 #pragma unroll
     for (int pass = 0; pass < 3; ++pass)
 #pragma unroll
@@ -465,14 +460,8 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
           const int f = ford[i];
           const int bt = f < 2 ? f : (f - 2) / 2 + 2;
           const int m = f < 2 ? 0 : (f - 2) % 2;
-          if (pass == 0) zp[rt][bt] = mfma_bf16(dph[rt][m], ph[f], zp[rt][bt]);
-          if (pass == 1) z2[rt][bt] = mfma_bf16(dpl[rt][m], ph[f], z2[rt][bt]);
-          if (pass == 2) zp[rt][bt] = mfma_bf16(dph[rt][m], pl[f], zp[rt][bt]);
+          zp[rt][bt] = mfma_bf16(pass == 1 ? dpl[rt][m] : dph[rt][m], pass == 2 ? pl[f] : ph[f], zp[rt][bt]);
         }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int bt = 0; bt < 4; ++bt) zp[rt][bt] += z2[rt][bt];
   };
   auto store_o = [&]() {
     // lane (q, g) of block bt holds token tp + 16 bt + q, value columns
@@ -690,15 +679,14 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 
       // ---- D = (Tau diag(beta)) R  (f: (bt, m) = (0,0),(1,0),(2,0),(2,1),(3,0),(3,1)) ----
       // fragments in the order 0, 2, 4, 1, 3, 5 (token blocks 0, 2, 3, 1, 2, 3)
-      // so that a block's two products are three issue slots apart; the
-      // hi-lo pass accumulates separately
+      // so that a block's two products are three issue slots apart; all
+      // three split passes share the accumulators
       f32x4 dd[RT][4];
       {
-        f32x4 d2[RT][4];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int bt = 0; bt < 4; ++bt) dd[rt][bt] = d2[rt][bt] = zero4();
+          for (int bt = 0; bt < 4; ++bt) dd[rt][bt] = zero4();
         constexpr int ford[kTauFrags] = {0, 2, 4, 1, 3, 5};
         bf16x8 th[kTauFrags], tl[kTauFrags];
 #pragma unroll
@@ -715,14 +703,8 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
               const int f = ford[i];
               const int bt = f < 2 ? f : (f - 2) / 2 + 2;
               const int m = f < 2 ? 0 : (f - 2) % 2;
-              if (pass == 0) dd[rt][bt] = mfma_bf16(th[f], rh[rt][m], dd[rt][bt]);
-              if (pass == 1) d2[rt][bt] = mfma_bf16(th[f], rl[rt][m], d2[rt][bt]);
-              if (pass == 2) dd[rt][bt] = mfma_bf16(tl[f], rh[rt][m], dd[rt][bt]);
+              dd[rt][bt] = mfma_bf16(pass == 2 ? tl[f] : th[f], pass == 1 ? rl[rt][m] : rh[rt][m], dd[rt][bt]);
             }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int bt = 0; bt < 4; ++bt) dd[rt][bt] += d2[rt][bt];
       }
 
       // ---- outputs: the previous chunk's finished and stored; this one's
