@@ -18,7 +18,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["replay", "chunk_operator", "compose", "GdnError", "library", "LIB_PATH"]
+__all__ = ["replay", "decode", "chunk_operator", "compose", "GdnError", "library", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
@@ -53,7 +53,8 @@ def library():
     lib.gdn_chunk_operator_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
     lib.gdn_compose.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]
     lib.gdn_compose_workspace_bytes.argtypes = [i32, i32, i32, i32]
-    for f in (lib.gdn_replay, lib.gdn_chunk_operator, lib.gdn_compose):
+    lib.gdn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, cint, vp, cint, vp, vp]
+    for f in (lib.gdn_replay, lib.gdn_chunk_operator, lib.gdn_compose, lib.gdn_decode):
         f.restype = cint
     for f in (lib.gdn_replay_workspace_bytes, lib.gdn_chunk_operator_workspace_bytes,
               lib.gdn_compose_workspace_bytes):
@@ -160,6 +161,44 @@ def replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=None,
     _check(lib.gdn_replay(_ptr(q) if want_o else None, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                           _ptr(S0), _ptr(cu_seqlens), N, T, H, dk, dv, in_code, _ptr(o),
                           o_code, _ptr(S), _ptr(ws), ws_bytes, _stream_ptr(stream)))
+    return o, S
+
+
+def decode(q, k, v, alpha, beta, S_in=None, want_o=True, o_dtype=None, out=None, S_out=None,
+           stream=None):
+    """One token per sequence from the states S_in (the step after a replay).
+
+    q, k [N, H, dk]; v [N, H, dv]; alpha, beta [N, H] (all float32 or all
+    bfloat16); S_in [N, H, dv, dk] float32 or None (zero state).  Returns
+    (o [N, H, dv] or None, S [N, H, dv, dk] float32).  ``S_out`` may be S_in
+    (the states are then updated in place).
+    """
+    torch = _torch()
+    lib = library()
+    for name, t in (("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("S_in", S_in)):
+        _dev(t, name)
+    if want_o:
+        _dev(q, "q")
+    N, H, dk = k.shape
+    dv = v.shape[2]
+    in_code = _dtype_code(k.dtype)
+    for name, t in (("q", q if want_o else None), ("v", v), ("alpha", alpha), ("beta", beta)):
+        if t is not None and t.dtype != k.dtype:
+            raise TypeError("%s must have the dtype of k" % name)
+    if S_in is not None and S_in.dtype != torch.float32:
+        raise TypeError("S_in must be float32")
+    o = None
+    o_code = GDN_F32
+    if want_o:
+        o_dt = torch.float32 if o_dtype is None else o_dtype
+        o = out if out is not None else torch.empty((N, H, dv), dtype=o_dt, device=k.device)
+        _dev(o, "out")
+        o_code = _dtype_code(o.dtype)
+    S = S_out if S_out is not None else torch.empty((N, H, dv, dk), dtype=torch.float32, device=k.device)
+    _dev(S, "S_out")
+    _check(lib.gdn_decode(_ptr(q) if want_o else None, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                          _ptr(S_in), N, H, dk, dv, in_code, _ptr(o), o_code, _ptr(S),
+                          _stream_ptr(stream)))
     return o, S
 
 

@@ -392,6 +392,43 @@ gdn_status gdn_compose(const float *S_in, const float *T_C, const float *S_local
   return launched(gdn::launch_seg_compose(c, st), "gdn_compose launch");
 }
 
+gdn_status gdn_decode(const void *q, const void *k, const void *v, const void *alpha, const void *beta,
+                      const float *S_in, int32_t n_seqs, int32_t n_heads, int32_t dk, int32_t dv,
+                      gdn_dtype in_dtype, void *o, gdn_dtype o_dtype, float *S_out, gdn_stream_t stream) {
+  if (!k || !v || !alpha || !beta || !S_out)
+    return fail(GDN_ERR_NULL_POINTER, "gdn_decode: k, v, alpha, beta and S_out are required");
+  if (o && !q) return fail(GDN_ERR_NULL_POINTER, "gdn_decode: o requested without q");
+  if (n_seqs < 0 || n_heads < 1 || dk < 1 || dv < 1)
+    return fail(GDN_ERR_BAD_SHAPE, "gdn_decode: need n_seqs >= 0 and n_heads >= 1 (got %d, %d)", n_seqs, n_heads);
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_decode: dk and dv must be 64 or 128 (got %d, %d)", dk, dv);
+  if (!valid_dtype(in_dtype) || (o && !valid_dtype(o_dtype)))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_decode: dtypes must be GDN_F32 or GDN_BF16");
+  if (n_heads > kMaxHeads || (int64_t)n_seqs * n_heads > INT32_MAX)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_decode: problem too large for one call");
+  gdn_status s;
+  if ((s = check_align("q", q)) || (s = check_align("k", k)) || (s = check_align("v", v)) ||
+      (s = check_align("alpha", alpha)) || (s = check_align("beta", beta)) || (s = check_align("S_in", S_in)) ||
+      (s = check_align("o", o)) || (s = check_align("S_out", S_out)))
+    return s;
+  gdn::DecodeLaunch p{};
+  p.q = o ? q : nullptr;
+  p.k = k;
+  p.v = v;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.S_in = S_in;
+  p.S_out = S_out;
+  p.o = o;
+  p.n_seqs = n_seqs;
+  p.H = n_heads;
+  p.dk = dk;
+  p.dv = dv;
+  p.in_bf16 = in_dtype == GDN_BF16;
+  p.o_bf16 = o_dtype == GDN_BF16;
+  return launched(gdn::launch_decode(p, reinterpret_cast<hipStream_t>(stream)), "gdn_decode launch");
+}
+
 const char *gdn_status_string(gdn_status status) {
   switch (status) {
     case GDN_OK: return "GDN_OK";

@@ -1,0 +1,122 @@
+// gdn_decode.hip -- one token per sequence from a given state: the step that
+// follows a replay when serving continues token by token.
+//
+// Page "Tail-Replay: Escaping the Curse of Linear Attention in Prefix Caching
+// for Hybrid LLMs": section 2 Eq. (1) (the per-token update) and section 3
+// (after the replay the model continues serving the request from the
+// reconstructed states).  For one token with state S (dv x dk):
+//     y = S k,   S <- alpha S + beta (v - alpha y) k^T,   o = S q
+// (Eq. (1) multiplied out; o with the updated state).
+//
+// Rows of S are independent, so the step is one streaming pass over the
+// state: 64 KiB read and 64 KiB written per (sequence, head) at dk = dv =
+// 128, bound by HBM bandwidth.  A workgroup of four waves takes one
+// (sequence, head); 16 lanes share a row (dk / 16 values each, 16- or
+// 32-byte contiguous pieces, so a wave reads four whole rows per step), the
+// two dot products are reduced across the 16 lanes with xor shuffles, and
+// the updated row is written back in place (S_out may alias S_in).  All
+// arithmetic is fp32.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int DNW = 4;
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x);
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float to_f32<bf16>(bf16 x) { return (float)x; }
+
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) x += __shfl_xor(x, m, 16);
+  return x;
+}
+
+template <int DK, typename TI>
+__global__ void __launch_bounds__(DNW * 64) decode_kernel(DecodeLaunch p) {
+  constexpr int PER = DK / 16;   // values of a row per lane
+  const int nh = blockIdx.x;
+  const int H = p.H, DV = p.dv;
+  const int w = wave_id(), l = lane_id(), r4 = l >> 4, c = l & 15;
+  const TI *q = reinterpret_cast<const TI *>(p.q), *k = reinterpret_cast<const TI *>(p.k);
+  const TI *v = reinterpret_cast<const TI *>(p.v);
+  const float alpha = to_f32(reinterpret_cast<const TI *>(p.alpha)[nh]);
+  const float beta = to_f32(reinterpret_cast<const TI *>(p.beta)[nh]);
+  float kk[PER], qq[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    kk[i] = to_f32(k[(int64_t)nh * DK + PER * c + i]);
+    qq[i] = p.o ? to_f32(q[(int64_t)nh * DK + PER * c + i]) : 0.f;
+  }
+  const int64_t base = (int64_t)nh * DV * DK;
+  // rows w * DV / 4 + 4 it + r4
+  for (int it = 0; it < DV / (4 * DNW); ++it) {
+    const int row = w * (DV / DNW) + 4 * it + r4;
+    const int64_t off = base + (int64_t)row * DK + PER * c;
+    float s[PER];
+    if (p.S_in) {
+#pragma unroll
+      for (int i = 0; i < PER; i += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(p.S_in + off + i);
+        s[i] = x[0];
+        s[i + 1] = x[1];
+        s[i + 2] = x[2];
+        s[i + 3] = x[3];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) s[i] = 0.f;
+    }
+    float y = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) y += s[i] * kk[i];
+    y = sum16(y);
+    const float coef = beta * (to_f32(v[(int64_t)nh * DV + row]) - alpha * y);
+    float o = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      s[i] = alpha * s[i] + coef * kk[i];
+      o += s[i] * qq[i];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; i += 4)
+      *reinterpret_cast<f32x4 *>(p.S_out + off + i) = f32x4{s[i], s[i + 1], s[i + 2], s[i + 3]};
+    if (p.o) {
+      o = sum16(o);
+      if (c == 0) {
+        if (p.o_bf16)
+          reinterpret_cast<bf16 *>(p.o)[(int64_t)nh * DV + row] = (bf16)o;
+        else
+          reinterpret_cast<float *>(p.o)[(int64_t)nh * DV + row] = o;
+      }
+    }
+  }
+}
+
+template <int DK>
+hipError_t launch_d(const DecodeLaunch &p, hipStream_t stream) {
+  const int64_t items = (int64_t)p.n_seqs * p.H;
+  if (items <= 0) return hipSuccess;
+  if (p.in_bf16)
+    hipLaunchKernelGGL((decode_kernel<DK, bf16>), dim3((unsigned)items), dim3(DNW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<DK, float>), dim3((unsigned)items), dim3(DNW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream) {
+  if (p.dv % (4 * DNW) != 0) return hipErrorInvalidValue;
+  if (p.dk == 64) return launch_d<64>(p, stream);
+  if (p.dk == 128) return launch_d<128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

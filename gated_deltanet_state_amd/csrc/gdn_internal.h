@@ -124,6 +124,17 @@ struct SegComposeLaunch {
   int from_start;
 };
 
+// One token per sequence from a given state (gdn_decode).
+struct DecodeLaunch {
+  const void *q, *k, *v, *alpha, *beta;   // q, k [n_seqs, H, dk]; v [n_seqs, H, dv]; alpha, beta [n_seqs, H]
+  const float *S_in;                      // [n_seqs, H, dv, dk] or null (zero)
+  float *S_out;                           // [n_seqs, H, dv, dk] (may be S_in)
+  void *o;                                // [n_seqs, H, dv] or null
+  int32_t n_seqs, H, dk, dv;
+  int in_bf16, o_bf16;
+};
+
+hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream);
 hipError_t launch_prep(const PrepLaunch &p, hipStream_t stream);        // dispatches bf16 inputs to launch_prep_bf16
 hipError_t launch_prep_bf16(const PrepLaunch &p, hipStream_t stream);
 hipError_t launch_chain(const ChainLaunch &p, hipStream_t stream);        // fp32 inputs

@@ -146,6 +146,28 @@ const char *gdn_status_string(gdn_status status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char *gdn_last_error(void);
 
+/*
+ * gdn_decode -- one token per sequence from a given state: the step after a
+ * replay, when serving continues token by token.
+ * Page: Tail-Replay, section 2 Eq. (1) (per-token update) and section 3
+ * (serving continues from the reconstructed states).  Per (sequence, head):
+ *     y = S k;  S <- alpha S + beta (v - alpha y) k^T;  o = S q
+ * (o with the updated state), in fp32.
+ *
+ *   q, k   [n_seqs, H, dk], v [n_seqs, H, dv], alpha, beta [n_seqs, H]  in_dtype
+ *          (q may be NULL when o is NULL)
+ *   S_in   [n_seqs, H, dv, dk] fp32, or NULL (zero state)
+ *   o      [n_seqs, H, dv] o_dtype, or NULL (state only)
+ *   S_out  [n_seqs, H, dv, dk] fp32 (may alias S_in: updated in place)
+ * Supported: dk, dv in {64, 128}; dtypes F32 or BF16; 1 <= n_heads <= 65536.
+ * No workspace; stream-ordered, no synchronisation.
+ */
+gdn_status gdn_decode(const void *q, const void *k, const void *v,
+                      const void *alpha, const void *beta, const float *S_in,
+                      int32_t n_seqs, int32_t n_heads, int32_t dk, int32_t dv,
+                      gdn_dtype in_dtype, void *o, gdn_dtype o_dtype,
+                      float *S_out, gdn_stream_t stream);
+
 /* GDN_ABI_VERSION of the loaded library. */
 int gdn_abi_version(void);
 

@@ -96,6 +96,21 @@ def test_compose_argument_checks(lib):
     assert cp() == WS                             # the converted operators need a workspace
 
 
+def test_decode_argument_checks(lib):
+    def dc(q=P, k=P, v=P, a=P, b=P, Si=None, N=4, H=2, dk=128, dv=128, dt=BF16, o=P, odt=0, So=P):
+        return lib.gdn_decode(q, k, v, a, b, Si, N, H, dk, dv, dt, o, odt, So, None)
+    assert dc(So=None) == NULLP
+    assert dc(k=None) == NULLP
+    assert dc(q=None) == NULLP                    # o requested without q
+    assert dc(N=-1) == SHAPE
+    assert dc(H=0) == SHAPE
+    assert dc(dk=96) == UNSUP
+    assert dc(dt=7) == UNSUP
+    assert dc(H=65537) == UNSUP
+    assert dc(Si=P + 8) == ALIGN
+    assert dc(N=0) == OK                          # nothing to do, nothing launched
+
+
 def test_workspace_queries(lib, monkeypatch):
     # one 13 KiB record of per-chunk factors ((I + A)^{-1} diag(beta) fragments and the gates) per chunk
     # slot and head; slots = n_tokens / 64 + n_seqs + 1 (sequence n's chunk j sits
