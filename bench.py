@@ -11,7 +11,9 @@ section 3, Eq. (2)).  Other workloads: 2 = 16 packed tails of 410..3277
 tokens with outputs; 3 = a 32768-token prefill with outputs; 4 = 64
 chunk operators of 512 tokens and their composition; 0 = one fp32 head.
 
-``--tail-curve`` instead reports the tail-replay state error against the
+``--decode N`` instead times single-token decode of N requests from given
+states (the serving step after a replay).  ``--tail-curve`` instead
+reports the tail-replay state error against the
 replayed fraction (the latest k tokens of a 32768-token prefix replayed
 from zero, against the full replay) next to the stored fp64 oracle curve.
 
@@ -233,6 +235,53 @@ def tail_curve_report(gdn, torch, np):
     print(json.dumps(out))
 
 
+def decode_report(args, gdn, torch, np):
+    """One JSON line: batched single-token decode (gdn_decode) from given
+    states, the serving step after a replay; HBM-bound (every state read and
+    written once)."""
+    import workloads
+    N, H, d = args.decode, 32, 128
+    inp = workloads.generate([1] * N, H=H, dk=d, dv=d, dtype="bf16", seed=5)
+    dd = to_dev(inp, torch, np)
+    rng = np.random.Generator(np.random.PCG64(6))
+    S_in = torch.from_numpy((rng.standard_normal((N, H, d, d)) * 0.3).astype(np.float32)).cuda()
+    S = torch.empty_like(S_in)
+    o = torch.empty((N, H, d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        gdn.decode(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], S_in=S_in, out=o, S_out=S)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    avg = sum(kern_ms) / len(kern_ms)
+    # per (sequence, head): state read and written (fp32), q, k, v (bf16), gates, o (fp32)
+    byt = N * H * (2 * d * d * 4 + 3 * d * 2 + 2 * 2 + d * 4)
+    achieved = byt / (avg / 1e3) / 1e9
+    line = dict(metric="GDN decode tokens·heads/s (one token per request from its state)",
+                value=round(N * H / (step_ms / 1e3), 1), unit="tokens·heads/s", n_gpus=1,
+                steps=args.steps, warmup=args.warmup, ms_per_step=round(step_ms, 5), higher_is_better=True,
+                scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+                config=dict(workload="decode-%dx1-H32-d128-bf16" % N, n_seqs=N, n_tokens=N, heads=H, dk=d, dv=d,
+                            outputs="o,S_final", state="fp32 in and out"),
+                roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, kernel="decode_kernel",
+                              algorithmic_bytes=byt, kernel_ms_avg=round(avg, 5),
+                              kernel_ms_min=round(min(kern_ms), 5)))
+    line["gpu_ms_per_step"] = round(avg, 5)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +297,8 @@ def main():
     ap.add_argument("--command", default="", help="with --summarize-counters: the command line profiled")
     ap.add_argument("--tail-curve", action="store_true",
                     help="only report the tail-replay state error against the replayed fraction")
+    ap.add_argument("--decode", type=int, default=0, metavar="N",
+                    help="only time single-token decode of N requests (H=32, d=128) from given states")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.workload, *args.summarize_counters, command=args.command)
@@ -277,6 +328,9 @@ def main():
 
     if args.tail_curve:
         tail_curve_report(gdn, torch, np)
+        return
+    if args.decode:
+        decode_report(args, gdn, torch, np)
         return
 
     wid = args.workload

@@ -12,10 +12,11 @@
 // state: 64 KiB read and 64 KiB written per (sequence, head) at dk = dv =
 // 128, bound by HBM bandwidth.  A workgroup of four waves takes one
 // (sequence, head); 16 lanes share a row (dk / 16 values each, 16- or
-// 32-byte contiguous pieces, so a wave reads four whole rows per step), the
-// two dot products are reduced across the 16 lanes with xor shuffles, and
-// the updated row is written back in place (S_out may alias S_in).  All
-// arithmetic is fp32.
+// 32-byte contiguous pieces, so a wave reads four whole rows per step), a
+// wave loads all of its rows before it updates any (its reads are then in
+// flight together), the two dot products are reduced across the 16 lanes
+// with xor shuffles, and each updated row is written back in place (S_out
+// may alias S_in).  All arithmetic is fp32.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -55,45 +56,52 @@ __global__ void __launch_bounds__(DNW * 64) decode_kernel(DecodeLaunch p) {
     qq[i] = p.o ? to_f32(q[(int64_t)nh * DK + PER * c + i]) : 0.f;
   }
   const int64_t base = (int64_t)nh * DV * DK;
-  // rows w * DV / 4 + 4 it + r4
-  for (int it = 0; it < DV / (4 * DNW); ++it) {
-    const int row = w * (DV / DNW) + 4 * it + r4;
-    const int64_t off = base + (int64_t)row * DK + PER * c;
-    float s[PER];
-    if (p.S_in) {
+  // rows w * DV / 4 + 4 it + r4.  Every row of the wave is loaded first, so
+  // all of its reads are in flight together (S_out may alias S_in, which
+  // would otherwise keep a read behind the previous row's write).
+  constexpr int IT = 128 / (4 * DNW);   // rows per lane at dv = 128 (half of them at dv = 64)
+  float s[IT][PER];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    if (it < DV / (4 * DNW)) {
+      const int64_t off = base + (int64_t)(w * (DV / DNW) + 4 * it + r4) * DK + PER * c;
 #pragma unroll
       for (int i = 0; i < PER; i += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(p.S_in + off + i);
-        s[i] = x[0];
-        s[i + 1] = x[1];
-        s[i + 2] = x[2];
-        s[i + 3] = x[3];
+        const f32x4 x = p.S_in ? *reinterpret_cast<const f32x4 *>(p.S_in + off + i) : zero4();
+        s[it][i] = x[0];
+        s[it][i + 1] = x[1];
+        s[it][i + 2] = x[2];
+        s[it][i + 3] = x[3];
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) s[i] = 0.f;
     }
-    float y = 0.f;
+  }
 #pragma unroll
-    for (int i = 0; i < PER; ++i) y += s[i] * kk[i];
-    y = sum16(y);
-    const float coef = beta * (to_f32(v[(int64_t)nh * DV + row]) - alpha * y);
-    float o = 0.f;
+  for (int it = 0; it < IT; ++it) {
+    if (it < DV / (4 * DNW)) {
+      const int row = w * (DV / DNW) + 4 * it + r4;
+      const int64_t off = base + (int64_t)row * DK + PER * c;
+      float y = 0.f;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      s[i] = alpha * s[i] + coef * kk[i];
-      o += s[i] * qq[i];
-    }
+      for (int i = 0; i < PER; ++i) y += s[it][i] * kk[i];
+      y = sum16(y);
+      const float coef = beta * (to_f32(v[(int64_t)nh * DV + row]) - alpha * y);
+      float o = 0.f;
 #pragma unroll
-    for (int i = 0; i < PER; i += 4)
-      *reinterpret_cast<f32x4 *>(p.S_out + off + i) = f32x4{s[i], s[i + 1], s[i + 2], s[i + 3]};
-    if (p.o) {
-      o = sum16(o);
-      if (c == 0) {
-        if (p.o_bf16)
-          reinterpret_cast<bf16 *>(p.o)[(int64_t)nh * DV + row] = (bf16)o;
-        else
-          reinterpret_cast<float *>(p.o)[(int64_t)nh * DV + row] = o;
+      for (int i = 0; i < PER; ++i) {
+        s[it][i] = alpha * s[it][i] + coef * kk[i];
+        o += s[it][i] * qq[i];
+      }
+#pragma unroll
+      for (int i = 0; i < PER; i += 4)
+        *reinterpret_cast<f32x4 *>(p.S_out + off + i) = f32x4{s[it][i], s[it][i + 1], s[it][i + 2], s[it][i + 3]};
+      if (p.o) {
+        o = sum16(o);
+        if (c == 0) {
+          if (p.o_bf16)
+            reinterpret_cast<bf16 *>(p.o)[(int64_t)nh * DV + row] = (bf16)o;
+          else
+            reinterpret_cast<float *>(p.o)[(int64_t)nh * DV + row] = o;
+        }
       }
     }
   }
