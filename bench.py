@@ -28,6 +28,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -102,6 +103,15 @@ def _csv_rows(folder, suffix):
 
 
 def _short(name):
+    # names with a bf16 template argument stay mangled in the trace
+    # (gdn::(anonymous)::NAME<int, bf16|float>(...))
+    m = re.match(r"_ZN3gdn12_GLOBAL__N_1(\d+)", name)
+    if m:
+        n = int(m.group(1))
+        base = name[m.end():m.end() + n]
+        args = re.findall(r"Li(\d+)E|(DF16b)|(?<=E)(f)(?=E)", name[m.end() + n:])
+        parts = [a or ("bf16" if b else "float") for a, b, c in args if a or b or c]
+        return "%s<%s>" % (base, ", ".join(parts)) if parts else base
     name = name.replace("void ", "").replace("gdn::(anonymous namespace)::", "")
     return name.split("(")[0]
 
@@ -118,14 +128,15 @@ def _counter_kib(folder, counter):
     return {k: sum(v.values()) / len(v) for k, v in per.items()}
 
 
-def summarize_counters(wid, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, command=""):
+def summarize_counters(wid, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, command="",
+                       name=None):
     """profiles/<workload>.md and profiles/traffic_<workload>.json from
     rocprofv3 runs of this script: a --kernel-trace --stats run, one --pmc
     FETCH_SIZE run, one --pmc WRITE_SIZE run, and the same two counters on a
     --calibrate-copy run (bytes = counter x 1024 / (counter bytes per byte
     copied))."""
     import workloads
-    wname = workloads.WORKLOADS[wid]["name"]
+    wname = name or workloads.WORKLOADS[wid]["name"]
     stats = [r for r in _csv_rows(stats_dir, "kernel_stats.csv") if "rocclr" not in r["Name"]]
     fetch, write = _counter_kib(fetch_dir, "FETCH_SIZE"), _counter_kib(write_dir, "WRITE_SIZE")
     cf, cw = _counter_kib(cal_fetch_dir, "FETCH_SIZE"), _counter_kib(cal_write_dir, "WRITE_SIZE")
@@ -275,7 +286,8 @@ def decode_report(args, gdn, torch, np):
                 config=dict(workload="decode-%dx1-H32-d128-bf16" % N, n_seqs=N, n_tokens=N, heads=H, dk=d, dv=d,
                             outputs="o,S_final", state="fp32 in and out"),
                 roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                              frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, kernel="decode_kernel",
+                              frac=round(achieved / HBM_PEAK_GBS, 4),
+                              traffic=measured_traffic("decode-%dx1-H32-d128-bf16" % N), kernel="decode_kernel",
                               algorithmic_bytes=byt, kernel_ms_avg=round(avg, 5),
                               kernel_ms_min=round(min(kern_ms), 5)))
     line["gpu_ms_per_step"] = round(avg, 5)
@@ -301,7 +313,8 @@ def main():
                     help="only time single-token decode of N requests (H=32, d=128) from given states")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(args.workload, *args.summarize_counters, command=args.command)
+        summarize_counters(args.workload, *args.summarize_counters, command=args.command,
+                           name=("decode-%dx1-H32-d128-bf16" % args.decode) if args.decode else None)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the replay path is a single-GPU kernel library "
