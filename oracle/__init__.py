@@ -4,8 +4,10 @@ TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
 CPU-baseline leg of the benchmark, never by the product path.  It shares no
 code with the HIP library and imports nothing from it.
 
-The arithmetic lives in ``gdn_oracle.c`` (plain sequential loops in double
-precision); this module only builds it with gcc and marshals numpy arrays.
+The recurrence's arithmetic lives in ``gdn_oracle.c`` (plain sequential
+loops in double precision); this module builds it with gcc and marshals numpy
+arrays.  The front end (normalisation and gate activations) is elementwise
+and written here in numpy float64.
 
 Sources: "Tail-Replay: Escaping the Curse of Linear Attention in Prefix Caching
 for Hybrid LLMs", section 2 Eq. (1) and section 3 Eq. (2); "LinearKV: One
@@ -13,7 +15,7 @@ Cached State Suffices for Position-Independent Caching in Hybrid LLMs", the
 affine chunk operator and its back-to-back composition in context order.
 
 Parity pins (tests/test_oracle_pins.py) tie every function here to facts the
-pages and the mathematics fix; none of the three functions is "parity unpinned".
+pages and the mathematics fix; none of the four functions is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -149,6 +151,23 @@ def compose(T_C, S_local, S_in=None, n_threads=0):
     if rc != 0:
         raise ValueError("oracle compose rejected its arguments")
     return out
+
+
+def front_end(q_raw, k_raw, g, b):
+    """The inputs of the recurrence from raw projections, in float64.
+
+    Tail-Replay, section 3 (the replayed hidden states produce the keys,
+    transitions and write strengths) and section 2 Eq. (1) (alpha in (0, 1]):
+    q and k divided by their Euclidean norm over the last axis (a zero row
+    stays zero), alpha = exp(g) from the log-gate, beta = the logistic
+    sigmoid of its logit.  q_raw may be None.  Returns (q, k, alpha, beta).
+    """
+    def unit(x):
+        x = _f64(x)
+        n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+    q = None if q_raw is None else unit(q_raw)
+    return q, unit(k_raw), np.exp(_f64(g)), 1.0 / (1.0 + np.exp(-_f64(b)))
 
 
 def rel_fro(x, ref) -> float:

@@ -289,7 +289,45 @@ def pin_tail_error_identity(orc):
     assert np.max(np.abs(rhs)) > 1e-6
 
 
+def pin_front_end_values(orc):
+    # Tail-Replay, section 3 (the replayed hidden states produce k, the
+    # transitions and beta) with section 2 Eq. (1): worked by hand.
+    # (3, 4) has norm 5; a zero row stays zero; exp(log 1/2) = 1/2;
+    # sigmoid(log 3) = 3/4 and sigmoid(-log 3) = 1/4.
+    k = np.array([[[3.0, 4.0, 0.0, 0.0]], [[0.0, 0.0, 0.0, 0.0]], [[-1.0, 1.0, -1.0, 1.0]]])
+    q = np.array([[[0.0, 0.0, 0.0, 2.0]], [[1e-3, 0.0, 0.0, 0.0]], [[1.0, 2.0, 2.0, 0.0]]])
+    g = np.array([[0.0], [np.log(0.5)], [-np.inf]])
+    b = np.array([[0.0], [np.log(3.0)], [-np.log(3.0)]])
+    qo, ko, a, be = orc.front_end(q, k, g, b)
+    assert np.array_equal(ko, [[[0.6, 0.8, 0.0, 0.0]], [[0.0, 0.0, 0.0, 0.0]], [[-0.5, 0.5, -0.5, 0.5]]])
+    assert np.allclose(qo, [[[0, 0, 0, 1.0]], [[1.0, 0, 0, 0]], [[1 / 3, 2 / 3, 2 / 3, 0]]], rtol=0, atol=1e-15)
+    assert np.allclose(a, [[1.0], [0.5], [0.0]], rtol=0, atol=1e-15)
+    assert np.allclose(be, [[0.5], [0.75], [0.25]], rtol=0, atol=1e-15)
+    assert orc.front_end(None, k, g, b)[0] is None
+
+
+def pin_front_end_invariants(orc):
+    # unit rows, invariance under positive scaling, oddness, alpha in (0, 1]
+    # for g <= 0, beta(b) + beta(-b) = 1
+    rng = _rng(31)
+    x = rng.standard_normal((50, 3, 128)) * rng.uniform(0.01, 100, (50, 3, 1))
+    g = -np.abs(rng.standard_normal((50, 3))) * 5
+    b = rng.standard_normal((50, 3)) * 4
+    q, k, a, be = orc.front_end(x, x, g, b)
+    assert np.max(np.abs(np.linalg.norm(k, axis=-1) - 1)) < 1e-14
+    assert np.array_equal(q, k)
+    _, k2, _, _ = orc.front_end(None, 7.5 * x, g, b)
+    assert np.max(np.abs(k2 - k)) < 1e-15
+    _, k3, _, _ = orc.front_end(None, -x, g, b)
+    assert np.array_equal(k3, -k)
+    assert np.max(np.abs(k * np.linalg.norm(x, axis=-1, keepdims=True) - x)) < 1e-12 * np.max(np.abs(x))
+    assert np.all((a > 0) & (a <= 1))
+    assert np.max(np.abs(be + orc.front_end(None, x, g, -b)[3] - 1)) < 1e-15
+
+
 ALL_PINS = [
+    pin_front_end_values,
+    pin_front_end_invariants,
     pin_literal_matrix_form,
     pin_exact_rational,
     pin_identity_gate,

@@ -151,6 +151,53 @@ def generate(lengths, H: int, dk: int, dv: int, dtype: str = "bf16",
     return Inputs(dtype=dtype, H=H, dk=dk, dv=dv, cu_seqlens=cu, **store)
 
 
+@dataclass
+class RawInputs:
+    """Projections before the front end: ``q_raw``, ``k_raw`` [T, H, dk] and
+    ``v`` [T, H, dv] ~ N(0, 1) with a per-(token, head) scale U[0.25, 4] on q
+    and k; the log-gate ``g`` = -c * softplus(x_alpha) and the beta logit
+    ``b`` = x_beta [T, H] (the recipe's steps 1-3 and 5, without step 4's
+    normalisation and activations).  Storage as in Inputs."""
+    dtype: str
+    H: int
+    dk: int
+    dv: int
+    cu_seqlens: np.ndarray
+    q_raw: np.ndarray
+    k_raw: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    b: np.ndarray
+
+    def f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        return bf16_to_f64(a) if self.dtype == "bf16" else a.astype(np.float64)
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+
+def generate_raw(lengths, H: int, dk: int, dv: int, dtype: str = "bf16", seed: int = 0,
+                 gate_scale: float = 0.1) -> RawInputs:
+    """Draw one packed batch of raw projections (see RawInputs)."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError("dtype must be 'f32' or 'bf16'")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = np.asarray(lengths, np.int64)
+    cu = np.zeros(lengths.shape[0] + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+    q = rng.standard_normal((T, H, dk)) * rng.uniform(0.25, 4.0, (T, H, 1))
+    k = rng.standard_normal((T, H, dk)) * rng.uniform(0.25, 4.0, (T, H, 1))
+    v = rng.standard_normal((T, H, dv))
+    xb = rng.standard_normal((T, H))
+    xa = rng.standard_normal((T, H))
+    arrs = dict(q_raw=q, k_raw=k, v=v, g=-gate_scale * _softplus(xa), b=xb)
+    rnd = bf16_bits if dtype == "bf16" else f32_round
+    return RawInputs(dtype=dtype, H=H, dk=dk, dv=dv, cu_seqlens=cu, **{n: rnd(a) for n, a in arrs.items()})
+
+
 # ---------------------------------------------------------------------------
 # The five workloads.  Shapes follow the pages: a 32768-token prefix with a
 # 10% tail (ceil(0.1 * 32768) = 3277), tails of 5-10% of 8K-32K prefixes
