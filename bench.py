@@ -12,7 +12,9 @@ tokens with outputs; 3 = a 32768-token prefill with outputs; 4 = 64
 chunk operators of 512 tokens and their composition; 0 = one fp32 head.
 
 ``--decode N`` instead times single-token decode of N requests from given
-states (the serving step after a replay).  ``--tail-curve`` instead
+states (the serving step after a replay).  ``--front-end`` instead times
+the front end (normalised q and k, activated gates) on the tail-replay
+shape (with ``--with-replay`` also before a state-only replay).  ``--tail-curve`` instead
 reports the tail-replay state error against the
 replayed fraction (the latest k tokens of a 32768-token prefix replayed
 from zero, against the full replay) next to the stored fp64 oracle curve.
@@ -294,6 +296,66 @@ def decode_report(args, gdn, torch, np):
     print(json.dumps(line), flush=True)
 
 
+FRONT_NAME = "front-end-T3277-H32-d128-bf16"
+
+
+def front_end_report(args, gdn, torch, np):
+    """One JSON line: gdn_front_end on the tail-replay shape (3277 tokens,
+    32 heads, dk = 128, bf16, queries and keys); HBM-bound (every raw input
+    read once and every prepared output written once).  Also the front end
+    without queries followed by the state-only replay, against the replay of
+    prepared inputs (``--with-replay``)."""
+    import workloads
+    T, H, d = workloads.tail_length(32768, "0.1"), 32, 128
+    raw = workloads.generate_raw([T], H=H, dk=d, dv=d, dtype="bf16", seed=7)
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    qr, kr, g, b, v = t(raw.q_raw), t(raw.k_raw), t(raw.g), t(raw.b), t(raw.v)
+    cu = torch.from_numpy(raw.cu_seqlens).cuda()
+    out = (torch.empty_like(qr), torch.empty_like(kr), torch.empty_like(g), torch.empty_like(b))
+    out_k = (None,) + out[1:]
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for a, e in ev:
+            a.record(stream)
+            fn()
+            e.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / args.steps
+        ms = [a.elapsed_time(e) for a, e in ev]
+        return sum(ms) / len(ms), min(ms), wall
+
+    avg, mn, wall = timed(lambda: gdn.front_end(qr, kr, g, b, out=out))
+    extra = {}
+    if args.with_replay:
+        both, _, _ = timed(lambda: gdn.replay(None, gdn.front_end(None, kr, g, b, out=out_k)[1], v, out[2], out[3],
+                                              cu, want_o=False))
+        alone, _, _ = timed(lambda: gdn.replay(None, out[1], v, out[2], out[3], cu, want_o=False))
+        extra = dict(state_only_replay=dict(prepared_inputs_ms=round(alone, 5), with_front_end_ms=round(both, 5)))
+    # q_raw, k_raw read and q, k written (bf16); g, b read and alpha, beta written (bf16)
+    byt = T * H * (4 * d * 2 + 4 * 2)
+    achieved = byt / (avg / 1e3) / 1e9
+    line = dict(metric="GDN front end tokens·heads/s (normalised q, k and activated gates)",
+                value=round(T * H / (wall / 1e3), 1), unit="tokens·heads/s", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=round(wall, 5), higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="bf16", data="synthetic",
+                config=dict(workload=FRONT_NAME, n_tokens=T, heads=H, dk=d, outputs="q,k,alpha,beta"),
+                roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(FRONT_NAME),
+                              kernel="front_kernel", algorithmic_bytes=byt, kernel_ms_avg=round(avg, 5),
+                              kernel_ms_min=round(mn, 5)), **extra)
+    line["gpu_ms_per_step"] = round(avg, 5)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,10 +373,14 @@ def main():
                     help="only report the tail-replay state error against the replayed fraction")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="only time single-token decode of N requests (H=32, d=128) from given states")
+    ap.add_argument("--front-end", action="store_true",
+                    help="only time the front end (normalised q, k and gates) on the tail-replay shape")
+    ap.add_argument("--with-replay", action="store_true",
+                    help="with --front-end: also time a state-only replay with and without the front end")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(args.workload, *args.summarize_counters, command=args.command,
-                           name=("decode-%dx1-H32-d128-bf16" % args.decode) if args.decode else None)
+        name = ("decode-%dx1-H32-d128-bf16" % args.decode) if args.decode else FRONT_NAME if args.front_end else None
+        summarize_counters(args.workload, *args.summarize_counters, command=args.command, name=name)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the replay path is a single-GPU kernel library "
@@ -344,6 +410,9 @@ def main():
         return
     if args.decode:
         decode_report(args, gdn, torch, np)
+        return
+    if args.front_end:
+        front_end_report(args, gdn, torch, np)
         return
 
     wid = args.workload

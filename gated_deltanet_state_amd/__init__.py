@@ -18,7 +18,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["replay", "decode", "chunk_operator", "compose", "GdnError", "library", "LIB_PATH"]
+__all__ = ["front_end", "replay", "decode", "chunk_operator", "compose", "GdnError", "library", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
@@ -54,7 +54,8 @@ def library():
     lib.gdn_compose.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]
     lib.gdn_compose_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.gdn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, cint, vp, cint, vp, vp]
-    for f in (lib.gdn_replay, lib.gdn_chunk_operator, lib.gdn_compose, lib.gdn_decode):
+    lib.gdn_front_end.argtypes = [vp, vp, vp, vp, i64, i32, i32, cint, vp, vp, vp, vp, vp]
+    for f in (lib.gdn_replay, lib.gdn_chunk_operator, lib.gdn_compose, lib.gdn_decode, lib.gdn_front_end):
         f.restype = cint
     for f in (lib.gdn_replay_workspace_bytes, lib.gdn_chunk_operator_workspace_bytes,
               lib.gdn_compose_workspace_bytes):
@@ -162,6 +163,38 @@ def replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=None,
                           _ptr(S0), _ptr(cu_seqlens), N, T, H, dk, dv, in_code, _ptr(o),
                           o_code, _ptr(S), _ptr(ws), ws_bytes, _stream_ptr(stream)))
     return o, S
+
+
+def front_end(q_raw, k_raw, g, b, out=None, stream=None):
+    """Normalised q and k and activated gates, the inputs of the recurrence.
+
+    q_raw, k_raw [T, H, dk]; g (log-gate), b (beta logit) [T, H]; all
+    float32 or all bfloat16; q_raw may be None.  Returns (q or None, k,
+    alpha, beta) in the input dtype: q / |q|, k / |k|, exp(g), sigmoid(b).
+    ``out`` = (q, k, alpha, beta) tensors to write into (they may be the
+    inputs themselves; q None when q_raw is None).
+    """
+    lib = library()
+    for name, t in (("k_raw", k_raw), ("g", g), ("b", b)):
+        _dev(t, name)
+    if q_raw is not None:
+        _dev(q_raw, "q_raw")
+    T, H, dk = k_raw.shape
+    code = _dtype_code(k_raw.dtype)
+    for name, t in (("q_raw", q_raw), ("g", g), ("b", b)):
+        if t is not None and t.dtype != k_raw.dtype:
+            raise TypeError("%s must have the dtype of k_raw" % name)
+    if out is None:
+        out = (None if q_raw is None else q_raw.new_empty(q_raw.shape), k_raw.new_empty(k_raw.shape),
+               g.new_empty(g.shape), b.new_empty(b.shape))
+    q, k, alpha, beta = out
+    for name, t in (("k", k), ("alpha", alpha), ("beta", beta)) + ((("q", q),) if q is not None else ()):
+        _dev(t, name)
+    if T == 0:    # empty tensors may have no storage; nothing to compute
+        return q, k, alpha, beta
+    _check(lib.gdn_front_end(_ptr(q_raw), _ptr(k_raw), _ptr(g), _ptr(b), T, H, dk, code, _ptr(q), _ptr(k),
+                             _ptr(alpha), _ptr(beta), _stream_ptr(stream)))
+    return q, k, alpha, beta
 
 
 def decode(q, k, v, alpha, beta, S_in=None, want_o=True, o_dtype=None, out=None, S_out=None,

@@ -429,6 +429,40 @@ gdn_status gdn_decode(const void *q, const void *k, const void *v, const void *a
   return launched(gdn::launch_decode(p, reinterpret_cast<hipStream_t>(stream)), "gdn_decode launch");
 }
 
+gdn_status gdn_front_end(const void *q_raw, const void *k_raw, const void *g, const void *b, int64_t n_tokens,
+                         int32_t n_heads, int32_t dk, gdn_dtype dtype, void *q, void *k, void *alpha, void *beta,
+                         gdn_stream_t stream) {
+  if (!k_raw || !g || !b || !k || !alpha || !beta)
+    return fail(GDN_ERR_NULL_POINTER, "gdn_front_end: k_raw, g, b, k, alpha and beta are required");
+  if (!q_raw != !q) return fail(GDN_ERR_NULL_POINTER, "gdn_front_end: q_raw and q must both be given or both NULL");
+  if (n_tokens < 0 || n_heads < 1)
+    return fail(GDN_ERR_BAD_SHAPE, "gdn_front_end: need n_tokens >= 0 and n_heads >= 1 (got %lld, %d)",
+                (long long)n_tokens, n_heads);
+  if (!supported_dim(dk)) return fail(GDN_ERR_UNSUPPORTED, "gdn_front_end: dk must be 64 or 128 (got %d)", dk);
+  if (!valid_dtype(dtype)) return fail(GDN_ERR_UNSUPPORTED, "gdn_front_end: dtype must be GDN_F32 or GDN_BF16");
+  if (n_heads > kMaxHeads || n_tokens > (int64_t)1 << 40)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_front_end: problem too large for one call");
+  gdn_status s;
+  if ((s = check_align("q_raw", q_raw)) || (s = check_align("k_raw", k_raw)) || (s = check_align("g", g)) ||
+      (s = check_align("b", b)) || (s = check_align("q", q)) || (s = check_align("k", k)) ||
+      (s = check_align("alpha", alpha)) || (s = check_align("beta", beta)))
+    return s;
+  gdn::FrontLaunch p{};
+  p.q_in = q_raw;
+  p.k_in = k_raw;
+  p.g = g;
+  p.b = b;
+  p.q_out = q;
+  p.k_out = k;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.n_tokens = n_tokens;
+  p.H = n_heads;
+  p.dk = dk;
+  p.in_bf16 = dtype == GDN_BF16;
+  return launched(gdn::launch_front(p, reinterpret_cast<hipStream_t>(stream)), "gdn_front_end launch");
+}
+
 const char *gdn_status_string(gdn_status status) {
   switch (status) {
     case GDN_OK: return "GDN_OK";

@@ -134,7 +134,17 @@ struct DecodeLaunch {
   int in_bf16, o_bf16;
 };
 
+// Normalised queries and keys and activated gates (gdn_front_end).
+struct FrontLaunch {
+  const void *q_in, *k_in, *g, *b;   // q_in, k_in [n_tokens, H, dk] (q_in may be null); g, b [n_tokens, H]
+  void *q_out, *k_out, *alpha, *beta; // same shapes (may alias the inputs)
+  int64_t n_tokens;
+  int32_t H, dk;
+  int in_bf16;
+};
+
 hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream);
+hipError_t launch_front(const FrontLaunch &p, hipStream_t stream);
 hipError_t launch_prep(const PrepLaunch &p, hipStream_t stream);        // dispatches bf16 inputs to launch_prep_bf16
 hipError_t launch_prep_bf16(const PrepLaunch &p, hipStream_t stream);
 hipError_t launch_chain(const ChainLaunch &p, hipStream_t stream);        // fp32 inputs

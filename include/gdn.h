@@ -168,6 +168,32 @@ gdn_status gdn_decode(const void *q, const void *k, const void *v,
                       gdn_dtype in_dtype, void *o, gdn_dtype o_dtype,
                       float *S_out, gdn_stream_t stream);
 
+/*
+ * gdn_front_end -- the step before the recurrence: queries and keys
+ * L2-normalised per (token, head), the decay from its log-gate and the write
+ * strength from its logit.
+ * Page: Tail-Replay, section 3 (the replayed hidden states produce the keys,
+ * values, transitions and write strengths) and section 2 Eq. (1) (alpha in
+ * (0, 1]).  Per (token, head), in fp32, each result rounded once to dtype:
+ *     q = q_raw / |q_raw|,  k = k_raw / |k_raw|   (a zero row gives zeros)
+ *     alpha = exp(g),       beta = 1 / (1 + exp(-b))
+ * The outputs are the q, k, alpha and beta that gdn_replay, gdn_chunk_operator
+ * and gdn_decode take (values v pass through unchanged and are not touched).
+ *
+ *   q_raw, k_raw  [n_tokens, H, dk]  dtype   (q_raw may be NULL, then q is too)
+ *   g, b          [n_tokens, H]      dtype   log-gate (g <= 0 keeps alpha in
+ *                                            (0, 1]; larger g is not rejected)
+ *                                            and beta logit
+ *   q, k          [n_tokens, H, dk]  dtype   outputs (may alias q_raw, k_raw)
+ *   alpha, beta   [n_tokens, H]      dtype   outputs (may alias g, b)
+ * Supported: dk in {64, 128}; dtypes F32 or BF16; 1 <= n_heads <= 65536;
+ * n_tokens <= 2^40.  No workspace; stream-ordered, no synchronisation.
+ */
+gdn_status gdn_front_end(const void *q_raw, const void *k_raw, const void *g,
+                         const void *b, int64_t n_tokens, int32_t n_heads,
+                         int32_t dk, gdn_dtype dtype, void *q, void *k,
+                         void *alpha, void *beta, gdn_stream_t stream);
+
 /* GDN_ABI_VERSION of the loaded library. */
 int gdn_abi_version(void);
 

@@ -111,6 +111,24 @@ def test_decode_argument_checks(lib):
     assert dc(N=0) == OK                          # nothing to do, nothing launched
 
 
+def test_front_end_argument_checks(lib):
+    def fe(qr=P, kr=P, g=P, b=P, T=8, H=2, dk=128, dt=BF16, q=P, k=P, a=P, be=P):
+        return lib.gdn_front_end(qr, kr, g, b, T, H, dk, dt, q, k, a, be, None)
+    assert fe(kr=None) == NULLP
+    assert fe(be=None) == NULLP
+    assert fe(q=None) == NULLP                    # q_raw without q
+    assert fe(qr=None) == NULLP                   # q without q_raw
+    assert fe(T=-1) == SHAPE
+    assert fe(H=0) == SHAPE
+    assert fe(dk=96) == UNSUP
+    assert fe(dt=7) == UNSUP
+    assert fe(H=65537) == UNSUP
+    assert fe(T=(1 << 40) + 1) == UNSUP
+    assert fe(g=P + 4) == ALIGN
+    assert fe(T=0) == OK                          # nothing to do, nothing launched
+    assert fe(qr=None, q=None, T=0) == OK
+
+
 def test_workspace_queries(lib, monkeypatch):
     # one 13 KiB record of per-chunk factors ((I + A)^{-1} diag(beta) fragments and the gates) per chunk
     # slot and head; slots = n_tokens / 64 + n_seqs + 1 (sequence n's chunk j sits
