@@ -14,7 +14,10 @@ chunk operators of 512 tokens and their composition; 0 = one fp32 head.
 ``--decode N`` instead times single-token decode of N requests from given
 states (the serving step after a replay).  ``--front-end`` instead times
 the front end (normalised q and k, activated gates) on the tail-replay
-shape (with ``--with-replay`` also before a state-only replay).  ``--tail-curve`` instead
+shape (with ``--with-replay`` also before a state-only replay).
+``--overlap MIB`` instead times a pinned-host -> device copy of MIB MiB on
+a copy stream beside ``--layers`` tail replays: alone, serialised and
+overlapped.  ``--tail-curve`` instead
 reports the tail-replay state error against the
 replayed fraction (the latest k tokens of a 32768-token prefix replayed
 from zero, against the full replay) next to the stored fp64 oracle curve.
@@ -299,6 +302,88 @@ def decode_report(args, gdn, torch, np):
 FRONT_NAME = "front-end-T3277-H32-d128-bf16"
 
 
+def overlap_report(args, gdn, torch, np):
+    """One JSON line: a pinned-host -> device copy of a synthetic attention
+    KV buffer on a copy stream, concurrent with tail replays on the compute
+    stream (the Tail-Replay page, section 3: the replay does not need the
+    attention layers' cached keys and values, so their transfer can run
+    beside it and is waited for only before the query's forward).  The
+    replays are the tail-replay workload (3277 tokens, 32 heads, d = 128,
+    state only), one per linear-attention layer of the group."""
+    import workloads
+    mib, layers = args.overlap, args.layers
+    inp = workloads.make_workload(1)
+    d = to_dev(inp, torch, np)
+    host = torch.empty(mib << 20, dtype=torch.uint8, pin_memory=True)
+    host.copy_(torch.from_numpy(np.random.Generator(np.random.PCG64(8)).integers(0, 256, mib << 20, dtype=np.uint8)))
+    dst = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    comp = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()    # default priority
+
+    def replays():
+        for _ in range(layers):
+            gdn.replay(None, d["k"], d["v"], d["alpha"], d["beta"], d["cu"], want_o=False, stream=comp)
+
+    def run(mode):
+        """Enqueue one step of the mode: the copy alone, the replays alone,
+        the copy then the replays on one stream (serialised), or the copy on
+        the copy stream beside the replays, joined at the end (overlapped)."""
+        if mode == "overlap":
+            ev0 = torch.cuda.Event()
+            ev0.record(comp)
+            copy.wait_event(ev0)
+            with torch.cuda.stream(copy):
+                dst.copy_(host, non_blocking=True)
+            evc = torch.cuda.Event()
+            evc.record(copy)
+            replays()
+            comp.wait_event(evc)
+            return
+        if mode != "replay":
+            dst.copy_(host, non_blocking=True)
+        if mode != "copy":
+            replays()
+
+    modes = ("copy", "replay", "serial", "overlap")
+    for mode in modes:
+        for _ in range(args.warmup):
+            run(mode)
+    torch.cuda.synchronize()
+    # the modes take turns, each step timed alone from an idle device (wall
+    # clock around synchronisations, as a time to first token would see it,
+    # and HIP events on the compute stream)
+    wall = {m: [] for m in modes}
+    gpu = {m: [] for m in modes}
+    for _ in range(args.steps):
+        for mode in modes:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            a.record(comp)
+            run(mode)
+            b.record(comp)
+            torch.cuda.synchronize()
+            wall[mode].append((time.perf_counter() - t0) * 1e3)
+            gpu[mode].append(a.elapsed_time(b))
+    res = {m: float(np.median(gpu[m])) for m in modes}
+    res_wall = {m: float(np.median(wall[m])) for m in modes}
+    assert torch.equal(dst[:4096].cpu(), host[:4096])
+    hidden = (res["serial"] - res["overlap"]) / min(res["copy"], res["replay"])
+    tok = layers * inp.n_tokens * inp.H
+    line = dict(metric="GDN replay tokens·heads/s beside a host-to-device KV copy (overlapped)",
+                value=round(tok / (res["overlap"] / 1e3), 1), unit="tokens·heads/s", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=round(res["overlap"], 5), higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="bf16", data="synthetic",
+                config=dict(workload="overlap-%dMiB-%dx-tail-replay-T3277-H32-d128-bf16" % (mib, layers),
+                            copy_mib=mib, replays=layers, n_tokens=inp.n_tokens, heads=inp.H),
+                ms=dict((k, round(v, 5)) for k, v in res.items()),
+                wall_ms=dict((k, round(v, 5)) for k, v in res_wall.items()),
+                copy_gbs=round((mib << 20) / (res["copy"] / 1e3) / 1e9, 2),
+                reduction_vs_serial=round(1 - res["overlap"] / res["serial"], 4),
+                hidden_fraction_of_shorter=round(hidden, 4))
+    print(json.dumps(line), flush=True)
+
+
 def front_end_report(args, gdn, torch, np):
     """One JSON line: gdn_front_end on the tail-replay shape (3277 tokens,
     32 heads, dk = 128, bf16, queries and keys); HBM-bound (every raw input
@@ -375,6 +460,10 @@ def main():
                     help="only time single-token decode of N requests (H=32, d=128) from given states")
     ap.add_argument("--front-end", action="store_true",
                     help="only time the front end (normalised q, k and gates) on the tail-replay shape")
+    ap.add_argument("--overlap", type=int, default=0, metavar="MIB",
+                    help="only time a MIB pinned-host -> device copy beside tail replays (serial and overlapped)")
+    ap.add_argument("--layers", type=int, default=3,
+                    help="with --overlap: tail replays per copy (linear-attention layers of one group)")
     ap.add_argument("--with-replay", action="store_true",
                     help="with --front-end: also time a state-only replay with and without the front end")
     args = ap.parse_args()
@@ -413,6 +502,9 @@ def main():
         return
     if args.front_end:
         front_end_report(args, gdn, torch, np)
+        return
+    if args.overlap:
+        overlap_report(args, gdn, torch, np)
         return
 
     wid = args.workload
