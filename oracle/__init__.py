@@ -6,8 +6,8 @@ code with the HIP library and imports nothing from it.
 
 The recurrence's arithmetic lives in ``gdn_oracle.c`` (plain sequential
 loops in double precision); this module builds it with gcc and marshals numpy
-arrays.  The front end (normalisation and gate activations) is elementwise
-and written here in numpy float64.
+arrays.  The front end (normalisation and gate activations) and the scalar-decay
+operator and composition are written here in numpy float64.
 
 Sources: "Tail-Replay: Escaping the Curse of Linear Attention in Prefix Caching
 for Hybrid LLMs", section 2 Eq. (1) and section 3 Eq. (2); "LinearKV: One
@@ -15,7 +15,7 @@ Cached State Suffices for Position-Independent Caching in Hybrid LLMs", the
 affine chunk operator and its back-to-back composition in context order.
 
 Parity pins (tests/test_oracle_pins.py) tie every function here to facts the
-pages and the mathematics fix; none of the four functions is "parity unpinned".
+pages and the mathematics fix; none of the six functions is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -168,6 +168,39 @@ def front_end(q_raw, k_raw, g, b):
         return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
     q = None if q_raw is None else unit(q_raw)
     return q, unit(k_raw), np.exp(_f64(g)), 1.0 / (1.0 + np.exp(-_f64(b)))
+
+
+def scalar_chunk_operator(k, alpha, beta, cu_chunks, v=None):
+    """Chunk operators of the scalar-decay recurrence, in float64.
+
+    LinearKV, the affine-operator paragraph (with a scalar per-token
+    transition the chunk's transition is a single scalar decay) and the
+    write term of Tail-Replay section 2 Eq. (1): per head,
+    S_t = alpha_t S_{t-1} + beta_t v_t k_t^T, run token by token from zero
+    over each chunk.  Returns (gamma [C, H], S_local [C, H, dv, dk] or None).
+    """
+    k, a, b = _f64(k), _f64(alpha), _f64(beta)
+    v = _f64(v)
+    cu = np.asarray(cu_chunks, np.int64)
+    C, H, dk = cu.shape[0] - 1, k.shape[1], k.shape[2]
+    gamma = np.ones((C, H))
+    SL = None if v is None else np.zeros((C, H, v.shape[2], dk))
+    for c in range(C):
+        for t in range(cu[c], cu[c + 1]):
+            gamma[c] *= a[t]
+            if SL is not None:
+                SL[c] = a[t][:, None, None] * SL[c] + b[t][:, None, None] * v[t][:, :, None] * k[t][:, None, :]
+    return gamma, SL
+
+
+def scalar_compose(gamma, S_local, S_in=None):
+    """Scalar-decay operators back to back in context order (LinearKV, the
+    composition paragraph): S <- gamma[c] S + S_local[c], from S_in or zero."""
+    g, SL = _f64(gamma), _f64(S_local)
+    S = np.zeros(SL.shape[1:]) if S_in is None else _f64(S_in).copy()
+    for c in range(SL.shape[0]):
+        S = g[c][:, None, None] * S + SL[c]
+    return S
 
 
 def rel_fro(x, ref) -> float:

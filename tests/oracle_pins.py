@@ -325,7 +325,63 @@ def pin_front_end_invariants(orc):
     assert np.max(np.abs(be + orc.front_end(None, x, g, -b)[3] - 1)) < 1e-15
 
 
+def pin_scalar_by_hand(orc):
+    # one head, dk = dv = 1, alpha = (1/2, 1/2, 1/4), beta = 1, v = (1, 2, 4),
+    # k = (1, 1, 1/2): S = 1; then 1/2 + 2 = 5/2; then 5/8 + 2 = 21/8;
+    # gamma = 1/16.  A second chunk that is empty gives gamma 1 and S 0.
+    k = np.array([[[1.0]], [[1.0]], [[0.5]]])
+    v = np.array([[[1.0]], [[2.0]], [[4.0]]])
+    a = np.array([[0.5], [0.5], [0.25]])
+    b = np.ones((3, 1))
+    g, SL = orc.scalar_chunk_operator(k, a, b, [0, 3, 3], v=v)
+    assert np.array_equal(g, [[1 / 16], [1.0]])
+    assert np.array_equal(SL[:, 0, 0, 0], [21 / 8, 0.0])
+    assert orc.scalar_chunk_operator(k, a, b, [0, 3])[1] is None
+    # composed from S_in = 8: 8/16 + 21/8 = 25/8, then the empty chunk
+    assert np.array_equal(orc.scalar_compose(g, SL, S_in=np.array([[[8.0]]])), [[[25 / 8]]])
+
+
+def pin_scalar_closed_forms(orc):
+    # alpha = 1: S_local = V^T diag(beta) K.  General alpha: the sum of
+    # beta_t (prod_{s>t} alpha_s) v_t k_t^T with the products formed one by one.
+    rng = _rng(41)
+    T, H, dk, dv = 37, 2, 5, 3
+    k = rng.standard_normal((T, H, dk))
+    v = rng.standard_normal((T, H, dv))
+    a = rng.uniform(0.5, 1.0, (T, H))
+    b = rng.uniform(0.0, 1.0, (T, H))
+    _, SL1 = orc.scalar_chunk_operator(k, np.ones((T, H)), b, [0, T], v=v)
+    for h in range(H):
+        ref = v[:, h].T @ np.diag(b[:, h]) @ k[:, h]
+        assert np.max(np.abs(SL1[0, h] - ref)) < 1e-12
+    g, SL = orc.scalar_chunk_operator(k, a, b, [0, T], v=v)
+    for h in range(H):
+        ref = sum(b[t, h] * np.prod(a[t + 1:, h]) * np.outer(v[t, h], k[t, h]) for t in range(T))
+        assert np.max(np.abs(SL[0, h] - ref)) < 1e-12
+        assert abs(g[0, h] - np.prod(a[:, h])) < 1e-15
+
+
+def pin_scalar_compose_is_concatenation(orc):
+    # composing the operators of consecutive chunks gives the operator of the
+    # whole span: gamma multiplies, S_local = gamma_2 S_1 + S_2
+    rng = _rng(42)
+    T, H, dk, dv = 90, 3, 4, 6
+    k = rng.standard_normal((T, H, dk))
+    v = rng.standard_normal((T, H, dv))
+    a = rng.uniform(0.8, 1.0, (T, H))
+    b = rng.uniform(0.0, 1.0, (T, H))
+    g, SL = orc.scalar_chunk_operator(k, a, b, [0, 20, 20, 61, 90], v=v)
+    g1, SL1 = orc.scalar_chunk_operator(k, a, b, [0, 90], v=v)
+    assert np.max(np.abs(orc.scalar_compose(g, SL) - SL1[0])) < 1e-12
+    assert np.max(np.abs(np.prod(g, axis=0) - g1[0])) < 1e-14
+    S0 = rng.standard_normal((H, dv, dk))
+    assert np.max(np.abs(orc.scalar_compose(g, SL, S_in=S0) - (g1[0][:, None, None] * S0 + SL1[0]))) < 1e-12
+
+
 ALL_PINS = [
+    pin_scalar_by_hand,
+    pin_scalar_closed_forms,
+    pin_scalar_compose_is_concatenation,
     pin_front_end_values,
     pin_front_end_invariants,
     pin_literal_matrix_form,
