@@ -17,7 +17,8 @@ the front end (normalised q and k, activated gates) on the tail-replay
 shape (with ``--with-replay`` also before a state-only replay).
 ``--overlap MIB`` instead times a pinned-host -> device copy of MIB MiB on
 a copy stream beside ``--layers`` tail replays: alone, serialised and
-overlapped.  ``--tail-curve`` instead
+overlapped.  ``--scalar-ops`` instead times the scalar-decay (Mamba-2
+family) chunk operators and their composition on the chunk-operator shape.  ``--tail-curve`` instead
 reports the tail-replay state error against the
 replayed fraction (the latest k tokens of a 32768-token prefix replayed
 from zero, against the full replay) next to the stored fp64 oracle curve.
@@ -300,6 +301,63 @@ def decode_report(args, gdn, torch, np):
 
 
 FRONT_NAME = "front-end-T3277-H32-d128-bf16"
+SCALAR_NAME = "scalar-ops-64x512-H32-d128-bf16"
+
+
+def scalar_ops_report(args, gdn, torch, np):
+    """One JSON line: scalar-decay chunk operators (the Mamba-2 family) on
+    the chunk-operator workload's shape (64 chunks of 512 tokens, 32 heads,
+    d = 128, bf16) and their composition; the operator kernel is HBM-bound
+    (keys, values and gates read once, S_local written once)."""
+    import workloads
+    w = workloads.WORKLOADS[4]
+    inp = workloads.make_workload(4)
+    d = to_dev(inp, torch, np)
+    cu = torch.from_numpy(workloads.chunk_bounds(inp.n_tokens, w["chunk"])).cuda()
+    C, H, dk, dv, T = cu.shape[0] - 1, inp.H, inp.dk, inp.dv, inp.n_tokens
+    S = torch.empty((H, dv, dk), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ops = [None, None]
+
+    def op():
+        ops[:] = gdn.scalar_chunk_operator(d["k"], d["alpha"], d["beta"], cu, v=d["v"])
+
+    def comp():
+        gdn.scalar_compose(ops[0], ops[1], out=S)
+
+    def timed(fns):
+        for _ in range(args.warmup):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for e in ev:
+            e[0].record(stream)
+            for i, f in enumerate(fns):
+                f()
+                e[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / args.steps
+        per = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / len(ev) for i in range(len(fns))]
+        return per, wall
+
+    (t_op, t_comp), wall = timed([op, comp])
+    # keys and values (bf16), gates (bf16) read; S_local (fp32) and gamma written
+    byt = T * H * (dk + dv) * 2 + T * H * 2 * 2 + C * H * (dv * dk + 1) * 4
+    achieved = byt / (t_op / 1e3) / 1e9
+    line = dict(metric="GDN scalar-decay chunk operators + composition, tokens·heads/s",
+                value=round(T * H / (wall / 1e3), 1), unit="tokens·heads/s", n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=round(wall, 5), higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="bf16", data="synthetic",
+                config=dict(workload=SCALAR_NAME, n_chunks=C, chunk=w["chunk"], n_tokens=T, heads=H, dk=dk, dv=dv,
+                            outputs="gamma,S_local,S"),
+                roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(SCALAR_NAME),
+                              kernel="scalar_op_kernel", algorithmic_bytes=byt, kernel_ms_avg=round(t_op, 5)),
+                compose_ms=round(t_comp, 5))
+    line["gpu_ms_per_step"] = round(t_op + t_comp, 5)
+    print(json.dumps(line), flush=True)
 
 
 def overlap_report(args, gdn, torch, np):
@@ -464,11 +522,14 @@ def main():
                     help="only time a MIB pinned-host -> device copy beside tail replays (serial and overlapped)")
     ap.add_argument("--layers", type=int, default=3,
                     help="with --overlap: tail replays per copy (linear-attention layers of one group)")
+    ap.add_argument("--scalar-ops", action="store_true",
+                    help="only time scalar-decay chunk operators and their composition (64 x 512 tokens)")
     ap.add_argument("--with-replay", action="store_true",
                     help="with --front-end: also time a state-only replay with and without the front end")
     args = ap.parse_args()
     if args.summarize_counters:
-        name = ("decode-%dx1-H32-d128-bf16" % args.decode) if args.decode else FRONT_NAME if args.front_end else None
+        name = (("decode-%dx1-H32-d128-bf16" % args.decode) if args.decode else FRONT_NAME if args.front_end
+                else SCALAR_NAME if args.scalar_ops else None)
         summarize_counters(args.workload, *args.summarize_counters, command=args.command, name=name)
         return
     if args.gpus != 1:
@@ -505,6 +566,9 @@ def main():
         return
     if args.overlap:
         overlap_report(args, gdn, torch, np)
+        return
+    if args.scalar_ops:
+        scalar_ops_report(args, gdn, torch, np)
         return
 
     wid = args.workload

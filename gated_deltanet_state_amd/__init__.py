@@ -18,7 +18,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["front_end", "replay", "decode", "chunk_operator", "compose", "GdnError", "library", "LIB_PATH"]
+__all__ = ["front_end", "replay", "decode", "chunk_operator", "compose", "scalar_chunk_operator", "scalar_compose", "GdnError", "library", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
@@ -55,7 +55,10 @@ def library():
     lib.gdn_compose_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.gdn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, cint, vp, cint, vp, vp]
     lib.gdn_front_end.argtypes = [vp, vp, vp, vp, i64, i32, i32, cint, vp, vp, vp, vp, vp]
-    for f in (lib.gdn_replay, lib.gdn_chunk_operator, lib.gdn_compose, lib.gdn_decode, lib.gdn_front_end):
+    lib.gdn_scalar_chunk_operator.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint, vp, vp, vp]
+    lib.gdn_scalar_compose.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
+    for f in (lib.gdn_replay, lib.gdn_chunk_operator, lib.gdn_compose, lib.gdn_decode, lib.gdn_front_end,
+              lib.gdn_scalar_chunk_operator, lib.gdn_scalar_compose):
         f.restype = cint
     for f in (lib.gdn_replay_workspace_bytes, lib.gdn_chunk_operator_workspace_bytes,
               lib.gdn_compose_workspace_bytes):
@@ -195,6 +198,39 @@ def front_end(q_raw, k_raw, g, b, out=None, stream=None):
     _check(lib.gdn_front_end(_ptr(q_raw), _ptr(k_raw), _ptr(g), _ptr(b), T, H, dk, code, _ptr(q), _ptr(k),
                              _ptr(alpha), _ptr(beta), _stream_ptr(stream)))
     return q, k, alpha, beta
+
+
+def scalar_chunk_operator(k, alpha, beta, cu_chunks, v=None, stream=None):
+    """Scalar-decay chunk operators: gamma [C, H] (the product of the
+    chunk's alphas) and S_local [C, H, dv, dk] (None when v is None), float32."""
+    torch = _torch()
+    lib = library()
+    for name, t in (("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("cu_chunks", cu_chunks)):
+        _dev(t, name)
+    T, H, dk = k.shape
+    dv = v.shape[2] if v is not None else dk
+    C = cu_chunks.shape[0] - 1
+    if cu_chunks.dtype != torch.int32:
+        raise TypeError("cu_chunks must be int32")
+    gamma = torch.empty((C, H), dtype=torch.float32, device=k.device)
+    SL = torch.empty((C, H, dv, dk), dtype=torch.float32, device=k.device) if v is not None else None
+    _check(lib.gdn_scalar_chunk_operator(_ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_chunks), C, T, H, dk,
+                                         dv, _dtype_code(k.dtype), _ptr(gamma), _ptr(SL), _stream_ptr(stream)))
+    return gamma, SL
+
+
+def scalar_compose(gamma, S_local, S_in=None, out=None, stream=None):
+    """S <- gamma[c] S + S_local[c] over the chunks in order, from S_in or zero."""
+    torch = _torch()
+    lib = library()
+    for name, t in (("gamma", gamma), ("S_local", S_local), ("S_in", S_in)):
+        _dev(t, name)
+    C, H, dv, dk = S_local.shape
+    S = out if out is not None else torch.empty((H, dv, dk), dtype=torch.float32, device=S_local.device)
+    _dev(S, "out")
+    _check(lib.gdn_scalar_compose(_ptr(S_in), _ptr(gamma), _ptr(S_local), C, H, dk, dv, _ptr(S),
+                                  _stream_ptr(stream)))
+    return S
 
 
 def decode(q, k, v, alpha, beta, S_in=None, want_o=True, o_dtype=None, out=None, S_out=None,

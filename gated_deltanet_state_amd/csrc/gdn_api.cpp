@@ -463,6 +463,65 @@ gdn_status gdn_front_end(const void *q_raw, const void *k_raw, const void *g, co
   return launched(gdn::launch_front(p, reinterpret_cast<hipStream_t>(stream)), "gdn_front_end launch");
 }
 
+gdn_status gdn_scalar_chunk_operator(const void *k, const void *v, const void *alpha, const void *beta,
+                                     const int32_t *cu_chunks, int32_t n_chunks, int64_t n_tokens, int32_t n_heads,
+                                     int32_t dk, int32_t dv, gdn_dtype in_dtype, float *gamma, float *S_local,
+                                     gdn_stream_t stream) {
+  if (!k || !alpha || !beta || !cu_chunks || !gamma)
+    return fail(GDN_ERR_NULL_POINTER, "gdn_scalar_chunk_operator: k, alpha, beta, cu_chunks and gamma are required");
+  if (S_local && !v) return fail(GDN_ERR_NULL_POINTER, "gdn_scalar_chunk_operator: S_local requested without v");
+  if (n_chunks < 0 || n_tokens < 0 || n_heads < 1)
+    return fail(GDN_ERR_BAD_SHAPE, "gdn_scalar_chunk_operator: need n_chunks >= 0, n_tokens >= 0, n_heads >= 1");
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_scalar_chunk_operator: dk and dv must be 64 or 128 (got %d, %d)", dk, dv);
+  if (!valid_dtype(in_dtype)) return fail(GDN_ERR_UNSUPPORTED, "gdn_scalar_chunk_operator: dtype must be F32 or BF16");
+  if (n_heads > kMaxHeads || (int64_t)n_chunks * n_heads > INT32_MAX || n_tokens > INT32_MAX)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_scalar_chunk_operator: problem too large for one call");
+  gdn_status s;
+  if ((s = check_align("k", k)) || (s = check_align("v", v)) || (s = check_align("alpha", alpha)) ||
+      (s = check_align("beta", beta)) || (s = check_align("cu_chunks", cu_chunks)) ||
+      (s = check_align("gamma", gamma)) || (s = check_align("S_local", S_local)))
+    return s;
+  gdn::ScalarOpLaunch p{};
+  p.k = k;
+  p.v = v;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.cu = cu_chunks;
+  p.gamma = gamma;
+  p.S_local = S_local;
+  p.n_chunks = n_chunks;
+  p.H = n_heads;
+  p.dk = dk;
+  p.dv = dv;
+  p.in_bf16 = in_dtype == GDN_BF16;
+  return launched(gdn::launch_scalar_op(p, reinterpret_cast<hipStream_t>(stream)), "gdn_scalar_chunk_operator launch");
+}
+
+gdn_status gdn_scalar_compose(const float *S_in, const float *gamma, const float *S_local, int32_t n_chunks,
+                              int32_t n_heads, int32_t dk, int32_t dv, float *S_out, gdn_stream_t stream) {
+  if (!S_out || (n_chunks > 0 && (!gamma || !S_local)))
+    return fail(GDN_ERR_NULL_POINTER, "gdn_scalar_compose: S_out, and gamma and S_local when n_chunks > 0, are required");
+  if (n_chunks < 0 || n_heads < 1) return fail(GDN_ERR_BAD_SHAPE, "gdn_scalar_compose: need n_chunks >= 0, n_heads >= 1");
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_scalar_compose: dk and dv must be 64 or 128 (got %d, %d)", dk, dv);
+  if (n_heads > kMaxHeads) return fail(GDN_ERR_UNSUPPORTED, "gdn_scalar_compose: too many heads");
+  gdn_status s;
+  if ((s = check_align("S_in", S_in)) || (s = check_align("gamma", gamma)) || (s = check_align("S_local", S_local)) ||
+      (s = check_align("S_out", S_out)))
+    return s;
+  gdn::ScalarComposeLaunch p{};
+  p.S_in = S_in;
+  p.gamma = gamma;
+  p.S_local = S_local;
+  p.S_out = S_out;
+  p.n_chunks = n_chunks;
+  p.H = n_heads;
+  p.dk = dk;
+  p.dv = dv;
+  return launched(gdn::launch_scalar_compose(p, reinterpret_cast<hipStream_t>(stream)), "gdn_scalar_compose launch");
+}
+
 const char *gdn_status_string(gdn_status status) {
   switch (status) {
     case GDN_OK: return "GDN_OK";

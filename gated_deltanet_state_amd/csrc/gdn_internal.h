@@ -143,6 +143,24 @@ struct FrontLaunch {
   int in_bf16;
 };
 
+// Scalar-decay chunk operators (gdn_scalar_chunk_operator) and their composition.
+struct ScalarOpLaunch {
+  const void *k, *v, *alpha, *beta;   // k [T, H, dk], v [T, H, dv], alpha, beta [T, H]
+  const int32_t *cu;                  // chunk bounds [n_chunks + 1]
+  float *gamma;                       // [n_chunks, H]
+  float *S_local;                     // [n_chunks, H, dv, dk] or null
+  int32_t n_chunks, H, dk, dv;
+  int in_bf16;
+};
+struct ScalarComposeLaunch {
+  const float *S_in;                  // [H, dv, dk] or null (zero)
+  const float *gamma, *S_local;       // [n_chunks, H], [n_chunks, H, dv, dk]
+  float *S_out;                       // [H, dv, dk] (may be S_in)
+  int32_t n_chunks, H, dk, dv;
+};
+hipError_t launch_scalar_op(const ScalarOpLaunch &p, hipStream_t stream);
+hipError_t launch_scalar_compose(const ScalarComposeLaunch &p, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeLaunch &p, hipStream_t stream);
 hipError_t launch_front(const FrontLaunch &p, hipStream_t stream);
 hipError_t launch_prep(const PrepLaunch &p, hipStream_t stream);        // dispatches bf16 inputs to launch_prep_bf16

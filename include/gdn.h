@@ -169,6 +169,49 @@ gdn_status gdn_decode(const void *q, const void *k, const void *v,
                       float *S_out, gdn_stream_t stream);
 
 /*
+ * gdn_scalar_chunk_operator -- the affine chunk operator when the per-token
+ * transition is a scalar decay (the Mamba-2 family): T_t = alpha_t I, so
+ * the chunk's transition is the scalar gamma = prod_t alpha_t.
+ * Page: LinearKV, the affine-operator paragraph (the two families differ
+ * only in what the chunk's transition is), with the write term of
+ * Tail-Replay section 2 Eq. (1):  S_t = alpha_t S_{t-1} + beta_t v_t k_t^T.
+ * From a zero start over chunk c:
+ *     gamma[c]   = prod_t alpha_t
+ *     S_local[c] = sum_t beta_t (prod_{s > t} alpha_s) v_t k_t^T
+ *
+ *   k [T, H, dk], v [T, H, dv], alpha, beta [T, H]   in_dtype (alpha > 0)
+ *   cu_chunks [n_chunks + 1] int32 (device), as for gdn_chunk_operator
+ *          (an empty chunk gives gamma = 1, S_local = 0)
+ *   gamma   [n_chunks, H] fp32 out
+ *   S_local [n_chunks, H, dv, dk] fp32 out, or NULL (then v may be NULL)
+ * Supported: dk, dv in {64, 128}; in_dtype F32 or BF16; 1 <= n_heads <= 65536;
+ * n_tokens < 2^31.  No workspace; stream-ordered, no synchronisation.
+ */
+gdn_status gdn_scalar_chunk_operator(const void *k, const void *v,
+                                     const void *alpha, const void *beta,
+                                     const int32_t *cu_chunks, int32_t n_chunks,
+                                     int64_t n_tokens, int32_t n_heads,
+                                     int32_t dk, int32_t dv, gdn_dtype in_dtype,
+                                     float *gamma, float *S_local,
+                                     gdn_stream_t stream);
+
+/*
+ * gdn_scalar_compose -- scalar-decay chunk operators back to back in context
+ * order (LinearKV, the composition paragraph, with a scalar transition):
+ *     S <- S_in (or zero);  for c = 0 .. n_chunks-1:  S <- gamma[c] S + S_local[c]
+ *
+ *   S_in  [H, dv, dk] fp32 or NULL (zero);  gamma [n_chunks, H] fp32;
+ *   S_local [n_chunks, H, dv, dk] fp32;  S_out [H, dv, dk] fp32 (may alias S_in)
+ * n_chunks may be 0 (S_out = S_in, or zero).  No workspace.
+ * The LinearKV last-block initializer, S_init = S_local of the last matched
+ * chunk, needs no call: it is S_local[n_chunks - 1] of either operator.
+ */
+gdn_status gdn_scalar_compose(const float *S_in, const float *gamma,
+                              const float *S_local, int32_t n_chunks,
+                              int32_t n_heads, int32_t dk, int32_t dv,
+                              float *S_out, gdn_stream_t stream);
+
+/*
  * gdn_front_end -- the step before the recurrence: queries and keys
  * L2-normalised per (token, head), the decay from its log-gate and the write
  * strength from its logit.

@@ -129,6 +129,31 @@ def test_front_end_argument_checks(lib):
     assert fe(qr=None, q=None, T=0) == OK
 
 
+def test_scalar_decay_argument_checks(lib):
+    def op(k=P, v=P, a=P, b=P, cu=P, C=4, T=100, H=2, dk=128, dv=128, dt=BF16, g=P, SL=P):
+        return lib.gdn_scalar_chunk_operator(k, v, a, b, cu, C, T, H, dk, dv, dt, g, SL, None)
+    assert op(g=None) == NULLP
+    assert op(cu=None) == NULLP
+    assert op(v=None) == NULLP                    # S_local without v
+    assert op(C=-1) == SHAPE
+    assert op(H=0) == SHAPE
+    assert op(dv=96) == UNSUP
+    assert op(dt=7) == UNSUP
+    assert op(T=1 << 31) == UNSUP
+    assert op(SL=P + 4) == ALIGN
+    assert op(C=0) == OK
+    assert op(v=None, SL=None, C=0) == OK
+
+    def co(Si=None, g=P, SL=P, C=3, H=2, dk=64, dv=64, So=P):
+        return lib.gdn_scalar_compose(Si, g, SL, C, H, dk, dv, So, None)
+    assert co(So=None) == NULLP
+    assert co(g=None) == NULLP
+    assert co(C=-1) == SHAPE
+    assert co(dk=32) == UNSUP
+    assert co(H=65537) == UNSUP
+    assert co(Si=P + 8) == ALIGN
+
+
 def test_workspace_queries(lib, monkeypatch):
     # one 13 KiB record of per-chunk factors ((I + A)^{-1} diag(beta) fragments and the gates) per chunk
     # slot and head; slots = n_tokens / 64 + n_seqs + 1 (sequence n's chunk j sits
