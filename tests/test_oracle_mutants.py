@@ -1,8 +1,9 @@
 """Plant plausible mistakes in copies of the oracle (on the CPU only) and
 check that the pins catch every one of them.
 
-Each mutant is a textual edit of gdn_oracle.c compiled into a temporary
-directory; the real oracle is never touched.
+Each mutant is a textual edit of gdn_oracle.c (the recurrence) or of the
+package's __init__.py (the numpy front end and scalar-decay functions) in a
+copy in a temporary directory; the real oracle is never touched.
 """
 import importlib.util
 import os
@@ -48,13 +49,32 @@ MUTANTS = {
 }
 
 
-def _load_mutant(tmp_path, name, old, new):
+PY_MUTANTS = {
+    # the norm's square root dropped
+    "front_no_sqrt": ("n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))",
+                      "n = np.sum(x * x, axis=-1, keepdims=True)"),
+    # sigmoid of the negated logit
+    "front_sigmoid_sign": ("1.0 / (1.0 + np.exp(-_f64(b)))", "1.0 / (1.0 + np.exp(_f64(b)))"),
+    # decay from the negated log-gate
+    "front_gate_sign": ("np.exp(_f64(g)), 1.0", "np.exp(-_f64(g)), 1.0"),
+    # the scalar decay not applied to the kept state
+    "scalar_no_decay": ("SL[c] = a[t][:, None, None] * SL[c] + b[t]", "SL[c] = SL[c] + b[t]"),
+    # the write strength dropped
+    "scalar_no_beta": ("+ b[t][:, None, None] * v[t]", "+ v[t]"),
+    # gamma as a sum instead of a product
+    "scalar_gamma_sum": ("gamma[c] *= a[t]", "gamma[c] += a[t] - 1"),
+    # composition without the decay of the incoming state
+    "scalar_compose_no_decay": ("S = g[c][:, None, None] * S + SL[c]", "S = S + SL[c]"),
+}
+
+
+def _load_mutant(tmp_path, name, old, new, fname="gdn_oracle.c"):
     d = tmp_path / ("oracle_" + name)
     shutil.copytree(os.path.join(ROOT, "oracle"), d,
                     ignore=shutil.ignore_patterns("*.so", "__pycache__", "*.tmp*"))
-    src = (d / "gdn_oracle.c").read_text()
+    src = (d / fname).read_text()
     assert src.count(old) == 1, name
-    (d / "gdn_oracle.c").write_text(src.replace(old, new))
+    (d / fname).write_text(src.replace(old, new))
     modname = "oracle_mutant_" + name
     spec = importlib.util.spec_from_file_location(modname, d / "__init__.py")
     mod = importlib.util.module_from_spec(spec)
@@ -68,6 +88,19 @@ def _load_mutant(tmp_path, name, old, new):
 def test_pins_catch_mutant(tmp_path, name):
     old, new = MUTANTS[name]
     mod = _load_mutant(tmp_path, name, old, new)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, "no pin caught mutant %s" % name
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_pins_catch_python_mutant(tmp_path, name):
+    old, new = PY_MUTANTS[name]
+    mod = _load_mutant(tmp_path, name, old, new, fname="__init__.py")
     caught = []
     for pin in ALL_PINS:
         try:
