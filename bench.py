@@ -75,9 +75,10 @@ def to_dev(inp, torch, np):
                 cu=torch.from_numpy(inp.cu_seqlens.astype(np.int32)).cuda())
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per call from the committed counter summary for this
-    workload, or None when the kernel sources changed since it was taken."""
+def measured_traffic(workload_name, kernel=None):
+    """HBM bytes per call (or per launch of the kernels whose names start
+    with ``kernel``) from the committed counter summary for this workload,
+    or None when the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload_name)
     if not os.path.exists(path):
         return None
@@ -85,6 +86,9 @@ def measured_traffic(workload_name):
         rec = json.load(f)
     if rec.get("workload") != workload_name or rec.get("sources_sha256") != sources_sha256():
         return None
+    if kernel is not None:
+        ks = [v for n, v in rec["kernels"].items() if n.startswith(kernel)]
+        return int(sum(v["fetch_bytes"] + v["write_bytes"] for v in ks)) if ks else None
     return int(rec["hbm_bytes_per_call"])
 
 
@@ -353,7 +357,7 @@ def scalar_ops_report(args, gdn, torch, np):
                 config=dict(workload=SCALAR_NAME, n_chunks=C, chunk=w["chunk"], n_tokens=T, heads=H, dk=dk, dv=dv,
                             outputs="gamma,S_local,S"),
                 roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                              frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(SCALAR_NAME),
+                              frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(SCALAR_NAME, "scalar_op_kernel"),
                               kernel="scalar_op_kernel", algorithmic_bytes=byt, kernel_ms_avg=round(t_op, 5)),
                 compose_ms=round(t_comp, 5))
     line["gpu_ms_per_step"] = round(t_op + t_comp, 5)
