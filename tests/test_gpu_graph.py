@@ -1,8 +1,9 @@
 """The calls under HIP graph capture.
 
-Every launch of gdn_replay, gdn_chunk_operator and gdn_compose is
-stream-ordered on the caller's stream with no host synchronisation, memset
-or copy, so a captured call replays the same kernels on the same buffers.
+Every launch of gdn_replay, gdn_chunk_operator, gdn_compose, gdn_front_end,
+gdn_decode and the scalar-decay calls is stream-ordered on the caller's
+stream with no host synchronisation, memset or copy, so a captured call
+replays the same kernels on the same buffers.
 Each case captures one call, then replays the graph several times with
 eager work (the outputs overwritten) and synchronisations in between; every
 replay must reproduce the eager result bit for bit (the kernels are
@@ -78,4 +79,23 @@ def test_chunk_operator_and_compose_under_graph_capture():
     def call():
         TC, SL = gdn.chunk_operator(d["k"], d["alpha"], d["beta"], cu, v=d["v"])
         return [TC, SL, gdn.compose(TC, SL, S_in=S_in)]
+    _capture_and_check(call)
+
+
+def test_front_end_decode_and_scalar_ops_under_graph_capture():
+    gdn, torch = _gdn()
+    raw = workloads.generate_raw([300], H=2, dk=128, dv=128, dtype="bf16", seed=85)
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    qr, kr, g, b, v = t(raw.q_raw), t(raw.k_raw), t(raw.g), t(raw.b), t(raw.v)
+    cu = torch.from_numpy(workloads.chunk_bounds(300, 128)).cuda()
+    S_in = torch.from_numpy(np.random.Generator(np.random.PCG64(86)).standard_normal((300, 2, 128, 128))
+                            .astype(np.float32) * 0.1).cuda()
+
+    def call():
+        q, k, a, be = gdn.front_end(qr, kr, g, b)
+        o, S = gdn.decode(q, k, v, a, be, S_in=S_in)
+        gam, SL = gdn.scalar_chunk_operator(k, a, be, cu, v=v)
+        return [q, k, a, be, o, S, gam, SL, gdn.scalar_compose(gam, SL)]
     _capture_and_check(call)
