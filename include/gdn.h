@@ -41,7 +41,7 @@ typedef enum gdn_status {
   GDN_OK = 0,
   GDN_ERR_NULL_POINTER = 1, /* a required pointer is NULL                        */
   GDN_ERR_BAD_SHAPE = 2,    /* negative / inconsistent sizes                     */
-  GDN_ERR_UNSUPPORTED = 3,  /* a size or dtype this build has no kernel for      */
+  GDN_ERR_UNSUPPORTED = 3,  /* a size or dtype the library has no kernel for    */
   GDN_ERR_ALIGNMENT = 4,    /* a pointer is not 16-byte aligned                  */
   GDN_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required        */
   GDN_ERR_HIP = 6           /* a HIP launch failed; see gdn_last_error()         */
