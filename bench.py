@@ -92,6 +92,18 @@ def measured_traffic(workload_name, kernel=None):
     return int(rec["hbm_bytes_per_call"])
 
 
+def uninstrumented_ms(fn, steps, torch):
+    """Wall-clock milliseconds per call of ``steps`` back-to-back calls with
+    no events between them, synchronised on both sides (the throughput pass;
+    event pairs around each call add a few microseconds per call)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def sources_sha256():
     import glob
     import hashlib
@@ -283,9 +295,10 @@ def decode_report(args, gdn, torch, np):
         call()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    step_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    instr_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
     kern_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     avg = sum(kern_ms) / len(kern_ms)
+    step_ms = uninstrumented_ms(call, args.steps, torch)
     # per (sequence, head): state read and written (fp32), q, k, v (bf16), gates, o (fp32)
     byt = N * H * (2 * d * d * 4 + 3 * d * 2 + 2 * 2 + d * 4)
     achieved = byt / (avg / 1e3) / 1e9
@@ -301,6 +314,7 @@ def decode_report(args, gdn, torch, np):
                               algorithmic_bytes=byt, kernel_ms_avg=round(avg, 5),
                               kernel_ms_min=round(min(kern_ms), 5)))
     line["gpu_ms_per_step"] = round(avg, 5)
+    line["instrumented_ms_per_step"] = round(instr_ms, 5)
     print(json.dumps(line), flush=True)
 
 
@@ -335,18 +349,21 @@ def scalar_ops_report(args, gdn, torch, np):
                 f()
         torch.cuda.synchronize()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(args.steps)]
-        t0 = time.perf_counter()
         for e in ev:
             e[0].record(stream)
             for i, f in enumerate(fns):
                 f()
                 e[i + 1].record(stream)
         torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1e3 / args.steps
         per = [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / len(ev) for i in range(len(fns))]
-        return per, wall
+        return per
 
-    (t_op, t_comp), wall = timed([op, comp])
+    t_op, t_comp = timed([op, comp])
+
+    def both():
+        op()
+        comp()
+    wall = uninstrumented_ms(both, args.steps, torch)
     # keys and values (bf16), gates (bf16) read; S_local (fp32) and gamma written
     byt = T * H * (dk + dv) * 2 + T * H * 2 * 2 + C * H * (dv * dk + 1) * 4
     achieved = byt / (t_op / 1e3) / 1e9
@@ -470,22 +487,21 @@ def front_end_report(args, gdn, torch, np):
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
-        t0 = time.perf_counter()
         for a, e in ev:
             a.record(stream)
             fn()
             e.record(stream)
         torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1e3 / args.steps
         ms = [a.elapsed_time(e) for a, e in ev]
-        return sum(ms) / len(ms), min(ms), wall
+        return sum(ms) / len(ms), min(ms)
 
-    avg, mn, wall = timed(lambda: gdn.front_end(qr, kr, g, b, out=out))
+    avg, mn = timed(lambda: gdn.front_end(qr, kr, g, b, out=out))
+    wall = uninstrumented_ms(lambda: gdn.front_end(qr, kr, g, b, out=out), args.steps, torch)
     extra = {}
     if args.with_replay:
-        both, _, _ = timed(lambda: gdn.replay(None, gdn.front_end(None, kr, g, b, out=out_k)[1], v, out[2], out[3],
+        both, _ = timed(lambda: gdn.replay(None, gdn.front_end(None, kr, g, b, out=out_k)[1], v, out[2], out[3],
                                               cu, want_o=False))
-        alone, _, _ = timed(lambda: gdn.replay(None, out[1], v, out[2], out[3], cu, want_o=False))
+        alone, _ = timed(lambda: gdn.replay(None, out[1], v, out[2], out[3], cu, want_o=False))
         extra = dict(state_only_replay=dict(prepared_inputs_ms=round(alone, 5), with_front_end_ms=round(both, 5)))
     # q_raw, k_raw read and q, k written (bf16); g, b read and alpha, beta written (bf16)
     byt = T * H * (4 * d * 2 + 4 * 2)
