@@ -45,8 +45,11 @@ namespace {
 constexpr int SNT = 256;   // threads per workgroup (4 waves)
 constexpr int SB = 32;     // tokens per step (one MFMA k block)
 
-template <int DK, int DV, typename TI>
-__global__ void __launch_bounds__(4 * DV) __attribute__((amdgpu_waves_per_eu(4))) scalar_op_kernel(ScalarOpLaunch p) {
+// MINW: waves per SIMD asked of the register allocator (4 for bf16 at
+// dk = dv = 128, where it lets two workgroups share a compute unit; 1, no
+// bound, elsewhere, where a bound of 4 would spill registers)
+template <int DK, int DV, typename TI, int MINW>
+__global__ void __launch_bounds__(4 * DV) __attribute__((amdgpu_waves_per_eu(MINW))) scalar_op_kernel(ScalarOpLaunch p) {
   constexpr bool EXACT_K = sizeof(TI) == 2;   // bf16 keys are exact MFMA operands
   constexpr int LDK = DK + 8, LDV = DV + 8;   // row padding (elements)
   constexpr int NT = 4 * DV;                  // threads: one wave per 16 rows of S_local
@@ -204,9 +207,10 @@ hipError_t launch_op(const ScalarOpLaunch &p, hipStream_t stream) {
   const int64_t items = (int64_t)p.n_chunks * p.H;
   if (items <= 0) return hipSuccess;
   if (p.in_bf16)
-    hipLaunchKernelGGL((scalar_op_kernel<DK, DV, bf16>), dim3((unsigned)items), dim3(4 * DV), 0, stream, p);
+    hipLaunchKernelGGL((scalar_op_kernel<DK, DV, bf16, (DK == 128 && DV == 128) ? 4 : 1>), dim3((unsigned)items),
+                       dim3(4 * DV), 0, stream, p);
   else
-    hipLaunchKernelGGL((scalar_op_kernel<DK, DV, float>), dim3((unsigned)items), dim3(4 * DV), 0, stream, p);
+    hipLaunchKernelGGL((scalar_op_kernel<DK, DV, float, 1>), dim3((unsigned)items), dim3(4 * DV), 0, stream, p);
   return hipGetLastError();
 }
 
