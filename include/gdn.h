@@ -35,7 +35,10 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+/* 1: gdn_replay, gdn_chunk_operator, gdn_compose and their helpers.
+ * 2: adds gdn_decode, gdn_front_end, gdn_scalar_chunk_operator and
+ *    gdn_scalar_compose; the version 1 calls are unchanged. */
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
   GDN_OK = 0,

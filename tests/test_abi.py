@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
     for code, name in [(0, b"GDN_OK"), (1, b"GDN_ERR_NULL_POINTER"), (2, b"GDN_ERR_BAD_SHAPE"),
                        (3, b"GDN_ERR_UNSUPPORTED"), (4, b"GDN_ERR_ALIGNMENT"),
                        (5, b"GDN_ERR_WORKSPACE"), (6, b"GDN_ERR_HIP")]:
