@@ -41,3 +41,17 @@ def test_workload_shapes_and_distributions():
     assert np.array_equal(w0.k, w0b.k)
     w1 = workloads.make_workload(1, H=1)
     assert w1.n_tokens == 3277
+
+
+def test_raw_inputs_recipe():
+    # raw projections: seeded, rounded to the dtype, log-gate <= 0, q and k
+    # not normalised (per-row scales in [0.25, 4])
+    a = workloads.generate_raw([5, 0, 70], H=3, dk=64, dv=128, dtype="bf16", seed=9)
+    b = workloads.generate_raw([5, 0, 70], H=3, dk=64, dv=128, dtype="bf16", seed=9)
+    assert a.q_raw.shape == (75, 3, 64) and a.v.shape == (75, 3, 128) and a.g.shape == (75, 3)
+    assert a.q_raw.dtype == np.uint16 and np.array_equal(a.k_raw, b.k_raw) and a.n_tokens == 75
+    assert np.all(a.f64("g") <= 0)
+    n = np.linalg.norm(a.f64("k_raw"), axis=-1)
+    assert n.min() > 0.25 * 4 and n.max() < 4 * 16 and np.std(n) > 1
+    f = workloads.generate_raw([8], H=1, dk=64, dv=64, dtype="f32", seed=9)
+    assert f.q_raw.dtype == np.float32
