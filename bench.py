@@ -3,13 +3,15 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ID] [--no-cpu]
 
 One step is one pass of the whole path over one batch of synthetic input
-already resident in HBM.  The default workload is a tail replay of one
-request: the latest 3277 tokens (10% of a 32768-token prefix) through 32
-heads with dk = dv = 128, bf16 inputs, fp32 state, zero start state, final
-state only (the "replay to rebuild the state" use of the Tail-Replay page,
-section 3, Eq. (2)).  Other workloads: 2 = 16 packed tails of 410..3277
-tokens with outputs; 3 = a 32768-token prefill with outputs; 4 = 64
-chunk operators of 512 tokens and their composition; 0 = one fp32 head.
+already resident in HBM.  The default workload (3) is the largest: one
+32768-token sequence through 32 heads with dk = dv = 128, bf16 inputs, fp32
+state, zero start state, outputs o (fp32) for every token and the final
+state -- the full-prefill shape that the Tail-Replay page compares replay
+against (section 4, Table 2, at 32K).  Other workloads: 1 = a tail replay of
+one request, the latest 3277 tokens (10% of a 32768-token prefix), final
+state only (section 3, Eq. (2)); 2 = 16 packed tails of 410..3277 tokens
+with outputs; 4 = 64 chunk operators of 512 tokens and their composition;
+0 = one fp32 head.
 
 ``--decode N`` instead times single-token decode of N requests from given
 states (the serving step after a replay).  ``--front-end`` instead times
@@ -524,7 +526,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--o-bf16", action="store_true", help="write o in bf16 (workloads 2, 3)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

@@ -9,9 +9,15 @@ If ``libgdn.so`` is missing or cannot be loaded, every call raises: there is
 no fallback implementation.
 
 Functions (same names as the C entry points, without the ``gdn_`` prefix):
-  replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=float32)
+  replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=float32,
+         segments=None)      (gdn_replay, or gdn_replay_segmented when segments is given)
   chunk_operator(k, alpha, beta, cu_chunks, v=None)
   compose(T_C, S_local, S_in=None)
+  decode, front_end, scalar_chunk_operator, scalar_compose
+
+Every call launches on ``stream`` (default: the current stream).  The
+workspace a call needs is allocated on that stream, so the caching allocator
+hands its memory to other work only after the call's kernels.
 """
 from __future__ import annotations
 
@@ -48,6 +54,9 @@ def library():
     lib.gdn_replay.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint,
                                vp, cint, vp, vp, sz, vp]
     lib.gdn_replay_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
+    lib.gdn_replay_segmented.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint,
+                                         vp, cint, vp, i32, vp, sz, vp]
+    lib.gdn_replay_segmented_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
     lib.gdn_chunk_operator.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint,
                                        vp, vp, vp, sz, vp]
     lib.gdn_chunk_operator_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
@@ -57,11 +66,11 @@ def library():
     lib.gdn_front_end.argtypes = [vp, vp, vp, vp, i64, i32, i32, cint, vp, vp, vp, vp, vp]
     lib.gdn_scalar_chunk_operator.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint, vp, vp, vp]
     lib.gdn_scalar_compose.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
-    for f in (lib.gdn_replay, lib.gdn_chunk_operator, lib.gdn_compose, lib.gdn_decode, lib.gdn_front_end,
-              lib.gdn_scalar_chunk_operator, lib.gdn_scalar_compose):
+    for f in (lib.gdn_replay, lib.gdn_replay_segmented, lib.gdn_chunk_operator, lib.gdn_compose,
+              lib.gdn_decode, lib.gdn_front_end, lib.gdn_scalar_chunk_operator, lib.gdn_scalar_compose):
         f.restype = cint
-    for f in (lib.gdn_replay_workspace_bytes, lib.gdn_chunk_operator_workspace_bytes,
-              lib.gdn_compose_workspace_bytes):
+    for f in (lib.gdn_replay_workspace_bytes, lib.gdn_replay_segmented_workspace_bytes,
+              lib.gdn_chunk_operator_workspace_bytes, lib.gdn_compose_workspace_bytes):
         f.restype = sz
     lib.gdn_status_string.argtypes = [cint]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -95,6 +104,11 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _launch_stream(stream, device):
+    torch = _torch()
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
 def _dtype_code(dt):
     torch = _torch()
     if dt == torch.float32:
@@ -114,15 +128,19 @@ def _dev(t, name):
     return t
 
 
-def _workspace(nbytes, device):
+def _workspace(nbytes, device, stream):
+    """Scratch for one call, allocated on the stream the call launches on:
+    the caching allocator then reuses the block only for work ordered after
+    the call's kernels on that stream (or after a synchronisation)."""
     torch = _torch()
     if nbytes == 0:
         return None, 0
-    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    with torch.cuda.stream(_launch_stream(stream, device)):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
 def replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=None,
-           out=None, S_out=None, stream=None):
+           out=None, S_out=None, stream=None, segments=None):
     """Replay packed sequences through the gated delta rule.
 
     q, k [T, H, dk]; v [T, H, dv]; alpha, beta [T, H] (all float32 or all
@@ -130,6 +148,8 @@ def replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=None,
     float32 or None (zero state).  Returns (o [T, H, dv] or None,
     S_final [N, H, dv, dk] float32).  ``out`` / ``S_out`` may supply the
     output tensors (S_out may be S0: the update is then in place).
+    ``segments`` (0 .. 64) calls gdn_replay_segmented with that many time
+    segments per sequence; None calls gdn_replay.
     """
     torch = _torch()
     lib = library()
@@ -160,11 +180,15 @@ def replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=None,
     S = S_out if S_out is not None else torch.empty((N, H, dv, dk), dtype=torch.float32,
                                                     device=k.device)
     _dev(S, "S_out")
-    ws_bytes = lib.gdn_replay_workspace_bytes(N, T, H, dk, dv)
-    ws, ws_bytes = _workspace(ws_bytes, k.device)
-    _check(lib.gdn_replay(_ptr(q) if want_o else None, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                          _ptr(S0), _ptr(cu_seqlens), N, T, H, dk, dv, in_code, _ptr(o),
-                          o_code, _ptr(S), _ptr(ws), ws_bytes, _stream_ptr(stream)))
+    args = (_ptr(q) if want_o else None, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+            _ptr(S0), _ptr(cu_seqlens), N, T, H, dk, dv, in_code, _ptr(o), o_code, _ptr(S))
+    if segments is None:
+        ws, ws_bytes = _workspace(lib.gdn_replay_workspace_bytes(N, T, H, dk, dv), k.device, stream)
+        _check(lib.gdn_replay(*args, _ptr(ws), ws_bytes, _stream_ptr(stream)))
+    else:
+        ws, ws_bytes = _workspace(lib.gdn_replay_segmented_workspace_bytes(N, T, H, dk, dv, int(segments)),
+                                  k.device, stream)
+        _check(lib.gdn_replay_segmented(*args, int(segments), _ptr(ws), ws_bytes, _stream_ptr(stream)))
     return o, S
 
 
@@ -287,7 +311,7 @@ def chunk_operator(k, alpha, beta, cu_chunks, v=None, stream=None):
     TC = torch.empty((C, H, dk, dk), dtype=torch.float32, device=k.device)
     SL = torch.empty((C, H, dv, dk), dtype=torch.float32, device=k.device) if v is not None else None
     ws_bytes = lib.gdn_chunk_operator_workspace_bytes(C, T, H, dk, dv)
-    ws, ws_bytes = _workspace(ws_bytes, k.device)
+    ws, ws_bytes = _workspace(ws_bytes, k.device, stream)
     _check(lib.gdn_chunk_operator(_ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_chunks), C, T,
                                   H, dk, dv, in_code, _ptr(TC), _ptr(SL), _ptr(ws), ws_bytes,
                                   _stream_ptr(stream)))
@@ -306,7 +330,7 @@ def compose(T_C, S_local, S_in=None, out=None, stream=None):
     S = out if out is not None else torch.empty((H, dv, dk), dtype=torch.float32, device=T_C.device)
     _dev(S, "out")
     ws_bytes = lib.gdn_compose_workspace_bytes(C, H, dk, dv)
-    ws, ws_bytes = _workspace(ws_bytes, T_C.device)
+    ws, ws_bytes = _workspace(ws_bytes, T_C.device, stream)
     _check(lib.gdn_compose(_ptr(S_in), _ptr(T_C), _ptr(S_local), C, H, dk, dv, _ptr(S),
                            _ptr(ws), ws_bytes, _stream_ptr(stream)))
     return S

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
 
-SOURCES = ["gdn_prep.hip", "gdn_prep_bf16.hip", "gdn_chain.hip", "gdn_chain_bf16.hip", "gdn_chain_dks.hip", "gdn_compose.hip", "gdn_decode.hip", "gdn_front.hip", "gdn_scalar.hip", "gdn_api.cpp"]
+SOURCES = ["gdn_prep.hip", "gdn_prep_bf16.hip", "gdn_chain.hip", "gdn_chain_bf16.hip", "gdn_compose.hip", "gdn_decode.hip", "gdn_front.hip", "gdn_scalar.hip", "gdn_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -10,6 +10,7 @@
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "gdn_internal.h"
@@ -57,36 +58,50 @@ gdn_status launched(hipError_t e, const char *what) {
   return ok();
 }
 
+// Compute units of the current device, read once per device
+// (hipDeviceAttributeMultiprocessorCount); 256 when no device answers.
+constexpr int kMaxDevices = 64;
+std::once_flag g_cu_once[kMaxDevices];
+int g_cus[kMaxDevices];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  std::call_once(g_cu_once[dev], [dev] {
+    int n = 0;
+    g_cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n
+                                                                                                             : 256;
+  });
+  return g_cus[dev];
+}
+
+// Largest segment count a caller may force.
+constexpr int32_t kMaxSegments = 64;
+
 // Segments per sequence for a state-only replay with bf16 inputs.  A
 // sequence cut into P segments of whole chunks runs as P independent
 // recurrences (segment 0 from S0 with its state rows only, later segments as
 // affine operators with dk transition rows as well), composed afterwards.
 // Cost model, in units of one chunk step of an eight-wave state workgroup
-// (one workgroup per compute unit, 256 compute units):
-//   P = 1:  (workgroups / 256 rounded up) x chunks per sequence
+// (one workgroup per compute unit):
+//   P = 1:  (workgroups / CUs rounded up) x chunks per sequence
 //   P > 1:  one workgroup of transition + state tiles per (sequence, head,
 //           segment), each chunk step about 1.25 units, plus about 0.3 units
 //           per composition step.
-// P = 1 unless splitting pays.  GDN_REPLAY_SEGMENTS=<n> overrides the
-// choice (tuning and tests).
-int replay_segments(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv) {
-  if (const char *env = std::getenv("GDN_REPLAY_SEGMENTS")) {
-    const int v = std::atoi(env);
-    if (v >= 1) return v < 64 ? v : 64;
-  }
+// P = 1 unless splitting pays.
+int replay_segments(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv, int cus) {
   if ((dk + dv) / 16 > 16) return 1;
   const double chunks = std::ceil((double)n_tokens / gdn::kChunk / (n_seqs > 0 ? n_seqs : 1));
   int pmax = (int)chunks;
   if (pmax > 16) pmax = 16;
   if (pmax < 1) pmax = 1;
-  constexpr int64_t kCUs = 256;
   const int64_t wg1 = (int64_t)n_seqs * n_heads * ((dv / 16 + 7) / 8);
   int best = 1;
-  double best_t = (double)((wg1 + kCUs - 1) / kCUs) * chunks;
+  double best_t = (double)((wg1 + cus - 1) / cus) * chunks;
   for (int P = 2; P <= pmax; ++P) {
     const int64_t wg = (int64_t)n_seqs * n_heads * P;
     if (wg > (int64_t(1) << 28)) break;
-    const double t = (double)((wg + kCUs - 1) / kCUs) * std::ceil(chunks / P) * 1.25 + 0.3 * (P - 1);
+    const double t = (double)((wg + cus - 1) / cus) * std::ceil(chunks / P) * 1.25 + 0.3 * (P - 1);
     if (t < best_t) {
       best = P;
       best_t = t;
@@ -95,37 +110,32 @@ int replay_segments(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t d
   return best;
 }
 
-// State-only bf16 replays can also run one workgroup per row tile whose
-// waves split the key dimension (gdn_chain_dks.hip): no time split, no
-// composition, but one chunk step per ~1.6 us, bound by staging a chunk's
-// keys and record into every tile's compute unit.  On one 3277-token tail
-// over 32 heads that is slower than the time split, so it runs only on
-// request: GDN_REPLAY_KEYSPLIT=1 (with at most 256 row tiles in all).
-bool replay_dks(int32_t n_seqs, int32_t n_heads, int32_t dv) {
-  const char *env = std::getenv("GDN_REPLAY_KEYSPLIT");
-  if (!env || std::atoi(env) != 1) return false;
-  return (int64_t)n_seqs * n_heads * (dv / 16) <= 256;
-}
-
 // Segments per sequence for a bf16 replay with outputs.  A split runs three
 // passes: the state-only segment operators, their composition (which also
 // yields every segment's true start state), and every segment again with
 // outputs from that start state.  Worth it when the (sequence, head) pairs
-// alone leave compute units idle: P fills 256 compute units with one
+// alone leave compute units idle: P fills the compute units with one
 // workgroup per (sequence, head, segment), with at least 8 chunks per
-// segment.  GDN_REPLAY_SEGMENTS=<n> overrides the choice.
-int replay_segments_o(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv) {
-  if (const char *env = std::getenv("GDN_REPLAY_SEGMENTS")) {
-    const int v = std::atoi(env);
-    if (v >= 1) return v < 64 ? v : 64;
-  }
+// segment.
+int replay_segments_o(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv, int cus) {
   if ((dk + dv) / 16 > 16) return 1;
   const int64_t chunks = (n_tokens / gdn::kChunk) / (n_seqs > 0 ? n_seqs : 1);
   const int64_t units = (int64_t)n_seqs * n_heads;
-  int64_t P = 256 / (units > 0 ? units : 1);
+  int64_t P = cus / (units > 0 ? units : 1);
   if (P > chunks / 8) P = chunks / 8;
   if (P > 8) P = 8;
   return P < 2 ? 1 : (int)P;
+}
+
+// Segment count of one call: `forced` (>= 1, from gdn_replay_segmented) or
+// the cost model; fp32 inputs never split.
+int32_t segments_for(bool bf, bool with_o, int32_t forced, int32_t n_seqs, int64_t n_tokens, int32_t n_heads,
+                     int32_t dk, int32_t dv) {
+  if (!bf) return 1;
+  if (forced >= 1) return forced < kMaxSegments ? forced : kMaxSegments;
+  const int cus = device_cus();
+  return with_o ? replay_segments_o(n_seqs, n_tokens, n_heads, dk, dv, cus)
+                : replay_segments(n_seqs, n_tokens, n_heads, dk, dv, cus);
 }
 
 // Segment operators and states: [n_seqs, P, H] x (dk x dk + dv x dk) fp32;
@@ -135,53 +145,48 @@ size_t seg_workspace_bytes(int32_t n_seqs, int32_t P, int32_t n_heads, int32_t d
   return (size_t)n_seqs * P * n_heads * ((size_t)dk * dk + (size_t)dv * dk * (prefix ? 2 : 1)) * sizeof(float);
 }
 
-}  // namespace
+// Workspace of one replay call (the records, then the segment operators and
+// states of a time split, or the longest-first order of an unsplit bf16 call).
+size_t replay_need(bool bf, bool with_o, int32_t P, int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk,
+                   int32_t dv) {
+  const bool ordered = bf && P == 1 && gdn::order_workspace_bytes(n_seqs) > 0;
+  return gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads) +
+         (P > 1 ? seg_workspace_bytes(n_seqs, P, n_heads, dk, dv, with_o)
+                : (ordered ? gdn::order_workspace_bytes(n_seqs) : 0));
+}
 
-extern "C" {
-
-size_t gdn_replay_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv) {
+// Enough for any call with these sizes (state only or with outputs, bf16 or
+// fp32 inputs).
+size_t replay_workspace_max(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv,
+                            int32_t forced) {
   if (n_seqs < 1 || n_tokens < 0 || n_heads < 1) return 0;
-  size_t seg = 0;
-  if (supported_dim(dk) && supported_dim(dv)) {
-    // enough for either use: state only, or with outputs
-    const size_t s1 = seg_workspace_bytes(n_seqs, replay_segments(n_seqs, n_tokens, n_heads, dk, dv), n_heads, dk, dv);
-    const size_t s2 =
-        seg_workspace_bytes(n_seqs, replay_segments_o(n_seqs, n_tokens, n_heads, dk, dv), n_heads, dk, dv, true);
-    seg = s1 > s2 ? s1 : s2;
-    const size_t s3 = gdn::order_workspace_bytes(n_seqs);   // (replays without a time split)
-    seg = seg > s3 ? seg : s3;
+  if (!supported_dim(dk) || !supported_dim(dv)) return gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads);
+  size_t best = 0;
+  for (int with_o = 0; with_o < 2; ++with_o) {
+    const int32_t P = segments_for(true, with_o != 0, forced, n_seqs, n_tokens, n_heads, dk, dv);
+    const size_t b = replay_need(true, with_o != 0, P, n_seqs, n_tokens, n_heads, dk, dv);
+    best = b > best ? b : best;
   }
-  return gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads) + seg;
+  return best;
 }
 
-size_t gdn_chunk_operator_workspace_bytes(int32_t n_chunks, int64_t n_tokens, int32_t n_heads, int32_t,
-                                          int32_t) {
-  if (n_chunks < 1 || n_tokens < 0 || n_heads < 1) return 0;
-  return gdn::tau_workspace_bytes(n_tokens, n_chunks, n_heads);
-}
-
-size_t gdn_compose_workspace_bytes(int32_t n_chunks, int32_t n_heads, int32_t dk, int32_t) {
-  // the operators as composition fragments: as many bytes as T_C
-  if (n_chunks < 1 || n_heads < 1 || dk < 1) return 0;
-  return (size_t)n_chunks * n_heads * dk * dk * sizeof(float);
-}
-
-gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *alpha, const void *beta,
-                      const float *S0, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
-                      int32_t n_heads, int32_t dk, int32_t dv, gdn_dtype in_dtype, void *o, gdn_dtype o_dtype,
-                      float *S_final, void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
+gdn_status replay_impl(const void *q, const void *k, const void *v, const void *alpha, const void *beta,
+                       const float *S0, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
+                       int32_t n_heads, int32_t dk, int32_t dv, gdn_dtype in_dtype, void *o, gdn_dtype o_dtype,
+                       float *S_final, int32_t forced_segments, void *workspace, size_t workspace_bytes,
+                       gdn_stream_t stream, const char *fn) {
   if (!k || !v || !alpha || !beta || !cu_seqlens || !S_final)
-    return fail(GDN_ERR_NULL_POINTER, "gdn_replay: k, v, alpha, beta, cu_seqlens and S_final are required");
-  if (o && !q) return fail(GDN_ERR_NULL_POINTER, "gdn_replay: o requested without q");
+    return fail(GDN_ERR_NULL_POINTER, "%s: k, v, alpha, beta, cu_seqlens and S_final are required", fn);
+  if (o && !q) return fail(GDN_ERR_NULL_POINTER, "%s: o requested without q", fn);
   if (n_seqs < 1 || n_tokens < 0 || n_heads < 1 || dk < 1 || dv < 1)
-    return fail(GDN_ERR_BAD_SHAPE, "gdn_replay: need n_seqs >= 1, n_tokens >= 0, n_heads >= 1 (got %d, %lld, %d)",
+    return fail(GDN_ERR_BAD_SHAPE, "%s: need n_seqs >= 1, n_tokens >= 0, n_heads >= 1 (got %d, %lld, %d)", fn,
                 n_seqs, (long long)n_tokens, n_heads);
   if (!supported_dim(dk) || !supported_dim(dv))
-    return fail(GDN_ERR_UNSUPPORTED, "gdn_replay: dk and dv must be 64 or 128 (got %d, %d)", dk, dv);
+    return fail(GDN_ERR_UNSUPPORTED, "%s: dk and dv must be 64 or 128 (got %d, %d)", fn, dk, dv);
   if (!valid_dtype(in_dtype) || (o && !valid_dtype(o_dtype)))
-    return fail(GDN_ERR_UNSUPPORTED, "gdn_replay: dtypes must be GDN_F32 or GDN_BF16");
+    return fail(GDN_ERR_UNSUPPORTED, "%s: dtypes must be GDN_F32 or GDN_BF16", fn);
   if (n_tokens > kMaxTokens || n_heads > kMaxHeads || (int64_t)n_seqs * n_heads * (dv / 16) > (int64_t(1) << 30))
-    return fail(GDN_ERR_UNSUPPORTED, "gdn_replay: problem too large for one call");
+    return fail(GDN_ERR_UNSUPPORTED, "%s: problem too large for one call", fn);
   gdn_status s;
   if ((s = check_align("q", q)) || (s = check_align("k", k)) || (s = check_align("v", v)) ||
       (s = check_align("alpha", alpha)) || (s = check_align("beta", beta)) || (s = check_align("S0", S0)) ||
@@ -189,17 +194,13 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
       (s = check_align("S_final", S_final)))
     return s;
   const bool bf = in_dtype == GDN_BF16;
-  const bool dks = bf && !o && replay_dks(n_seqs, n_heads, dv);
-  const int32_t P = (!bf || dks) ? 1
-                                 : (o ? replay_segments_o(n_seqs, n_tokens, n_heads, dk, dv)
-                                      : replay_segments(n_seqs, n_tokens, n_heads, dk, dv));
+  const int32_t P = segments_for(bf, o != nullptr, forced_segments, n_seqs, n_tokens, n_heads, dk, dv);
   const size_t tau_bytes = gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads);
   // longest-first sequence order (bf16 replays without a time split, built by the prep kernel)
-  const bool ordered = bf && !dks && P == 1 && gdn::order_workspace_bytes(n_seqs) > 0;
-  const size_t need = tau_bytes + (P > 1 ? seg_workspace_bytes(n_seqs, P, n_heads, dk, dv, o != nullptr)
-                                         : (ordered ? gdn::order_workspace_bytes(n_seqs) : 0));
+  const bool ordered = bf && P == 1 && gdn::order_workspace_bytes(n_seqs) > 0;
+  const size_t need = replay_need(bf, o != nullptr, P, n_seqs, n_tokens, n_heads, dk, dv);
   if (workspace_bytes < need || !workspace)
-    return fail(GDN_ERR_WORKSPACE, "gdn_replay: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes required (got %zu)", fn, need, workspace_bytes);
   if ((s = check_align("workspace", workspace))) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   gdn::PrepLaunch pp{};
@@ -242,7 +243,6 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
     p.T_out = nullptr;
     p.tiles_T = 0;
     p.tiles_S = dv / 16;
-    if (dks) return launched(gdn::launch_chain_dks(p, st), "gdn_replay launch");
     return launched(bf ? gdn::launch_chain_bf16(p, st) : gdn::launch_chain(p, st), "gdn_replay launch");
   }
   // time split: segment operators, then their composition
@@ -285,6 +285,52 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
   r.T_frags = 0;
   r.fuse_prep = 0;
   return launched(gdn::launch_chain_bf16(r, st), "gdn_replay segment output launch");
+}
+
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_replay_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv) {
+  return replay_workspace_max(n_seqs, n_tokens, n_heads, dk, dv, 0);
+}
+
+size_t gdn_replay_segmented_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk,
+                                            int32_t dv, int32_t segments) {
+  if (segments < 0) return 0;
+  return replay_workspace_max(n_seqs, n_tokens, n_heads, dk, dv, segments);
+}
+
+size_t gdn_chunk_operator_workspace_bytes(int32_t n_chunks, int64_t n_tokens, int32_t n_heads, int32_t,
+                                          int32_t) {
+  if (n_chunks < 1 || n_tokens < 0 || n_heads < 1) return 0;
+  return gdn::tau_workspace_bytes(n_tokens, n_chunks, n_heads);
+}
+
+size_t gdn_compose_workspace_bytes(int32_t n_chunks, int32_t n_heads, int32_t dk, int32_t) {
+  // the operators as composition fragments: as many bytes as T_C
+  if (n_chunks < 1 || n_heads < 1 || dk < 1) return 0;
+  return (size_t)n_chunks * n_heads * dk * dk * sizeof(float);
+}
+
+gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *alpha, const void *beta,
+                      const float *S0, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
+                      int32_t n_heads, int32_t dk, int32_t dv, gdn_dtype in_dtype, void *o, gdn_dtype o_dtype,
+                      float *S_final, void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
+  return replay_impl(q, k, v, alpha, beta, S0, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, in_dtype, o, o_dtype,
+                     S_final, 0, workspace, workspace_bytes, stream, "gdn_replay");
+}
+
+gdn_status gdn_replay_segmented(const void *q, const void *k, const void *v, const void *alpha, const void *beta,
+                                const float *S0, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
+                                int32_t n_heads, int32_t dk, int32_t dv, gdn_dtype in_dtype, void *o,
+                                gdn_dtype o_dtype, float *S_final, int32_t segments, void *workspace,
+                                size_t workspace_bytes, gdn_stream_t stream) {
+  if (segments < 0 || segments > kMaxSegments)
+    return fail(GDN_ERR_BAD_SHAPE, "gdn_replay_segmented: segments must be 0 .. %d (got %d)", kMaxSegments, segments);
+  return replay_impl(q, k, v, alpha, beta, S0, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, in_dtype, o, o_dtype,
+                     S_final, segments, workspace, workspace_bytes, stream, "gdn_replay_segmented");
 }
 
 gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, const void *beta,

@@ -21,10 +21,8 @@
 // T_C are rows of a "state" that starts as the identity and receives no
 // value input.
 //
-// Precision (bf16 inputs, fp32 state): K, Q, V are exact in bf16; the
-// state, R, D, Tau and M o QK^T enter products as split bf16 (hi + lo), so
-// every product is within a few fp32 ulps (split-bfloat16, gdn_device.h).
-// fp32 inputs use the fp32 MFMA.
+// This kernel serves fp32 inputs (bf16 inputs have gdn_chain_bf16.hip): every
+// product runs on the fp32 MFMA (v_mfma_f32_16x16x4_f32).
 //
 // Four waves; wave w owns token block w (16 tokens) of every 16 x 64 tile
 // (Y, R, D, O) and state column tiles w, w + 4.  Per chunk, three phases
@@ -39,8 +37,6 @@
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
-#include <type_traits>
-
 namespace gdn {
 
 namespace {
@@ -50,61 +46,49 @@ constexpr int NW = 4;       // waves per workgroup
 constexpr int NT = NW * 64; // threads per workgroup
 constexpr int RT = 16;      // state rows per workgroup
 
-template <class Tin, int DK, bool WANT_O>
+template <int DK, bool WANT_O>
 struct Cfg {
-  static constexpr bool BF = std::is_same<Tin, bf16>::value;
-  using PT = typename std::conditional<BF, bf16, float>::type;  // plane element type
-  // leading dimensions (elements): bf16 paths read 16-byte rows; fp32 paths
-  // read single elements and use odd strides against bank conflicts
-  static constexpr int LDK = BF ? DK + 8 : DK + 1;   // sK, sQ [CH][LDK] Tin
-  static constexpr int LDC = BF ? CH + 4 : CH + 1;   // sP [CH][LDC] fp32
-  static constexpr int LDSP = BF ? DK + 8 : DK + 1;  // state planes [RT][LDSP]
-  static constexpr int LDRP = BF ? CH + 8 : CH + 1;  // R, D, Dd planes [RT][LDRP]
-  static constexpr int NPL = BF ? 2 : 1;             // planes per split operand
+  // leading dimensions (elements): single-element reads, odd strides against
+  // bank conflicts
+  static constexpr int LDK = DK + 1;   // sK, sQ [CH][LDK]
+  static constexpr int LDC = CH + 1;   // sP [CH][LDC]
+  static constexpr int LDSP = DK + 1;  // state [RT][LDSP]
+  static constexpr int LDRP = CH + 1;  // R, D, Dd [RT][LDRP]
 
   static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
-  static constexpr size_t KBYTES = al(sizeof(Tin) * CH * LDK);
+  static constexpr size_t KBYTES = al(4 * CH * LDK);
   static constexpr size_t oK = 0;                     // two buffers (chunk parity)
   static constexpr size_t oQ = oK + 2 * KBYTES;
-  static constexpr size_t oP = oQ + (WANT_O ? al(sizeof(Tin) * CH * LDK) : 0);
+  static constexpr size_t oP = oQ + (WANT_O ? al(4 * CH * LDK) : 0);
   static constexpr size_t oS = oP + (WANT_O ? al(4 * CH * LDC) : 0);
-  static constexpr size_t oR = oS + NPL * al(sizeof(PT) * RT * LDSP);
-  static constexpr size_t oD = oR + NPL * al(sizeof(PT) * RT * LDRP);
-  static constexpr size_t oDd = oD + (WANT_O ? NPL * al(sizeof(PT) * RT * LDRP) : 0);
-  static constexpr size_t oGate = oDd + NPL * al(sizeof(PT) * RT * LDRP);
+  static constexpr size_t oR = oS + al(4 * RT * LDSP);
+  static constexpr size_t oD = oR + al(4 * RT * LDRP);
+  static constexpr size_t oDd = oD + (WANT_O ? al(4 * RT * LDRP) : 0);
+  static constexpr size_t oGate = oDd + al(4 * RT * LDRP);
   static constexpr size_t GBYTES = al(4 * 5 * CH);
   static constexpr size_t TOTAL = oGate + 2 * GBYTES;  // two gate buffers
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 
   static constexpr int NST = DK / 16;          // state column tiles
   static constexpr int SPW = (NST + NW - 1) / NW;
-  static constexpr int VEC = 16 / sizeof(Tin);
+  static constexpr int VEC = 4;                // floats per 16-byte load
   static constexpr int KSEG = DK / VEC;        // 16-byte segments per key row
   static constexpr int NKP = (CH * KSEG + NT - 1) / NT;
-  // Tau row fragments per lane: bf16 policy 2 k-steps of 8 floats, fp32
-  // policy 16 single elements (k step 4)
-  static constexpr int NTF = 4;
+  static constexpr int NTF = 4;                // Tau row: 16 single elements (k step 4)
 };
 
-
-
-template <class Tin, int DK, bool WANT_O>
+template <int DK, bool WANT_O>
 __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
-  using C = Cfg<Tin, DK, WANT_O>;
-  constexpr bool BF = C::BF;
-  using PT = typename C::PT;
+  using C = Cfg<DK, WANT_O>;
+  using Tin = float;
   __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
-  Tin *sK0 = reinterpret_cast<Tin *>(smem + C::oK);
-  Tin *sQ = reinterpret_cast<Tin *>(smem + C::oQ);
+  float *sK0 = reinterpret_cast<float *>(smem + C::oK);
+  float *sQ = reinterpret_cast<float *>(smem + C::oQ);
   float *sP = reinterpret_cast<float *>(smem + C::oP);
-  PT *sSh = reinterpret_cast<PT *>(smem + C::oS);
-  PT *sSl = sSh + (BF ? RT * C::LDSP : 0);
-  PT *sRh = reinterpret_cast<PT *>(smem + C::oR);
-  PT *sRl = sRh + (BF ? RT * C::LDRP : 0);
-  PT *sDh = reinterpret_cast<PT *>(smem + C::oD);
-  PT *sDl = sDh + (BF ? RT * C::LDRP : 0);
-  PT *sDdh = reinterpret_cast<PT *>(smem + C::oDd);
-  PT *sDdl = sDdh + (BF ? RT * C::LDRP : 0);
+  float *sSh = reinterpret_cast<float *>(smem + C::oS);
+  float *sRh = reinterpret_cast<float *>(smem + C::oR);
+  float *sDh = reinterpret_cast<float *>(smem + C::oD);
+  float *sDdh = reinterpret_cast<float *>(smem + C::oDd);
   // gate buffer (per chunk parity): g_r | beta_r (0 past the chunk end) |
   // e^{g_r} | e^{g_L - g_r} (0 past the end) | [0] = e^{g_L}
   float *sGate0 = reinterpret_cast<float *>(smem + C::oGate);
@@ -155,7 +139,7 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
   f32x4 pk[C::NKP], pq[C::NKP];
   f32x4 ptau[C::NTF], ctau[C::NTF];
   // V[t0 + 16 cb + (l & 15)][row0 + 4 (l >> 4) .. + 3]
-  using VRaw = typename std::conditional<BF, uint2, f32x4>::type;
+  using VRaw = f32x4;
   VRaw pvv, cvv;
   // gates are carried as loaded (no conversion) so that issuing the next
   // chunk's loads never waits for them
@@ -179,23 +163,10 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
     // Tau rows 16 cb + (l & 15) of this chunk
     const float *tau = p.tau + (slot * H + h) * (int64_t)kRecFloats + tau_off(cb) + (l & 15) * 16 * (cb + 1);
     const int ncol = 16 * (cb + 1);
-    if constexpr (BF) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int s0 = 32 * ks + 8 * (l >> 4);
-        ptau[2 * ks] = zero4();
-        ptau[2 * ks + 1] = zero4();
-        if (s0 < ncol) {
-          ptau[2 * ks] = *reinterpret_cast<const f32x4 *>(tau + s0);
-          ptau[2 * ks + 1] = *reinterpret_cast<const f32x4 *>(tau + s0 + 4);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int s = 4 * i + (l >> 4);
-        ptau[i >> 2][i & 3] = (s < ncol) ? tau[s] : 0.f;
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int s = 4 * i + (l >> 4);
+      ptau[i >> 2][i & 3] = (s < ncol) ? tau[s] : 0.f;
     }
     pvv = VRaw{};
     const int r = 16 * cb + (l & 15);
@@ -223,21 +194,16 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
       const int s = tid + i * NT;
       if (s < CH * C::KSEG) {
         const int r = s / C::KSEG, seg = s % C::KSEG;
-        if constexpr (BF) {
-          *reinterpret_cast<f32x4 *>(sKb + r * C::LDK + seg * C::VEC) = pk[i];
-          if (WANT_O) *reinterpret_cast<f32x4 *>(sQ + r * C::LDK + seg * C::VEC) = pq[i];
-        } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sKb[r * C::LDK + seg * 4 + e] = pk[i][e];
-            if (WANT_O) sQ[r * C::LDK + seg * 4 + e] = pq[i][e];
-          }
+        for (int e = 0; e < 4; ++e) {
+          sKb[r * C::LDK + seg * 4 + e] = pk[i][e];
+          if (WANT_O) sQ[r * C::LDK + seg * 4 + e] = pq[i][e];
         }
       }
     }
     if (w == 0) {
       float *sGb = sGate0 + kb * (C::GBYTES / 4);
-      const float g = wave_inclusive_scan((l < Lc) ? logf(to_f32(pa)) : 0.f);
+      const float g = wave_inclusive_scan((l < Lc) ? log_gate(to_f32(pa)) : 0.f);
       const float gL = lane_value(g, Lc - 1);
       sGb[l] = g;
       sGb[CH + l] = (l < Lc) ? to_f32(pb) : 0.f;
@@ -253,12 +219,7 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
 #pragma unroll
     for (int u = 0; u < C::SPW; ++u) {
       const int ct = w + u * NW;
-      if (ct < C::NST) {
-        if constexpr (BF)
-          store_tile_planes(sSh, sSl, C::LDSP, 0, 16 * ct, sacc[u]);
-        else
-          store_tile(sSh, C::LDSP, 0, 16 * ct, sacc[u]);
-      }
+      if (ct < C::NST) store_tile(sSh, C::LDSP, 0, 16 * ct, sacc[u]);
     }
   };
 
@@ -281,35 +242,17 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
     // ================= P1: Y -> R ; Z, P =================
     {
       f32x4 c = zero4();
-      if constexpr (BF)
-        mma_bf16<2, 1>(c, Planes{sSh, sSl, C::LDSP}, RowMajor<bf16>{sK, C::LDK}, 0, 16 * cb, 0, DK);
-      else
-        mma_f32(c, RowMajor<float>{sSh, C::LDSP}, RowMajor<float>{sK, C::LDK}, 0, 16 * cb, 0, DK);
+      mma_f32(c, RowMajor<float>{sSh, C::LDSP}, RowMajor<float>{sK, C::LDK}, 0, 16 * cb, 0, DK);
       const int r = 16 * cb + (l & 15);
       const float bet = sBeta[r], gam = sGam[r];
-      float vj[4];
-      if constexpr (BF) {
-        const bf16 *vb = reinterpret_cast<const bf16 *>(&cvv);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vj[i] = (float)vb[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vj[i] = cvv[i];
-      }
       f32x4 rv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rv[i] = bet * (vj[i] - gam * c[i]);
-      if constexpr (BF)
-        store_tile_planes(sRh, sRl, C::LDRP, 0, 16 * cb, rv);
-      else
-        store_tile(sRh, C::LDRP, 0, 16 * cb, rv);
+      for (int i = 0; i < 4; ++i) rv[i] = bet * (cvv[i] - gam * c[i]);
+      store_tile(sRh, C::LDRP, 0, 16 * cb, rv);
     }
     f32x4 oacc = zero4();
     if (WANT_O) {
-      if constexpr (BF)
-        mma_bf16<2, 1>(oacc, Planes{sSh, sSl, C::LDSP}, RowMajor<bf16>{sQ, C::LDK}, 0, 16 * cb, 0, DK);
-      else
-        mma_f32(oacc, RowMajor<float>{sSh, C::LDSP}, RowMajor<float>{sQ, C::LDK}, 0, 16 * cb, 0, DK);
+      mma_f32(oacc, RowMajor<float>{sSh, C::LDSP}, RowMajor<float>{sQ, C::LDK}, 0, 16 * cb, 0, DK);
       const float gam = sGam[16 * cb + (l & 15)];
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[i] *= gam;
@@ -324,10 +267,7 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
           continue;
         }
         f32x4 c = zero4();
-        if constexpr (BF)
-          mma_bf16<1, 1>(c, RowMajor<bf16>{sQ, C::LDK}, RowMajor<bf16>{sK, C::LDK}, 16 * bi, 16 * bj, 0, DK);
-        else
-          mma_f32(c, RowMajor<float>{sQ, C::LDK}, RowMajor<float>{sK, C::LDK}, 16 * bi, 16 * bj, 0, DK);
+        mma_f32(c, RowMajor<float>{sQ, C::LDK}, RowMajor<float>{sK, C::LDK}, 16 * bi, 16 * bj, 0, DK);
         const float gc = sG[col];
         const f32x4 gr = *reinterpret_cast<const f32x4 *>(sG + rb);
 #pragma unroll
@@ -339,50 +279,24 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
     // ================= P2: D = R Tau^T =================
     {
       f32x4 c = zero4();
-      if constexpr (BF) {
-        const int nks = (cb + 2) >> 1;
-        const int rr = l & 15, kq = 8 * (l >> 4);
+      const int rr = l & 15, kk = l >> 4;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (ks < nks) {
-            bf16x8 ah, al_, bh, bl;
-            load8<true>(Planes{sRh, sRl, C::LDRP}, rr, 32 * ks + kq, ah, al_);
-            const float xb[8] = {ctau[2 * ks][0], ctau[2 * ks][1], ctau[2 * ks][2], ctau[2 * ks][3],
-                                 ctau[2 * ks + 1][0], ctau[2 * ks + 1][1], ctau[2 * ks + 1][2], ctau[2 * ks + 1][3]};
-            split8(xb, bh, bl);
-            c = mfma_bf16(ah, bh, c);
-            c = mfma_bf16(ah, bl, c);
-            c = mfma_bf16(al_, bh, c);
-          }
-        }
-      } else {
-        const int rr = l & 15, kk = l >> 4;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (i < 4 * (cb + 1)) c = mfma_f32(sRh[rr * C::LDRP + 4 * i + kk], ctau[i >> 2][i & 3], c);
-        }
+      for (int i = 0; i < 16; ++i) {
+        if (i < 4 * (cb + 1)) c = mfma_f32(sRh[rr * C::LDRP + 4 * i + kk], ctau[i >> 2][i & 3], c);
       }
       const float dec = sDec[16 * cb + (l & 15)];
       f32x4 cd;
 #pragma unroll
       for (int i = 0; i < 4; ++i) cd[i] = c[i] * dec;
-      if constexpr (BF) {
-        if (WANT_O) store_tile_planes(sDh, sDl, C::LDRP, 0, 16 * cb, c);
-        store_tile_planes(sDdh, sDdl, C::LDRP, 0, 16 * cb, cd);
-      } else {
-        if (WANT_O) store_tile(sDh, C::LDRP, 0, 16 * cb, c);
-        store_tile(sDdh, C::LDRP, 0, 16 * cb, cd);
-      }
+      if (WANT_O) store_tile(sDh, C::LDRP, 0, 16 * cb, c);
+      store_tile(sDdh, C::LDRP, 0, 16 * cb, cd);
     }
     lds_barrier();
 
     // ================= P3: outputs; state update; stage the next chunk =================
     if (WANT_O) {
-      const int kend = BF ? 32 * ((cb + 2) >> 1) : 16 * (cb + 1);
-      if constexpr (BF)
-        mma_bf16<2, 2>(oacc, Planes{sDh, sDl, C::LDRP}, RowMajor<float>{sP, C::LDC}, 0, 16 * cb, 0, kend);
-      else
-        mma_f32(oacc, RowMajor<float>{sDh, C::LDRP}, RowMajor<float>{sP, C::LDC}, 0, 16 * cb, 0, kend);
+      const int kend = 16 * (cb + 1);
+      mma_f32(oacc, RowMajor<float>{sDh, C::LDRP}, RowMajor<float>{sP, C::LDC}, 0, 16 * cb, 0, kend);
       const int r = 16 * cb + (l & 15);
       if (r < Lc) {
         const int64_t base = ((int64_t)(t0 + r) * H + h) * DV + row0 + 4 * (l >> 4);
@@ -404,10 +318,7 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
         if (ct < C::NST) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) sacc[u][i] *= gl;
-          if constexpr (BF)
-            mma_bf16<2, 1>(sacc[u], Planes{sDdh, sDdl, C::LDRP}, ColMajor<bf16>{sK, C::LDK}, 0, 16 * ct, 0, CH);
-          else
-            mma_f32(sacc[u], RowMajor<float>{sDdh, C::LDRP}, ColMajor<float>{sK, C::LDK}, 0, 16 * ct, 0, CH);
+          mma_f32(sacc[u], RowMajor<float>{sDdh, C::LDRP}, ColMajor<float>{sK, C::LDK}, 0, 16 * ct, 0, CH);
         }
       }
     }
@@ -440,30 +351,25 @@ __global__ void __launch_bounds__(NT) chain_kernel(ChainLaunch p, int n_items) {
   }
 }
 
-template <class Tin, int DK, bool WANT_O>
+template <int DK, bool WANT_O>
 hipError_t launch_t(const ChainLaunch &p, hipStream_t stream) {
   const int64_t items = (int64_t)p.n_seqs * p.H * (p.tiles_T + p.tiles_S);
   if (items <= 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((chain_kernel<Tin, DK, WANT_O>), dim3((unsigned)grid), dim3(NT), 0, stream, p, (int)items);
-  return hipGetLastError();
+  return launch_kernel(chain_kernel<DK, WANT_O>, dim3((unsigned)grid), dim3(NT), 0, stream, p, (int)items);
 }
 
-template <class Tin, int DK>
+template <int DK>
 hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
-  return p.o ? launch_t<Tin, DK, true>(p, stream) : launch_t<Tin, DK, false>(p, stream);
+  return p.o ? launch_t<DK, true>(p, stream) : launch_t<DK, false>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_chain(const ChainLaunch &p, hipStream_t stream) {
-  if (p.in_bf16) {
-    if (p.dk == 64) return launch_dk<bf16, 64>(p, stream);
-    if (p.dk == 128) return launch_dk<bf16, 128>(p, stream);
-  } else {
-    if (p.dk == 64) return launch_dk<float, 64>(p, stream);
-    if (p.dk == 128) return launch_dk<float, 128>(p, stream);
-  }
+  if (p.in_bf16) return hipErrorInvalidValue;   // bf16 inputs: launch_chain_bf16
+  if (p.dk == 64) return launch_dk<64>(p, stream);
+  if (p.dk == 128) return launch_dk<128>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -321,7 +321,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   auto gates = [&](int b, int Lc) {
     if (w != 0) return;
     float *sG = sG0 + b * C::GN;
-    const float g = wave_inclusive_scan((l < Lc) ? logf(__uint_as_float((unsigned)pa << 16)) : 0.f);
+    const float g = wave_inclusive_scan((l < Lc) ? log_gate(__uint_as_float((unsigned)pa << 16)) : 0.f);
     const float gL = lane_value(g, Lc - 1);
     sG[G_EG + l] = __expf(g);
     sG[G_DEC + l] = (l < Lc) ? __expf(gL - g) : 0.f;
@@ -854,9 +854,8 @@ hipError_t launch_b(const ChainLaunch &p, hipStream_t stream) {
   const int64_t items = (int64_t)p.n_seqs * p.H * per_nh;
   if (items <= 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((chain_bf16_kernel<DK, WANT_O, NW, RT, FUSED>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, p,
-                     (int)items);
-  return hipGetLastError();
+  return launch_kernel(chain_bf16_kernel<DK, WANT_O, NW, RT, FUSED>, dim3((unsigned)grid), dim3(NW * 64), 0, stream, p,
+                       (int)items);
 }
 
 template <int DK>

@@ -59,9 +59,8 @@ __global__ void __launch_bounds__(FNW * 64) op_frag_kernel(const float *T, char 
 template <int DK>
 hipError_t launch_of(const float *T, int64_t n_ops, void *frag, hipStream_t stream) {
   if (n_ops <= 0) return hipSuccess;
-  hipLaunchKernelGGL((op_frag_kernel<DK>), dim3((unsigned)(n_ops * (DK / 32))), dim3(FNW * 64), 0, stream, T,
-                     static_cast<char *>(frag));
-  return hipGetLastError();
+  return launch_kernel(op_frag_kernel<DK>, dim3((unsigned)(n_ops * (DK / 32))), dim3(FNW * 64), 0, stream, T,
+                       static_cast<char *>(frag));
 }
 
 // ---------------------------------------------------------------------------
@@ -241,8 +240,7 @@ hipError_t launch_sc(const SegComposeLaunch &p, hipStream_t stream) {
   const int64_t items = (int64_t)p.n_seqs * p.H * (p.dv / 32);
   if (items <= 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((seg_compose_kernel<DK>), dim3((unsigned)grid), dim3(SNW * 64), 0, stream, p, (int)items);
-  return hipGetLastError();
+  return launch_kernel(seg_compose_kernel<DK>, dim3((unsigned)grid), dim3(SNW * 64), 0, stream, p, (int)items);
 }
 
 }  // namespace

@@ -112,10 +112,8 @@ hipError_t launch_d(const DecodeLaunch &p, hipStream_t stream) {
   const int64_t items = (int64_t)p.n_seqs * p.H;
   if (items <= 0) return hipSuccess;
   if (p.in_bf16)
-    hipLaunchKernelGGL((decode_kernel<DK, bf16>), dim3((unsigned)items), dim3(DNW * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_kernel<DK, float>), dim3((unsigned)items), dim3(DNW * 64), 0, stream, p);
-  return hipGetLastError();
+    return launch_kernel(decode_kernel<DK, bf16>, dim3((unsigned)items), dim3(DNW * 64), 0, stream, p);
+  return launch_kernel(decode_kernel<DK, float>, dim3((unsigned)items), dim3(DNW * 64), 0, stream, p);
 }
 
 }  // namespace

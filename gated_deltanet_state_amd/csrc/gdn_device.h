@@ -231,6 +231,16 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
+// log(alpha) of a gate with a finite floor.  Decays are formed as
+// exp(g_r - g_s) from cumulative sums g of these values; a gate of 0 (or one
+// below e^kLogGateFloor, including subnormals) would make g = -inf and
+// (-inf) - (-inf) = NaN.  With the floor such a gate scales the carried
+// state by e^-60 (about 8.8e-27) instead of 0: far below any tolerance,
+// while 64 floored gates in one chunk keep |g| <= 3840, where the fp32
+// rounding of the sums stays near 1e-4 absolute.
+constexpr float kLogGateFloor = -60.f;
+__device__ __forceinline__ float log_gate(float alpha) { return fmaxf(logf(alpha), kLogGateFloor); }
+
 // ---------------------------------------------------------------------------
 // Fragments with a permuted contraction index.  A C-layout 16 x 16 result
 // (lane l holds rows 4 (l >> 4) .. + 3 of column l & 15) is used directly as

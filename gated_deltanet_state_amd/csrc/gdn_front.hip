@@ -143,10 +143,8 @@ hipError_t launch_f(const FrontLaunch &p, hipStream_t stream) {
   const int64_t want = (n_rows + FU * (FNT / 16) - 1) / (FU * (FNT / 16));
   const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
   if (p.in_bf16)
-    hipLaunchKernelGGL((front_kernel<DK, bf16>), dim3(grid), dim3(FNT), 0, stream, p);
-  else
-    hipLaunchKernelGGL((front_kernel<DK, float>), dim3(grid), dim3(FNT), 0, stream, p);
-  return hipGetLastError();
+    return launch_kernel(front_kernel<DK, bf16>, dim3(grid), dim3(FNT), 0, stream, p);
+  return launch_kernel(front_kernel<DK, float>, dim3(grid), dim3(FNT), 0, stream, p);
 }
 
 }  // namespace

@@ -6,7 +6,27 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace gdn {
+
+// Launch `kernel` on `stream` and return the status of this launch alone.
+// (A triple-chevron launch reports its error only through hipGetLastError,
+// which also returns errors left by earlier, unrelated calls of the thread.)
+template <typename... KArgs, size_t... I>
+inline hipError_t launch_tuple(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                               std::tuple<KArgs...> &args, std::index_sequence<I...>) {
+  void *ptrs[] = {static_cast<void *>(&std::get<I>(args))...};
+  return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, shmem, stream);
+}
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                                Args &&...args) {
+  static_assert(sizeof...(KArgs) > 0 && sizeof...(KArgs) == sizeof...(Args), "kernel arguments");
+  std::tuple<KArgs...> a(std::forward<Args>(args)...);
+  return launch_tuple(kernel, grid, block, shmem, stream, a, std::index_sequence_for<KArgs...>{});
+}
 
 // ---------------------------------------------------------------------------
 // Chunk slots.  Sequence n (tokens cu[n] .. cu[n+1]-1) is cut into 64-token
@@ -167,7 +187,6 @@ hipError_t launch_prep(const PrepLaunch &p, hipStream_t stream);        // dispa
 hipError_t launch_prep_bf16(const PrepLaunch &p, hipStream_t stream);
 hipError_t launch_chain(const ChainLaunch &p, hipStream_t stream);        // fp32 inputs
 hipError_t launch_chain_bf16(const ChainLaunch &p, hipStream_t stream);   // bf16 inputs
-hipError_t launch_chain_dks(const ChainLaunch &p, hipStream_t stream);    // bf16, state only, few row tiles
 // fp32 operators [n_ops, dk, dk] into composition fragments (n_ops * dk * dk * 4 bytes)
 hipError_t launch_op_frags(const float *T, int64_t n_ops, int32_t dk, void *frag, hipStream_t stream);
 hipError_t launch_seg_compose(const SegComposeLaunch &p, hipStream_t stream);

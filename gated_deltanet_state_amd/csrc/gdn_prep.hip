@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
     float g = 0.f, b = 0.f;
     if (l < Lc) {
       const int64_t gi = (int64_t)(t0 + l) * H + h;
-      g = logf(ld_in(reinterpret_cast<const Tin *>(p.alpha), gi));
+      g = log_gate(ld_in(reinterpret_cast<const Tin *>(p.alpha), gi));
       b = ld_in(reinterpret_cast<const Tin *>(p.beta), gi);
     }
     g = wave_inclusive_scan(g);
@@ -191,8 +191,7 @@ __global__ void __launch_bounds__(PNT) prep_kernel(PrepLaunch p) {
 template <class Tin, int DK>
 hipError_t launch_p(const PrepLaunch &p, hipStream_t stream) {
   if (p.n_slots <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prep_kernel<Tin, DK>), dim3((unsigned)p.n_slots, (unsigned)p.H), dim3(PNT), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(prep_kernel<Tin, DK>, dim3((unsigned)p.n_slots, (unsigned)p.H), dim3(PNT), 0, stream, p);
 }
 
 }  // namespace

@@ -65,9 +65,8 @@ __global__ void __launch_bounds__(PW * 64) prep_bf16_kernel(PrepLaunch p) {
 template <int DK>
 hipError_t launch_pb(const PrepLaunch &p, hipStream_t stream) {
   if (p.n_slots <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prep_bf16_kernel<DK>), dim3((unsigned)((p.n_slots + PW - 1) / PW), (unsigned)p.H), dim3(PW * 64),
-                     0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(prep_bf16_kernel<DK>, dim3((unsigned)((p.n_slots + PW - 1) / PW), (unsigned)p.H),
+                       dim3(PW * 64), 0, stream, p);
 }
 
 }  // namespace

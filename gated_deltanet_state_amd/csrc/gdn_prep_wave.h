@@ -100,7 +100,7 @@ __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 
     float g = 0.f, b = 0.f;
     if (l < Lc) {
       const int64_t gi = (int64_t)(t0 + l) * H + h;
-      g = logf((float)alpha[gi]);
+      g = log_gate((float)alpha[gi]);
       b = (float)beta[gi];
     }
     const float gs = wave_inclusive_scan(g);

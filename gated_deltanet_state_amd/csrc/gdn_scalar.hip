@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(4 * DV) __attribute__((amdgpu_waves_per_eu(MIN
       if (e < SB * (PK + PV)) *reinterpret_cast<uint4 *>((isk ? sK + rr * LDK : sV + rr * LDV) + q * EPP) = pre[j];
     }
     if (w == 0) {
-      const float P = wave_inclusive_scan(logf(pa));
+      const float P = wave_inclusive_scan(log_gate(pa));
       const float tot = lane_value(P, 63);
       if (l < SB) sU[l] = pb * later * expf(tot - P);
       later *= expf(tot);
@@ -207,11 +207,9 @@ hipError_t launch_op(const ScalarOpLaunch &p, hipStream_t stream) {
   const int64_t items = (int64_t)p.n_chunks * p.H;
   if (items <= 0) return hipSuccess;
   if (p.in_bf16)
-    hipLaunchKernelGGL((scalar_op_kernel<DK, DV, bf16, (DK == 128 && DV == 128) ? 4 : 1>), dim3((unsigned)items),
-                       dim3(4 * DV), 0, stream, p);
-  else
-    hipLaunchKernelGGL((scalar_op_kernel<DK, DV, float, 1>), dim3((unsigned)items), dim3(4 * DV), 0, stream, p);
-  return hipGetLastError();
+    return launch_kernel(scalar_op_kernel<DK, DV, bf16, (DK == 128 && DV == 128) ? 4 : 1>, dim3((unsigned)items),
+                         dim3(4 * DV), 0, stream, p);
+  return launch_kernel(scalar_op_kernel<DK, DV, float, 1>, dim3((unsigned)items), dim3(4 * DV), 0, stream, p);
 }
 
 }  // namespace
@@ -227,8 +225,7 @@ hipError_t launch_scalar_op(const ScalarOpLaunch &p, hipStream_t stream) {
 hipError_t launch_scalar_compose(const ScalarComposeLaunch &p, hipStream_t stream) {
   const int64_t n4 = (int64_t)p.H * p.dv * p.dk / 4;
   if (n4 <= 0) return hipSuccess;
-  hipLaunchKernelGGL(scalar_compose_kernel, dim3((unsigned)((n4 + SNT - 1) / SNT)), dim3(SNT), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(scalar_compose_kernel, dim3((unsigned)((n4 + SNT - 1) / SNT)), dim3(SNT), 0, stream, p);
 }
 
 }  // namespace gdn

@@ -10,7 +10,9 @@
  * longer message is available from gdn_last_error(), per calling thread).
  * Device-side data are not validated: cu_seqlens / cu_chunks must be
  * nondecreasing with first entry 0 and last entry n_tokens, and every gate
- * alpha must lie in (0, 1].
+ * alpha must lie in [0, 1].  The kernels take log(alpha) with a floor of -60:
+ * a gate below e^-60 (about 8.8e-27), 0 included, acts as e^-60, i.e. it
+ * scales the carried state by that factor instead of erasing it exactly.
  *
  * Pointer arguments are DEVICE pointers unless stated otherwise, 16-byte
  * aligned (GDN_ERR_ALIGNMENT otherwise), row-major and contiguous.
@@ -37,8 +39,10 @@ extern "C" {
 
 /* 1: gdn_replay, gdn_chunk_operator, gdn_compose and their helpers.
  * 2: adds gdn_decode, gdn_front_end, gdn_scalar_chunk_operator and
- *    gdn_scalar_compose; the version 1 calls are unchanged. */
-#define GDN_ABI_VERSION 2
+ *    gdn_scalar_compose; the version 1 calls are unchanged.
+ * 3: adds gdn_replay_segmented; gates alpha = 0 are accepted (see above);
+ *    the earlier calls are unchanged. */
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -47,7 +51,9 @@ typedef enum gdn_status {
   GDN_ERR_UNSUPPORTED = 3,  /* a size or dtype the library has no kernel for    */
   GDN_ERR_ALIGNMENT = 4,    /* a pointer is not 16-byte aligned                  */
   GDN_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required        */
-  GDN_ERR_HIP = 6           /* a HIP launch failed; see gdn_last_error()         */
+  GDN_ERR_HIP = 6           /* one of this call's own kernel launches failed
+                               (errors left by earlier calls are not
+                               reported); see gdn_last_error()            */
 } gdn_status;
 
 typedef enum gdn_dtype {
@@ -66,7 +72,7 @@ typedef void *gdn_stream_t;
  *   q      [T, H, dk]  in_dtype   may be NULL when o is NULL
  *   k      [T, H, dk]  in_dtype   keys (used as given: no normalisation, no scale)
  *   v      [T, H, dv]  in_dtype
- *   alpha  [T, H]      in_dtype   gates in (0, 1]
+ *   alpha  [T, H]      in_dtype   gates in [0, 1]
  *   beta   [T, H]      in_dtype
  *   S0     [n_seqs, H, dv, dk] fp32 starting states, or NULL for zero
  *   cu_seqlens [n_seqs + 1] int32 (device): sequence n is tokens
@@ -89,8 +95,46 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v,
                       gdn_dtype o_dtype, float *S_final, void *workspace,
                       size_t workspace_bytes, gdn_stream_t stream);
 
+/* Workspace bytes for gdn_replay with these sizes (enough for a state-only
+ * call and a call with outputs, either dtype).  The split of long bf16
+ * replays into time segments, and so the size, depends on the compute-unit
+ * count of the current device (read once per device); call it with the
+ * device of the replay's stream current. */
 size_t gdn_replay_workspace_bytes(int32_t n_seqs, int64_t n_tokens,
                                   int32_t n_heads, int32_t dk, int32_t dv);
+
+/*
+ * gdn_replay_segmented -- gdn_replay with the number of time segments per
+ * sequence given by the caller instead of the library's cost model (tuning
+ * and tests).  A bf16 sequence cut into `segments` pieces of whole 64-token
+ * chunks runs as that many independent recurrences: the first from S0, the
+ * others as affine chunk operators (page "LinearKV: One Cached State
+ * Suffices for Position-Independent Caching in Hybrid LLMs", affine-operator
+ * and composition paragraphs) composed back to back; with outputs each
+ * segment then runs again from its composed start state.  The result equals
+ * gdn_replay's up to rounding.
+ *
+ *   segments: 0 = the cost model (exactly gdn_replay), 1 = no split,
+ *             2 .. 64 = that many segments (segments past a sequence's end
+ *             are empty).  fp32 inputs never split (the value is ignored).
+ *   Other arguments as gdn_replay; the workspace must hold
+ *   gdn_replay_segmented_workspace_bytes(..., segments) bytes.
+ *   Errors: GDN_ERR_BAD_SHAPE for segments outside 0 .. 64, otherwise as
+ *   gdn_replay.
+ */
+gdn_status gdn_replay_segmented(const void *q, const void *k, const void *v,
+                                const void *alpha, const void *beta,
+                                const float *S0, const int32_t *cu_seqlens,
+                                int32_t n_seqs, int64_t n_tokens,
+                                int32_t n_heads, int32_t dk, int32_t dv,
+                                gdn_dtype in_dtype, void *o, gdn_dtype o_dtype,
+                                float *S_final, int32_t segments,
+                                void *workspace, size_t workspace_bytes,
+                                gdn_stream_t stream);
+
+size_t gdn_replay_segmented_workspace_bytes(int32_t n_seqs, int64_t n_tokens,
+                                            int32_t n_heads, int32_t dk,
+                                            int32_t dv, int32_t segments);
 
 /*
  * gdn_chunk_operator -- the affine operator of each chunk.
@@ -182,7 +226,7 @@ gdn_status gdn_decode(const void *q, const void *k, const void *v,
  *     gamma[c]   = prod_t alpha_t
  *     S_local[c] = sum_t beta_t (prod_{s > t} alpha_s) v_t k_t^T
  *
- *   k [T, H, dk], v [T, H, dv], alpha, beta [T, H]   in_dtype (alpha > 0)
+ *   k [T, H, dk], v [T, H, dv], alpha, beta [T, H]   in_dtype (alpha in [0, 1])
  *   cu_chunks [n_chunks + 1] int32 (device), as for gdn_chunk_operator
  *          (an empty chunk gives gamma = 1, S_local = 0)
  *   gamma   [n_chunks, H] fp32 out
@@ -220,7 +264,7 @@ gdn_status gdn_scalar_compose(const float *S_in, const float *gamma,
  * strength from its logit.
  * Page: Tail-Replay, section 3 (the replayed hidden states produce the keys,
  * values, transitions and write strengths) and section 2 Eq. (1) (alpha in
- * (0, 1]).  Per (token, head), in fp32, each result rounded once to dtype:
+ * (0, 1]; an underflow to 0 is accepted by the calls above).  Per (token, head), in fp32, each result rounded once to dtype:
  *     q = q_raw / |q_raw|,  k = k_raw / |k_raw|   (a zero row gives zeros)
  *     alpha = exp(g),       beta = 1 / (1 + exp(-b))
  * The outputs are the q, k, alpha and beta that gdn_replay, gdn_chunk_operator
@@ -228,8 +272,11 @@ gdn_status gdn_scalar_compose(const float *S_in, const float *gamma,
  *
  *   q_raw, k_raw  [n_tokens, H, dk]  dtype   (q_raw may be NULL, then q is too)
  *   g, b          [n_tokens, H]      dtype   log-gate (g <= 0 keeps alpha in
- *                                            (0, 1]; larger g is not rejected)
- *                                            and beta logit
+ *                                            [0, 1]: exp(g) rounds to 0 below
+ *                                            about -104 in fp32 and -92 in
+ *                                            bf16, which the replay accepts;
+ *                                            larger g is not rejected) and
+ *                                            beta logit
  *   q, k          [n_tokens, H, dk]  dtype   outputs (may alias q_raw, k_raw)
  *   alpha, beta   [n_tokens, H]      dtype   outputs (may alias g, b)
  * Supported: dk in {64, 128}; dtypes F32 or BF16; 1 <= n_heads <= 65536;

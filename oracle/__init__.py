@@ -15,7 +15,8 @@ Cached State Suffices for Position-Independent Caching in Hybrid LLMs", the
 affine chunk operator and its back-to-back composition in context order.
 
 Parity pins (tests/test_oracle_pins.py) tie every function here to facts the
-pages and the mathematics fix; none of the six functions is "parity unpinned".
+pages and the mathematics fix, the two error measures (rel_fro,
+rel_fro_blocks) included; none of them is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -215,3 +216,31 @@ def rel_fro(x, ref) -> float:
     den = float(np.linalg.norm(ref.ravel()))
     num = float(np.linalg.norm((x - ref).ravel()))
     return num / den if den > 0 else num
+
+
+def rel_fro_blocks(x, ref, nred: int, floor: float = 0.0) -> np.ndarray:
+    """Relative Frobenius error of every block of a tensor.
+
+    A block is one index of the leading axes, the last ``nred`` axes being
+    reduced: for a state [N, H, dv, dk] with nred = 2 a block is one
+    (sequence, head) matrix; for outputs [T, H, dv] with nred = 1 a block is
+    one token row of one head.  Block b's error is
+        ||x_b - ref_b||_F / max(||ref_b||_F, floor * r),
+    r being the root mean square of ||ref_b||_F over all blocks, so that a
+    block whose reference is tiny against the rest is measured against a
+    fraction ``floor`` of the typical block (0 = plain relative error).
+    Where that denominator is 0 the block's absolute error is returned.
+    The per-block form of the LinearKV state probe's relative error.
+    """
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if x.shape != ref.shape or not 0 <= nred <= ref.ndim:
+        raise ValueError("rel_fro_blocks: shapes %s / %s, nred %d" % (x.shape, ref.shape, nred))
+    lead = ref.shape[:ref.ndim - nred]
+    d = (x - ref).reshape(lead + (-1,))
+    r = ref.reshape(lead + (-1,))
+    num = np.asarray(np.sqrt(np.sum(d * d, axis=-1)))
+    den = np.asarray(np.sqrt(np.sum(r * r, axis=-1)))
+    if floor > 0 and den.size:
+        den = np.maximum(den, floor * np.sqrt(np.mean(den * den)))
+    return np.divide(num, den, out=np.array(num), where=den > 0)

@@ -378,7 +378,54 @@ def pin_scalar_compose_is_concatenation(orc):
     assert np.max(np.abs(orc.scalar_compose(g, SL, S_in=S0) - (g1[0][:, None, None] * S0 + SL1[0]))) < 1e-12
 
 
+def pin_error_measures(orc):
+    """The relative Frobenius error and its per-block form on hand-worked
+    values (the LinearKV state probe's measure, ||x - ref|| / ||ref||)."""
+    import math
+    # ||(3, 4) - (0, 5)|| / ||(0, 5)|| = ||(3, -1)|| / 5 = sqrt(10) / 5
+    assert abs(orc.rel_fro([3.0, 4.0], [0.0, 5.0]) - math.sqrt(10) / 5) < 1e-15
+    # equal norms but different vectors: not zero
+    assert abs(orc.rel_fro([5.0, 0.0], [0.0, 5.0]) - math.sqrt(2)) < 1e-15
+    assert orc.rel_fro([1.0, 2.0], [1.0, 2.0]) == 0.0
+    # zero reference: the absolute norm of x
+    assert abs(orc.rel_fro([0.0, 3.0, 4.0], [0.0, 0.0, 0.0]) - 5.0) < 1e-15
+    # scale invariance in the pair
+    assert abs(orc.rel_fro([6.0, 8.0], [0.0, 10.0]) - math.sqrt(10) / 5) < 1e-15
+    # blocks: rows of a 2 x 2 array
+    x = np.array([[3.0, 4.0], [1.0, 1.0]])
+    ref = np.array([[0.0, 5.0], [1.0, 0.0]])
+    e = orc.rel_fro_blocks(x, ref, 1)
+    assert e.shape == (2,)
+    assert abs(e[0] - math.sqrt(10) / 5) < 1e-15 and abs(e[1] - 1.0) < 1e-15
+    # reducing every axis gives the whole-tensor error (one block)
+    whole = orc.rel_fro_blocks(x, ref, 2)
+    assert whole.shape == () and abs(float(whole) - orc.rel_fro(x, ref)) < 1e-15
+    assert abs(float(whole) - math.sqrt(11) / math.sqrt(26)) < 1e-15
+    # floor: a tiny reference row is measured against floor * rms(row norms)
+    x2 = np.array([[0.0, 5.0], [0.0, 0.2]])
+    ref2 = np.array([[0.0, 5.0], [0.0, 0.1]])
+    rms = math.sqrt((25.0 + 0.01) / 2)
+    e2 = orc.rel_fro_blocks(x2, ref2, 1, floor=0.1)
+    assert e2[0] == 0.0 and abs(e2[1] - 0.1 / (0.1 * rms)) < 1e-12
+    assert abs(orc.rel_fro_blocks(x2, ref2, 1)[1] - 1.0) < 1e-12
+    # blocks over leading axes [2, 3] with a reduced trailing pair [2, 2]
+    rng = _rng(99)
+    big = rng.standard_normal((2, 3, 2, 2))
+    noisy = big + 1e-3 * rng.standard_normal(big.shape)
+    eb = orc.rel_fro_blocks(noisy, big, 2)
+    assert eb.shape == (2, 3)
+    for i in range(2):
+        for j in range(3):
+            num = math.sqrt(sum((noisy[i, j] - big[i, j]).ravel() ** 2))
+            den = math.sqrt(sum(big[i, j].ravel() ** 2))
+            assert abs(eb[i, j] - num / den) < 1e-12
+    # zero reference block (empty sequence): absolute error
+    z = orc.rel_fro_blocks(np.array([[0.0, 0.0], [3.0, 4.0]]), np.zeros((2, 2)), 1)
+    assert z[0] == 0.0 and abs(z[1] - 5.0) < 1e-15
+
+
 ALL_PINS = [
+    pin_error_measures,
     pin_scalar_by_hand,
     pin_scalar_closed_forms,
     pin_scalar_compose_is_concatenation,

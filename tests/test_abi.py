@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
     for code, name in [(0, b"GDN_OK"), (1, b"GDN_ERR_NULL_POINTER"), (2, b"GDN_ERR_BAD_SHAPE"),
                        (3, b"GDN_ERR_UNSUPPORTED"), (4, b"GDN_ERR_ALIGNMENT"),
                        (5, b"GDN_ERR_WORKSPACE"), (6, b"GDN_ERR_HIP")]:
@@ -69,6 +69,22 @@ def test_replay_argument_checks(lib):
     assert b"k is not 16-byte aligned" in lib.gdn_last_error()
     assert replay(lib, S0=P + 8) == ALIGN
     assert replay(lib, o=P + 4) == ALIGN
+
+
+def test_segmented_replay_argument_checks(lib):
+    lib.gdn_replay_segmented.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int32, ctypes.c_int64] + \
+        [ctypes.c_int32] * 3 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int32,
+                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+
+    def rs(segments, k=P, ws=None, nbytes=0):
+        return lib.gdn_replay_segmented(P, k, P, P, P, None, P, 1, 10, 2, 64, 64, BF16, P, F32, P, segments, ws,
+                                        nbytes, None)
+    assert rs(-1) == SHAPE and b"segments" in lib.gdn_last_error()
+    assert rs(65) == SHAPE
+    assert rs(3, k=None) == NULLP
+    assert rs(3) == WS                              # workspace checked before any launch
+    assert b"gdn_replay_segmented" in lib.gdn_last_error()
+    assert rs(0, k=P + 2) == ALIGN
 
 
 def test_chunk_operator_argument_checks(lib):
@@ -154,11 +170,14 @@ def test_scalar_decay_argument_checks(lib):
     assert co(Si=P + 8) == ALIGN
 
 
-def test_workspace_queries(lib, monkeypatch):
+def test_workspace_queries(lib):
     # one 13 KiB record of per-chunk factors ((I + A)^{-1} diag(beta) fragments and the gates) per chunk
     # slot and head; slots = n_tokens / 64 + n_seqs + 1 (sequence n's chunk j sits
     # in slot floor(cu[n] / 64) + n + j)
-    monkeypatch.delenv("GDN_REPLAY_SEGMENTS", raising=False)
+    lib.gdn_replay_segmented_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.gdn_replay_segmented_workspace_bytes.restype = ctypes.c_size_t
+    seg_ws = lib.gdn_replay_segmented_workspace_bytes
     tau = lambda n_seqs, n_tokens, H: (n_tokens // 64 + n_seqs + 1) * H * 13312
     # 16 sequences x 32 heads already fill the chip: no time split, and room
     # for the longest-first order of the 16 sequences (256 bytes)
@@ -169,13 +188,14 @@ def test_workspace_queries(lib, monkeypatch):
     extra = lib.gdn_replay_workspace_bytes(1, 3277, 32, 128, 128) - tau(1, 3277, 32)
     per_seg = 32 * (128 * 128 + 128 * 128) * 4
     assert extra % per_seg == 0 and 2 <= extra // per_seg <= 16
-    # the override sets P directly
-    monkeypatch.setenv("GDN_REPLAY_SEGMENTS", "5")
+    # a forced segment count sets P directly
     # (room for the replay with outputs: segment operators, states and start states)
-    assert lib.gdn_replay_workspace_bytes(2, 300, 4, 64, 128) == tau(2, 300, 4) + 2 * 5 * 4 * (64 * 64 + 2 * 128 * 64) * 4
-    monkeypatch.setenv("GDN_REPLAY_SEGMENTS", "1")
-    assert lib.gdn_replay_workspace_bytes(1, 3277, 32, 128, 128) == tau(1, 3277, 32)
-    monkeypatch.delenv("GDN_REPLAY_SEGMENTS")
+    assert seg_ws(2, 300, 4, 64, 128, 5) == tau(2, 300, 4) + 2 * 5 * 4 * (64 * 64 + 2 * 128 * 64) * 4
+    assert seg_ws(1, 3277, 32, 128, 128, 1) == tau(1, 3277, 32)
+    # 0 is the cost model, exactly gdn_replay's size; out-of-range counts give 0
+    for args in [(1, 3277, 32, 128, 128), (16, 30000, 32, 128, 128), (2, 300, 4, 64, 128)]:
+        assert seg_ws(*args, 0) == lib.gdn_replay_workspace_bytes(*args)
+    assert seg_ws(1, 3277, 32, 128, 128, -1) == 0
     # gdn_compose: the operators converted to fragments, as many bytes as T_C
     assert lib.gdn_compose_workspace_bytes(64, 32, 128, 128) == 64 * 32 * 128 * 128 * 4
     assert lib.gdn_compose_workspace_bytes(0, 32, 128, 128) == 0

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import workloads
-from tests.gpu_helpers import TOL_BF16, TOL_F32, dev, oracle_replay, rel, to_np
+from tests.gpu_helpers import check_out, check_state, dev, oracle_replay, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -38,9 +38,8 @@ def test_decode_matches_oracle(dtype, dk, dv):
     o, S = gdn.decode(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S_in=torch.from_numpy(S_in).cuda())
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_replay(inp, S0=S_in.astype(np.float64))
-    eo, eS = rel(to_np(o), o_ref), rel(to_np(S), S_ref)
-    print("decode %s dk=%d dv=%d err_o %.2e err_S %.2e" % (dtype, dk, dv, eo, eS), flush=True)
-    assert eo <= TOL_F32 and eS <= TOL_F32
+    check_out("decode %s %dx%d o" % (dtype, dv, dk), to_np(o), o_ref, "f32")
+    check_state("decode %s %dx%d S" % (dtype, dv, dk), to_np(S), S_ref, "f32")
 
 
 def test_decode_zero_state_in_place_state_only_and_bf16_output():
@@ -52,7 +51,8 @@ def test_decode_zero_state_in_place_state_only_and_bf16_output():
     o, S = gdn.decode(d["q"], d["k"], d["v"], d["alpha"], d["beta"])
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_replay(inp)
-    assert rel(to_np(o), o_ref) <= TOL_F32 and rel(to_np(S), S_ref) <= TOL_F32
+    check_out("decode zero state o", to_np(o), o_ref, "f32")
+    check_state("decode zero state S", to_np(S), S_ref, "f32")
     # in place, state only
     S_in = states(N, H, 128, 128, 104)
     buf = torch.from_numpy(S_in).cuda()
@@ -60,13 +60,14 @@ def test_decode_zero_state_in_place_state_only_and_bf16_output():
     torch.cuda.synchronize()
     assert o2 is None and S2 is buf
     _, S_ref2 = oracle_replay(inp, S0=S_in.astype(np.float64), want_o=False)
-    assert rel(to_np(buf), S_ref2) <= TOL_F32
+    check_state("decode in place", to_np(buf), S_ref2, "f32")
     # bf16 outputs: rounding o to bf16 costs ~2e-3 of relative error
     o3, _ = gdn.decode(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S_in=torch.from_numpy(S_in).cuda(),
                        o_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     o_ref3, _ = oracle_replay(inp, S0=S_in.astype(np.float64))
-    assert o3.dtype == torch.bfloat16 and rel(to_np(o3), o_ref3) <= TOL_BF16
+    assert o3.dtype == torch.bfloat16
+    check_out("decode bf16 o", to_np(o3), o_ref3, "f32", o_bf16=True)
 
 
 def test_replay_then_decode_equals_longer_replay():
@@ -80,5 +81,5 @@ def test_replay_then_decode_equals_longer_replay():
     o1, S1 = gdn.decode(d["q"][T:], d["k"][T:], d["v"][T:], d["alpha"][T:], d["beta"][T:], S_in=S_T)
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_replay(inp)
-    assert rel(to_np(S1), S_ref) <= TOL_BF16
-    assert rel(to_np(o1), o_ref[T:]) <= TOL_BF16
+    check_state("replay then decode S", to_np(S1), S_ref, "bf16")
+    check_out("replay then decode o", to_np(o1), o_ref[T:], "bf16")

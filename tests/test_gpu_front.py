@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_helpers import TOL_BF16, oracle_replay, rel, to_np
+from tests.gpu_helpers import check_out, check_state, oracle_replay, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -104,6 +104,5 @@ def test_front_end_then_replay():
     inp = workloads.Inputs(dtype="bf16", H=2, dk=128, dv=128, cu_seqlens=raw.cu_seqlens, q=bits(rq), k=bits(rk),
                            v=raw.v, alpha=bits(ra), beta=bits(rb))
     o_ref, S_ref = oracle_replay(inp)
-    eo, eS = rel(to_np(o), o_ref), rel(to_np(S), S_ref)
-    print("front end + replay: err_o %.2e err_S %.2e" % (eo, eS), flush=True)
-    assert eo <= TOL_BF16 and eS <= TOL_BF16
+    check_out("front end + replay o", to_np(o), o_ref, "bf16")
+    check_state("front end + replay S", to_np(S), S_ref, "bf16")

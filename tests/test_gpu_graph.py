@@ -50,20 +50,18 @@ def _capture_and_check(fn):
 
 
 @pytest.mark.parametrize("case", ["packed_with_outputs", "split_state_only", "split_with_outputs"])
-def test_replay_under_graph_capture(case, monkeypatch):
+def test_replay_under_graph_capture(case):
     gdn, torch = _gdn()
     if case == "packed_with_outputs":
-        monkeypatch.delenv("GDN_REPLAY_SEGMENTS", raising=False)
         inp = workloads.generate([300, 0, 700, 65], H=2, dk=128, dv=128, dtype="bf16", seed=81)
-        want_o = True
+        want_o, P = True, None
     else:
-        monkeypatch.setenv("GDN_REPLAY_SEGMENTS", "3")
         inp = workloads.generate([1000], H=2, dk=128, dv=128, dtype="bf16", seed=82)
-        want_o = case == "split_with_outputs"
+        want_o, P = case == "split_with_outputs", 3
     d = dev(inp)
 
     def call():
-        o, S = gdn.replay(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu"], want_o=want_o)
+        o, S = gdn.replay(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu"], want_o=want_o, segments=P)
         return [S] + ([o] if want_o else [])
     _capture_and_check(call)
 

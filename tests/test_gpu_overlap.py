@@ -16,11 +16,10 @@ from tests.gpu_helpers import dev
 pytestmark = pytest.mark.gpu
 
 
-def test_replay_beside_pinned_copy(monkeypatch):
+def test_replay_beside_pinned_copy():
     import torch
     assert torch.cuda.is_available()
     import gated_deltanet_state_amd as gdn
-    monkeypatch.delenv("GDN_REPLAY_SEGMENTS", raising=False)
     inp = workloads.generate([1500, 700], H=4, dk=128, dv=128, dtype="bf16", seed=121)
     d = dev(inp)
     n = 16 << 20

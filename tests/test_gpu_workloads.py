@@ -1,21 +1,26 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times.  The GPU runs every head; the oracle recomputes a sample of
-heads (heads are independent, so a head's outputs depend only on its own
-inputs) and the comparison is over those heads' whole outputs."""
+eight heads spread over all 32 (heads are independent, so a head's outputs
+depend only on its own inputs), and the comparison covers those heads' whole
+outputs with the bars of tests/gpu_helpers.py: the whole-tensor relative
+error, the worst (sequence, head) state and the worst (token, head) output
+row."""
 import numpy as np
 import pytest
 
 import oracle
 import workloads
-from tests.gpu_helpers import dev, oracle_replay, rel, to_np
+from tests.gpu_helpers import BLOCK_TOL, TOL_BF16, check_close, check_out, check_state, dev, oracle_replay, rel, to_np
 
 pytestmark = pytest.mark.gpu
 
+HEADS = [0, 4, 9, 13, 18, 22, 27, 31]
 _CACHE = {}
 
 
 def wl(i):
     if i not in _CACHE:
+        _CACHE.clear()
         _CACHE[i] = workloads.make_workload(i)
     return _CACHE[i]
 
@@ -39,29 +44,25 @@ def test_workload1_tail_replay_state_only_all_heads():
     inp = wl(1)
     o, S = replay_all(inp, want_o=False)
     _, S_ref = oracle_replay(inp, want_o=False)
-    e = rel(to_np(S), S_ref)
-    print("workload 1 err_S %.3e" % e, flush=True)
-    assert e <= 3e-3
+    check_state("workload 1 S_final (32 heads)", to_np(S), S_ref, "bf16")
 
 
-@pytest.mark.parametrize("wid,heads", [(1, [0, 31]), (2, [0, 9, 31]), (3, [0, 17, 31])])
-def test_full_size_with_outputs_sampled_heads(wid, heads):
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_full_size_with_outputs_sampled_heads(wid):
     inp = wl(wid)
     o, S = replay_all(inp, want_o=True)
-    o_ref, S_ref = oracle_replay(inp, want_o=True, heads=heads)
-    eo = rel(to_np(o[:, heads]), o_ref)
-    eS = rel(to_np(S[:, heads]), S_ref)
-    print("workload %d heads %s err_o %.3e err_S %.3e" % (wid, heads, eo, eS), flush=True)
-    assert eo <= 3e-3 and eS <= 3e-3
+    o_ref, S_ref = oracle_replay(inp, want_o=True, heads=HEADS)
+    check_out("workload %d o heads %s" % (wid, HEADS), to_np(o[:, HEADS]), o_ref, "bf16")
+    check_state("workload %d S_final heads %s" % (wid, HEADS), to_np(S[:, HEADS]), S_ref, "bf16")
     # every head's outputs are finite; the state-only replay (which may run
-    # time-split and composed, rounding differently) meets the same bar and
-    # stays within twice the bar's noise of the replay with outputs
+    # time-split and composed, rounding differently) meets the same bars and
+    # stays within a few times the measured noise of the replay with outputs
     assert bool(o.isfinite().all())
     _, S2 = replay_all(inp, want_o=False)
-    eS2 = rel(to_np(S2[:, heads]), S_ref)
+    check_state("workload %d state-only S_final" % wid, to_np(S2[:, HEADS]), S_ref, "bf16")
     d = rel(to_np(S2), to_np(S).astype(np.float64))
-    print("state-only err_S %.3e, |S_state_only - S_with_o| / |S| %.3e" % (eS2, d), flush=True)
-    assert eS2 <= 3e-3 and d <= 1e-4
+    print("|S_state_only - S_with_o| / |S| %.3e" % d, flush=True)
+    assert d <= 1e-4
 
 
 def test_workload4_chunk_operators_and_composition():
@@ -73,14 +74,14 @@ def test_workload4_chunk_operators_and_composition():
     TC, SL = gdn.chunk_operator(d["k"], d["alpha"], d["beta"], cu, v=d["v"])
     S = gdn.compose(TC, SL)
     torch.cuda.synchronize()
-    heads = [0, 21]
     f = inp.f64
-    TC_ref, SL_ref = oracle.chunk_operator(f["k"][:, heads], f["alpha"][:, heads],
-                                           f["beta"][:, heads], bounds, v=f["v"][:, heads])
-    eT = rel(to_np(TC[:, heads]), TC_ref)
-    eL = rel(to_np(SL[:, heads]), SL_ref)
-    _, S_seq = oracle.replay(None, f["k"][:, heads], f["v"][:, heads], f["alpha"][:, heads],
-                             f["beta"][:, heads], [0, inp.n_tokens], want_o=False)
-    eC = rel(to_np(S[heads]), S_seq[0])
-    print("workload 4 err_T %.3e err_Sloc %.3e err_composed %.3e" % (eT, eL, eC), flush=True)
-    assert eT <= 3e-3 and eL <= 3e-3 and eC <= 3e-3
+    TC_ref, SL_ref = oracle.chunk_operator(f["k"][:, HEADS], f["alpha"][:, HEADS],
+                                           f["beta"][:, HEADS], bounds, v=f["v"][:, HEADS])
+    # T_C per (chunk, head), each against its own norm: with the workload gates
+    # a 512-token chunk's transition product is ~1e-18 in norm, and the
+    # kernels keep relative accuracy through the decays
+    check_close("workload 4 T_C", to_np(TC[:, HEADS]), TC_ref, 2, TOL_BF16, BLOCK_TOL["bf16"])
+    check_state("workload 4 S_local", to_np(SL[:, HEADS]), SL_ref, "bf16")
+    _, S_seq = oracle.replay(None, f["k"][:, HEADS], f["v"][:, HEADS], f["alpha"][:, HEADS],
+                             f["beta"][:, HEADS], [0, inp.n_tokens], want_o=False)
+    check_state("workload 4 composed", to_np(S[HEADS]), S_seq[0], "bf16")

@@ -65,6 +65,18 @@ PY_MUTANTS = {
     "scalar_gamma_sum": ("gamma[c] *= a[t]", "gamma[c] += a[t] - 1"),
     # composition without the decay of the incoming state
     "scalar_compose_no_decay": ("S = g[c][:, None, None] * S + SL[c]", "S = S + SL[c]"),
+    # the error measure as a difference of norms instead of the norm of the difference
+    "rel_fro_norm_difference": ("num = float(np.linalg.norm((x - ref).ravel()))",
+                                "num = abs(float(np.linalg.norm(x.ravel())) - den)"),
+    # the error measure not divided by the reference norm
+    "rel_fro_absolute": ("return num / den if den > 0 else num", "return num"),
+    # per-block errors divided by the whole tensor's norm
+    "blocks_global_denominator": ("den = np.asarray(np.sqrt(np.sum(r * r, axis=-1)))",
+                                  "den = np.full(num.shape, np.sqrt(np.sum(r * r)))"),
+    # per-block errors with the floor ignored
+    "blocks_no_floor": ("den = np.maximum(den, floor * np.sqrt(np.mean(den * den)))", "den = den"),
+    # per-block errors reduced over the wrong axes (leading instead of trailing)
+    "blocks_wrong_axes": ("lead = ref.shape[:ref.ndim - nred]", "lead = ref.shape[nred:]"),
 }
 
 

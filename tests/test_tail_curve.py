@@ -83,11 +83,16 @@ def test_gpu_tail_curve_matches_oracle(law):
     import torch
     import bench
     import gated_deltanet_state_amd as gdn
-    from tests.gpu_helpers import TOL_BF16
+    from tests.gpu_helpers import BLOCK_TOL
     ref = _stored()["laws"][law]["err"]
     got = bench.tail_curve_gpu(law, gdn, torch, np)
     print(law, " ".join("%.2e/%.2e" % (g, r) for g, r in zip(got, ref)), flush=True)
     for g, r in zip(got, ref):
-        # each GPU state is within TOL_BF16 of the oracle's (relative Frobenius),
-        # and ||S_tail|| <= (1 + err) ||S_full||
-        assert abs(g - r) <= TOL_BF16 * (2 + 2 * r)
+        # A curve point compares two GPU states, each within its element bar
+        # (1e-4 relative per (sequence, head); measured ~5e-6) of the oracle's
+        # state, so it moves by at most about the sum of the two errors,
+        # scaled by (1 + r) since ||S_tail|| <= (1 + r) ||S_full||.  Points
+        # well above that rounding level are also held to 1e-3 of their value.
+        assert abs(g - r) <= 2 * BLOCK_TOL["bf16"] * (1 + r), (g, r)
+        if r > 1e-2:
+            assert abs(g - r) <= 1e-3 * r, (g, r)

@@ -10,7 +10,13 @@ Recipe (one numpy PCG64 generator per call, seeded by the caller):
   2. q, k, v ~ N(0, 1) in float64 with shape [T_tot, H, d];
   3. beta-logit then alpha-logit ~ N(0, 1) with shape [T_tot, H];
   4. q and k are L2-normalised per (token, head); beta = sigmoid(x_beta);
-     alpha = exp(-c * softplus(x_alpha)) with c = 0.1 by default;
+     alpha = exp(-c * softplus(x_alpha)) with c = 0.1 by default (0.001 is
+     the slow-decay stress law, 5 the strong-decay law whose in-chunk
+     cumulative gates reach exp(-100) and below);
+  4b. optional, drawn after everything above so that the other recipes keep
+     their values: a per-(token, head) key scale s ~ U[lo, hi] (keys of
+     non-unit norm: k <- s k), then a fraction of the gates set to exactly 0
+     (a uniform draw per (token, head));
   5. values are rounded to float32 (round to nearest even) and, for bf16
      inputs, further to bfloat16 (round to nearest even).  The oracle is fed
      the rounded values, upcast exactly.
@@ -122,13 +128,16 @@ def _unit_rows(x):
 
 def generate(lengths, H: int, dk: int, dv: int, dtype: str = "bf16",
              seed: int = 0, gate_scale: float = 0.1, rng=None,
-             alpha_one: bool = False, beta_value: Optional[float] = None) -> Inputs:
+             alpha_one: bool = False, beta_value: Optional[float] = None,
+             key_scale: Optional[tuple] = None, alpha_zero_frac: float = 0.0) -> Inputs:
     """Draw one packed batch with the recipe in the module docstring.
 
     ``lengths``: per-sequence token counts (any may be 0).
     ``gate_scale``: c in alpha = exp(-c * softplus(x)); 0.1 is the workload law,
-    0.001 the slow-decay stress law.  ``alpha_one`` forces alpha = 1 and
-    ``beta_value`` forces a constant beta (stress / invariant cases).
+    0.001 the slow-decay stress law, 5 the strong-decay law.  ``alpha_one``
+    forces alpha = 1 and ``beta_value`` forces a constant beta (stress /
+    invariant cases).  ``key_scale`` = (lo, hi) scales each normalised key by
+    U[lo, hi]; ``alpha_zero_frac`` sets that fraction of the gates to 0.
     """
     if dtype not in ("f32", "bf16"):
         raise ValueError("dtype must be 'f32' or 'bf16'")
@@ -145,6 +154,10 @@ def generate(lengths, H: int, dk: int, dv: int, dtype: str = "bf16",
     q, k = _unit_rows(q), _unit_rows(k)
     beta = 1.0 / (1.0 + np.exp(-xb)) if beta_value is None else np.full((T, H), beta_value)
     alpha = np.ones((T, H)) if alpha_one else np.exp(-gate_scale * _softplus(xa))
+    if key_scale is not None:
+        k = k * rng.uniform(key_scale[0], key_scale[1], (T, H, 1))
+    if alpha_zero_frac > 0:
+        alpha = np.where(rng.uniform(0.0, 1.0, (T, H)) < alpha_zero_frac, 0.0, alpha)
     arrs = dict(q=q, k=k, v=v, alpha=alpha, beta=beta)
     rnd = bf16_bits if dtype == "bf16" else f32_round
     store = {name: rnd(a) for name, a in arrs.items()}
