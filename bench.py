@@ -152,8 +152,41 @@ def _counter_kib(folder, counter):
     return {k: sum(v.values()) / len(v) for k, v in per.items()}
 
 
+ISSUE_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                  "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "GRBM_GUI_ACTIVE"]
+
+
+def issue_table(mfma_dir, stats):
+    """Rows of the MFMA / issue table from one --pmc run of ISSUE_COUNTERS:
+    per kernel, the executed bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16
+    counts them in units of 512) over the kernel's average time from the
+    trace, as a fraction of the 2.52 PFLOP/s dense bf16 peak, and the vector,
+    MFMA, LDS and scalar instructions issued per wave."""
+    vals = {c: _counter_kib(mfma_dir, c) for c in ISSUE_COUNTERS}
+    avg_us = {_short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in stats}
+    rows = {}
+    for k in sorted(vals["SQ_WAVES"]):
+        if "rocclr" in k:
+            continue
+        waves = vals["SQ_WAVES"].get(k, 0.0) or float("nan")
+        flops = vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"].get(k, 0.0) * 512
+        t = avg_us.get(k)
+        rows[k] = dict(waves=waves, valu_per_wave=vals["SQ_INSTS_VALU"].get(k, 0.0) / waves,
+                       mfma_per_wave=vals["SQ_INSTS_MFMA"].get(k, 0.0) / waves,
+                       lds_per_wave=vals["SQ_INSTS_LDS"].get(k, 0.0) / waves,
+                       salu_per_wave=vals["SQ_INSTS_SALU"].get(k, 0.0) / waves,
+                       mfma_bf16_flops=flops,
+                       mfma_tflops=(flops / (t * 1e-6) / 1e12) if t else None,
+                       mfma_busy_cycles=vals["SQ_VALU_MFMA_BUSY_CYCLES"].get(k, 0.0),
+                       sq_busy_cycles=vals["SQ_BUSY_CYCLES"].get(k, 0.0),
+                       grbm_gui_active=vals["GRBM_GUI_ACTIVE"].get(k, 0.0))
+        if t:
+            rows[k]["mfma_frac_of_peak"] = rows[k]["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS
+    return rows
+
+
 def summarize_counters(wid, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, command="",
-                       name=None):
+                       name=None, mfma_dir=None):
     """profiles/<workload>.md and profiles/traffic_<workload>.json from
     rocprofv3 runs of this script: a --kernel-trace --stats run, one --pmc
     FETCH_SIZE run, one --pmc WRITE_SIZE run, and the same two counters on a
@@ -179,6 +212,9 @@ def summarize_counters(wid, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_
     rec = dict(workload=wname, sources_sha256=sources_sha256(),
                calibration=dict(copy_mib=cal_mib, fetch_factor=round(ff, 4), write_factor=round(wf, 4)),
                kernels=kernels, hbm_bytes_per_call=int(total))
+    issue = issue_table(mfma_dir, stats) if mfma_dir else None
+    if issue:
+        rec["issue"] = issue
     with open(os.path.join(ROOT, "profiles", "traffic_%s.json" % wname), "w") as f:
         json.dump(rec, f, indent=1)
     lines = ["# %s: kernel times and HBM traffic" % wname, "",
@@ -199,6 +235,22 @@ def summarize_counters(wid, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_
         lines.append("| %s | %.0f | %.0f | %.1f | %.1f |" % (k, v["fetch_kib"], v["write_kib"], v["fetch_bytes"] / 1e6,
                                                            v["write_bytes"] / 1e6))
     lines += ["", "HBM bytes per call: %.1f MB." % (total / 1e6), ""]
+    if issue:
+        lines += ["MFMA use and instruction issue per dispatch (one `--pmc` run of %s; executed bf16 MFMA "
+                  "flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, over the kernel's average time above, against "
+                  "the %.1f TFLOP/s dense bf16 peak; instructions per wave = SQ_INSTS_* / SQ_WAVES):"
+                  % (", ".join(ISSUE_COUNTERS), BF16_MFMA_PEAK_TFLOPS), "",
+                  "| kernel | waves | executed bf16 MFMA (GFLOP) | MFMA TFLOP/s | of bf16 peak | VALU / wave | "
+                  "MFMA / wave | LDS / wave | SALU / wave | SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE |",
+                  "|---|---|---|---|---|---|---|---|---|---|---|"]
+        for k, v in issue.items():
+            lines.append("| %s | %.0f | %.2f | %s | %s | %.0f | %.0f | %.0f | %.0f | %.3g | %.3g |" % (
+                k, v["waves"], v["mfma_bf16_flops"] / 1e9,
+                "%.1f" % v["mfma_tflops"] if v["mfma_tflops"] is not None else "-",
+                "%.1f%%" % (100 * v["mfma_frac_of_peak"]) if "mfma_frac_of_peak" in v else "-",
+                v["valu_per_wave"], v["mfma_per_wave"], v["lds_per_wave"], v["salu_per_wave"],
+                v["mfma_busy_cycles"], v["grbm_gui_active"]))
+        lines.append("")
     with open(os.path.join(ROOT, "profiles", "%s.md" % wname), "w") as f:
         f.write("\n".join(lines))
     print("wrote profiles/%s.md and profiles/traffic_%s.json" % (wname, wname))
@@ -534,6 +586,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs=5, metavar=("STATS", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="write profiles/ summaries from rocprofv3 output folders (no GPU needed)")
     ap.add_argument("--command", default="", help="with --summarize-counters: the command line profiled")
+    ap.add_argument("--issue-counters", default=None, metavar="DIR",
+                    help="with --summarize-counters: a --pmc run of the MFMA / issue counters (ISSUE_COUNTERS)")
     ap.add_argument("--tail-curve", action="store_true",
                     help="only report the tail-replay state error against the replayed fraction")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
@@ -552,7 +606,8 @@ def main():
     if args.summarize_counters:
         name = (("decode-%dx1-H32-d128-bf16" % args.decode) if args.decode else FRONT_NAME if args.front_end
                 else SCALAR_NAME if args.scalar_ops else None)
-        summarize_counters(args.workload, *args.summarize_counters, command=args.command, name=name)
+        summarize_counters(args.workload, *args.summarize_counters, command=args.command, name=name,
+                           mfma_dir=args.issue_counters)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the replay path is a single-GPU kernel library "
