@@ -13,6 +13,7 @@ Functions (same names as the C entry points, without the ``gdn_`` prefix):
          segments=None)      (gdn_replay, or gdn_replay_segmented when segments is given)
   chunk_operator(k, alpha, beta, cu_chunks, v=None)
   compose(T_C, S_local, S_in=None)
+  replay_noalloc(...)  (gdn_replay_noalloc: no workspace, the library's built-in scratch)
   decode, front_end, scalar_chunk_operator, scalar_compose
 
 Every call launches on ``stream`` (default: the current stream).  The
@@ -24,7 +25,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["front_end", "replay", "decode", "chunk_operator", "compose", "scalar_chunk_operator", "scalar_compose", "GdnError", "library", "LIB_PATH"]
+__all__ = ["front_end", "replay", "replay_noalloc", "decode", "chunk_operator", "compose", "scalar_chunk_operator", "scalar_compose", "GdnError", "library", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
@@ -57,6 +58,8 @@ def library():
     lib.gdn_replay_segmented.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint,
                                          vp, cint, vp, i32, vp, sz, vp]
     lib.gdn_replay_segmented_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
+    lib.gdn_replay_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint,
+                                       vp, cint, vp, vp]
     lib.gdn_chunk_operator.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint,
                                        vp, vp, vp, sz, vp]
     lib.gdn_chunk_operator_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
@@ -66,7 +69,7 @@ def library():
     lib.gdn_front_end.argtypes = [vp, vp, vp, vp, i64, i32, i32, cint, vp, vp, vp, vp, vp]
     lib.gdn_scalar_chunk_operator.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint, vp, vp, vp]
     lib.gdn_scalar_compose.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
-    for f in (lib.gdn_replay, lib.gdn_replay_segmented, lib.gdn_chunk_operator, lib.gdn_compose,
+    for f in (lib.gdn_replay, lib.gdn_replay_segmented, lib.gdn_replay_noalloc, lib.gdn_chunk_operator, lib.gdn_compose,
               lib.gdn_decode, lib.gdn_front_end, lib.gdn_scalar_chunk_operator, lib.gdn_scalar_compose):
         f.restype = cint
     for f in (lib.gdn_replay_workspace_bytes, lib.gdn_replay_segmented_workspace_bytes,
@@ -189,6 +192,42 @@ def replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=None,
         ws, ws_bytes = _workspace(lib.gdn_replay_segmented_workspace_bytes(N, T, H, dk, dv, int(segments)),
                                   k.device, stream)
         _check(lib.gdn_replay_segmented(*args, int(segments), _ptr(ws), ws_bytes, _stream_ptr(stream)))
+    return o, S
+
+
+def replay_noalloc(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=None,
+                   out=None, S_out=None, stream=None):
+    """replay() through gdn_replay_noalloc: no workspace is allocated; the
+    library's built-in per-GPU scratch serves instead (calls that overlap on
+    one GPU race on it).  Pass ``out`` / ``S_out`` to allocate nothing at all
+    (e.g. under graph capture); otherwise the outputs are allocated here.
+    """
+    torch = _torch()
+    lib = library()
+    for name, t in (("k", k), ("v", v), ("alpha", alpha), ("beta", beta),
+                    ("cu_seqlens", cu_seqlens), ("S0", S0)):
+        _dev(t, name)
+    if want_o:
+        _dev(q, "q")
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    in_code = _dtype_code(k.dtype)
+    for name, t in (("q", q if want_o else None), ("v", v), ("alpha", alpha), ("beta", beta)):
+        if t is not None and t.dtype != k.dtype:
+            raise TypeError("%s must have the dtype of k" % name)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    o, o_code = None, GDN_F32
+    if want_o:
+        o = out if out is not None else torch.empty((T, H, dv), dtype=o_dtype or torch.float32, device=k.device)
+        _dev(o, "out")
+        o_code = _dtype_code(o.dtype)
+    S = S_out if S_out is not None else torch.empty((N, H, dv, dk), dtype=torch.float32, device=k.device)
+    _dev(S, "S_out")
+    _check(lib.gdn_replay_noalloc(_ptr(q) if want_o else None, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                  _ptr(S0), _ptr(cu_seqlens), N, T, H, dk, dv, in_code, _ptr(o), o_code,
+                                  _ptr(S), _stream_ptr(stream)))
     return o, S
 
 

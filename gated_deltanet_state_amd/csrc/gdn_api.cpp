@@ -288,6 +288,38 @@ gdn_status replay_impl(const void *q, const void *k, const void *v, const void *
 }
 
 
+// ---------------------------------------------------------------------------
+// Built-in scratch of gdn_replay_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it only names a stand-in): the device address
+// of this GPU's copy comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address is used.
+// ---------------------------------------------------------------------------
+__device__ __attribute__((aligned(256))) char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// This device's copy of the scratch array (nullptr and a failed status if
+// the current device cannot be read or the symbol has no address).
+void *device_scratch(hipError_t &err) {
+  int dev = 0;
+  err = hipGetDevice(&dev);
+  if (err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -331,6 +363,33 @@ gdn_status gdn_replay_segmented(const void *q, const void *k, const void *v, con
     return fail(GDN_ERR_BAD_SHAPE, "gdn_replay_segmented: segments must be 0 .. %d (got %d)", kMaxSegments, segments);
   return replay_impl(q, k, v, alpha, beta, S0, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, in_dtype, o, o_dtype,
                      S_final, segments, workspace, workspace_bytes, stream, "gdn_replay_segmented");
+}
+
+gdn_status gdn_replay_noalloc(const void *q, const void *k, const void *v, const void *alpha, const void *beta,
+                              const float *S0, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
+                              int32_t n_heads, int32_t dk, int32_t dv, gdn_dtype in_dtype, void *o,
+                              gdn_dtype o_dtype, float *S_final, gdn_stream_t stream) {
+  // the sizes are checked first (host only), so an oversized call fails
+  // before the device is touched
+  if (n_seqs >= 1 && n_tokens >= 0 && n_heads >= 1 && supported_dim(dk) && supported_dim(dv) &&
+      valid_dtype(in_dtype) && n_tokens <= kMaxTokens && n_heads <= kMaxHeads) {
+    const bool bf = in_dtype == GDN_BF16;
+    const int32_t P = segments_for(bf, o != nullptr, 0, n_seqs, n_tokens, n_heads, dk, dv);
+    const size_t need = replay_need(bf, o != nullptr, P, n_seqs, n_tokens, n_heads, dk, dv);
+    if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+      return fail(GDN_ERR_WORKSPACE,
+                  "gdn_replay_noalloc: this replay needs %zu bytes of scratch, more than the built-in %zu; "
+                  "call gdn_replay with a workspace",
+                  need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+  }
+  hipError_t e = hipSuccess;
+  void *ws = nullptr;
+  if (k && v && alpha && beta && cu_seqlens && S_final) {
+    ws = device_scratch(e);
+    if (!ws) return fail(GDN_ERR_HIP, "gdn_replay_noalloc: no device address for the scratch: %s", hipGetErrorString(e));
+  }
+  return replay_impl(q, k, v, alpha, beta, S0, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, in_dtype, o, o_dtype,
+                     S_final, 0, ws, GDN_NOALLOC_SCRATCH_BYTES, stream, "gdn_replay_noalloc");
 }
 
 gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, const void *beta,

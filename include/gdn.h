@@ -40,8 +40,8 @@ extern "C" {
 /* 1: gdn_replay, gdn_chunk_operator, gdn_compose and their helpers.
  * 2: adds gdn_decode, gdn_front_end, gdn_scalar_chunk_operator and
  *    gdn_scalar_compose; the version 1 calls are unchanged.
- * 3: adds gdn_replay_segmented; gates alpha = 0 are accepted (see above);
- *    the earlier calls are unchanged. */
+ * 3: adds gdn_replay_segmented and gdn_replay_noalloc; gates alpha = 0
+ *    are accepted (see above); the earlier calls are unchanged. */
 #define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
@@ -135,6 +135,37 @@ gdn_status gdn_replay_segmented(const void *q, const void *k, const void *v,
 size_t gdn_replay_segmented_workspace_bytes(int32_t n_seqs, int64_t n_tokens,
                                             int32_t n_heads, int32_t dk,
                                             int32_t dv, int32_t segments);
+
+/*
+ * gdn_replay_noalloc -- gdn_replay for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels, with their scratch (per-chunk records,
+ * time-split segment operators and states, the longest-first sequence
+ * order) in a built-in device array of GDN_NOALLOC_SCRATCH_BYTES instead of
+ * a caller's workspace.  The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine.
+ *
+ *   Arguments as gdn_replay, without the workspace.
+ *   Each GPU the library runs on holds its own copy of the array (64 MiB)
+ *   from the library's load until the process ends; its device address is
+ *   looked up on the first call on each device (with that device current).
+ *   The array keeps the last call's contents; nothing in it needs to start
+ *   at zero.  Calls that overlap on one GPU (on different streams, or from
+ *   different threads without ordering) share the array and RACE: order
+ *   them on one stream.
+ *   Errors: GDN_ERR_WORKSPACE when the replay needs more scratch than the
+ *   array holds (e.g. more than ~4,700 (chunk, head) records); GDN_ERR_HIP
+ *   when the array's device address cannot be read; otherwise as gdn_replay.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+gdn_status gdn_replay_noalloc(const void *q, const void *k, const void *v,
+                              const void *alpha, const void *beta,
+                              const float *S0, const int32_t *cu_seqlens,
+                              int32_t n_seqs, int64_t n_tokens,
+                              int32_t n_heads, int32_t dk, int32_t dv,
+                              gdn_dtype in_dtype, void *o, gdn_dtype o_dtype,
+                              float *S_final, gdn_stream_t stream);
 
 /*
  * gdn_chunk_operator -- the affine operator of each chunk.
