@@ -49,7 +49,13 @@ def library():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError("libgdn.so is not built (run python -m gated_deltanet_state_amd.build)")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def declare(lib):
+    """Set the C signatures of the entry points on a loaded library (the
+    product library, or its host-sanitized build in the tests)."""
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     cint = ctypes.c_int
     lib.gdn_replay.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint,
@@ -81,7 +87,6 @@ def library():
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_abi_version.argtypes = []
     lib.gdn_abi_version.restype = cint
-    _lib = lib
     return lib
 
 

@@ -1,6 +1,6 @@
 """Build libgdn.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-Usage: python -m gated_deltanet_state_amd.build  (or build() from Python).
+Usage: python -m gated_deltanet_state_amd.build [--asan]  (or build() from Python).
 Every HIP translation unit is compiled with packed-fp32 instructions turned
 off; the host code of the ABI is compiled by the same driver.
 """
@@ -31,9 +31,9 @@ DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-munsafe-fp-atomics"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + DEVICE + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, bdir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(bdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + COMMON + DEVICE + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -41,21 +41,43 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+# Host-side AddressSanitizer build of the library (CPU checks of the C ABI's
+# argument handling): the host code of every translation unit is
+# instrumented, the device code is built as usual.  Load it with the ASan
+# runtime preloaded (asan_runtime()).
+LIB_ASAN = os.path.join(HERE, "libgdn_asan.so")
+ASAN_HOST = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime matching hipcc's host compiler."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no clang ASan runtime under /opt/rocm/llvm")
+    return hits[-1]
+
+
+def build(verbose: bool = False, asan: bool = False) -> str:
+    """Compile every translation unit and link libgdn.so (libgdn_asan.so with
+    asan=True)."""
+    out_lib = LIB_ASAN if asan else LIB
+    bdir = os.path.join(BUILD_DIR, "asan") if asan else BUILD_DIR
+    os.makedirs(bdir, exist_ok=True)
+    extra = ASAN_HOST if asan else []
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+        objs = list(ex.map(lambda src: _compile(src, bdir, extra), SOURCES))
+    tmp = out_lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH] + extra + ["-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("link of libgdn.so failed")
-    os.replace(tmp, LIB)
+        raise RuntimeError("link of %s failed" % os.path.basename(out_lib))
+    os.replace(tmp, out_lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out_lib)
+    return out_lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, asan="--asan" in sys.argv)

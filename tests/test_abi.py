@@ -18,7 +18,10 @@ F32, BF16 = 0, 1
 
 @pytest.fixture(scope="module")
 def lib():
-    return gdn.library()
+    # GDN_TEST_LIB names another build of the library to check (the
+    # host-sanitized one, from tests/test_abi_asan.py); default: the product
+    path = os.environ.get("GDN_TEST_LIB")
+    return gdn.declare(ctypes.CDLL(path)) if path else gdn.library()
 
 
 def declared_functions():
