@@ -279,7 +279,9 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     const int r = u_lds / C::VU, u = min((u_lds % C::VU) ^ vswz<C::VU>(r), 2 * max(nS, 1) - 1);
     off_v[j] = (uint32_t)r * tok_v + 16 * u;
   }
-  auto issue_dma = [&](int b, int t0, int64_t slot, bool with_rec = true) {
+  // part 0: K (and Q) fragments; part 1: the record and the value slab;
+  // -1: all of them
+  auto issue_dma = [&](int b, int t0, int64_t slot, bool with_rec = true, int part = -1) {
     char *buf = smem + b * C::BUF;
     const int64_t left = T_all - t0;   // tokens from the chunk's first to the end of the tensor
     const int64_t lim = 0xFFFFFFFFll;
@@ -290,7 +292,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 #pragma unroll
     for (int j = 0; j < JK; ++j) {                           // K (and Q) A fragments
       const int f = j * NW + w;
-      if (C::NKA % NW == 0 || f < C::NKA) {
+      if (part != 1 && (C::NKA % NW == 0 || f < C::NKA)) {
         dma16_buffer(kb, nk, (lds_void *)(buf + (C::bKA + f) * 1024), off_kq[j]);
         if (WANT_O) dma16_buffer(qb, nk, (lds_void *)(buf + (C::bQA + f) * 1024), off_kq[j]);
       }
@@ -298,11 +300,11 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 #pragma unroll
     for (int j = 0; j < JT; ++j) {                           // Tau diag(beta) fragments (record)
       const int f = j * NW + w;
-      if (with_rec && (C::NTF % NW == 0 || f < C::NTF)) {
+      if (part != 0 && with_rec && (C::NTF % NW == 0 || f < C::NTF)) {
         dma16_buffer(rec, kRecFloats * 4, (lds_void *)(buf + (C::bTF + f) * 1024), 16 * l, f * 1024);
       }
     }
-    if (grp_S) {                                             // value slab of the workgroup
+    if (part != 0 && grp_S) {                                // value slab of the workgroup
       const char *vb = reinterpret_cast<const char *>(gv + ((int64_t)t0 * H + h) * DV + vcol0);
       const uint32_t nv = (uint32_t)min(left * tok_v - ((int64_t)h * DV + vcol0) * 2, lim);
 #pragma unroll
@@ -491,15 +493,14 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     const int Lc = min(CH, tend - t0);
     const bool more = t0 + CH < tend;
     const int L1 = more ? min(CH, tend - t0 - CH) : 0;
-    // the previous chunk's outputs: its M o Q K^T became visible at the
-    // hand-over barrier just passed
-    if (WANT_O && active && Lp > 0) {
-      finish_o(b ^ 1);
-      store_o();
-    }
-    // operands of the next chunk: in flight while this one runs
+    // Operands of the next chunk: in flight while this one runs.  With
+    // outputs the copies go out in two halves, the second one in the middle
+    // of the step next to the stores of the previous chunk's outputs: issued
+    // by every wave at once right after the hand-over barrier, all of them
+    // together stall the waves' instruction issue for about 2,000 cycles
+    // (timed in-kernel with s_memtime on the 32768-token prefill).
     if (more) {
-      issue_dma(b ^ 1, t0 + CH, slot + 1);
+      issue_dma(b ^ 1, t0 + CH, slot + 1, true, WANT_O ? 0 : -1);
       load_alpha(t0 + CH, L1);
     }
     const char *buf = smem + b * C::BUF;
@@ -626,9 +627,11 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
           upd_mfma(kt, eh1, el1, st[1]);
         }
       }
-    } else if (active) {
+    } else {
       // ---- S^T as k = 32 B fragments ----
       bf16x8 sh[RT][C::NKS], sl[RT][C::NKS];
+      f32x4 dd[RT][4];
+      if (active) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -681,7 +684,6 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       // fragments in the order 0, 2, 4, 1, 3, 5 (token blocks 0, 2, 3, 1, 2, 3)
       // so that a block's two products are three issue slots apart; all
       // three split passes share the accumulators
-      f32x4 dd[RT][4];
       {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -706,7 +708,19 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
               dd[rt][bt] = mfma_bf16(pass == 2 ? tl[f] : th[f], pass == 1 ? rl[rt][m] : rh[rt][m], dd[rt][bt]);
             }
       }
+      }  // active
 
+      if constexpr (WANT_O) {
+        // the previous chunk's outputs (its M o Q K^T became visible at the
+        // hand-over barrier), then the second half of the next chunk's copies
+        if (active && Lp > 0) {
+          finish_o(b ^ 1);
+          store_o();
+        }
+        if (more) issue_dma(b ^ 1, t0 + CH, slot + 1, true, 1);
+      }
+
+      if (active) {
       // ---- outputs: the previous chunk's finished and stored; this one's
       // e^g Q S^T (every Q fragment read once for the wave's row tiles) and
       // its D, pending ----
@@ -783,6 +797,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 #pragma unroll
           for (int d = 0; d < C::NSB; ++d) st[rt][d] = mfma_bf16(a[d], el[rt][m], st[rt][d]);
       }
+      }  // active
     }
 
     if (WANT_O) build_p(b);
