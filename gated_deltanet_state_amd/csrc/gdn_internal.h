@@ -36,18 +36,15 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 // without reading cu (which lives on the device).
 // ---------------------------------------------------------------------------
 constexpr int kChunk = 64;
-// Per-chunk factor record, one per (slot, head), 13 KiB:
+// Per-chunk factor record, one per (slot, head), 12 KiB:
 //   * fp32 inputs: Tau = (I + A)^{-1}, lower 16 x 16 block rows packed, block
 //     row b holds 16 rows x 16 (b + 1) columns, row-major, at element offset
 //     256 * b (b + 1) / 2 (2560 floats);
-//   * bf16 inputs: bytes [0, 12 KiB): Tau diag(beta) as the six A operands of
-//     the k = 32 MFMAs that apply it to a 64 x 16 right-hand side given as
-//     C-layout tiles (see kTauFrags), split bf16 planes [hi/lo][fragment]
-//     [lane][8]; bytes [12 KiB, 13 KiB): the chunk's gates as fp32,
-//     [0, 64) e^{g_t}, [64, 128) e^{g_L - g_t} (0 past the chunk),
-//     [128] e^{g_L}, with g the cumulative log-gate and L the chunk length.
-constexpr int kRecFloats = 3328;
-constexpr int kRecGateOffsetBytes = 12288;
+//   * bf16 inputs: Tau diag(beta) as the six A operands of the k = 32 MFMAs
+//     that apply it to a 64 x 16 right-hand side given as C-layout tiles (see
+//     kTauFrags), split bf16 planes [hi/lo][fragment][lane][8].
+// (The recurrence forms the chunk's gates itself from alpha.)
+constexpr int kRecFloats = 3072;
 // Fragment f of Tau covers token block row bt and the pair of 16-column
 // blocks (2m, 2m + 1): f = 0: (0,0), 1: (1,0), 2: (2,0), 3: (2,1), 4: (3,0),
 // 5: (3,1).  Lane l holds row 16 bt + (l & 15), columns

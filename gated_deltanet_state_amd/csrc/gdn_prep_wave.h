@@ -13,8 +13,7 @@
 // the recurrence.  Steps:
 //   1. keys straight into registers as MFMA fragments (rows past the chunk
 //      repeat its last row; they meet beta = 0 below); cumulative
-//      log-gates by a wave-wide scan, and the gates e^g, e^{g_L - g},
-//      e^{g_L} into the record
+//      log-gates by a wave-wide scan
 //   2. the 10 lower 16 x 16 blocks of A on bf16 MFMA (keys are exact in
 //      bf16), ten independent accumulators
 //   3. the four diagonal blocks inverted at once by forward substitution:
@@ -106,12 +105,6 @@ __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 
     const float gs = wave_inclusive_scan(g);
     sG[l] = gs;
     sB[l] = b;
-    // the chunk's gates, for recurrences that take them from the record
-    const float gL = lane_value(gs, Lc - 1);
-    float *gr = reinterpret_cast<float *>(rec + kRecGateOffsetBytes);
-    gr[l] = __expf(gs);
-    gr[64 + l] = (l < Lc) ? __expf(gL - gs) : 0.f;
-    if (l == 0) gr[128] = __expf(gL);
   }
   wave_lds_fence();
 

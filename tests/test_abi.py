@@ -174,14 +174,14 @@ def test_scalar_decay_argument_checks(lib):
 
 
 def test_workspace_queries(lib):
-    # one 13 KiB record of per-chunk factors ((I + A)^{-1} diag(beta) fragments and the gates) per chunk
+    # one 12 KiB record of per-chunk factors ((I + A)^{-1} diag(beta) fragments) per chunk
     # slot and head; slots = n_tokens / 64 + n_seqs + 1 (sequence n's chunk j sits
     # in slot floor(cu[n] / 64) + n + j)
     lib.gdn_replay_segmented_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.gdn_replay_segmented_workspace_bytes.restype = ctypes.c_size_t
     seg_ws = lib.gdn_replay_segmented_workspace_bytes
-    tau = lambda n_seqs, n_tokens, H: (n_tokens // 64 + n_seqs + 1) * H * 13312
+    tau = lambda n_seqs, n_tokens, H: (n_tokens // 64 + n_seqs + 1) * H * 12288
     # 16 sequences x 32 heads already fill the chip: no time split, and room
     # for the longest-first order of the 16 sequences (256 bytes)
     assert lib.gdn_replay_workspace_bytes(16, 30000, 32, 128, 128) == tau(16, 30000, 32) + 256

@@ -70,7 +70,7 @@ def test_default_choice_splits_a_single_long_tail():
     # without a forced count a single 3277-token sequence on 32 heads is split
     gdn, torch = _gdn()
     lib = gdn.library()
-    tau = (3277 // 64 + 2) * 32 * 13312
+    tau = (3277 // 64 + 2) * 32 * 12288
     assert lib.gdn_replay_workspace_bytes(1, 3277, 32, 128, 128) > tau
     inp = workloads.generate([3277], H=32, dk=128, dv=128, dtype="bf16", seed=46)
     _, S = run_replay(inp, want_o=False)
