@@ -108,38 +108,61 @@ __device__ __forceinline__ int vswz(int r) {
 // columns c .. c + 7 of its 32-column step) by the transposing LDS read:
 // fragment (d, m), lane (q, g) gets K[32 m + 4 g + e (+16)][32 (d >> 1) +
 // 8 (q >> 2) + 4 (d & 1) + (q & 3)], e < 4 -- the dk order of the S^T blocks
-// and the token order of the paired right-hand sides.  Inline assembly with
-// its own lgkmcnt wait: the transposing read carries no alias information,
+// and the token order of the paired right-hand sides.  Inline assembly, one
+// group of reads per token half with its own lgkmcnt wait (one LDS round
+// trip per half): the transposing read carries no alias information,
 // and as a compiler builtin it would be made to wait for the load-to-LDS
 // copies of the next chunk that are in flight meanwhile.  The results are
 // early-clobber operands: a read's data may land before the next read of
 // the group has taken its address, so no result may share a register with
 // the address.
-template <int NKS, int D>
-__device__ __forceinline__ void kt_pair(uint32_t addr, int m, bf16x8 &a0, bf16x8 &a1) {
-  // two dk blocks D, D + 1 of token half m: four 8-byte reads
-  constexpr int o0 = (D >> 1) * 1024 + 8 * (D & 1), o1 = ((D + 1) >> 1) * 1024 + 8 * ((D + 1) & 1);
-  uint2 r0, r1, r2, r3;
-  const uint32_t base = addr + (uint32_t)(2 * m * NKS * 1024);
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4 offset:%c5\n\t"
-      "ds_read_b64_tr_b16 %1, %4 offset:%c6\n\t"
-      "ds_read_b64_tr_b16 %2, %4 offset:%c7\n\t"
-      "ds_read_b64_tr_b16 %3, %4 offset:%c8\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-      : "v"(base), "i"(o0), "i"(o0 + NKS * 1024), "i"(o1), "i"(o1 + NKS * 1024));
-  a0 = cat_bf16x8(r0, r1);
-  a1 = cat_bf16x8(r2, r3);
-}
 template <int NKS, int NSB>
 __device__ __forceinline__ void kt_frags(int m, uint32_t addr, bf16x8 (&a)[NSB]) {
-  kt_pair<NKS, 0>(addr, m, a[0], a[1]);
-  kt_pair<NKS, 2>(addr, m, a[2], a[3]);
-  if constexpr (NSB > 4) {
-    kt_pair<NKS, 4>(addr, m, a[4], a[5]);
-    kt_pair<NKS, 6>(addr, m, a[6], a[7]);
+  // all NSB fragments of token half m in one group, one wait: fragment d
+  // from the 8-byte reads at (d >> 1) KiB + 8 (d & 1) and that plus NKS KiB
+  // (the next 16 key rows)
+  static_assert((NKS == 4 && NSB == 8) || (NKS == 2 && NSB == 4), "dk = 128 or 64");
+  const uint32_t base = addr + (uint32_t)(2 * m * NKS * 1024);
+  uint2 r[2 * NSB];
+  if constexpr (NSB == 8) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %2, %16 offset:8\n\t"
+        "ds_read_b64_tr_b16 %3, %16 offset:4104\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %5, %16 offset:5120\n\t"
+        "ds_read_b64_tr_b16 %6, %16 offset:1032\n\t"
+        "ds_read_b64_tr_b16 %7, %16 offset:5128\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %9, %16 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %10, %16 offset:2056\n\t"
+        "ds_read_b64_tr_b16 %11, %16 offset:6152\n\t"
+        "ds_read_b64_tr_b16 %12, %16 offset:3072\n\t"
+        "ds_read_b64_tr_b16 %13, %16 offset:7168\n\t"
+        "ds_read_b64_tr_b16 %14, %16 offset:3080\n\t"
+        "ds_read_b64_tr_b16 %15, %16 offset:7176\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+          "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]),
+          "=&v"(r[15])
+        : "v"(base));
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:8\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:2056\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:3072\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:1032\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:3080\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(base));
   }
+#pragma unroll
+  for (int d = 0; d < NSB; ++d) a[d] = cat_bf16x8(r[2 * d], r[2 * d + 1]);
 }
 
 template <int DK, bool WANT_O, int NW, int RT, bool FUSED>
