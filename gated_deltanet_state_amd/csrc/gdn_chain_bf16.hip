@@ -90,8 +90,9 @@ struct Cfg {
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
-// Gate buffer: [0, 64) e^g, [64, 128) e^{g_L - g} (0 past the chunk),
-// [128, 192) g, [192] e^{g_L}.
+// Gate buffer (see the running scale gam in the kernel): [0, 64) gam e^g,
+// [64, 128) e^{g_L - g} / gam' (0 past the chunk), [128, 192) g, [192] the
+// factor the chunk applies to the state registers (gam e^{g_L}, or 1: none).
 constexpr int G_EG = 0, G_DEC = 64, G_G = 128, G_EGL = 192;
 
 // Unit swizzle of the staged value slab (VU 16-byte units per row): unit u
@@ -343,15 +344,34 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     pa = 0x3f80;
     if (w == 0 && l < Lc) pa = ga[(int64_t)(t0 + l) * H + h];
   };
-  auto gates = [&](int b, int Lc) {
+  // Running scale of the state.  The registers hold S / gam, gam a scalar
+  // of the workgroup's (sequence, segment, head) that wave 0 tracks.  A
+  // chunk folds its decay e^{g_L} into gam and leaves the registers alone;
+  // the per-token vectors are scaled to match (e^g by gam for the reads of
+  // the state, e^{g_L - g} by 1 / gam' for the corrections added to it).
+  // When gam' would drop below 2^-40, and at a sequence's last chunk, the
+  // chunk instead scales the registers by gam e^{g_L} and resets gam to 1,
+  // so that the state written out is S itself.  This spares the multiply of
+  // every state element by e^{g_L} in most chunks.
+  float gam = 1.f;
+  auto gates = [&](int b, int Lc, bool last) {
     if (w != 0) return;
     float *sG = sG0 + b * C::GN;
     const float g = wave_inclusive_scan((l < Lc) ? log_gate(__uint_as_float((unsigned)pa << 16)) : 0.f);
     const float gL = lane_value(g, Lc - 1);
-    sG[G_EG + l] = __expf(g);
-    sG[G_DEC + l] = (l < Lc) ? __expf(gL - g) : 0.f;
+    const float cand = gam * __expf(gL);
+    const bool apply = last || !(cand >= 0x1p-40f);
+    const float gnew = apply ? 1.f : cand;
+    const float inv = 1.f / gnew;
+    sG[G_EG + l] = gam * __expf(g);
+    sG[G_DEC + l] = (l < Lc) ? __expf(gL - g) * inv : 0.f;
     sG[G_G + l] = g;
-    if (l == 0) sG[G_EGL] = __expf(gL);
+    if (l == 0) sG[G_EGL] = apply ? cand : 1.f;   // the registers' scale factor (1: none)
+    gam = gnew;
+  };
+  // the registers' scale factor of the chunk in gate set sG, uniform
+  auto state_scale = [&](const float *sG) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sG[G_EGL])));
   };
 
   // Value columns of the staged chunk in buffer set b, transposed to the
@@ -403,12 +423,12 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     }
     wait_vmem();
     __syncthreads();
-    if (tbeg < tend) gates(0, min(CH, tend - tbeg));
+    if (tbeg < tend) gates(0, min(CH, tend - tbeg), tend - tbeg <= CH);
   } else if (tbeg < tend) {
     const int L0 = min(CH, tend - tbeg);
     issue_dma(0, tbeg, slot0);
     load_alpha(tbeg, L0);
-    gates(0, L0);
+    gates(0, L0, tend - tbeg <= CH);
   }
   wait_vmem();
   lds_barrier();
@@ -596,11 +616,13 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
           }
           b_frag_split(de[0], de[1], eh[0], el[0]);
           b_frag_split(de[2], de[3], eh[1], el[1]);
-          const float gl = sG[G_EGL];
+          const float gl = state_scale(sG);
+          if (gl != 1.f) {
 #pragma unroll
-          for (int d = 0; d < NSB; ++d)
+            for (int d = 0; d < NSB; ++d)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sv[d][e] *= gl;
+              for (int e = 0; e < 4; ++e) sv[d][e] *= gl;
+          }
         };
         // S^T += K^T D': each state block is touched once every NSB products
         auto upd_mfma = [&](const bf16x8 (&kt)[2][NSB], const bf16x8 (&eh)[2], const bf16x8 (&el)[2],
@@ -800,13 +822,15 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       // K^T fragments of one token half m for all dk blocks, then the four
       // (m, pass) sweeps over the dk blocks: each state block is touched
       // once every NSB products
-      const float gl = sG[G_EGL];
+      const float gl = state_scale(sG);
+      if (gl != 1.f) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int d = 0; d < C::NSB; ++d)
+          for (int d = 0; d < C::NSB; ++d)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) st[rt][d][e] *= gl;
+            for (int e = 0; e < 4; ++e) st[rt][d][e] *= gl;
+      }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         bf16x8 a[C::NSB];
@@ -825,7 +849,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 
     if (WANT_O) build_p(b);
     // ---- hand over to the next chunk ----
-    if (more) gates(b ^ 1, L1);
+    if (more) gates(b ^ 1, L1, t0 + 2 * CH >= tend);
     wait_vmem();
     lds_barrier();
     if (more) read_v(b ^ 1);
