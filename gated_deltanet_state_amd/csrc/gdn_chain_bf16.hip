@@ -542,6 +542,14 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     // by every wave at once right after the hand-over barrier, all of them
     // together stall the waves' instruction issue for about 2,000 cycles
     // (timed in-kernel with s_memtime on the 32768-token prefill).
+    //
+    // Wave priority falls along the step (3 at the top, 0 for the state
+    // update): the two waves of a SIMD otherwise issue oldest first, the
+    // younger one finishes its step alone with nothing to hide its MFMA and
+    // LDS latencies, and the barrier waits for it.  A wave behind in the
+    // step now wins issue, so both reach the barrier together (3% on the
+    // 32768-token prefill and the 3277-token tail, 1% on packed tails).
+    __builtin_amdgcn_s_setprio(3);
     if (more) {
       issue_dma(b ^ 1, t0 + CH, slot + 1, true, WANT_O ? 0 : -1);
       load_alpha(t0 + CH, L1);
@@ -651,6 +659,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
           r_valu(vt[0], y0, rh0, rl0);
           y_mfma(ka, sh1, sl1, y1);
         }
+        __builtin_amdgcn_s_setprio(2);
         {
           bf16x8 th[kTauFrags], tl[kTauFrags];
 #pragma unroll
@@ -663,6 +672,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
           de_valu(d0, st[0], eh0, el0);
           d_mfma(th, tl, rh1, rl1, d1);
         }
+        __builtin_amdgcn_s_setprio(1);
         {
           bf16x8 kt[2][NSB];
           kt_frags<NKS, NSB>(0, kt_lds + (uint32_t)(b * C::BUF), kt[0]);
@@ -707,6 +717,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
           for (int bt = 0; bt < 4; ++bt) y[rt][bt] = mfma_bf16(a[bt], sl[rt][m], y[rt][bt]);
       }
 
+      __builtin_amdgcn_s_setprio(2);
       // ---- R = V - e^g Y  (beta is folded into the Tau fragments) ----
       bf16x8 rh[RT][2], rl[RT][2];
 #pragma unroll
@@ -755,6 +766,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       }
       }  // active
 
+      __builtin_amdgcn_s_setprio(1);
       if constexpr (WANT_O) {
         // the previous chunk's outputs (its M o Q K^T became visible at the
         // hand-over barrier), then the second half of the next chunk's copies
@@ -805,6 +817,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
         Lp = Lc;
       }
 
+      __builtin_amdgcn_s_setprio(0);
       // ---- S^T <- e^{g_L} S^T + K^T diag(e^{g_L - g}) D ----
       bf16x8 eh[RT][2], el[RT][2];
 #pragma unroll
@@ -847,6 +860,7 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
       }  // active
     }
 
+    __builtin_amdgcn_s_setprio(0);
     if (WANT_O) build_p(b);
     // ---- hand over to the next chunk ----
     if (more) gates(b ^ 1, L1, t0 + 2 * CH >= tend);
