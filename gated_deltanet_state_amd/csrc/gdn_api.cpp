@@ -111,20 +111,21 @@ int replay_segments(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t d
 }
 
 // Segments per sequence for a bf16 replay with outputs.  A split runs three
-// passes: the state-only segment operators, their composition (which also
-// yields every segment's true start state), and every segment again with
-// outputs from that start state.  Worth it when the (sequence, head) pairs
-// alone leave compute units idle: P fills the compute units with one
-// workgroup per (sequence, head, segment), with at least 8 chunks per
-// segment.
+// passes: the segment launch (a short lead segment 0 with its outputs from
+// S0, beside the transition and state rows of the middle segments), the
+// composition (every later segment's true start state), and the output
+// launch (segments 1 .. P - 1 with outputs from those states).  Worth it
+// when the (sequence, head) pairs alone leave compute units idle: the P - 1
+// later segments fill the compute units with one workgroup per (sequence,
+// head, segment), with at least 8 chunks per segment.
 int replay_segments_o(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv, int cus) {
   if ((dk + dv) / 16 > 16) return 1;
   const int64_t chunks = (n_tokens / gdn::kChunk) / (n_seqs > 0 ? n_seqs : 1);
   const int64_t units = (int64_t)n_seqs * n_heads;
-  int64_t P = cus / (units > 0 ? units : 1);
-  if (P > chunks / 8) P = chunks / 8;
-  if (P > 8) P = 8;
-  return P < 2 ? 1 : (int)P;
+  int64_t Q = cus / (units > 0 ? units : 1);
+  if (Q > chunks / 8) Q = chunks / 8;
+  if (Q > 8) Q = 8;
+  return Q < 2 ? 1 : (int)Q + 1;
 }
 
 // Segment count of one call: `forced` (>= 1, from gdn_replay_segmented) or
@@ -250,7 +251,7 @@ gdn_status replay_impl(const void *q, const void *k, const void *v, const void *
   float *Sseg = Tseg + (size_t)n_seqs * P * n_heads * dk * dk;
   float *Spre = Sseg + (size_t)n_seqs * P * n_heads * dv * dk;   // start states (with outputs)
   p.n_segs = P;
-  p.seg_uniform = o ? 1 : 0;
+  p.lead = o ? 1 : 0;   // with outputs: segment 0 runs with them here
   p.fuse_prep = 1;
   p.skip_T0 = 1;
   p.T_frags = 1;
@@ -258,7 +259,6 @@ gdn_status replay_impl(const void *q, const void *k, const void *v, const void *
   p.tiles_S = dv / 16;
   p.T_out = Tseg;
   p.S_out = Sseg;
-  p.o = nullptr;
   if ((s = launched(gdn::launch_chain_bf16(p, st), "gdn_replay segment launch"))) return s;
   gdn::SegComposeLaunch c{};
   c.S_seg = Sseg;
@@ -268,18 +268,19 @@ gdn_status replay_impl(const void *q, const void *k, const void *v, const void *
   c.H = n_heads;
   c.dk = dk;
   c.dv = dv;
-  c.S_out = S_final;
+  c.S_out = o ? nullptr : S_final;
   c.S_prefix = o ? Spre : nullptr;
   c.S0 = S0;
+  c.lead = o ? 1 : 0;
   if ((s = launched(gdn::launch_seg_compose(c, st), "gdn_replay segment compose launch"))) return s;
   if (!o) return ok();
-  // outputs: every segment again from its start state, with the records
-  // (Tau and M o Q K^T) the segment launch built
+  // outputs: segments 1 .. P - 1 from their start states, with the records
+  // the segment launch built; the last one ends in S_final
   gdn::ChainLaunch r = p;
-  r.o = o;
   r.S0 = nullptr;
   r.S0_seg = Spre;
   r.S_out = nullptr;
+  r.S_last = S_final;
   r.T_out = nullptr;
   r.tiles_T = 0;
   r.T_frags = 0;

@@ -166,36 +166,69 @@ __device__ __forceinline__ void kt_frags(int m, uint32_t addr, bf16x8 (&a)[NSB])
   for (int d = 0; d < NSB; ++d) a[d] = cat_bf16x8(r[2 * d], r[2 * d + 1]);
 }
 
+// Segments of whole chunks: chunks [cb, cb + cl) of segment seg of a
+// sequence of nch chunks, cut into P = n_segs segments.
+//   * Plain layout: segment 0 carries state rows only (no transition rows)
+//     and steps about 1.6 times faster, so it takes a larger share:
+//     e = round(chunks / (P - 1 + 1.6)) chunks for each later segment, the
+//     rest for segment 0.  When the workgroups build their own records
+//     first (fused), segment 0 keeps to one record per prologue wave
+//     (npw; a second round of the prologue costs more than a chunk step
+//     elsewhere) and the later segments take ceil(rest / (P - 1)) each.
+//   * Lead layout (time split with outputs): the later segments, which all
+//     run the output recurrence from their composed start states, take e =
+//     round(chunks / (P - 1 + 3/4)) each and the lead the rest: the lead
+//     runs beside the transition segments and also builds the last
+//     segment's records.
+// Segments past the end are empty.
+__device__ __forceinline__ void seg_chunks(const ChainLaunch &p, int nch, int seg, int npw, int &cb, int &cl) {
+  const int P = p.n_segs;
+  int e, c0;
+  if (p.lead) {
+    const int den = 4 * (P - 1) + 3;
+    e = max(1, (4 * nch + den / 2) / den);
+    c0 = max(0, nch - (P - 1) * e);
+  } else {
+    const int den = 5 * (P - 1) + 8;
+    e = max(1, (5 * nch + den / 2) / den);
+    c0 = max(0, nch - (P - 1) * e);
+    if (npw > 0 && c0 > npw) {
+      c0 = npw;
+      e = (nch - c0 + P - 2) / (P - 1);
+    }
+  }
+  cb = seg == 0 ? 0 : c0 + (seg - 1) * e;
+  cl = seg == 0 ? c0 : e;
+  cb = min(cb, nch);
+  cl = min(cl, nch - cb);
+}
+
+// Workgroups of one (sequence, head) in a launch: the segments first ..
+// first + count - 1, grp0 workgroups for segment 0 (when it runs; tw0 row
+// tiles each) and grpA for every later one (tw row tiles each).
+struct SegGroups {
+  int first, count, grp0, grpA, per_nh;
+};
+__host__ __device__ inline SegGroups seg_groups(const ChainLaunch &p, int tw, int tw0) {
+  SegGroups g;
+  const int tilesA = p.tiles_T + p.tiles_S;
+  const int tiles0 = p.skip_T0 ? p.tiles_S : tilesA;
+  g.first = (p.lead && p.tiles_T == 0) ? 1 : 0;
+  g.count = p.lead ? p.n_segs - 1 : p.n_segs;
+  g.grp0 = g.first == 0 ? (tiles0 + tw0 - 1) / tw0 : 0;
+  g.grpA = (tilesA + tw - 1) / tw;
+  g.per_nh = g.grp0 + (g.count - (g.first == 0 ? 1 : 0)) * g.grpA;
+  return g;
+}
+
+// One workgroup: row-tile group grp of segment seg of (sequence n, head h).
 template <int DK, bool WANT_O, int NW, int RT, bool FUSED>
-__global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int n_items) {
+__device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, const int h, const int seg,
+                                           const int grp, char *smem) {
   static_assert(RT == 1 || RT == 2, "one or two row tiles per wave");
   using C = Cfg<DK, WANT_O, NW, RT, FUSED>;
   constexpr int TW = C::TW;
-  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   float *sG0 = reinterpret_cast<float *>(smem + C::oG);
-
-  // ---- work item ----
-  const int tilesA = p.tiles_T + p.tiles_S;
-  const int tiles0 = p.skip_T0 ? p.tiles_S : tilesA;
-  const int grp0 = (tiles0 + TW - 1) / TW, grpA = (tilesA + TW - 1) / TW;
-  const int per_nh = grp0 + (p.n_segs - 1) * grpA;
-  // One workgroup per (sequence, head) with a longest-first sequence order:
-  // items in block order (the dispatcher deals blocks round-robin over the
-  // XCDs, so the longest items start first everywhere).  Otherwise
-  // XCD-aware: consecutive items (workgroups of one sequence and head,
-  // which stage the same operands) share one XCD's L2.
-  const bool ordered = p.order != nullptr && per_nh == 1;
-  const int per = (int)(gridDim.x >> 3);
-  const int item = ordered ? (int)blockIdx.x : (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  if (item >= n_items) return;
-  const int nh = item / per_nh;
-  int rem = item % per_nh, seg = 0, grp = rem;
-  if (rem >= grp0) {
-    rem -= grp0;
-    seg = 1 + rem / grpA;
-    grp = rem % grpA;
-  }
-  const int n = ordered ? p.order[nh / p.H] : nh / p.H, h = nh % p.H;
   const int H = p.H, DV = p.dv;
   const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id();
   const int g4 = l >> 4, jl = l & 15;
@@ -217,29 +250,13 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
 
   // ---- this segment's token range ----
   const int cbeg = p.cu[n], cend = p.cu[n + 1];
+  const int nch_seq = (cend - cbeg + CH - 1) / CH;
   int tbeg = cbeg, tend = cend;
   if (p.n_segs > 1) {
-    // Segments of whole chunks.  Segment 0 carries state rows only (no
-    // transition rows) and steps about 1.6 times faster, so it takes a
-    // larger share: e = round(chunks / (P - 1 + 1.6)) chunks for each later
-    // segment, the rest for segment 0 (with seg_uniform: ceil(chunks / P)
-    // each).  When the workgroup builds its own records first, segment 0
-    // keeps to one record per prologue wave (a second round of the
-    // prologue costs more than a chunk step elsewhere) and the later
-    // segments take ceil(rest / (P - 1)) each.  Segments past the end are
-    // empty.
-    const int P = p.n_segs, nch = (cend - cbeg + CH - 1) / CH;
-    const int den = 5 * (P - 1) + 8;
-    int e = p.seg_uniform ? (nch + P - 1) / P : max(1, (5 * nch + den / 2) / den);
-    int c0 = p.seg_uniform ? e : max(0, nch - (P - 1) * e);
-    if (FUSED && !p.seg_uniform && c0 > C::NPW) {
-      c0 = C::NPW;
-      e = (nch - c0 + P - 2) / (P - 1);
-    }
-    const int64_t off = seg == 0 ? 0 : (int64_t)(c0 + (seg - 1) * e) * CH;
-    const int64_t len = (int64_t)(seg == 0 ? c0 : e) * CH;
-    tbeg = (int)min((int64_t)cend, (int64_t)cbeg + off);
-    tend = (int)min((int64_t)cend, (int64_t)tbeg + len);
+    int cb, cl;
+    seg_chunks(p, nch_seq, seg, FUSED ? C::NPW : 0, cb, cl);
+    tbeg = cbeg + cb * CH;
+    tend = min(cend, tbeg + cl * CH);
   }
   const int64_t slot0 = (int64_t)(cbeg / CH) + n + (tbeg - cbeg) / CH;
 
@@ -414,12 +431,17 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
     }
     float *scr = reinterpret_cast<float *>(smem + C::PSCR) + (w % C::NPW) * (kPrepWaveLds / 4);
     const int nch = (tend - tbeg + CH - 1) / CH;
-    for (int c = w; c < nch && w < C::NPW; c += C::NPW) {
-      const int tc = tbeg + c * CH;
+    // the lead also builds the records of the last segment (chunks xb ..
+    // xb + nx - 1 of the sequence), which the segment launch does not run
+    int xb = 0, nx = 0;
+    if (WANT_O && p.lead && seg == 0) seg_chunks(p, nch_seq, p.n_segs - 1, 0, xb, nx);
+    for (int c = w; c < nch + nx && w < C::NPW; c += C::NPW) {
+      const bool own = c < nch;
+      const int tc = own ? tbeg + c * CH : cbeg + (xb + c - nch) * CH;
+      const int64_t sl = (int64_t)(cbeg / CH) + n + (tc - cbeg) / CH;
       prep_chunk_wave<DK>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta), H, h,
-                          tc, min(CH, tend - tc),
-                          const_cast<char *>(grec) + ((slot0 + c) * H + h) * (int64_t)(kRecFloats * 4), scr,
-                          c == 0 ? smem + C::bTF * 1024 : nullptr);
+                          tc, min(CH, cend - tc), const_cast<char *>(grec) + (sl * H + h) * (int64_t)(kRecFloats * 4),
+                          scr, (own && c == 0) ? smem + C::bTF * 1024 : nullptr);
     }
     wait_vmem();
     __syncthreads();
@@ -918,26 +940,71 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
         *reinterpret_cast<f32x4 *>(out + (int64_t)r * DK + c0) = st[rt][d];
       }
   }
+  if (active && !is_T && p.S_last && seg == p.n_segs - 1) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int d = 0; d < C::NSB; ++d) {
+        const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1), r = row0 + 16 * rt + jl;
+        *reinterpret_cast<f32x4 *>(p.S_last + (((int64_t)n * H + h) * DV + r) * DK + c0) = st[rt][d];
+      }
+  }
 }
 
-template <int DK, bool WANT_O, int NW, int RT, bool FUSED = false>
+// The launch: one workgroup per (sequence, head, segment, row-tile group).
+// With LEAD (segment launch of the lead layout) segment 0 runs the output
+// recurrence, one row tile per wave, and the other segments this body.
+template <int DK, bool WANT_O, int NW, int RT, bool FUSED, bool LEAD = false>
+__global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int n_items) {
+  using C = Cfg<DK, WANT_O, NW, RT, FUSED>;
+  using CL = Cfg<DK, true, NW, 1, FUSED>;
+  constexpr size_t SM = (LEAD && CL::SMEM > C::SMEM) ? CL::SMEM : C::SMEM;
+  __shared__ __attribute__((aligned(16))) char smem[SM];
+  const SegGroups sg = seg_groups(p, C::TW, LEAD ? NW : C::TW);
+  // One workgroup per (sequence, head) with a longest-first sequence order:
+  // items in block order (the dispatcher deals blocks round-robin over the
+  // XCDs, so the longest items start first everywhere).  Otherwise
+  // XCD-aware: consecutive items (workgroups of one sequence and head,
+  // which stage the same operands) share one XCD's L2.
+  const bool ordered = p.order != nullptr && sg.per_nh == 1;
+  const int per = (int)(gridDim.x >> 3);
+  const int item = ordered ? (int)blockIdx.x : (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (item >= n_items) return;
+  const int nh = item / sg.per_nh;
+  int rem = item % sg.per_nh, seg = sg.first, grp = rem;
+  if (rem >= sg.grp0) {
+    rem -= sg.grp0;
+    seg = sg.first + (sg.grp0 > 0 ? 1 : 0) + rem / sg.grpA;
+    grp = rem % sg.grpA;
+  }
+  const int n = ordered ? p.order[nh / p.H] : nh / p.H, h = nh % p.H;
+  if constexpr (LEAD) {
+    if (seg == 0) {
+      chain_body<DK, true, NW, 1, FUSED>(p, n, h, 0, grp, smem);
+      return;
+    }
+  }
+  chain_body<DK, WANT_O, NW, RT, FUSED>(p, n, h, seg, grp, smem);
+}
+
+template <int DK, bool WANT_O, int NW, int RT, bool FUSED = false, bool LEAD = false>
 hipError_t launch_b(const ChainLaunch &p, hipStream_t stream) {
   constexpr int TW = NW * RT;
   if (p.tiles_T % RT != 0 || p.tiles_S % RT != 0 || p.tiles_T > 8 || p.tiles_S > 8) return hipErrorInvalidValue;
-  const int tilesA = p.tiles_T + p.tiles_S;
-  const int tiles0 = p.skip_T0 ? p.tiles_S : tilesA;
-  const int64_t per_nh = (tiles0 + TW - 1) / TW + (int64_t)(p.n_segs - 1) * ((tilesA + TW - 1) / TW);
-  const int64_t items = (int64_t)p.n_seqs * p.H * per_nh;
+  if (LEAD && p.tiles_S > NW) return hipErrorInvalidValue;
+  const SegGroups sg = seg_groups(p, TW, LEAD ? NW : TW);
+  const int64_t items = (int64_t)p.n_seqs * p.H * sg.per_nh;
   if (items <= 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
-  return launch_kernel(chain_bf16_kernel<DK, WANT_O, NW, RT, FUSED>, dim3((unsigned)grid), dim3(NW * 64), 0, stream, p,
-                       (int)items);
+  return launch_kernel(chain_bf16_kernel<DK, WANT_O, NW, RT, FUSED, LEAD>, dim3((unsigned)grid), dim3(NW * 64), 0,
+                       stream, p, (int)items);
 }
 
 template <int DK>
 hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
-  if (p.o) {
-    if (p.tiles_T != 0 || p.fuse_prep) return hipErrorInvalidValue;
+  if (p.lead && (p.n_segs < 2 || !p.o)) return hipErrorInvalidValue;
+  if (p.o && p.tiles_T == 0) {
+    if (p.fuse_prep || (p.lead && !p.S0_seg)) return hipErrorInvalidValue;
     // one eight-wave workgroup per (sequence, segment, head): two waves per
     // SIMD interleave their work (measured on 16 packed tails: 668 us
     // against 933 us for two four-wave workgroups per head and 826 us for
@@ -951,6 +1018,14 @@ hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
   // State-only replays keep one row tile per wave (shorter chunk steps).
   const int tilesA = p.tiles_T + p.tiles_S;
   if (p.T_frags && p.tiles_T * 16 != p.dk) return hipErrorInvalidValue;
+  if (p.tiles_T > 0 && p.lead) {
+    // segment launch of the lead layout: segment 0 with its outputs
+    if (!p.fuse_prep || p.S0_seg) return hipErrorInvalidValue;
+    if (tilesA <= 8) return launch_b<DK, false, 4, 2, true, true>(p, stream);
+    if (tilesA <= 16) return launch_b<DK, false, 8, 2, true, true>(p, stream);
+    return hipErrorInvalidValue;
+  }
+  if (p.o) return hipErrorInvalidValue;
   if (p.tiles_T > 0) {
     // one workgroup per (sequence, segment, head): it may build its own
     // segment's records first

@@ -214,20 +214,23 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
       for (int i = 0; i < JBW; ++i) acc[rt][i] = c[rt][i];
   };
 
+  // operators applied: s0 .. PE - 1 (lead layout: the last segment has none,
+  // and the state entering it is the result)
+  const int PE = p.lead ? P - 1 : P;
   StepRegs<DK> R0, R1, R2;
-  if (s0 < P) load(s0, R0);
-  if (s0 + 1 < P) load(s0 + 1, R1);
-  for (int s = s0; s < P; s += 3) {
-    if (s + 2 < P) load(s + 2, R2);
+  if (s0 < PE) load(s0, R0);
+  if (s0 + 1 < PE) load(s0 + 1, R1);
+  for (int s = s0; s < PE; s += 3) {
+    if (s + 2 < PE) load(s + 2, R2);
     step(s, R0);
-    if (s + 1 >= P) break;
-    if (s + 3 < P) load(s + 3, R0);
+    if (s + 1 >= PE) break;
+    if (s + 3 < PE) load(s + 3, R0);
     step(s + 1, R1);
-    if (s + 2 >= P) break;
-    if (s + 4 < P) load(s + 4, R1);
+    if (s + 2 >= PE) break;
+    if (s + 4 < PE) load(s + 4, R1);
     step(s + 2, R2);
   }
-  float *out = p.S_out + head;
+  float *out = p.lead ? p.S_prefix + (((int64_t)n * P + P - 1) * H + h) * DV * DK : p.S_out + head;
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -236,7 +239,7 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
 
 template <int DK>
 hipError_t launch_sc(const SegComposeLaunch &p, hipStream_t stream) {
-  if (p.dv % 32 != 0) return hipErrorInvalidValue;
+  if (p.dv % 32 != 0 || (p.lead && (p.from_start || !p.S_prefix || p.n_segs < 2))) return hipErrorInvalidValue;
   const int64_t items = (int64_t)p.n_seqs * p.H * (p.dv / 32);
   if (items <= 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;

@@ -105,9 +105,17 @@ struct ChainLaunch {
   // every segment runs independently (state tiles of segment 0 from S0, of
   // later segments from S0_seg or zero; transition tiles from the identity).
   int32_t n_segs;           // >= 1
-  int seg_uniform;          // equal segments (else segment 0 takes a larger share)
   const float *S0_seg;      // [n_seqs, n_segs, H, dv, dk]: start of every segment (replaces S0), or null
   int skip_T0;              // segment 0 has no transition tiles
+  // Time split with outputs ("lead" layout, n_segs >= 2): segment 0 (the
+  // lead) is shorter than the others, which all have one length.  The
+  // segment launch (transition tiles) runs segments 0 .. n_segs - 2: the
+  // lead from S0 with its outputs, into o, and it also builds the records
+  // of the last segment; the output launch (no transition tiles) runs
+  // segments 1 .. n_segs - 1 from S0_seg and writes the last segment's end
+  // state to S_last.
+  int lead;
+  float *S_last;            // [n_seqs, H, dv, dk] or null
   // write each segment's T as composition fragments (kSegOpFragments)
   // instead of row-major fp32
   int T_frags;
@@ -139,6 +147,10 @@ struct SegComposeLaunch {
   // start from S0 and apply every operator, segment 0's included (else
   // S_seg[0] is the state after segment 0 and T_frag[0] is unused)
   int from_start;
+  // lead layout of a time split with outputs (ChainLaunch::lead): the last
+  // segment has no operator; the state entering it goes to S_prefix and
+  // S_out is unused
+  int lead;
 };
 
 // One token per sequence from a given state (gdn_decode).
