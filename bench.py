@@ -16,7 +16,9 @@ with outputs; 4 = 64 chunk operators of 512 tokens and their composition;
 ``--decode N`` instead times single-token decode of N requests from given
 states (the serving step after a replay).  ``--front-end`` instead times
 the front end (normalised q and k, activated gates) on the tail-replay
-shape (with ``--with-replay`` also before a state-only replay).
+shape (with ``--with-replay`` also the front end followed by a replay
+against gdn_replay_raw, the front end inside the replay, on the tail and on
+the 32768-token prefill with outputs).
 ``--overlap MIB`` instead times a pinned-host -> device copy of MIB MiB on
 a copy stream beside ``--layers`` tail replays: alone, serialised and
 overlapped.  ``--scalar-ops`` instead times the scalar-decay (Mamba-2
@@ -520,9 +522,11 @@ def overlap_report(args, gdn, torch, np):
 def front_end_report(args, gdn, torch, np):
     """One JSON line: gdn_front_end on the tail-replay shape (3277 tokens,
     32 heads, dk = 128, bf16, queries and keys); HBM-bound (every raw input
-    read once and every prepared output written once).  Also the front end
-    without queries followed by the state-only replay, against the replay of
-    prepared inputs (``--with-replay``)."""
+    read once and every prepared output written once).  With
+    ``--with-replay`` also: the front end without queries followed by the
+    state-only replay, the replay of prepared inputs, and gdn_replay_raw
+    (the front end inside the replay) on that shape; and the same three on
+    the 32768-token prefill with outputs."""
     import workloads
     T, H, d = workloads.tail_length(32768, "0.1"), 32, 128
     raw = workloads.generate_raw([T], H=H, dk=d, dv=d, dtype="bf16", seed=7)
@@ -556,7 +560,29 @@ def front_end_report(args, gdn, torch, np):
         both, _ = timed(lambda: gdn.replay(None, gdn.front_end(None, kr, g, b, out=out_k)[1], v, out[2], out[3],
                                               cu, want_o=False))
         alone, _ = timed(lambda: gdn.replay(None, out[1], v, out[2], out[3], cu, want_o=False))
-        extra = dict(state_only_replay=dict(prepared_inputs_ms=round(alone, 5), with_front_end_ms=round(both, 5)))
+        fused, _ = timed(lambda: gdn.replay_raw(None, kr, v, g, b, cu, want_o=False))
+        extra = dict(state_only_replay=dict(prepared_inputs_ms=round(alone, 5), with_front_end_ms=round(both, 5),
+                                            fused_front_end_ms=round(fused, 5)))
+        # the 32768-token prefill with outputs from raw projections: the
+        # front end then the replay, against gdn_replay_raw
+        TP = 32768
+        rp = workloads.generate_raw([TP], H=H, dk=d, dv=d, dtype="bf16", seed=8)
+        qp, kp, gp, bp, vp = t(rp.q_raw), t(rp.k_raw), t(rp.g), t(rp.b), t(rp.v)
+        del rp
+        cup = torch.tensor([0, TP], dtype=torch.int32, device="cuda")
+        outp = (torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(gp), torch.empty_like(bp))
+        op = torch.empty((TP, H, d), dtype=torch.float32, device="cuda")
+        Sp = torch.empty((1, H, d, d), dtype=torch.float32, device="cuda")
+
+        def two_calls():
+            gdn.front_end(qp, kp, gp, bp, out=outp)
+            gdn.replay(outp[0], outp[1], vp, outp[2], outp[3], cup, want_o=True, out=op, S_out=Sp)
+        two, _ = timed(two_calls)
+        fusedp, _ = timed(lambda: gdn.replay_raw(qp, kp, vp, gp, bp, cup, want_o=True, out=op, S_out=Sp))
+        prepared, _ = timed(lambda: gdn.replay(outp[0], outp[1], vp, outp[2], outp[3], cup, want_o=True, out=op,
+                                               S_out=Sp))
+        extra["prefill_with_outputs"] = dict(n_tokens=TP, prepared_inputs_ms=round(prepared, 5),
+                                             with_front_end_ms=round(two, 5), fused_front_end_ms=round(fusedp, 5))
     # q_raw, k_raw read and q, k written (bf16); g, b read and alpha, beta written (bf16)
     byt = T * H * (4 * d * 2 + 4 * 2)
     achieved = byt / (avg / 1e3) / 1e9

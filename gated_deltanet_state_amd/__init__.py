@@ -66,6 +66,9 @@ def declare(lib):
     lib.gdn_replay_segmented_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32]
     lib.gdn_replay_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint,
                                        vp, cint, vp, vp]
+    lib.gdn_replay_raw.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint,
+                                   vp, cint, vp, vp, sz, vp]
+    lib.gdn_replay_raw_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
     lib.gdn_chunk_operator.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint,
                                        vp, vp, vp, sz, vp]
     lib.gdn_chunk_operator_workspace_bytes.argtypes = [i32, i64, i32, i32, i32]
@@ -75,11 +78,13 @@ def declare(lib):
     lib.gdn_front_end.argtypes = [vp, vp, vp, vp, i64, i32, i32, cint, vp, vp, vp, vp, vp]
     lib.gdn_scalar_chunk_operator.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, cint, vp, vp, vp]
     lib.gdn_scalar_compose.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
-    for f in (lib.gdn_replay, lib.gdn_replay_segmented, lib.gdn_replay_noalloc, lib.gdn_chunk_operator, lib.gdn_compose,
-              lib.gdn_decode, lib.gdn_front_end, lib.gdn_scalar_chunk_operator, lib.gdn_scalar_compose):
+    for f in (lib.gdn_replay, lib.gdn_replay_segmented, lib.gdn_replay_noalloc, lib.gdn_replay_raw,
+              lib.gdn_chunk_operator, lib.gdn_compose, lib.gdn_decode, lib.gdn_front_end,
+              lib.gdn_scalar_chunk_operator, lib.gdn_scalar_compose):
         f.restype = cint
     for f in (lib.gdn_replay_workspace_bytes, lib.gdn_replay_segmented_workspace_bytes,
-              lib.gdn_chunk_operator_workspace_bytes, lib.gdn_compose_workspace_bytes):
+              lib.gdn_replay_raw_workspace_bytes, lib.gdn_chunk_operator_workspace_bytes,
+              lib.gdn_compose_workspace_bytes):
         f.restype = sz
     lib.gdn_status_string.argtypes = [cint]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -159,6 +164,19 @@ def replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=None,
     ``segments`` (0 .. 64) calls gdn_replay_segmented with that many time
     segments per sequence; None calls gdn_replay.
     """
+    return _replay(q, k, v, alpha, beta, cu_seqlens, S0, want_o, o_dtype, out, S_out, stream, segments, False)
+
+
+def replay_raw(q_raw, k_raw, v, g, b, cu_seqlens, S0=None, want_o=True, o_dtype=None,
+               out=None, S_out=None, stream=None):
+    """gdn_replay_raw: the front end (normalised q and k, alpha = exp(g),
+    beta = sigmoid(b)) inside the replay, from raw bfloat16 projections.
+    Arguments and results as replay, with q_raw, k_raw, g and b in place of
+    q, k, alpha and beta."""
+    return _replay(q_raw, k_raw, v, g, b, cu_seqlens, S0, want_o, o_dtype, out, S_out, stream, None, True)
+
+
+def _replay(q, k, v, alpha, beta, cu_seqlens, S0, want_o, o_dtype, out, S_out, stream, segments, raw):
     torch = _torch()
     lib = library()
     for name, t in (("k", k), ("v", v), ("alpha", alpha), ("beta", beta),
@@ -190,7 +208,10 @@ def replay(q, k, v, alpha, beta, cu_seqlens, S0=None, want_o=True, o_dtype=None,
     _dev(S, "S_out")
     args = (_ptr(q) if want_o else None, _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
             _ptr(S0), _ptr(cu_seqlens), N, T, H, dk, dv, in_code, _ptr(o), o_code, _ptr(S))
-    if segments is None:
+    if raw:
+        ws, ws_bytes = _workspace(lib.gdn_replay_raw_workspace_bytes(N, T, H, dk, dv), k.device, stream)
+        _check(lib.gdn_replay_raw(*args, _ptr(ws), ws_bytes, _stream_ptr(stream)))
+    elif segments is None:
         ws, ws_bytes = _workspace(lib.gdn_replay_workspace_bytes(N, T, H, dk, dv), k.device, stream)
         _check(lib.gdn_replay(*args, _ptr(ws), ws_bytes, _stream_ptr(stream)))
     else:

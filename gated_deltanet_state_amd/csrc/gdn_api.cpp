@@ -171,11 +171,14 @@ size_t replay_workspace_max(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, i
   return best;
 }
 
+// raw: the inputs are raw projections (gdn_replay_raw; bf16 only): the
+// record builder normalises keys and queries and activates the gates, and
+// the workspace ends with their reciprocal norms.
 gdn_status replay_impl(const void *q, const void *k, const void *v, const void *alpha, const void *beta,
                        const float *S0, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
                        int32_t n_heads, int32_t dk, int32_t dv, gdn_dtype in_dtype, void *o, gdn_dtype o_dtype,
                        float *S_final, int32_t forced_segments, void *workspace, size_t workspace_bytes,
-                       gdn_stream_t stream, const char *fn) {
+                       gdn_stream_t stream, const char *fn, bool raw = false) {
   if (!k || !v || !alpha || !beta || !cu_seqlens || !S_final)
     return fail(GDN_ERR_NULL_POINTER, "%s: k, v, alpha, beta, cu_seqlens and S_final are required", fn);
   if (o && !q) return fail(GDN_ERR_NULL_POINTER, "%s: o requested without q", fn);
@@ -186,6 +189,7 @@ gdn_status replay_impl(const void *q, const void *k, const void *v, const void *
     return fail(GDN_ERR_UNSUPPORTED, "%s: dk and dv must be 64 or 128 (got %d, %d)", fn, dk, dv);
   if (!valid_dtype(in_dtype) || (o && !valid_dtype(o_dtype)))
     return fail(GDN_ERR_UNSUPPORTED, "%s: dtypes must be GDN_F32 or GDN_BF16", fn);
+  if (raw && in_dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "%s: raw inputs must be GDN_BF16", fn);
   if (n_tokens > kMaxTokens || n_heads > kMaxHeads || (int64_t)n_seqs * n_heads * (dv / 16) > (int64_t(1) << 30))
     return fail(GDN_ERR_UNSUPPORTED, "%s: problem too large for one call", fn);
   gdn_status s;
@@ -199,12 +203,17 @@ gdn_status replay_impl(const void *q, const void *k, const void *v, const void *
   const size_t tau_bytes = gdn::tau_workspace_bytes(n_tokens, n_seqs, n_heads);
   // longest-first sequence order (bf16 replays without a time split, built by the prep kernel)
   const bool ordered = bf && P == 1 && gdn::order_workspace_bytes(n_seqs) > 0;
-  const size_t need = replay_need(bf, o != nullptr, P, n_seqs, n_tokens, n_heads, dk, dv);
+  const size_t base = replay_need(bf, o != nullptr, P, n_seqs, n_tokens, n_heads, dk, dv);
+  const size_t need = base + (raw ? gdn::norm_workspace_bytes(n_tokens, n_seqs, n_heads) : 0);
   if (workspace_bytes < need || !workspace)
     return fail(GDN_ERR_WORKSPACE, "%s: workspace of %zu bytes required (got %zu)", fn, need, workspace_bytes);
   if ((s = check_align("workspace", workspace))) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float *norms = raw ? reinterpret_cast<float *>(static_cast<char *>(workspace) + base) : nullptr;
   gdn::PrepLaunch pp{};
+  pp.raw = raw ? 1 : 0;
+  pp.q = o ? q : nullptr;
+  pp.norms = norms;
   pp.k = k;
   pp.alpha = alpha;
   pp.beta = beta;
@@ -237,6 +246,8 @@ gdn_status replay_impl(const void *q, const void *k, const void *v, const void *
   p.in_bf16 = in_dtype == GDN_BF16;
   p.o = o;
   p.o_bf16 = o_dtype == GDN_BF16;
+  p.raw = raw ? 1 : 0;
+  p.norms = norms;
   p.n_segs = 1;
   if (P == 1) {
     p.order = order;
@@ -353,6 +364,19 @@ gdn_status gdn_replay(const void *q, const void *k, const void *v, const void *a
                       float *S_final, void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
   return replay_impl(q, k, v, alpha, beta, S0, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, in_dtype, o, o_dtype,
                      S_final, 0, workspace, workspace_bytes, stream, "gdn_replay");
+}
+
+size_t gdn_replay_raw_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t dk, int32_t dv) {
+  const size_t b = replay_workspace_max(n_seqs, n_tokens, n_heads, dk, dv, 0);
+  return b ? b + gdn::norm_workspace_bytes(n_tokens, n_seqs, n_heads) : 0;
+}
+
+gdn_status gdn_replay_raw(const void *q_raw, const void *k_raw, const void *v, const void *g, const void *b,
+                          const float *S0, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
+                          int32_t n_heads, int32_t dk, int32_t dv, gdn_dtype in_dtype, void *o, gdn_dtype o_dtype,
+                          float *S_final, void *workspace, size_t workspace_bytes, gdn_stream_t stream) {
+  return replay_impl(q_raw, k_raw, v, g, b, S0, cu_seqlens, n_seqs, n_tokens, n_heads, dk, dv, in_dtype, o, o_dtype,
+                     S_final, 0, workspace, workspace_bytes, stream, "gdn_replay_raw", true);
 }
 
 gdn_status gdn_replay_segmented(const void *q, const void *k, const void *v, const void *alpha, const void *beta,

@@ -74,7 +74,7 @@ struct Cfg {
   static constexpr int bKA = 0, bTF = NKA, bV = bTF + NTF, bQA = bV + NVB;
   static constexpr int NBLK = bQA + (WANT_O ? NKA : 0);
   static constexpr size_t BUF = (size_t)NBLK * 1024;
-  static constexpr int GN = 3 * CH + 4;        // gate floats per buffer set
+  static constexpr int GN = 6 * CH + 4;        // gate floats per buffer set
   static constexpr size_t oG = 2 * BUF;
   // outputs: M o Q K^T of two chunks as split-bf16 fragments (hi, lo planes)
   static constexpr size_t PSET = (size_t)2 * kTauFragPlane * 2;
@@ -90,10 +90,13 @@ struct Cfg {
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
-// Gate buffer (see the running scale gam in the kernel): [0, 64) gam e^g,
-// [64, 128) e^{g_L - g} / gam' (0 past the chunk), [128, 192) g, [192] the
+// Gate buffer (see the running scale gam in the kernel), per token: [0, 64)
+// gam e^g / |k| (the state read by the keys), [64, 128) e^{g_L - g} / gam' /
+// |k| (0 past the chunk), [128, 192) g, [192, 256) gam e^g / |q| (the state
+// read by the queries), [256, 320) 1 / |q|, [320, 384) 1 / |k|; [384] the
 // factor the chunk applies to the state registers (gam e^{g_L}, or 1: none).
-constexpr int G_EG = 0, G_DEC = 64, G_G = 128, G_EGL = 192;
+// The norms are 1 except for raw inputs (ChainLaunch::raw).
+constexpr int G_EG = 0, G_DEC = 64, G_G = 128, G_EQ = 192, G_RQ = 256, G_RK = 320, G_EGL = 384;
 
 // Unit swizzle of the staged value slab (VU 16-byte units per row): unit u
 // of row r sits at unit u ^ vswz(r), so that the 8 rows x 4 quads of a
@@ -356,10 +359,21 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     }
   };
 
-  unsigned short pa = 0x3f80;   // wave 0: alpha bits of token t0 + l (1.0 past the end)
+  // wave 0: alpha bits of token t0 + l (1.0 past the end; raw inputs: the
+  // log-gate, 0 past the end) and, for raw inputs, the token's reciprocal
+  // key and query norms
+  unsigned short pa = 0;
+  float rk = 1.f, rq = 1.f;
   auto load_alpha = [&](int t0, int Lc) {
-    pa = 0x3f80;
+    pa = p.raw ? 0 : 0x3f80;
     if (w == 0 && l < Lc) pa = ga[(int64_t)(t0 + l) * H + h];
+  };
+  auto load_norms = [&](int64_t slot, int Lc) {
+    if (p.raw && w == 0 && l < Lc) {
+      const float *nb = p.norms + (slot * H + h) * kNormFloats;
+      rk = nb[l];
+      rq = nb[kChunk + l];
+    }
   };
   // Running scale of the state.  The registers hold S / gam, gam a scalar
   // of the workgroup's (sequence, segment, head) that wave 0 tracks.  A
@@ -374,15 +388,21 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
   auto gates = [&](int b, int Lc, bool last) {
     if (w != 0) return;
     float *sG = sG0 + b * C::GN;
-    const float g = wave_inclusive_scan((l < Lc) ? log_gate(__uint_as_float((unsigned)pa << 16)) : 0.f);
+    const float x = __uint_as_float((unsigned)pa << 16);
+    const float lg = p.raw ? fmaxf(x, kLogGateFloor) : log_gate(x);
+    const float g = wave_inclusive_scan((l < Lc) ? lg : 0.f);
     const float gL = lane_value(g, Lc - 1);
     const float cand = gam * __expf(gL);
     const bool apply = last || !(cand >= 0x1p-40f);
     const float gnew = apply ? 1.f : cand;
     const float inv = 1.f / gnew;
-    sG[G_EG + l] = gam * __expf(g);
-    sG[G_DEC + l] = (l < Lc) ? __expf(gL - g) * inv : 0.f;
+    const float eg = gam * __expf(g);
+    sG[G_EG + l] = eg * rk;
+    sG[G_EQ + l] = eg * rq;
+    sG[G_DEC + l] = (l < Lc) ? __expf(gL - g) * inv * rk : 0.f;
     sG[G_G + l] = g;
+    sG[G_RQ + l] = rq;
+    sG[G_RK + l] = rk;
     if (l == 0) sG[G_EGL] = apply ? cand : 1.f;   // the registers' scale factor (1: none)
     gam = gnew;
   };
@@ -439,17 +459,26 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
       const bool own = c < nch;
       const int tc = own ? tbeg + c * CH : cbeg + (xb + c - nch) * CH;
       const int64_t sl = (int64_t)(cbeg / CH) + n + (tc - cbeg) / CH;
-      prep_chunk_wave<DK>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta), H, h,
-                          tc, min(CH, cend - tc), const_cast<char *>(grec) + (sl * H + h) * (int64_t)(kRecFloats * 4),
-                          scr, (own && c == 0) ? smem + C::bTF * 1024 : nullptr);
+      char *rec = const_cast<char *>(grec) + (sl * H + h) * (int64_t)(kRecFloats * 4);
+      char *lrec = (own && c == 0) ? smem + C::bTF * 1024 : nullptr;
+      if (p.raw)
+        prep_chunk_wave<DK, true>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta),
+                                  H, h, tc, min(CH, cend - tc), rec, scr, lrec, gq, p.norms + (sl * H + h) * kNormFloats);
+      else
+        prep_chunk_wave<DK>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta), H,
+                            h, tc, min(CH, cend - tc), rec, scr, lrec);
     }
     wait_vmem();
     __syncthreads();
-    if (tbeg < tend) gates(0, min(CH, tend - tbeg), tend - tbeg <= CH);
+    if (tbeg < tend) {
+      load_norms(slot0, min(CH, tend - tbeg));
+      gates(0, min(CH, tend - tbeg), tend - tbeg <= CH);
+    }
   } else if (tbeg < tend) {
     const int L0 = min(CH, tend - tbeg);
     issue_dma(0, tbeg, slot0);
     load_alpha(tbeg, L0);
+    load_norms(slot0, L0);
     gates(0, L0, tend - tbeg <= CH);
   }
   wait_vmem();
@@ -502,6 +531,12 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
       f32x4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = (s0 + e <= r) ? __expf(gr - gs[e]) * c[e] : 0.f;
+      if (p.raw) {   // the normalised query and key rows
+        const float qr = sG[G_RQ + r];
+        const f32x4 ks = *reinterpret_cast<const f32x4 *>(sG + G_RK + s0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] *= qr * ks[e];
+      }
       bf16x4 hi, lo;
       split4(x, hi, lo);
       *reinterpret_cast<bf16x4 *>(sP + (f * 64 + l) * 8 + 4 * half) = hi;
@@ -575,6 +610,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     if (more) {
       issue_dma(b ^ 1, t0 + CH, slot + 1, true, WANT_O ? 0 : -1);
       load_alpha(t0 + CH, L1);
+      load_norms(slot + 1, L1);
     }
     const char *buf = smem + b * C::BUF;
     const float *sG = sG0 + b * C::GN;
@@ -829,7 +865,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
         }
 #pragma unroll
         for (int bt = 0; bt < 4; ++bt) {
-          const float eg = sG[G_EG + 16 * bt + jl];
+          const float eg = sG[G_EQ + 16 * bt + jl];
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll

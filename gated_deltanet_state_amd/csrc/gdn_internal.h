@@ -50,12 +50,25 @@ constexpr int kRecFloats = 3072;
 // 5: (3,1).  Lane l holds row 16 bt + (l & 15), columns
 // 32 m + 4 (l >> 4) + {0..3} then 32 m + 16 + 4 (l >> 4) + {0..3}.
 constexpr int kTauFrags = 6;
+
+// Raw inputs (gdn_replay_raw: the front end folded into the replay).  The
+// gate arrays hold the log-gates g (alpha = e^g) and the write-strength
+// logits (beta = 1 / (1 + e^-b)), and the keys and queries are raw
+// projections.  The record builder stores, per (chunk slot, head), the
+// reciprocal norms 1 / |k_t| of the chunk's keys, then 1 / |q_t| of its
+// queries (0 for a zero row, and for queries when none are needed); every
+// product with a key or query row carries that factor.
+constexpr int kNormFloats = 2 * kChunk;
+
 constexpr int kTauFragPlane = kTauFrags * 64 * 8;  // bf16 elements per plane
 
 inline int64_t slot_count(int64_t n_tokens, int32_t n_seqs) { return n_tokens / kChunk + n_seqs + 1; }
 
 inline size_t tau_workspace_bytes(int64_t n_tokens, int32_t n_seqs, int32_t n_heads) {
   return (size_t)slot_count(n_tokens, n_seqs) * (size_t)n_heads * kRecFloats * sizeof(float);
+}
+inline size_t norm_workspace_bytes(int64_t n_tokens, int32_t n_seqs, int32_t n_heads) {
+  return (size_t)slot_count(n_tokens, n_seqs) * (size_t)n_heads * kNormFloats * sizeof(float);
 }
 
 // Longest-first order of the sequences of a packed replay that runs without
@@ -78,6 +91,11 @@ struct PrepLaunch {
   float *tau;        // [n_slots, H, kRecFloats] per-chunk factor records
   int64_t n_slots;
   int32_t *order;    // [n_seqs] longest-first sequence order to build, or null (bf16 only)
+  // raw inputs (bf16 only, see kNormFloats): k raw keys, alpha log-gates,
+  // beta logits; q raw queries (or null: no query norms needed)
+  int raw;
+  const void *q;
+  float *norms;      // [n_slots, H, kNormFloats]
 };
 
 // One launch of the chunked recurrence kernel.  A work item is one tile of
@@ -125,6 +143,11 @@ struct ChainLaunch {
   // [n_seqs] longest-first sequence order (PrepLaunch::order), or null;
   // used by the bf16 recurrence when each (sequence, head) is one workgroup
   const int32_t *order;
+  // raw inputs (kNormFloats): alpha holds log-gates, beta logits, k and q
+  // raw projections; norms [n_slots, H, kNormFloats] come from the record
+  // builder (written by the fused prologue, read by the recurrence)
+  int raw;
+  float *norms;
 };
 
 

@@ -43,7 +43,7 @@ __device__ __forceinline__ void rank_sequences(const int32_t *cu, int n_seqs, in
   }
 }
 
-template <int DK>
+template <int DK, bool RAW>
 __global__ void __launch_bounds__(PW * 64) prep_bf16_kernel(PrepLaunch p) {
   __shared__ __attribute__((aligned(16))) float scratch[PW][kPrepWaveLds / 4];
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
@@ -58,15 +58,18 @@ __global__ void __launch_bounds__(PW * 64) prep_bf16_kernel(PrepLaunch p) {
   const int t0 = tbeg + (int)j * kChunk;
   const int Lc = min(kChunk, len - (int)j * kChunk);
   char *rec = reinterpret_cast<char *>(p.tau + (slot * H + h) * (int64_t)kRecFloats);
-  prep_chunk_wave<DK>(reinterpret_cast<const bf16 *>(p.k), reinterpret_cast<const bf16 *>(p.alpha),
-                      reinterpret_cast<const bf16 *>(p.beta), H, h, t0, Lc, rec, scratch[w], nullptr);
+  prep_chunk_wave<DK, RAW>(reinterpret_cast<const bf16 *>(p.k), reinterpret_cast<const bf16 *>(p.alpha),
+                           reinterpret_cast<const bf16 *>(p.beta), H, h, t0, Lc, rec, scratch[w], nullptr,
+                           reinterpret_cast<const bf16 *>(p.q), RAW ? p.norms + (slot * H + h) * kNormFloats : nullptr);
 }
 
 template <int DK>
 hipError_t launch_pb(const PrepLaunch &p, hipStream_t stream) {
   if (p.n_slots <= 0) return hipSuccess;
-  return launch_kernel(prep_bf16_kernel<DK>, dim3((unsigned)((p.n_slots + PW - 1) / PW), (unsigned)p.H),
-                       dim3(PW * 64), 0, stream, p);
+  if (p.raw && !p.norms) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((p.n_slots + PW - 1) / PW), (unsigned)p.H);
+  return p.raw ? launch_kernel(prep_bf16_kernel<DK, true>, grid, dim3(PW * 64), 0, stream, p)
+               : launch_kernel(prep_bf16_kernel<DK, false>, grid, dim3(PW * 64), 0, stream, p);
 }
 
 }  // namespace

@@ -22,8 +22,14 @@
 //      split-bf16 k = 16 MFMAs, in three dependency levels
 //   5. Tau diag(beta) as split-bf16 A fragments of the recurrence kernel's
 //      k = 32 products (record layout of gdn_internal.h).
+// Raw inputs (RAW, gdn_internal.h kNormFloats): the gates come from the
+// log-gates and logits, and the keys are normalised on the way: the
+// diagonal blocks of K K^T hold |k_t|^2, so A takes the factor
+// 1 / (|k_r| |k_s|); the query norms come from the diagonal blocks of
+// Q Q^T the same way, and both reciprocal norms go to the chunk's norms
+// block.
 // LDS per wave: kPrepWaveLds bytes (A blocks, overwritten in place by the
-// Tau blocks; gates).
+// Tau blocks; gates; reciprocal norms).
 #pragma once
 
 #include "gdn_device.h"
@@ -31,7 +37,7 @@
 
 namespace gdn {
 
-constexpr int kPrepWaveLds = (10 * 256 + 2 * 64) * 4;
+constexpr int kPrepWaveLds = (10 * 256 + 4 * 64) * 4;
 
 namespace prep_detail {
 
@@ -79,19 +85,40 @@ __device__ __forceinline__ void prep_load_keys(const bf16 *k, int H, int h, int 
   }
 }
 
+// Offsets in the per-wave LDS scratch (floats): A / Tau blocks, cumulative
+// log-gates, betas, reciprocal key norms, reciprocal query norms.
+constexpr int kPrepG = 10 * 256, kPrepB = kPrepG + 64, kPrepK = kPrepB + 64, kPrepQ = kPrepK + 64;
+
+// The reciprocal norms of the diagonal blocks acc[blk(b, b)] of X X^T (C
+// layout: lane (c, g) holds rows 4 g .. 4 g + 3 of column c, so the lanes
+// with g = c >> 2 hold the diagonal) into dst[0 .. 63]; 0 for a zero row.
+__device__ __forceinline__ void diag_rnorms(const f32x4 (&d)[4], float *dst) {
+  const int l = lane_id(), g4 = l >> 4, jl = l & 15;
+  if (g4 == (jl >> 2)) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float n2 = d[b][jl & 3];
+      dst[16 * b + jl] = n2 > 0.f ? rsqrtf(n2) : 0.f;
+    }
+  }
+}
+
 // Record of one (chunk, head) from its keys kf (prep_load_keys): tokens
 // t0 .. t0 + Lc - 1 (1 <= Lc <= 64) of head h, gates alpha / beta [T, H]
 // (bf16); rec receives kRecFloats * 4 bytes; scratch is this wave's
 // kPrepWaveLds bytes of LDS; lds_rec (may be null) receives a second copy of
-// the Tau fragments in LDS.
-template <int DK>
+// the Tau fragments in LDS.  RAW: alpha and beta hold log-gates and logits,
+// the keys are raw, and norms (kNormFloats floats) receives the reciprocal
+// key norms and, when q (raw queries [T, H, DK]) is given, the query ones.
+template <int DK, bool RAW = false>
 __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 32], const bf16 *alpha,
                                                      const bf16 *beta, int H, int h, int t0, int Lc, char *rec,
-                                                     float *scratch, char *lds_rec = nullptr) {
+                                                     float *scratch, char *lds_rec = nullptr,
+                                                     const bf16 *q = nullptr, float *norms = nullptr) {
   using namespace prep_detail;
   constexpr int NKS = DK / 32;
   float *sA = scratch;             // 10 blocks 16 x 16 row-major: A, then Tau
-  float *sG = sA + 10 * 256, *sB = sG + 64;
+  float *sG = scratch + kPrepG, *sB = scratch + kPrepB, *sK = scratch + kPrepK, *sQ = scratch + kPrepQ;
   const int l = lane_id(), g4 = l >> 4, jl = l & 15;
 
   // ---- 1. gates (the keys are in kf) ----
@@ -99,8 +126,13 @@ __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 
     float g = 0.f, b = 0.f;
     if (l < Lc) {
       const int64_t gi = (int64_t)(t0 + l) * H + h;
-      g = log_gate((float)alpha[gi]);
-      b = (float)beta[gi];
+      if constexpr (RAW) {
+        g = fmaxf((float)alpha[gi], kLogGateFloor);
+        b = 1.f / (1.f + __expf(-(float)beta[gi]));
+      } else {
+        g = log_gate((float)alpha[gi]);
+        b = (float)beta[gi];
+      }
     }
     const float gs = wave_inclusive_scan(g);
     sG[l] = gs;
@@ -119,6 +151,11 @@ __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
         for (int bj = 0; bj <= bi; ++bj) acc[blk(bi, bj)] = mfma_bf16(kf[bi][m], kf[bj][m], acc[blk(bi, bj)]);
+    if constexpr (RAW) {
+      const f32x4 dg[4] = {acc[blk(0, 0)], acc[blk(1, 1)], acc[blk(2, 2)], acc[blk(3, 3)]};
+      diag_rnorms(dg, sK);
+      wave_lds_fence();
+    }
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
@@ -126,7 +163,13 @@ __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 
         const int col = 16 * bj + jl, row0 = 16 * bi + 4 * g4;
         const float gc = sG[col];
         const f32x4 gr = *reinterpret_cast<const f32x4 *>(sG + row0);
-        const f32x4 br = *reinterpret_cast<const f32x4 *>(sB + row0);
+        f32x4 br = *reinterpret_cast<const f32x4 *>(sB + row0);
+        if constexpr (RAW) {   // beta_r / (|k_r| |k_s|)
+          const float kc = sK[col];
+          const f32x4 kr = *reinterpret_cast<const f32x4 *>(sK + row0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) br[e] *= kr[e] * kc;
+        }
         float *dst = sA + blk(bi, bj) * 256 + 4 * g4 * 16 + jl;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -258,15 +301,39 @@ __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 
     }
   };
   write_frags(rec, lds_rec, true);
+
+  if constexpr (RAW) {
+    if (!q) sQ[l] = 0.f;   // (else prep_chunk_wave put the query norms there)
+    wave_lds_fence();
+    norms[l] = sK[l];
+    norms[kChunk + l] = sQ[l];
+  }
 }
 
 // Record of one (chunk, head), keys loaded here (see prep_chunk_wave_keys).
-template <int DK>
+template <int DK, bool RAW = false>
 __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha, const bf16 *beta, int H, int h,
-                                                int t0, int Lc, char *rec, float *scratch, char *lds_rec = nullptr) {
+                                                int t0, int Lc, char *rec, float *scratch, char *lds_rec = nullptr,
+                                                const bf16 *q = nullptr, float *norms = nullptr) {
+  if constexpr (RAW) {
+    // query norms first (the diagonal blocks of Q Q^T), before the keys
+    // take their registers
+    if (q) {
+      bf16x8 qf[4][DK / 32];
+      prep_load_keys<DK>(q, H, h, t0, Lc, qf);
+      f32x4 dq[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        dq[b] = zero4();
+#pragma unroll
+        for (int m = 0; m < DK / 32; ++m) dq[b] = mfma_bf16(qf[b][m], qf[b][m], dq[b]);
+      }
+      diag_rnorms(dq, scratch + kPrepQ);
+    }
+  }
   bf16x8 kf[4][DK / 32];
   prep_load_keys<DK>(k, H, h, t0, Lc, kf);
-  prep_chunk_wave_keys<DK>(kf, alpha, beta, H, h, t0, Lc, rec, scratch, lds_rec);
+  prep_chunk_wave_keys<DK, RAW>(kf, alpha, beta, H, h, t0, Lc, rec, scratch, lds_rec, q, norms);
 }
 
 }  // namespace gdn

@@ -41,8 +41,9 @@ extern "C" {
  * 2: adds gdn_decode, gdn_front_end, gdn_scalar_chunk_operator and
  *    gdn_scalar_compose; the version 1 calls are unchanged.
  * 3: adds gdn_replay_segmented and gdn_replay_noalloc; gates alpha = 0
- *    are accepted (see above); the earlier calls are unchanged. */
-#define GDN_ABI_VERSION 3
+ *    are accepted (see above); the earlier calls are unchanged.
+ * 4: adds gdn_replay_raw; the earlier calls are unchanged. */
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -135,6 +136,43 @@ gdn_status gdn_replay_segmented(const void *q, const void *k, const void *v,
 size_t gdn_replay_segmented_workspace_bytes(int32_t n_seqs, int64_t n_tokens,
                                             int32_t n_heads, int32_t dk,
                                             int32_t dv, int32_t segments);
+
+/*
+ * gdn_replay_raw -- gdn_front_end followed by gdn_replay in one call, from
+ * the raw projections: the front end runs inside the replay's own kernels,
+ * so the normalised queries and keys and the activated gates are never
+ * written to memory or rounded to bf16.
+ * Page: Tail-Replay, section 3 (the replayed hidden states produce the keys,
+ * values, transitions and write strengths at each replay step) with
+ * section 2 Eq. (1).  Per (token, head), in fp32:
+ *     q = q_raw / |q_raw|,  k = k_raw / |k_raw|   (a zero row gives zeros)
+ *     alpha = exp(g),       beta = 1 / (1 + exp(-b))
+ * then the recurrence of gdn_replay with those inputs.  The log-gate has the
+ * floor of gdn_replay (log alpha >= -60), taken on g directly.
+ *
+ *   q_raw, k_raw  [n_tokens, H, dk]  bf16 (q_raw only read when o is given)
+ *   v             [n_tokens, H, dv]  bf16
+ *   g, b          [n_tokens, H]      bf16 log-gates and write-strength logits
+ *   S0, cu_seqlens, o, o_dtype, S_final: as gdn_replay.
+ *   in_dtype must be GDN_BF16 (GDN_ERR_UNSUPPORTED otherwise).
+ *   workspace: gdn_replay_raw_workspace_bytes(...) bytes (the replay's
+ *   workspace and 512 bytes of reciprocal norms per chunk slot and head).
+ * Errors and everything else as gdn_replay.  The result equals
+ * gdn_front_end + gdn_replay up to the rounding of the normalised inputs to
+ * bf16, which this call skips.
+ */
+gdn_status gdn_replay_raw(const void *q_raw, const void *k_raw, const void *v,
+                          const void *g, const void *b, const float *S0,
+                          const int32_t *cu_seqlens, int32_t n_seqs,
+                          int64_t n_tokens, int32_t n_heads, int32_t dk,
+                          int32_t dv, gdn_dtype in_dtype, void *o,
+                          gdn_dtype o_dtype, float *S_final, void *workspace,
+                          size_t workspace_bytes, gdn_stream_t stream);
+
+/* Workspace bytes for gdn_replay_raw (as gdn_replay_workspace_bytes, with
+ * the norms). */
+size_t gdn_replay_raw_workspace_bytes(int32_t n_seqs, int64_t n_tokens,
+                                      int32_t n_heads, int32_t dk, int32_t dv);
 
 /*
  * gdn_replay_noalloc -- gdn_replay for callers that cannot allocate device

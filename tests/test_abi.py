@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
     for code, name in [(0, b"GDN_OK"), (1, b"GDN_ERR_NULL_POINTER"), (2, b"GDN_ERR_BAD_SHAPE"),
                        (3, b"GDN_ERR_UNSUPPORTED"), (4, b"GDN_ERR_ALIGNMENT"),
                        (5, b"GDN_ERR_WORKSPACE"), (6, b"GDN_ERR_HIP")]:
@@ -88,6 +88,21 @@ def test_segmented_replay_argument_checks(lib):
     assert rs(3) == WS                              # workspace checked before any launch
     assert b"gdn_replay_segmented" in lib.gdn_last_error()
     assert rs(0, k=P + 2) == ALIGN
+
+
+def test_raw_replay_argument_checks(lib):
+    def rr(dt=BF16, k=P, ws=None, nbytes=0):
+        return lib.gdn_replay_raw(P, k, P, P, P, None, P, 1, 10, 2, 64, 64, dt, P, F32, P, ws, nbytes, None)
+    assert rr(dt=F32) == UNSUP and b"GDN_BF16" in lib.gdn_last_error()
+    assert rr(k=None) == NULLP
+    assert rr() == WS and b"gdn_replay_raw" in lib.gdn_last_error()
+    # the workspace adds 512 bytes of reciprocal norms per chunk slot and
+    # head to the replay's; a single long sequence over few heads takes the
+    # time split (segment operators beyond the records and norms)
+    slots = 4000 // 64 + 1 + 1
+    assert lib.gdn_replay_raw_workspace_bytes(1, 4000, 4, 128, 128) == \
+        lib.gdn_replay_workspace_bytes(1, 4000, 4, 128, 128) + slots * 4 * 512
+    assert lib.gdn_replay_workspace_bytes(1, 4000, 4, 128, 128) > slots * 4 * 12288
 
 
 def test_chunk_operator_argument_checks(lib):
