@@ -263,11 +263,23 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
   }
   const int64_t slot0 = (int64_t)(cbeg / CH) + n + (tbeg - cbeg) / CH;
 
+  // Staged K and Q fragments.  Element (row r, 8-column group g) of a 1 KiB
+  // fragment block -- lane r + 16 g of the MFMA A operand -- sits in 16-byte
+  // slot 16 g + (r ^ 12 (g & 1)) (kq_slot).  A 16-byte read by lane services
+  // each half-wave in two passes of 16 lanes, the quads whose index has even,
+  // then odd, bit parity; with this order each pass meets 16 distinct
+  // 16-byte bank groups, as in the plain order.  The transposing 8-byte
+  // reads of K^T service 32 lanes at once and read the same half of 32
+  // slots: in the plain order those fall on 8 bank groups (4-way conflicts),
+  // in this one on 16 (2-way, the least for same-half reads).  (Lane grouping
+  // and conflict counts measured with SQ_LDS_BANK_CONFLICT on MI355X.)
+  auto kq_slot = [](int r, int g) { return 16 * g + (r ^ (12 * (g & 1))); };
+  const int kq_l = kq_slot(jl, g4);   // this lane's own slot (A operand reads)
   // LDS byte address (buffer set 0) of this lane's transposing reads of the
   // staged keys: key row 4 g + (jl >> 2) of a 16-row block, 8-column group
   // jl & 3 (see kt_frags)
   const uint32_t kt_lds = (uint32_t)(uintptr_t)(lds_void *)(smem + C::bKA * 1024) +
-                          16u * (uint32_t)(4 * g4 + (jl >> 2) + 16 * (jl & 3));
+                          16u * (uint32_t)kq_slot(4 * g4 + (jl >> 2), jl & 3);
   const bf16 *gk = reinterpret_cast<const bf16 *>(p.k);
   const bf16 *gq = reinterpret_cast<const bf16 *>(p.q);
   const bf16 *gv = reinterpret_cast<const bf16 *>(p.v);
@@ -312,9 +324,9 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
   constexpr int JK = (C::NKA + NW - 1) / NW, JT = (C::NTF + NW - 1) / NW, JV = (C::NVB + NW - 1) / NW;
   uint32_t off_kq[JK], off_v[JV];
 #pragma unroll
-  for (int j = 0; j < JK; ++j) {                 // K (and Q) A fragment (bt, m): key row 16 bt + jl
-    const int f = j * NW + w, bt = f / C::NKS, m = f % C::NKS;
-    off_kq[j] = (uint32_t)(16 * bt + jl) * tok_k + 64 * m + 16 * g4;
+  for (int j = 0; j < JK; ++j) {                 // K (and Q) A fragment (bt, m): slot l holds key row
+    const int f = j * NW + w, bt = f / C::NKS, m = f % C::NKS;   // 16 bt + r, group g with kq_slot(r, g) = l
+    off_kq[j] = (uint32_t)(16 * bt + (jl ^ (12 * (g4 & 1)))) * tok_k + 64 * m + 16 * g4;
   }
 #pragma unroll
   for (int j = 0; j < JV; ++j) {                 // value slab: logical unit u (8 columns) of row r
@@ -520,8 +532,8 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
       if (bj <= bi) {
 #pragma unroll
         for (int m = 0; m < C::NKS; ++m) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(buf + (C::bKA + bj * C::NKS + m) * 1024 + 16 * l);
-          const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(buf + (C::bQA + bi * C::NKS + m) * 1024 + 16 * l);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(buf + (C::bKA + bj * C::NKS + m) * 1024 + 16 * kq_l);
+          const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(buf + (C::bQA + bi * C::NKS + m) * 1024 + 16 * kq_l);
           c = mfma_bf16(ka, qb, c);
         }
       }
@@ -615,6 +627,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     const char *buf = smem + b * C::BUF;
     const float *sG = sG0 + b * C::GN;
     auto frag = [&](int blk) { return *reinterpret_cast<const bf16x8 *>(buf + blk * 1024 + 16 * l); };
+    auto kqfrag = [&](int blk) { return *reinterpret_cast<const bf16x8 *>(buf + blk * 1024 + 16 * kq_l); };
 
     if constexpr (RT == 2 && !WANT_O) {
       // ---- two row tiles, skewed by one stage: tile 1's vector-ALU work
@@ -710,7 +723,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
 #pragma unroll
           for (int bt = 0; bt < 4; ++bt)
 #pragma unroll
-            for (int m = 0; m < NKS; ++m) ka[bt][m] = frag(C::bKA + bt * NKS + m);
+            for (int m = 0; m < NKS; ++m) ka[bt][m] = kqfrag(C::bKA + bt * NKS + m);
           split_s(st[0], sh0, sl0);
           y_mfma(ka, sh0, sl0, y0);
           split_s(st[1], sh1, sl1);
@@ -764,7 +777,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
       for (int m = 0; m < C::NKS; ++m) {
         bf16x8 a[4];
 #pragma unroll
-        for (int bt = 0; bt < 4; ++bt) a[bt] = frag(C::bKA + bt * C::NKS + m);
+        for (int bt = 0; bt < 4; ++bt) a[bt] = kqfrag(C::bKA + bt * C::NKS + m);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -853,7 +866,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
         for (int m = 0; m < C::NKS; ++m) {
           bf16x8 a[4];
 #pragma unroll
-          for (int bt = 0; bt < 4; ++bt) a[bt] = frag(C::bQA + bt * C::NKS + m);
+          for (int bt = 0; bt < 4; ++bt) a[bt] = kqfrag(C::bQA + bt * C::NKS + m);
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
