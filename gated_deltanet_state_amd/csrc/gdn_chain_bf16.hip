@@ -577,6 +577,44 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
           zp[rt][bt] = mfma_bf16(pass == 1 ? dpl[rt][m] : dph[rt][m], pass == 2 ? pl[f] : ph[f], zp[rt][bt]);
         }
   };
+  // Finished outputs wait in zs (tokens ts .. ts + Ls - 1) until the end of
+  // the chunk step and are stored after its wait for the load-to-LDS copies:
+  // that wait (vmcnt 0) covers every outstanding vector memory operation of
+  // the wave, stores included, so stores issued earlier in the step hold up
+  // the hand-over barrier (and every wave with it); issued after the wait,
+  // they have the whole next step to drain.  (32768-token prefill -1.9%,
+  // packed tails -3.4% against storing right after the outputs are
+  // finished, in the middle of the step.)
+  f32x4 zs[RT][4];
+  int ts = 0, Ls = 0;
+  auto stash_o = [&]() {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) zs[rt][bt] = zp[rt][bt];
+    ts = tp;
+    Ls = Lp;
+    Lp = 0;
+  };
+  auto store_s = [&]() {
+    const int64_t tok = (int64_t)H * DV;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int64_t ob = ((int64_t)(ts + jl) * H + h) * DV + row0 + 16 * rt + 4 * g4;
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        if (16 * bt + jl < Ls) {
+          if (p.o_bf16) {
+            *reinterpret_cast<uint2 *>(reinterpret_cast<bf16 *>(p.o) + ob + 16 * bt * tok) =
+                uint2{pack_bf16x2(zs[rt][bt][0], zs[rt][bt][1]), pack_bf16x2(zs[rt][bt][2], zs[rt][bt][3])};
+          } else {
+            *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.o) + ob + 16 * bt * tok) = zs[rt][bt];
+          }
+        }
+      }
+    }
+    Ls = 0;
+  };
   auto store_o = [&]() {
     // lane (q, g) of block bt holds token tp + 16 bt + q, value columns
     // row0 + 16 rt + 4 g .. + 3: one 16-byte (8-byte in bf16) store each
@@ -843,7 +881,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
         // hand-over barrier), then the second half of the next chunk's copies
         if (active && Lp > 0) {
           finish_o(b ^ 1);
-          store_o();
+          stash_o();
         }
         if (more) issue_dma(b ^ 1, t0 + CH, slot + 1, true, 1);
       }
@@ -936,6 +974,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     // ---- hand over to the next chunk ----
     if (more) gates(b ^ 1, L1, t0 + 2 * CH >= tend);
     wait_vmem();
+    if (WANT_O && active && Ls > 0) store_s();
     lds_barrier();
     if (more) read_v(b ^ 1);
   }
