@@ -187,8 +187,35 @@ def issue_table(mfma_dir, stats):
     return rows
 
 
+CYCLE_COUNTERS = ["SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                  "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"]
+
+
+def cycle_table(cycle_dir):
+    """Rows of the wave-cycle table from one --pmc run of CYCLE_COUNTERS: per
+    kernel, the share of its waves' cycles spent issuing any instruction,
+    vector-ALU and LDS instructions, waiting on a dependency (s_waitcnt,
+    barrier), and ready but not chosen for issue (another wave of the SIMD
+    issued); and the share of the LDS's active cycles lost to bank
+    conflicts."""
+    vals = {c: _counter_kib(cycle_dir, c) for c in CYCLE_COUNTERS}
+    rows = {}
+    for k in sorted(vals["SQ_WAVE_CYCLES"]):
+        if "rocclr" in k:
+            continue
+        wc = vals["SQ_WAVE_CYCLES"][k] or float("nan")
+        idx = vals["SQ_LDS_IDX_ACTIVE"].get(k, 0.0)
+        rows[k] = dict(active=vals["SQ_ACTIVE_INST_ANY"].get(k, 0.0) / wc,
+                       valu=vals["SQ_ACTIVE_INST_VALU"].get(k, 0.0) / wc,
+                       lds=vals["SQ_ACTIVE_INST_LDS"].get(k, 0.0) / wc,
+                       wait=vals["SQ_WAIT_ANY"].get(k, 0.0) / wc,
+                       wait_issue=vals["SQ_WAIT_INST_ANY"].get(k, 0.0) / wc,
+                       lds_conflict=(vals["SQ_LDS_BANK_CONFLICT"].get(k, 0.0) / idx) if idx else None)
+    return rows
+
+
 def summarize_counters(wid, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, command="",
-                       name=None, mfma_dir=None):
+                       name=None, mfma_dir=None, cycle_dir=None):
     """profiles/<workload>.md and profiles/traffic_<workload>.json from
     rocprofv3 runs of this script: a --kernel-trace --stats run, one --pmc
     FETCH_SIZE run, one --pmc WRITE_SIZE run, and the same two counters on a
@@ -217,6 +244,9 @@ def summarize_counters(wid, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_
     issue = issue_table(mfma_dir, stats) if mfma_dir else None
     if issue:
         rec["issue"] = issue
+    cycles = cycle_table(cycle_dir) if cycle_dir else None
+    if cycles:
+        rec["wave_cycles"] = cycles
     with open(os.path.join(ROOT, "profiles", "traffic_%s.json" % wname), "w") as f:
         json.dump(rec, f, indent=1)
     lines = ["# %s: kernel times and HBM traffic" % wname, "",
@@ -252,6 +282,19 @@ def summarize_counters(wid, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_
                 "%.1f%%" % (100 * v["mfma_frac_of_peak"]) if "mfma_frac_of_peak" in v else "-",
                 v["valu_per_wave"], v["mfma_per_wave"], v["lds_per_wave"], v["salu_per_wave"],
                 v["mfma_busy_cycles"], v["grbm_gui_active"]))
+        lines.append("")
+    if cycles:
+        lines += ["Where the waves' cycles go (one `--pmc` run of %s; shares of SQ_WAVE_CYCLES: issuing any "
+                  "instruction (SQ_ACTIVE_INST_ANY), of which vector ALU and LDS, waiting on a dependency or "
+                  "barrier (SQ_WAIT_ANY), ready but not issued because another wave of the SIMD issued "
+                  "(SQ_WAIT_INST_ANY); LDS bank conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE):"
+                  % ", ".join(CYCLE_COUNTERS), "",
+                  "| kernel | issuing | vector ALU | LDS | waiting | not chosen | LDS bank-conflict cycles |",
+                  "|---|---|---|---|---|---|---|"]
+        for k, v in cycles.items():
+            lines.append("| %s | %.1f%% | %.1f%% | %.1f%% | %.1f%% | %.1f%% | %s |" % (
+                k, 100 * v["active"], 100 * v["valu"], 100 * v["lds"], 100 * v["wait"], 100 * v["wait_issue"],
+                "%.1f%%" % (100 * v["lds_conflict"]) if v["lds_conflict"] is not None else "-"))
         lines.append("")
     with open(os.path.join(ROOT, "profiles", "%s.md" % wname), "w") as f:
         f.write("\n".join(lines))
@@ -614,6 +657,8 @@ def main():
     ap.add_argument("--command", default="", help="with --summarize-counters: the command line profiled")
     ap.add_argument("--issue-counters", default=None, metavar="DIR",
                     help="with --summarize-counters: a --pmc run of the MFMA / issue counters (ISSUE_COUNTERS)")
+    ap.add_argument("--cycle-counters", default=None, metavar="DIR",
+                    help="with --summarize-counters: a --pmc run of the wave-cycle counters (CYCLE_COUNTERS)")
     ap.add_argument("--tail-curve", action="store_true",
                     help="only report the tail-replay state error against the replayed fraction")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
@@ -633,7 +678,7 @@ def main():
         name = (("decode-%dx1-H32-d128-bf16" % args.decode) if args.decode else FRONT_NAME if args.front_end
                 else SCALAR_NAME if args.scalar_ops else None)
         summarize_counters(args.workload, *args.summarize_counters, command=args.command, name=name,
-                           mfma_dir=args.issue_counters)
+                           mfma_dir=args.issue_counters, cycle_dir=args.cycle_counters)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the replay path is a single-GPU kernel library "
