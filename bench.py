@@ -690,14 +690,23 @@ def main():
     import torch
 
     if args.calibrate_copy:
+        # also the practical ceiling of a streaming kernel: a device copy
+        # (each byte read once and written once), timed with HIP events
         n = args.calibrate_copy * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        for _ in range(args.warmup + args.steps):
+        for _ in range(args.warmup):
             dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e1.record()
         torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
         print(json.dumps(dict(calibration="copy", bytes_read=n * 4, bytes_written=n * 4,
-                              launches=args.warmup + args.steps)))
+                              launches=args.warmup + args.steps, ms_per_copy=round(ms, 5),
+                              read_plus_write_GBps=round(2 * n * 4 / (ms / 1e3) / 1e9, 1))))
         return
 
     import gated_deltanet_state_amd as gdn
