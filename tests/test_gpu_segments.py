@@ -101,6 +101,20 @@ def test_split_with_outputs_shapes(dk, dv):
     check_o(inp, S0=start_state(2, 2, dv, dk, 54), P=4)
 
 
+@pytest.mark.parametrize("law", ["workload", "strong"])
+def test_split_with_outputs_lead_layout_many_segments(law):
+    # the layout of a long split with outputs: a short lead segment that
+    # runs with its outputs beside the transition segments (and builds the
+    # last segment's records), then every later segment with outputs; nine
+    # segments as the cost model picks for one sequence over 32 heads, here
+    # on sequences of different lengths (one of them shorter than the
+    # segment count in chunks, one empty) with a start state
+    kw = dict(gate_scale=5.0) if law == "strong" else {}
+    lengths = [2000, 1500, 0, 300, 640]
+    inp = workloads.generate(lengths, H=2, dk=128, dv=128, dtype="bf16", seed=60, **kw)
+    check_o(inp, S0=start_state(len(lengths), 2, 128, 128, 61), P=9)
+
+
 def test_split_with_outputs_alpha_one_matches_unsplit():
     # alpha = 1: every segment's start state carries real weight
     inp = workloads.generate([1500], H=4, dk=128, dv=128, dtype="bf16", seed=55, alpha_one=True)
