@@ -69,8 +69,12 @@ hipError_t launch_of(const float *T, int64_t n_ops, void *frag, hipStream_t stre
 // applied (from_start: gdn_compose), then S <- S T_seg[s] + S_seg[s],
 // computed as S_new^T = T^T S^T + S_seg^T.  The operators arrive as
 // split-bf16 MFMA fragments (gdn_internal.h).
-// Workgroup = 4 waves on 32 rows of one (sequence, head); wave w owns dk
-// blocks JBW w .. JBW w + JBW - 1 of S^T (C layout) for both 16-row tiles,
+// Workgroup = 4 waves on 32 rows (RTC = 2 row tiles) of one (sequence,
+// head), or on 16 rows (RTC = 1) when the 32-row workgroups would leave
+// compute units idle (the chain is bound by its per-step latency, so twice
+// the workgroups halve each one's products: 64 operators over 32 heads in
+// 0.130 against 0.149 ms); wave w owns dk
+// blocks JBW w .. JBW w + JBW - 1 of S^T (C layout) for its row tiles,
 // so it needs only its own fragments of each operator: those, and its rows
 // of each local state, are loaded straight into registers two steps ahead
 // (three register sets in rotation), which hides the load latency of the
@@ -90,33 +94,34 @@ struct SegCfg {
 
 // One step's operands of a wave: its operator fragments (hi, lo) and its
 // rows of the local state.
-template <int DK>
+template <int DK, int RTC>
 struct StepRegs {
   bf16x8 h[SegCfg<DK>::JBW][SegCfg<DK>::NKS], l[SegCfg<DK>::JBW][SegCfg<DK>::NKS];
-  f32x4 loc[2][SegCfg<DK>::JBW];
+  f32x4 loc[RTC][SegCfg<DK>::JBW];
 };
 
-template <int DK>
+template <int DK, int RTC>
 __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch p, int n_items) {
   using C = SegCfg<DK>;
   constexpr int NKS = C::NKS, JBW = C::JBW, NF = C::NF, LDB = C::LDB;
-  __shared__ __attribute__((aligned(16))) bf16 sSh[32 * LDB];
-  __shared__ __attribute__((aligned(16))) bf16 sSl[32 * LDB];
+  constexpr int NP = RTC == 1 ? 3 : 1;   // accumulators per product (the split passes apart when few rotate)
+  __shared__ __attribute__((aligned(16))) bf16 sSh[16 * RTC * LDB];
+  __shared__ __attribute__((aligned(16))) bf16 sSl[16 * RTC * LDB];
 
   const int per = (int)(gridDim.x >> 3);
   const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (item >= n_items) return;
-  const int groups = p.dv / 32;
+  const int groups = p.dv / (16 * RTC);
   const int nh = item / groups, rg = item % groups;
   const int n = nh / p.H, h = nh % p.H;
   const int H = p.H, DV = p.dv, P = p.n_segs;
   const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), g4 = l >> 4, jl = l & 15;
   const int jb0 = JBW * w;
   // lane's element offset of row tile rt, dk block jb0 + i: row 32 rg + 16 rt + jl, columns 16 jb + 4 g4 ..
-  auto eoff = [&](int rt, int i) { return (int64_t)(32 * rg + 16 * rt + jl) * DK + 16 * (jb0 + i) + 4 * g4; };
+  auto eoff = [&](int rt, int i) { return (int64_t)(16 * RTC * rg + 16 * rt + jl) * DK + 16 * (jb0 + i) + 4 * g4; };
   const int64_t head = ((int64_t)n * H + h) * DV * DK;
 
-  auto load = [&](int s, StepRegs<DK> &R) {
+  auto load = [&](int s, StepRegs<DK, RTC> &R) {
     const char *op = reinterpret_cast<const char *>(p.T_frag) + (((int64_t)n * P + s) * H + h) * (int64_t)C::OPB + 16 * l;
 #pragma unroll
     for (int i = 0; i < JBW; ++i)
@@ -128,48 +133,48 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
       }
     const float *Ls = p.S_seg + (((int64_t)n * P + s) * H + h) * DV * DK;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
       for (int i = 0; i < JBW; ++i) R.loc[rt][i] = *reinterpret_cast<const f32x4 *>(Ls + eoff(rt, i));
   };
 
-  f32x4 acc[2][JBW];
+  f32x4 acc[RTC][JBW];
   const int s0 = p.from_start ? 0 : 1;   // first operator applied
   {
     // the state entering the chain: S0 (or zero), or segment 0's own state
     // (S0 may alias S_out: every workgroup reads its own rows here, first)
     const float *src = (p.from_start || p.S_prefix) ? (p.S0 ? p.S0 + head : nullptr) : nullptr;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
       for (int i = 0; i < JBW; ++i) acc[rt][i] = src ? *reinterpret_cast<const f32x4 *>(src + eoff(rt, i)) : zero4();
     if (p.S_prefix) {   // the state entering segment 0
       float *pre = p.S_prefix + ((int64_t)n * P * H + h) * DV * DK;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
         for (int i = 0; i < JBW; ++i) *reinterpret_cast<f32x4 *>(pre + eoff(rt, i)) = acc[rt][i];
     }
     if (!p.from_start) {
       const float *L0 = p.S_seg + ((int64_t)n * P * H + h) * DV * DK;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
         for (int i = 0; i < JBW; ++i) acc[rt][i] = *reinterpret_cast<const f32x4 *>(L0 + eoff(rt, i));
     }
   }
 
-  auto step = [&](int s, const StepRegs<DK> &R) {
+  auto step = [&](int s, const StepRegs<DK, RTC> &R) {
     if (p.S_prefix) {   // the state entering segment s
       float *pre = p.S_prefix + (((int64_t)n * P + s) * H + h) * DV * DK;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
         for (int i = 0; i < JBW; ++i) *reinterpret_cast<f32x4 *>(pre + eoff(rt, i)) = acc[rt][i];
     }
     // this wave's columns of both row tiles, split, to LDS
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
       for (int i = 0; i < JBW; ++i) {
         bf16x4 hi, lo;
@@ -179,45 +184,54 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
         *reinterpret_cast<bf16x4 *>(sSl + o) = lo;
       }
     lds_barrier();
-    f32x4 c[2][JBW];
+    f32x4 c[NP][RTC][JBW];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
-      for (int i = 0; i < JBW; ++i) c[rt][i] = R.loc[rt][i];
+      for (int i = 0; i < JBW; ++i) {
+        c[0][rt][i] = R.loc[rt][i];
+#pragma unroll
+        for (int q = 1; q < NP; ++q) c[q][rt][i] = zero4();
+      }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 bh[2], bl[2];
+      bf16x8 bh[RTC], bl[RTC];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+      for (int rt = 0; rt < RTC; ++rt) {
         const int o = (16 * rt + jl) * LDB + 32 * ks + 8 * g4;
         bh[rt] = *reinterpret_cast<const bf16x8 *>(sSh + o);
         bl[rt] = *reinterpret_cast<const bf16x8 *>(sSl + o);
       }
-      // the three split passes share each accumulator; 2 JBW of them rotate
+      // the three split passes share each accumulator when 2 JBW of them
+      // rotate (two row tiles), else each pass has its own
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
-        for (int i = 0; i < JBW; ++i) c[rt][i] = mfma_bf16(R.h[i][ks], bh[rt], c[rt][i]);
+        for (int i = 0; i < JBW; ++i) c[0][rt][i] = mfma_bf16(R.h[i][ks], bh[rt], c[0][rt][i]);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
-        for (int i = 0; i < JBW; ++i) c[rt][i] = mfma_bf16(R.h[i][ks], bl[rt], c[rt][i]);
+        for (int i = 0; i < JBW; ++i) c[NP > 1 ? 1 : 0][rt][i] = mfma_bf16(R.h[i][ks], bl[rt], c[NP > 1 ? 1 : 0][rt][i]);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
-        for (int i = 0; i < JBW; ++i) c[rt][i] = mfma_bf16(R.l[i][ks], bh[rt], c[rt][i]);
+        for (int i = 0; i < JBW; ++i) c[NP > 1 ? 2 : 0][rt][i] = mfma_bf16(R.l[i][ks], bh[rt], c[NP > 1 ? 2 : 0][rt][i]);
     }
     lds_barrier();   // every wave has read the planes before the next step rewrites them
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
-      for (int i = 0; i < JBW; ++i) acc[rt][i] = c[rt][i];
+      for (int i = 0; i < JBW; ++i) {
+        acc[rt][i] = c[0][rt][i];
+#pragma unroll
+        for (int q = 1; q < NP; ++q) acc[rt][i] += c[q][rt][i];
+      }
   };
 
   // operators applied: s0 .. PE - 1 (lead layout: the last segment has none,
   // and the state entering it is the result)
   const int PE = p.lead ? P - 1 : P;
-  StepRegs<DK> R0, R1, R2;
+  StepRegs<DK, RTC> R0, R1, R2;
   if (s0 < PE) load(s0, R0);
   if (s0 + 1 < PE) load(s0 + 1, R1);
   for (int s = s0; s < PE; s += 3) {
@@ -232,7 +246,7 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
   }
   float *out = p.lead ? p.S_prefix + (((int64_t)n * P + P - 1) * H + h) * DV * DK : p.S_out + head;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
     for (int i = 0; i < JBW; ++i) *reinterpret_cast<f32x4 *>(out + eoff(rt, i)) = acc[rt][i];
 }
@@ -240,10 +254,15 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
 template <int DK>
 hipError_t launch_sc(const SegComposeLaunch &p, hipStream_t stream) {
   if (p.dv % 32 != 0 || (p.lead && (p.from_start || !p.S_prefix || p.n_segs < 2))) return hipErrorInvalidValue;
-  const int64_t items = (int64_t)p.n_seqs * p.H * (p.dv / 32);
-  if (items <= 0) return hipSuccess;
-  const int64_t grid = (items + 7) / 8 * 8;
-  return launch_kernel(seg_compose_kernel<DK>, dim3((unsigned)grid), dim3(SNW * 64), 0, stream, p, (int)items);
+  const int64_t items32 = (int64_t)p.n_seqs * p.H * (p.dv / 32);
+  if (items32 <= 0) return hipSuccess;
+  // 32-row workgroups, or 16-row ones while 32-row ones leave compute units idle
+  if (items32 >= 256) {
+    const int64_t grid = (items32 + 7) / 8 * 8;
+    return launch_kernel(seg_compose_kernel<DK, 2>, dim3((unsigned)grid), dim3(SNW * 64), 0, stream, p, (int)items32);
+  }
+  const int64_t items = 2 * items32, grid = (items + 7) / 8 * 8;
+  return launch_kernel(seg_compose_kernel<DK, 1>, dim3((unsigned)grid), dim3(SNW * 64), 0, stream, p, (int)items);
 }
 
 }  // namespace
