@@ -100,7 +100,7 @@ struct StepRegs {
   f32x4 loc[RTC][SegCfg<DK>::JBW];
 };
 
-template <int DK, int RTC>
+template <int DK, int RTC, bool PRE>
 __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch p, int n_items) {
   using C = SegCfg<DK>;
   constexpr int NKS = C::NKS, JBW = C::JBW, NF = C::NF, LDB = C::LDB;
@@ -143,12 +143,12 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
   {
     // the state entering the chain: S0 (or zero), or segment 0's own state
     // (S0 may alias S_out: every workgroup reads its own rows here, first)
-    const float *src = (p.from_start || p.S_prefix) ? (p.S0 ? p.S0 + head : nullptr) : nullptr;
+    const float *src = (p.from_start || PRE) ? (p.S0 ? p.S0 + head : nullptr) : nullptr;
 #pragma unroll
     for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
       for (int i = 0; i < JBW; ++i) acc[rt][i] = src ? *reinterpret_cast<const f32x4 *>(src + eoff(rt, i)) : zero4();
-    if (p.S_prefix) {   // the state entering segment 0
+    if (PRE) {   // the state entering segment 0
       float *pre = p.S_prefix + ((int64_t)n * P * H + h) * DV * DK;
 #pragma unroll
       for (int rt = 0; rt < RTC; ++rt)
@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
   }
 
   auto step = [&](int s, const StepRegs<DK, RTC> &R) {
-    if (p.S_prefix) {   // the state entering segment s
+    if (PRE) {   // the state entering segment s
       float *pre = p.S_prefix + (((int64_t)n * P + s) * H + h) * DV * DK;
 #pragma unroll
       for (int rt = 0; rt < RTC; ++rt)
@@ -231,20 +231,31 @@ __global__ void __launch_bounds__(SNW * 64) seg_compose_kernel(SegComposeLaunch 
   // operators applied: s0 .. PE - 1 (lead layout: the last segment has none,
   // and the state entering it is the result)
   const int PE = p.lead ? P - 1 : P;
-  StepRegs<DK, RTC> R0, R1, R2;
-  if (s0 < PE) load(s0, R0);
-  if (s0 + 1 < PE) load(s0 + 1, R1);
-  for (int s = s0; s < PE; s += 3) {
-    if (s + 2 < PE) load(s + 2, R2);
-    step(s, R0);
-    if (s + 1 >= PE) break;
-    if (s + 3 < PE) load(s + 3, R0);
-    step(s + 1, R1);
-    if (s + 2 >= PE) break;
-    if (s + 4 < PE) load(s + 4, R1);
-    step(s + 2, R2);
+  if (s0 < PE) {
+    // The waits for the prefetched registers are counted by the compiler
+    // from the order of the memory operations, which is therefore the same
+    // on every path: the entering state has landed before the first
+    // prefetch, the prefetches are unconditional (past the last operator
+    // they load the last one again) and stores depend on a template
+    // argument only.  Otherwise a use inside the loop waits for every load
+    // outstanding, the prefetch of two steps ahead included.
+    wait_vmem();
+    auto nxt = [&](int s) { return s < PE ? s : PE - 1; };
+    StepRegs<DK, RTC> R0, R1, R2;
+    load(s0, R0);
+    load(nxt(s0 + 1), R1);
+    for (int s = s0; s < PE; s += 3) {
+      load(nxt(s + 2), R2);
+      step(s, R0);
+      if (s + 1 >= PE) break;
+      load(nxt(s + 3), R0);
+      step(s + 1, R1);
+      if (s + 2 >= PE) break;
+      load(nxt(s + 4), R1);
+      step(s + 2, R2);
+    }
   }
-  float *out = p.lead ? p.S_prefix + (((int64_t)n * P + P - 1) * H + h) * DV * DK : p.S_out + head;
+  float *out = PRE && p.lead ? p.S_prefix + (((int64_t)n * P + P - 1) * H + h) * DV * DK : p.S_out + head;
 #pragma unroll
   for (int rt = 0; rt < RTC; ++rt)
 #pragma unroll
@@ -257,12 +268,15 @@ hipError_t launch_sc(const SegComposeLaunch &p, hipStream_t stream) {
   const int64_t items32 = (int64_t)p.n_seqs * p.H * (p.dv / 32);
   if (items32 <= 0) return hipSuccess;
   // 32-row workgroups, or 16-row ones while 32-row ones leave compute units idle
+  const bool pre = p.S_prefix != nullptr;
   if (items32 >= 256) {
     const int64_t grid = (items32 + 7) / 8 * 8;
-    return launch_kernel(seg_compose_kernel<DK, 2>, dim3((unsigned)grid), dim3(SNW * 64), 0, stream, p, (int)items32);
+    return launch_kernel(pre ? seg_compose_kernel<DK, 2, true> : seg_compose_kernel<DK, 2, false>, dim3((unsigned)grid),
+                         dim3(SNW * 64), 0, stream, p, (int)items32);
   }
   const int64_t items = 2 * items32, grid = (items + 7) / 8 * 8;
-  return launch_kernel(seg_compose_kernel<DK, 1>, dim3((unsigned)grid), dim3(SNW * 64), 0, stream, p, (int)items);
+  return launch_kernel(pre ? seg_compose_kernel<DK, 1, true> : seg_compose_kernel<DK, 1, false>, dim3((unsigned)grid),
+                       dim3(SNW * 64), 0, stream, p, (int)items);
 }
 
 }  // namespace
