@@ -26,8 +26,9 @@ namespace gdn {
 namespace {
 
 constexpr int FNT = 256;   // threads per workgroup
-constexpr int FU = 1;      // rows a 16-lane group loads before reducing (1, 2, 4 and 8
-                           // measured: 20.5, 21.4, 24.4 and 28 us on 3277 x 32 rows of q and k)
+constexpr int FU = 2;      // rows a 16-lane group loads before reducing (1, 2 and 4 measured
+                           // with unconditional loads: 22.6, 20.7 and 21.7 us on 3277 x 32 rows
+                           // of q and k, against 22.2-23.8 us for one row loaded under a branch)
 
 __device__ __forceinline__ float sum16(float x) {
 #pragma unroll
@@ -95,15 +96,15 @@ __global__ void __launch_bounds__(FNT) front_kernel(FrontLaunch p) {
   for (int64_t r0 = g0; r0 < n_rows; r0 += FU * groups) {
     float x[FU][PER];
     bool live[FU];
+    // every row slot is loaded (a slot past the end reloads the last row and
+    // is not stored): loads under a branch would each be waited for at once
 #pragma unroll
     for (int u = 0; u < FU; ++u) {
-      const int64_t r = r0 + u * groups;
-      live[u] = r < n_rows;
-      if (live[u]) {
-        const bool is_q = p.q_in && r < rows;
-        const TI *src = reinterpret_cast<const TI *>(is_q ? p.q_in : p.k_in);
-        load_row<PER>(src + (is_q ? r : r - (p.q_in ? rows : 0)) * DK + PER * c, x[u]);
-      }
+      const int64_t r = min(r0 + u * groups, n_rows - 1);
+      live[u] = r0 + u * groups < n_rows;
+      const bool is_q = p.q_in && r < rows;
+      const TI *src = reinterpret_cast<const TI *>(is_q ? p.q_in : p.k_in);
+      load_row<PER>(src + (is_q ? r : r - (p.q_in ? rows : 0)) * DK + PER * c, x[u]);
     }
 #pragma unroll
     for (int u = 0; u < FU; ++u) {
@@ -128,8 +129,9 @@ __global__ void __launch_bounds__(FNT) front_kernel(FrontLaunch p) {
   const TI *g = reinterpret_cast<const TI *>(p.g), *b = reinterpret_cast<const TI *>(p.b);
   TI *alpha = reinterpret_cast<TI *>(p.alpha), *beta = reinterpret_cast<TI *>(p.beta);
   for (int64_t e = (int64_t)blockIdx.x * FNT + threadIdx.x; e < rows; e += threads) {
-    alpha[e] = from_f32<TI>(expf(to_f32(g[e])));
-    beta[e] = from_f32<TI>(1.f / (1.f + expf(-to_f32(b[e]))));
+    const TI ge = g[e], be = b[e];   // both loads in flight before either is used
+    alpha[e] = from_f32<TI>(expf(to_f32(ge)));
+    beta[e] = from_f32<TI>(1.f / (1.f + expf(-to_f32(be))));
   }
 }
 
