@@ -321,6 +321,12 @@ __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha
     if (q) {
       bf16x8 qf[4][DK / 32];
       prep_load_keys<DK>(q, H, h, t0, Lc, qf);
+      // all of them in registers at once: one wait for the whole group (left
+      // to itself the compiler reuses a few registers and waits per load)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int m = 0; m < DK / 32; ++m) asm volatile("" : "+v"(qf[b][m]));
       f32x4 dq[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
