@@ -625,6 +625,7 @@ gdn_status gdn_scalar_chunk_operator(const void *k, const void *v, const void *a
   p.dk = dk;
   p.dv = dv;
   p.in_bf16 = in_dtype == GDN_BF16;
+  p.n_tokens = n_tokens;
   return launched(gdn::launch_scalar_op(p, reinterpret_cast<hipStream_t>(stream)), "gdn_scalar_chunk_operator launch");
 }
 

@@ -340,7 +340,22 @@ __device__ __forceinline__ void dma16_global(const void *src, lds_void *dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 #endif
 }
+// 4 bytes per lane through a raw descriptor: lane l copies the dword at
+// base + voff (4-byte aligned) to dst + 4 l.
+__device__ __forceinline__ void dma4_buffer(const void *base, uint32_t nbytes, lds_void *dst, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, 0, 0, 0);
+#endif
+}
 
+// Wait until at most N vector-memory operations of this wave are
+// outstanding (vmcnt is split across bits 3:0 and 15:14 of the immediate).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 // Wait for all outstanding vector-memory loads of this wave (vmcnt(0)).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

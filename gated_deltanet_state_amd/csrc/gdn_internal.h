@@ -203,6 +203,7 @@ struct ScalarOpLaunch {
   float *S_local;                     // [n_chunks, H, dv, dk] or null
   int32_t n_chunks, H, dk, dv;
   int in_bf16;
+  int64_t n_tokens;                   // rows of k, v, alpha, beta
 };
 struct ScalarComposeLaunch {
   const float *S_in;                  // [H, dv, dk] or null (zero)
