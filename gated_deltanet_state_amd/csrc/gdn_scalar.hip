@@ -127,7 +127,7 @@ __global__ void __launch_bounds__(4 * DV) __attribute__((amdgpu_waves_per_eu(MIN
       if (l < SB) sU[l] = pb * later * expf(tot - P);
       later *= expf(tot);
     }
-    __syncthreads();
+    lds_barrier();   // (LDS only: __syncthreads' fence would also wait for the loads in flight)
     fetch(pre, pa, pb, s0 - 2 * SB);
     bf16x8 bh[NB], bl[NB];
     float a[8];
@@ -170,7 +170,7 @@ __global__ void __launch_bounds__(4 * DV) __attribute__((amdgpu_waves_per_eu(MIN
       acc[j] = mfma_bf16(al, bh[j], acc[j]);
       if constexpr (!EXACT_K) acc[j] = mfma_bf16(ah, bl[j], acc[j]);
     }
-    __syncthreads();
+    lds_barrier();
   };
   const int first = L > 0 ? (L - 1) / SB * SB : -SB;   // steps run from the chunk's end backwards
   fetch(preA, paA, pbA, first);
