@@ -287,25 +287,36 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
   const char *grec = reinterpret_cast<const char *>(p.tau);
 
   // ---- S^T in registers (dk order of the header comment) ----
+  // Transition rows start at the identity; state rows at the segment's start
+  // state, S0 (segment 0) or zero.  The start state's loads sit in one
+  // branch, so they are issued together and waited for once (a branch per
+  // load made the compiler wait for each load before issuing the next).
   f32x4 st[RT][C::NSB];
+  const float *s_src = nullptr;
+  if (active && !is_T) {
+    if (p.S0_seg)
+      s_src = p.S0_seg + (((int64_t)n * p.n_segs + seg) * H + h) * DV * DK;
+    else if (p.S0 && seg == 0)
+      s_src = p.S0 + ((int64_t)n * H + h) * DV * DK;
+  }
+  if (s_src) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int d = 0; d < C::NSB; ++d) {
-      const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1), r = row0 + 16 * rt + jl;
-      st[rt][d] = zero4();
-      if (active) {
-        if (is_T) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) st[rt][d][e] = (r == c0 + e) ? 1.f : 0.f;
-        } else if (p.S0_seg) {
-          st[rt][d] = *reinterpret_cast<const f32x4 *>(
-              p.S0_seg + ((((int64_t)n * p.n_segs + seg) * H + h) * DV + r) * DK + c0);
-        } else if (p.S0 && seg == 0) {
-          st[rt][d] = *reinterpret_cast<const f32x4 *>(p.S0 + (((int64_t)n * H + h) * DV + r) * DK + c0);
-        }
+      for (int d = 0; d < C::NSB; ++d) {
+        const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1), r = row0 + 16 * rt + jl;
+        st[rt][d] = *reinterpret_cast<const f32x4 *>(s_src + (int64_t)r * DK + c0);
       }
-    }
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int d = 0; d < C::NSB; ++d) {
+        const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1), r = row0 + 16 * rt + jl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[rt][d][e] = (is_T && r == c0 + e) ? 1.f : 0.f;
+      }
+  }
 
   // ---- DMA of one chunk's operands into buffer set b ----
   // Every wave issues whole 1 KiB blocks (one 16-byte copy per lane); the
