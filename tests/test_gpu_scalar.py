@@ -87,3 +87,33 @@ def test_last_block_initializer_is_replay_of_the_last_chunk():
                           np.array([0, 512], np.int32), want_o=False)[1]
     check_state("last-block initializer", to_np(SL[3]), S_ref[0], "bf16")
     check_state("replay of the last chunk", to_np(S[0]), S_ref[0], "bf16")
+
+
+def test_scalar_operator_past_the_dma_size_limit():
+    """Keys and values of 2^31 bytes or more go through the generic kernel
+    (the load-to-LDS path addresses them with 31-bit offsets): 65536 tokens x
+    128 heads at d = 128 in bf16.  Two generated heads are repeated to 128
+    (heads are independent); sampled chunks of every kind of head copy are
+    checked against the oracle."""
+    gdn, torch = _gdn()
+    T, Hs, R, d, CH = 65536, 2, 64, 128, 512
+    inp = workloads.generate([T], H=Hs, dk=d, dv=d, dtype="bf16", seed=137, gate_scale=0.01)
+    dd = dev(inp)
+    big = {n: dd[n].repeat(1, R, 1) if dd[n].dim() == 3 else dd[n].repeat(1, R) for n in ("k", "v", "alpha", "beta")}
+    H = Hs * R
+    assert big["k"].shape == (T, H, d) and big["k"].numel() * 2 >= 2 ** 31
+    cu_np = np.arange(0, T + 1, CH, dtype=np.int32)
+    g, SL = gdn.scalar_chunk_operator(big["k"], big["alpha"], big["beta"], torch.from_numpy(cu_np).cuda(),
+                                      v=big["v"])
+    torch.cuda.synchronize()
+    f = inp.f64
+    for c in (0, 63, T // CH - 1):
+        t0, t1 = int(cu_np[c]), int(cu_np[c + 1])
+        g_ref, SL_ref = oracle.scalar_chunk_operator(f["k"][t0:t1], f["alpha"][t0:t1], f["beta"][t0:t1],
+                                                     [0, t1 - t0], v=f["v"][t0:t1])
+        for h in (0, 1, H // 2, H - 1):
+            lab = "scalar large chunk %d head %d" % (c, h)
+            check_close(lab + " gamma", to_np(g[c, h:h + 1]), g_ref[0, h % Hs:h % Hs + 1], 0, TOL_F32,
+                        BLOCK_TOL["f32"])
+            check_state(lab + " S_local", to_np(SL[c, h]), SL_ref[0, h % Hs], "f32")
+    del big, SL
