@@ -212,7 +212,6 @@ gdn_status replay_impl(const void *q, const void *k, const void *v, const void *
   float *norms = raw ? reinterpret_cast<float *>(static_cast<char *>(workspace) + base) : nullptr;
   gdn::PrepLaunch pp{};
   pp.raw = raw ? 1 : 0;
-  pp.q = o ? q : nullptr;
   pp.norms = norms;
   pp.k = k;
   pp.alpha = alpha;

@@ -92,10 +92,12 @@ struct Cfg {
 
 // Gate buffer (see the running scale gam in the kernel), per token: [0, 64)
 // gam e^g / |k| (the state read by the keys), [64, 128) e^{g_L - g} / gam' /
-// |k| (0 past the chunk), [128, 192) g, [192, 256) gam e^g / |q| (the state
-// read by the queries), [256, 320) 1 / |q|, [320, 384) 1 / |k|; [384] the
-// factor the chunk applies to the state registers (gam e^{g_L}, or 1: none).
-// The norms are 1 except for raw inputs (ChainLaunch::raw).
+// |k| (0 past the chunk), [128, 192) g, [192, 256) gam e^g (the state read
+// by the queries), [256, 320) 1 / |q| (raw inputs with outputs: formed from
+// the staged queries during the chunk's own step and applied to its output
+// rows when they are stored), [320, 384) 1 / |k|; [384] the factor the chunk
+// applies to the state registers (gam e^{g_L}, or 1: none).  The key norms
+// are 1 except for raw inputs (ChainLaunch::raw).
 constexpr int G_EG = 0, G_DEC = 64, G_G = 128, G_EQ = 192, G_RQ = 256, G_RK = 320, G_EGL = 384;
 
 // Unit swizzle of the staged value slab (VU 16-byte units per row): unit u
@@ -225,7 +227,9 @@ __host__ __device__ inline SegGroups seg_groups(const ChainLaunch &p, int tw, in
 }
 
 // One workgroup: row-tile group grp of segment seg of (sequence n, head h).
-template <int DK, bool WANT_O, int NW, int RT, bool FUSED>
+// QN (with outputs of raw inputs, ChainLaunch::raw): the query norms are
+// formed from the staged queries and applied to the stored output rows.
+template <int DK, bool WANT_O, int NW, int RT, bool FUSED, bool QN = false>
 __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, const int h, const int seg,
                                            const int grp, char *smem) {
   static_assert(RT == 1 || RT == 2, "one or two row tiles per wave");
@@ -384,18 +388,16 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
 
   // wave 0: alpha bits of token t0 + l (1.0 past the end; raw inputs: the
   // log-gate, 0 past the end) and, for raw inputs, the token's reciprocal
-  // key and query norms
+  // key norm
   unsigned short pa = 0;
-  float rk = 1.f, rq = 1.f;
+  float rk = 1.f;
   auto load_alpha = [&](int t0, int Lc) {
     pa = p.raw ? 0 : 0x3f80;
     if (w == 0 && l < Lc) pa = ga[(int64_t)(t0 + l) * H + h];
   };
   auto load_norms = [&](int64_t slot, int Lc) {
     if (p.raw && w == 0 && l < Lc) {
-      const float *nb = p.norms + (slot * H + h) * kNormFloats;
-      rk = nb[l];
-      rq = nb[kChunk + l];
+      rk = p.norms[(slot * H + h) * kNormFloats + l];
     }
   };
   // Running scale of the state.  The registers hold S / gam, gam a scalar
@@ -421,10 +423,9 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     const float inv = 1.f / gnew;
     const float eg = gam * __expf(g);
     sG[G_EG + l] = eg * rk;
-    sG[G_EQ + l] = eg * rq;
+    sG[G_EQ + l] = eg;
     sG[G_DEC + l] = (l < Lc) ? __expf(gL - g) * inv * rk : 0.f;
     sG[G_G + l] = g;
-    sG[G_RQ + l] = rq;
     sG[G_RK + l] = rk;
     if (l == 0) sG[G_EGL] = apply ? cand : 1.f;   // the registers' scale factor (1: none)
     gam = gnew;
@@ -486,7 +487,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
       char *lrec = (own && c == 0) ? smem + C::bTF * 1024 : nullptr;
       if (p.raw)
         prep_chunk_wave<DK, true>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta),
-                                  H, h, tc, min(CH, cend - tc), rec, scr, lrec, gq, p.norms + (sl * H + h) * kNormFloats);
+                                  H, h, tc, min(CH, cend - tc), rec, scr, lrec, p.norms + (sl * H + h) * kNormFloats);
       else
         prep_chunk_wave<DK>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta), H,
                             h, tc, min(CH, cend - tc), rec, scr, lrec);
@@ -554,11 +555,10 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
       f32x4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = (s0 + e <= r) ? __expf(gr - gs[e]) * c[e] : 0.f;
-      if (p.raw) {   // the normalised query and key rows
-        const float qr = sG[G_RQ + r];
+      if (p.raw) {   // the normalised key rows (the query norms are applied to the outputs)
         const f32x4 ks = *reinterpret_cast<const f32x4 *>(sG + G_RK + s0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] *= qr * ks[e];
+        for (int e = 0; e < 4; ++e) x[e] *= ks[e];
       }
       bf16x4 hi, lo;
       split4(x, hi, lo);
@@ -607,13 +607,34 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     Ls = Lp;
     Lp = 0;
   };
-  auto store_s = [&]() {
+  // raw inputs with outputs: 1 / |q_t| of the chunk staged in buffer set b,
+  // into its gate set (waves 0..3, 16 tokens each: the squares of the wave's
+  // query fragments summed over the four lanes that hold a token)
+  auto query_norms = [&](int b) {
+    if (!(WANT_O && QN) || w >= 4) return;
+    const char *buf = smem + b * C::BUF;
+    float q2 = 0.f;
+#pragma unroll
+    for (int m = 0; m < C::NKS; ++m) {
+      const bf16x8 f = *reinterpret_cast<const bf16x8 *>(buf + (C::bQA + w * C::NKS + m) * 1024 + 16 * kq_l);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q2 += (float)f[i] * (float)f[i];
+    }
+    q2 += __shfl_xor(q2, 16, 64);
+    q2 += __shfl_xor(q2, 32, 64);
+    if (g4 == 0) sG0[b * C::GN + G_RQ + 16 * w + jl] = q2 > 0.f ? rsqrtf(q2) : 0.f;
+  };
+  // an output row is linear in its token's query: raw inputs scale it by
+  // 1 / |q_t| (gate set gs) as it is stored
+  auto out_scale = [&](int gs, int bt) { return sG0[gs * C::GN + G_RQ + 16 * bt + jl]; };
+  auto store_s = [&](int gs) {
     const int64_t tok = (int64_t)H * DV;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int64_t ob = ((int64_t)(ts + jl) * H + h) * DV + row0 + 16 * rt + 4 * g4;
 #pragma unroll
       for (int bt = 0; bt < 4; ++bt) {
+        if constexpr (QN) zs[rt][bt] *= out_scale(gs, bt);
         if (16 * bt + jl < Ls) {
           if (p.o_bf16) {
             *reinterpret_cast<uint2 *>(reinterpret_cast<bf16 *>(p.o) + ob + 16 * bt * tok) =
@@ -626,7 +647,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     }
     Ls = 0;
   };
-  auto store_o = [&]() {
+  auto store_o = [&](int gs) {
     // lane (q, g) of block bt holds token tp + 16 bt + q, value columns
     // row0 + 16 rt + 4 g .. + 3: one 16-byte (8-byte in bf16) store each
     const int64_t tok = (int64_t)H * DV;
@@ -635,6 +656,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
       const int64_t ob = ((int64_t)(tp + jl) * H + h) * DV + row0 + 16 * rt + 4 * g4;
 #pragma unroll
       for (int bt = 0; bt < 4; ++bt) {
+        if constexpr (QN) zp[rt][bt] *= out_scale(gs, bt);
         if (16 * bt + jl < Lp) {
           if (p.o_bf16) {
             *reinterpret_cast<uint2 *>(reinterpret_cast<bf16 *>(p.o) + ob + 16 * bt * tok) =
@@ -673,6 +695,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
       load_alpha(t0 + CH, L1);
       load_norms(slot + 1, L1);
     }
+    query_norms(b);   // (raw inputs with outputs; read when this chunk's outputs are stored)
     const char *buf = smem + b * C::BUF;
     const float *sG = sG0 + b * C::GN;
     auto frag = [&](int blk) { return *reinterpret_cast<const bf16x8 *>(buf + blk * 1024 + 16 * l); };
@@ -985,7 +1008,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     // ---- hand over to the next chunk ----
     if (more) gates(b ^ 1, L1, t0 + 2 * CH >= tend);
     wait_vmem();
-    if (WANT_O && active && Ls > 0) store_s();
+    if (WANT_O && active && Ls > 0) store_s(b ^ 1);   // the previous chunk's outputs
     lds_barrier();
     if (more) read_v(b ^ 1);
   }
@@ -993,7 +1016,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
   // ---------------- epilogue: final rows ----------------
   if (WANT_O && active && Lp > 0) {
     finish_o(b ^ 1);   // the last chunk's set (b has moved past it)
-    store_o();
+    store_o(b ^ 1);
   }
   const int64_t unit = ((int64_t)n * p.n_segs + seg) * H + h;
   if (p.T_frags) {
@@ -1053,7 +1076,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
 // The launch: one workgroup per (sequence, head, segment, row-tile group).
 // With LEAD (segment launch of the lead layout) segment 0 runs the output
 // recurrence, one row tile per wave, and the other segments this body.
-template <int DK, bool WANT_O, int NW, int RT, bool FUSED, bool LEAD = false>
+template <int DK, bool WANT_O, int NW, int RT, bool FUSED, bool LEAD = false, bool QN = false>
 __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int n_items) {
   using C = Cfg<DK, WANT_O, NW, RT, FUSED>;
   using CL = Cfg<DK, true, NW, 1, FUSED>;
@@ -1079,14 +1102,14 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   const int n = ordered ? p.order[nh / p.H] : nh / p.H, h = nh % p.H;
   if constexpr (LEAD) {
     if (seg == 0) {
-      chain_body<DK, true, NW, 1, FUSED>(p, n, h, 0, grp, smem);
+      chain_body<DK, true, NW, 1, FUSED, QN>(p, n, h, 0, grp, smem);
       return;
     }
   }
-  chain_body<DK, WANT_O, NW, RT, FUSED>(p, n, h, seg, grp, smem);
+  chain_body<DK, WANT_O, NW, RT, FUSED, WANT_O && QN>(p, n, h, seg, grp, smem);
 }
 
-template <int DK, bool WANT_O, int NW, int RT, bool FUSED = false, bool LEAD = false>
+template <int DK, bool WANT_O, int NW, int RT, bool FUSED = false, bool LEAD = false, bool QN = false>
 hipError_t launch_b(const ChainLaunch &p, hipStream_t stream) {
   constexpr int TW = NW * RT;
   if (p.tiles_T % RT != 0 || p.tiles_S % RT != 0 || p.tiles_T > 8 || p.tiles_S > 8) return hipErrorInvalidValue;
@@ -1095,8 +1118,8 @@ hipError_t launch_b(const ChainLaunch &p, hipStream_t stream) {
   const int64_t items = (int64_t)p.n_seqs * p.H * sg.per_nh;
   if (items <= 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
-  return launch_kernel(chain_bf16_kernel<DK, WANT_O, NW, RT, FUSED, LEAD>, dim3((unsigned)grid), dim3(NW * 64), 0,
-                       stream, p, (int)items);
+  return launch_kernel(chain_bf16_kernel<DK, WANT_O, NW, RT, FUSED, LEAD, QN>, dim3((unsigned)grid), dim3(NW * 64),
+                       0, stream, p, (int)items);
 }
 
 template <int DK>
@@ -1108,8 +1131,10 @@ hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
     // SIMD interleave their work (measured on 16 packed tails: 668 us
     // against 933 us for two four-wave workgroups per head and 826 us for
     // four waves with two row tiles each)
-    if (p.tiles_S % 8 == 0) return launch_b<DK, true, 8, 1>(p, stream);
-    return launch_b<DK, true, 4, 1>(p, stream);
+    // (raw inputs: the variant that forms the query norms)
+    if (p.tiles_S % 8 == 0)
+      return p.raw ? launch_b<DK, true, 8, 1, false, false, true>(p, stream) : launch_b<DK, true, 8, 1>(p, stream);
+    return p.raw ? launch_b<DK, true, 4, 1, false, false, true>(p, stream) : launch_b<DK, true, 4, 1>(p, stream);
   }
   // Transition and state tiles of a segment share one workgroup, two row
   // tiles per wave: every fragment read from LDS then feeds two products,
@@ -1120,8 +1145,12 @@ hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
   if (p.tiles_T > 0 && p.lead) {
     // segment launch of the lead layout: segment 0 with its outputs
     if (!p.fuse_prep || p.S0_seg) return hipErrorInvalidValue;
-    if (tilesA <= 8) return launch_b<DK, false, 4, 2, true, true>(p, stream);
-    if (tilesA <= 16) return launch_b<DK, false, 8, 2, true, true>(p, stream);
+    if (tilesA <= 8)
+      return p.raw ? launch_b<DK, false, 4, 2, true, true, true>(p, stream)
+                   : launch_b<DK, false, 4, 2, true, true>(p, stream);
+    if (tilesA <= 16)
+      return p.raw ? launch_b<DK, false, 8, 2, true, true, true>(p, stream)
+                   : launch_b<DK, false, 8, 2, true, true>(p, stream);
     return hipErrorInvalidValue;
   }
   if (p.o) return hipErrorInvalidValue;

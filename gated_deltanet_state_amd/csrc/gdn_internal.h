@@ -55,10 +55,11 @@ constexpr int kTauFrags = 6;
 // gate arrays hold the log-gates g (alpha = e^g) and the write-strength
 // logits (beta = 1 / (1 + e^-b)), and the keys and queries are raw
 // projections.  The record builder stores, per (chunk slot, head), the
-// reciprocal norms 1 / |k_t| of the chunk's keys, then 1 / |q_t| of its
-// queries (0 for a zero row, and for queries when none are needed); every
-// product with a key or query row carries that factor.
-constexpr int kNormFloats = 2 * kChunk;
+// reciprocal norms 1 / |k_t| of the chunk's keys (0 for a zero row); every
+// product with a key row carries that factor.  The query norms are formed by
+// the output recurrence from the queries it stages (outputs are linear in
+// their token's query, so each output row is scaled when it is stored).
+constexpr int kNormFloats = kChunk;
 
 constexpr int kTauFragPlane = kTauFrags * 64 * 8;  // bf16 elements per plane
 
@@ -92,9 +93,8 @@ struct PrepLaunch {
   int64_t n_slots;
   int32_t *order;    // [n_seqs] longest-first sequence order to build, or null (bf16 only)
   // raw inputs (bf16 only, see kNormFloats): k raw keys, alpha log-gates,
-  // beta logits; q raw queries (or null: no query norms needed)
+  // beta logits
   int raw;
-  const void *q;
   float *norms;      // [n_slots, H, kNormFloats]
 };
 

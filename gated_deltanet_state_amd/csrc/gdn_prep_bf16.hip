@@ -60,7 +60,7 @@ __global__ void __launch_bounds__(PW * 64) prep_bf16_kernel(PrepLaunch p) {
   char *rec = reinterpret_cast<char *>(p.tau + (slot * H + h) * (int64_t)kRecFloats);
   prep_chunk_wave<DK, RAW>(reinterpret_cast<const bf16 *>(p.k), reinterpret_cast<const bf16 *>(p.alpha),
                            reinterpret_cast<const bf16 *>(p.beta), H, h, t0, Lc, rec, scratch[w], nullptr,
-                           reinterpret_cast<const bf16 *>(p.q), RAW ? p.norms + (slot * H + h) * kNormFloats : nullptr);
+                           RAW ? p.norms + (slot * H + h) * kNormFloats : nullptr);
 }
 
 template <int DK>

@@ -25,8 +25,7 @@
 // Raw inputs (RAW, gdn_internal.h kNormFloats): the gates come from the
 // log-gates and logits, and the keys are normalised on the way: the
 // diagonal blocks of K K^T hold |k_t|^2, so A takes the factor
-// 1 / (|k_r| |k_s|); the query norms come from the diagonal blocks of
-// Q Q^T the same way, and both reciprocal norms go to the chunk's norms
+// 1 / (|k_r| |k_s|), and the reciprocal key norms go to the chunk's norms
 // block.
 // LDS per wave: kPrepWaveLds bytes (A blocks, overwritten in place by the
 // Tau blocks; gates; reciprocal norms).
@@ -37,7 +36,7 @@
 
 namespace gdn {
 
-constexpr int kPrepWaveLds = (10 * 256 + 4 * 64) * 4;
+constexpr int kPrepWaveLds = (10 * 256 + 3 * 64) * 4;
 
 namespace prep_detail {
 
@@ -86,8 +85,8 @@ __device__ __forceinline__ void prep_load_keys(const bf16 *k, int H, int h, int 
 }
 
 // Offsets in the per-wave LDS scratch (floats): A / Tau blocks, cumulative
-// log-gates, betas, reciprocal key norms, reciprocal query norms.
-constexpr int kPrepG = 10 * 256, kPrepB = kPrepG + 64, kPrepK = kPrepB + 64, kPrepQ = kPrepK + 64;
+// log-gates, betas, reciprocal key norms.
+constexpr int kPrepG = 10 * 256, kPrepB = kPrepG + 64, kPrepK = kPrepB + 64;
 
 // The reciprocal norms of the diagonal blocks acc[blk(b, b)] of X X^T (C
 // layout: lane (c, g) holds rows 4 g .. 4 g + 3 of column c, so the lanes
@@ -109,16 +108,16 @@ __device__ __forceinline__ void diag_rnorms(const f32x4 (&d)[4], float *dst) {
 // kPrepWaveLds bytes of LDS; lds_rec (may be null) receives a second copy of
 // the Tau fragments in LDS.  RAW: alpha and beta hold log-gates and logits,
 // the keys are raw, and norms (kNormFloats floats) receives the reciprocal
-// key norms and, when q (raw queries [T, H, DK]) is given, the query ones.
+// key norms.
 template <int DK, bool RAW = false>
 __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 32], const bf16 *alpha,
                                                      const bf16 *beta, int H, int h, int t0, int Lc, char *rec,
                                                      float *scratch, char *lds_rec = nullptr,
-                                                     const bf16 *q = nullptr, float *norms = nullptr) {
+                                                     float *norms = nullptr) {
   using namespace prep_detail;
   constexpr int NKS = DK / 32;
   float *sA = scratch;             // 10 blocks 16 x 16 row-major: A, then Tau
-  float *sG = scratch + kPrepG, *sB = scratch + kPrepB, *sK = scratch + kPrepK, *sQ = scratch + kPrepQ;
+  float *sG = scratch + kPrepG, *sB = scratch + kPrepB, *sK = scratch + kPrepK;
   const int l = lane_id(), g4 = l >> 4, jl = l & 15;
 
   // ---- 1. gates (the keys are in kf) ----
@@ -303,10 +302,8 @@ __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 
   write_frags(rec, lds_rec, true);
 
   if constexpr (RAW) {
-    if (!q) sQ[l] = 0.f;   // (else prep_chunk_wave put the query norms there)
     wave_lds_fence();
     norms[l] = sK[l];
-    norms[kChunk + l] = sQ[l];
   }
 }
 
@@ -314,32 +311,10 @@ __device__ __forceinline__ void prep_chunk_wave_keys(const bf16x8 (&kf)[4][DK / 
 template <int DK, bool RAW = false>
 __device__ __forceinline__ void prep_chunk_wave(const bf16 *k, const bf16 *alpha, const bf16 *beta, int H, int h,
                                                 int t0, int Lc, char *rec, float *scratch, char *lds_rec = nullptr,
-                                                const bf16 *q = nullptr, float *norms = nullptr) {
-  if constexpr (RAW) {
-    // query norms first (the diagonal blocks of Q Q^T), before the keys
-    // take their registers
-    if (q) {
-      bf16x8 qf[4][DK / 32];
-      prep_load_keys<DK>(q, H, h, t0, Lc, qf);
-      // all of them in registers at once: one wait for the whole group (left
-      // to itself the compiler reuses a few registers and waits per load)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int m = 0; m < DK / 32; ++m) asm volatile("" : "+v"(qf[b][m]));
-      f32x4 dq[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        dq[b] = zero4();
-#pragma unroll
-        for (int m = 0; m < DK / 32; ++m) dq[b] = mfma_bf16(qf[b][m], qf[b][m], dq[b]);
-      }
-      diag_rnorms(dq, scratch + kPrepQ);
-    }
-  }
+                                                float *norms = nullptr) {
   bf16x8 kf[4][DK / 32];
   prep_load_keys<DK>(k, H, h, t0, Lc, kf);
-  prep_chunk_wave_keys<DK, RAW>(kf, alpha, beta, H, h, t0, Lc, rec, scratch, lds_rec, q, norms);
+  prep_chunk_wave_keys<DK, RAW>(kf, alpha, beta, H, h, t0, Lc, rec, scratch, lds_rec, norms);
 }
 
 }  // namespace gdn

@@ -156,7 +156,8 @@ size_t gdn_replay_segmented_workspace_bytes(int32_t n_seqs, int64_t n_tokens,
  *   S0, cu_seqlens, o, o_dtype, S_final: as gdn_replay.
  *   in_dtype must be GDN_BF16 (GDN_ERR_UNSUPPORTED otherwise).
  *   workspace: gdn_replay_raw_workspace_bytes(...) bytes (the replay's
- *   workspace and 512 bytes of reciprocal norms per chunk slot and head).
+ *   workspace and 256 bytes of reciprocal key norms per chunk slot and
+ *   head; the query norms are formed where the outputs are).
  * Errors and everything else as gdn_replay.  The result equals
  * gdn_front_end + gdn_replay up to the rounding of the normalised inputs to
  * bf16, which this call skips.

@@ -96,12 +96,12 @@ def test_raw_replay_argument_checks(lib):
     assert rr(dt=F32) == UNSUP and b"GDN_BF16" in lib.gdn_last_error()
     assert rr(k=None) == NULLP
     assert rr() == WS and b"gdn_replay_raw" in lib.gdn_last_error()
-    # the workspace adds 512 bytes of reciprocal norms per chunk slot and
-    # head to the replay's; a single long sequence over few heads takes the
-    # time split (segment operators beyond the records and norms)
+    # the workspace adds 256 bytes of reciprocal key norms per chunk slot
+    # and head to the replay's; a single long sequence over few heads takes
+    # the time split (segment operators beyond the records and norms)
     slots = 4000 // 64 + 1 + 1
     assert lib.gdn_replay_raw_workspace_bytes(1, 4000, 4, 128, 128) == \
-        lib.gdn_replay_workspace_bytes(1, 4000, 4, 128, 128) + slots * 4 * 512
+        lib.gdn_replay_workspace_bytes(1, 4000, 4, 128, 128) + slots * 4 * 256
     assert lib.gdn_replay_workspace_bytes(1, 4000, 4, 128, 128) > slots * 4 * 12288
 
 
