@@ -473,8 +473,8 @@ def scalar_ops_report(args, gdn, torch, np):
                 config=dict(workload=SCALAR_NAME, n_chunks=C, chunk=w["chunk"], n_tokens=T, heads=H, dk=dk, dv=dv,
                             outputs="gamma,S_local,S"),
                 roofline=dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                              frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(SCALAR_NAME, "scalar_op_kernel"),
-                              kernel="scalar_op_kernel", algorithmic_bytes=byt, kernel_ms_avg=round(t_op, 5)),
+                              frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(SCALAR_NAME, "scalar_op"),
+                              kernel="scalar_op_dma_kernel", algorithmic_bytes=byt, kernel_ms_avg=round(t_op, 5)),
                 compose_ms=round(t_comp, 5))
     line["gpu_ms_per_step"] = round(t_op + t_comp, 5)
     print(json.dumps(line), flush=True)
