@@ -182,16 +182,18 @@ __device__ __forceinline__ void kt_frags(int m, uint32_t addr, bf16x8 (&a)[NSB])
 //     elsewhere) and the later segments take ceil(rest / (P - 1)) each.
 //   * Lead layout (time split with outputs): the later segments, which all
 //     run the output recurrence from their composed start states, take e =
-//     round(chunks / (P - 1 + 3/4)) each and the lead the rest: the lead
-//     runs beside the transition segments and also builds the last
-//     segment's records.
+//     round(chunks / P) each and the lead the rest.  The lead runs its
+//     outputs beside the transition segments, which also build the last
+//     segment's records (lead_extras).  (32768-token prefill: leads of
+//     0.75, 0.875, 1.125 and 1.25 times e took 1.7%, 0.6%, 2.2% and 5.8%
+//     longer than e; with the lead building the last segment's records
+//     itself, 0.75 e was best.)
 // Segments past the end are empty.
 __device__ __forceinline__ void seg_chunks(const ChainLaunch &p, int nch, int seg, int npw, int &cb, int &cl) {
   const int P = p.n_segs;
   int e, c0;
   if (p.lead) {
-    const int den = 4 * (P - 1) + 3;
-    e = max(1, (4 * nch + den / 2) / den);
+    e = max(1, (nch + P / 2) / P);
     c0 = max(0, nch - (P - 1) * e);
   } else {
     const int den = 5 * (P - 1) + 8;
@@ -206,6 +208,26 @@ __device__ __forceinline__ void seg_chunks(const ChainLaunch &p, int nch, int se
   cl = seg == 0 ? c0 : e;
   cb = min(cb, nch);
   cl = min(cl, nch - cb);
+}
+
+// Lead layout: the records of the last segment (which the segment launch
+// does not run) that segment seg builds in its prologue, chunks xb .. xb +
+// nx - 1 of the sequence: an equal share for each transition segment
+// 1 .. P - 2, or all of them for the lead when there is none.
+__device__ __forceinline__ void lead_extras(const ChainLaunch &p, int nch, int seg, int &xb, int &nx) {
+  const int P = p.n_segs;
+  int lb, ln;
+  seg_chunks(p, nch, P - 1, 0, lb, ln);
+  xb = lb;
+  nx = 0;
+  if (P == 2) {
+    if (seg == 0) nx = ln;
+    return;
+  }
+  if (seg == 0) return;
+  const int q = (ln + P - 3) / (P - 2);
+  xb = lb + min(ln, (seg - 1) * q);
+  nx = min(q, lb + ln - xb);
 }
 
 // Workgroups of one (sequence, head) in a launch: the segments first ..
@@ -475,10 +497,10 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     }
     float *scr = reinterpret_cast<float *>(smem + C::PSCR) + (w % C::NPW) * (kPrepWaveLds / 4);
     const int nch = (tend - tbeg + CH - 1) / CH;
-    // the lead also builds the records of the last segment (chunks xb ..
+    // lead layout: a share of the records of the last segment (chunks xb ..
     // xb + nx - 1 of the sequence), which the segment launch does not run
     int xb = 0, nx = 0;
-    if (WANT_O && p.lead && seg == 0) seg_chunks(p, nch_seq, p.n_segs - 1, 0, xb, nx);
+    if (p.lead && p.tiles_T > 0) lead_extras(p, nch_seq, seg, xb, nx);
     for (int c = w; c < nch + nx && w < C::NPW; c += C::NPW) {
       const bool own = c < nch;
       const int tc = own ? tbeg + c * CH : cbeg + (xb + c - nch) * CH;
