@@ -103,8 +103,8 @@ def test_split_with_outputs_shapes(dk, dv):
 
 @pytest.mark.parametrize("law", ["workload", "strong"])
 def test_split_with_outputs_lead_layout_many_segments(law):
-    # the layout of a long split with outputs: a short lead segment that
-    # runs with its outputs beside the transition segments (and builds the
+    # the layout of a long split with outputs: a lead segment that runs
+    # with its outputs beside the transition segments (which also build the
     # last segment's records), then every later segment with outputs; nine
     # segments as the cost model picks for one sequence over 32 heads, here
     # on sequences of different lengths (one of them shorter than the
