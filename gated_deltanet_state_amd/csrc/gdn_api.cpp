@@ -111,8 +111,8 @@ int replay_segments(int32_t n_seqs, int64_t n_tokens, int32_t n_heads, int32_t d
 }
 
 // Segments per sequence for a bf16 replay with outputs.  A split runs three
-// passes: the segment launch (a short lead segment 0 with its outputs from
-// S0, beside the transition and state rows of the middle segments), the
+// passes: the segment launch (the lead segment 0 with its outputs from S0,
+// beside the transition and state rows of the middle segments), the
 // composition (every later segment's true start state), and the output
 // launch (segments 1 .. P - 1 with outputs from those states).  Worth it
 // when the (sequence, head) pairs alone leave compute units idle: the P - 1

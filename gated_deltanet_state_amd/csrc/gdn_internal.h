@@ -125,13 +125,14 @@ struct ChainLaunch {
   int32_t n_segs;           // >= 1
   const float *S0_seg;      // [n_seqs, n_segs, H, dv, dk]: start of every segment (replaces S0), or null
   int skip_T0;              // segment 0 has no transition tiles
-  // Time split with outputs ("lead" layout, n_segs >= 2): segment 0 (the
-  // lead) is shorter than the others, which all have one length.  The
-  // segment launch (transition tiles) runs segments 0 .. n_segs - 2: the
-  // lead from S0 with its outputs, into o, and it also builds the records
-  // of the last segment; the output launch (no transition tiles) runs
-  // segments 1 .. n_segs - 1 from S0_seg and writes the last segment's end
-  // state to S_last.
+  // Time split with outputs ("lead" layout, n_segs >= 2): segments 1 ..
+  // n_segs - 1 all have one length and segment 0 (the lead) takes the rest.
+  // The segment launch (transition tiles) runs segments 0 .. n_segs - 2:
+  // the lead from S0 with its outputs, into o, and the others with
+  // transition rows, which also build the records of the last segment (the
+  // lead does when there are no others); the output launch (no transition
+  // tiles) runs segments 1 .. n_segs - 1 from S0_seg and writes the last
+  // segment's end state to S_last.
   int lead;
   float *S_last;            // [n_seqs, H, dv, dk] or null
   // write each segment's T as composition fragments (kSegOpFragments)
