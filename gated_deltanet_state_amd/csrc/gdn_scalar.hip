@@ -51,6 +51,28 @@ constexpr int SB = 32;     // tokens per step (one MFMA k block)
 // MINW: waves per SIMD asked of the register allocator (4 for bf16 at
 // dk = dv = 128, where it lets two workgroups share a compute unit; 1, no
 // bound, elsewhere, where a bound of 4 would spill registers)
+// gamma of a chunk, in wave 0: lane l multiplies the alphas of tokens l,
+// l + 64, l + 128, ... in that order, then the lanes are combined by xor
+// shuffles.  The loads go out eight at a time (indices clamped into the
+// chunk, the surplus multiplied as 1): a load per iteration, each waited
+// for before the next was issued, made the rest of the workgroup wait at
+// its first barrier for eight memory round trips per 512 tokens.
+template <typename TI>
+__device__ __forceinline__ float chunk_gate_product(const TI *alpha, int64_t t0, int L, int H, int h) {
+  const int l = lane_id();
+  float g = 1.f;
+  for (int j0 = 0; j0 < L; j0 += 8 * 64) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = to_f32(alpha[(t0 + min(j0 + 64 * u + l, L - 1)) * H + h]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) g *= j0 + 64 * u + l < L ? x[u] : 1.f;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) g *= __shfl_xor(g, m, 64);
+  return g;
+}
+
 template <int DK, int DV, typename TI, int MINW>
 __global__ void __launch_bounds__(4 * DV) __attribute__((amdgpu_waves_per_eu(MINW))) scalar_op_kernel(ScalarOpLaunch p) {
   constexpr bool EXACT_K = sizeof(TI) == 2;   // bf16 keys are exact MFMA operands
@@ -67,10 +89,7 @@ __global__ void __launch_bounds__(4 * DV) __attribute__((amdgpu_waves_per_eu(MIN
 
   // gamma = the product of the chunk's alphas (wave 0)
   if (w == 0) {
-    float g = 1.f;
-    for (int j = l; j < L; j += 64) g *= to_f32(alpha[(int64_t)(t0 + j) * p.H + h]);
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) g *= __shfl_xor(g, m, 64);
+    const float g = chunk_gate_product(alpha, t0, L, p.H, h);
     if (l == 0) p.gamma[(int64_t)c * p.H + h] = g;
   }
   if (!p.S_local) return;
@@ -267,10 +286,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) s
   const bf16 *alpha = reinterpret_cast<const bf16 *>(p.alpha), *beta = reinterpret_cast<const bf16 *>(p.beta);
 
   if (w == 0) {   // gamma = the product of the chunk's alphas
-    float g = 1.f;
-    for (int j = l; j < L; j += 64) g *= (float)alpha[(int64_t)(t0 + j) * p.H + h];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) g *= __shfl_xor(g, m, 64);
+    const float g = chunk_gate_product(alpha, t0, L, p.H, h);
     if (l == 0) p.gamma[(int64_t)c * p.H + h] = g;
   }
   if (!p.S_local) return;
