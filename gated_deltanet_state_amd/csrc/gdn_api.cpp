@@ -477,6 +477,13 @@ gdn_status gdn_chunk_operator(const void *k, const void *v, const void *alpha, c
   p.tiles_T = dk / 16;
   p.tiles_S = v ? dv / 16 : 0;
   p.fuse_prep = fuse ? 1 : 0;
+  // bf16 with transition and state rows in one workgroup per (chunk, head),
+  // more of them than two per compute unit: one workgroup per compute unit,
+  // each running its run of (chunk, head) items as one stream of chunks
+  // (records of all of them built first, an item's first copies issued
+  // during the previous item's last chunk)
+  const int cus = device_cus();
+  if (fuse && (dk + (v ? dv : 0)) / 16 > 8 && (int64_t)n_chunks * n_heads > 2 * (int64_t)cus) p.multi_wgs = cus;
   return launched(p.in_bf16 ? gdn::launch_chain_bf16(p, st) : gdn::launch_chain(p, st),
                   "gdn_chunk_operator launch");
 }

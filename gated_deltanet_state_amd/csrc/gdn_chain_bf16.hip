@@ -251,9 +251,17 @@ __host__ __device__ inline SegGroups seg_groups(const ChainLaunch &p, int tw, in
 // One workgroup: row-tile group grp of segment seg of (sequence n, head h).
 // QN (with outputs of raw inputs, ChainLaunch::raw): the query norms are
 // formed from the staged queries and applied to the stored output rows.
-template <int DK, bool WANT_O, int NW, int RT, bool FUSED, bool QN = false>
-__device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, const int h, const int seg,
-                                           const int grp, char *smem) {
+// MULTI (chunk operators without a time split, state and transition rows in
+// one workgroup per (sequence, head)): the workgroup runs the items it ..
+// it_end - 1 (item i: sequence i / H, head i % H) as one stream of chunks.
+// Its prologue builds the records of all of them; the copies of an item's
+// first chunk go out during the previous item's last chunk, whose operator
+// is written as the registers start over.  An empty item's operator
+// (identity, zero) is written as the stream passes it.
+template <int DK, bool WANT_O, int NW, int RT, bool FUSED, bool QN = false, bool MULTI = false>
+__device__ __forceinline__ void chain_body(const ChainLaunch &p, int n, int h, const int seg, const int grp,
+                                           char *smem, int it = 0, const int it_end = 0) {
+  static_assert(!MULTI || (FUSED && !WANT_O), "item streams: chunk operators only");
   static_assert(RT == 1 || RT == 2, "one or two row tiles per wave");
   using C = Cfg<DK, WANT_O, NW, RT, FUSED>;
   constexpr int TW = C::TW;
@@ -276,6 +284,37 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
   const bool grp_S = s_hi > s_lo;
   const int sfirst = s_lo - tT, nS = s_hi - s_lo;
   const int vcol0 = 16 * sfirst;
+
+  // MULTI: this lane's first operator element of item (n2, h2) (row row0 +
+  // jl, column 8 g4); element (rt, d, e) sits 16 rt DK + 32 (d >> 1) + 4 (d & 1)
+  // + e floats on
+  auto op_base = [&](int n2, int h2) {
+    const int64_t u2 = (int64_t)n2 * H + h2;
+    return (is_T ? p.T_out + u2 * DK * DK : p.S_out + u2 * DV * DK) + (int64_t)(row0 + jl) * DK + 8 * g4;
+  };
+  auto op_off = [](int rt, int d) { return 16 * rt * DK + 32 * (d >> 1) + 4 * (d & 1); };
+  auto start_value = [&](int rt, int d, int e) {   // identity transition rows, zero state rows
+    const int c0 = 32 * (d >> 1) + 8 * g4 + 4 * (d & 1), r = row0 + 16 * rt + jl;
+    return (is_T && r == c0 + e) ? 1.f : 0.f;
+  };
+  if constexpr (MULTI) {
+    // the operators of the empty items (identity, zero) first
+    for (int i2 = it; i2 < it_end; ++i2) {
+      if (!active || p.cu[i2 / H + 1] > p.cu[i2 / H]) continue;
+      float *ob = op_base(i2 / H, i2 % H);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int d = 0; d < C::NSB; ++d)
+          *reinterpret_cast<f32x4 *>(ob + op_off(rt, d)) =
+              f32x4{start_value(rt, d, 0), start_value(rt, d, 1), start_value(rt, d, 2), start_value(rt, d, 3)};
+    }
+    while (it < it_end && p.cu[it / H + 1] == p.cu[it / H]) ++it;
+    if (it >= it_end) return;
+    n = it / H;
+    h = it % H;
+  }
+  int hn = h;   // head of the chunk being staged (MULTI: the next item's, near an item's end)
 
   // ---- this segment's token range ----
   const int cbeg = p.cu[n], cend = p.cu[n + 1];
@@ -378,10 +417,10 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     char *buf = smem + b * C::BUF;
     const int64_t left = T_all - t0;   // tokens from the chunk's first to the end of the tensor
     const int64_t lim = 0xFFFFFFFFll;
-    const char *kb = reinterpret_cast<const char *>(gk + ((int64_t)t0 * H + h) * DK);
-    const uint32_t nk = (uint32_t)min(left * tok_k - (int64_t)h * DK * 2, lim);
-    const char *qb = WANT_O ? reinterpret_cast<const char *>(gq + ((int64_t)t0 * H + h) * DK) : nullptr;
-    const char *rec = grec + (slot * H + h) * (int64_t)(kRecFloats * 4);
+    const char *kb = reinterpret_cast<const char *>(gk + ((int64_t)t0 * H + hn) * DK);
+    const uint32_t nk = (uint32_t)min(left * tok_k - (int64_t)hn * DK * 2, lim);
+    const char *qb = WANT_O ? reinterpret_cast<const char *>(gq + ((int64_t)t0 * H + hn) * DK) : nullptr;
+    const char *rec = grec + (slot * H + hn) * (int64_t)(kRecFloats * 4);
 #pragma unroll
     for (int j = 0; j < JK; ++j) {                           // K (and Q) A fragments
       const int f = j * NW + w;
@@ -398,8 +437,8 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
       }
     }
     if (part != 0 && grp_S) {                                // value slab of the workgroup
-      const char *vb = reinterpret_cast<const char *>(gv + ((int64_t)t0 * H + h) * DV + vcol0);
-      const uint32_t nv = (uint32_t)min(left * tok_v - ((int64_t)h * DV + vcol0) * 2, lim);
+      const char *vb = reinterpret_cast<const char *>(gv + ((int64_t)t0 * H + hn) * DV + vcol0);
+      const uint32_t nv = (uint32_t)min(left * tok_v - ((int64_t)hn * DV + vcol0) * 2, lim);
 #pragma unroll
       for (int j = 0; j < JV; ++j) {
         const int f = j * NW + w;
@@ -415,11 +454,11 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
   float rk = 1.f;
   auto load_alpha = [&](int t0, int Lc) {
     pa = p.raw ? 0 : 0x3f80;
-    if (w == 0 && l < Lc) pa = ga[(int64_t)(t0 + l) * H + h];
+    if (w == 0 && l < Lc) pa = ga[(int64_t)(t0 + l) * H + hn];
   };
   auto load_norms = [&](int64_t slot, int Lc) {
     if (p.raw && w == 0 && l < Lc) {
-      rk = p.norms[(slot * H + h) * kNormFloats + l];
+      rk = p.norms[(slot * H + hn) * kNormFloats + l];
     }
   };
   // Running scale of the state.  The registers hold S / gam, gam a scalar
@@ -501,6 +540,27 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     // xb + nx - 1 of the sequence), which the segment launch does not run
     int xb = 0, nx = 0;
     if (p.lead && p.tiles_T > 0) lead_extras(p, nch_seq, seg, xb, nx);
+    if constexpr (MULTI) {
+      // the records of every chunk of the items it .. it_end - 1,
+      // round-robin over the waves
+      int c = 0;
+      for (int i2 = it; i2 < it_end; ++i2) {
+        const int n2 = i2 / H, h2 = i2 % H, b2 = p.cu[n2], e2 = p.cu[n2 + 1];
+        for (int tc = b2; tc < e2; tc += CH, ++c) {
+          if (w >= C::NPW || c % C::NPW != w) continue;
+          const int64_t sl = (int64_t)(b2 / CH) + n2 + (tc - b2) / CH;
+          char *rec = const_cast<char *>(grec) + (sl * H + h2) * (int64_t)(kRecFloats * 4);
+          char *lrec = c == 0 ? smem + C::bTF * 1024 : nullptr;
+          if (p.raw)
+            prep_chunk_wave<DK, true>(gk, reinterpret_cast<const bf16 *>(p.alpha),
+                                      reinterpret_cast<const bf16 *>(p.beta), H, h2, tc, min(CH, e2 - tc), rec, scr,
+                                      lrec, p.norms + (sl * H + h2) * kNormFloats);
+          else
+            prep_chunk_wave<DK>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta),
+                                H, h2, tc, min(CH, e2 - tc), rec, scr, lrec);
+        }
+      }
+    } else {
     for (int c = w; c < nch + nx && w < C::NPW; c += C::NPW) {
       const bool own = c < nch;
       const int tc = own ? tbeg + c * CH : cbeg + (xb + c - nch) * CH;
@@ -513,6 +573,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
       else
         prep_chunk_wave<DK>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta), H,
                             h, tc, min(CH, cend - tc), rec, scr, lrec);
+    }
     }
     wait_vmem();
     __syncthreads();
@@ -696,8 +757,29 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
   int b = 0;
   for (int t0 = tbeg; t0 < tend; t0 += CH, ++slot, b ^= 1) {
     const int Lc = min(CH, tend - t0);
-    const bool more = t0 + CH < tend;
-    const int L1 = more ? min(CH, tend - t0 - CH) : 0;
+    // the next chunk: tokens nt0 .. min(nt0 + CH, ntend) - 1, record slot
+    // nslot (MULTI: past this item's end, the first chunk of item nit)
+    int nt0 = t0 + CH, ntend = tend, nn = n;
+    int64_t nslot = slot + 1;
+    if constexpr (MULTI) {
+      if (nt0 >= tend) {
+        // the next item with chunks: the next head of this sequence, else
+        // head 0 of the next sequence that has chunks (all heads of a
+        // sequence have its chunks)
+        hn = h + 1;
+        if (hn == H) {
+          hn = 0;
+          do ++nn; while (nn * H < it_end && p.cu[nn + 1] == p.cu[nn]);
+        }
+        if (nn * H + hn < it_end) {
+          nt0 = p.cu[nn];
+          ntend = p.cu[nn + 1];
+          nslot = (int64_t)(nt0 / CH) + nn;
+        }
+      }
+    }
+    const bool more = nt0 < ntend;
+    const int L1 = more ? min(CH, ntend - nt0) : 0;
     // Operands of the next chunk: in flight while this one runs.  With
     // outputs the copies go out in two halves, the second one in the middle
     // of the step next to the stores of the previous chunk's outputs: issued
@@ -713,9 +795,9 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     // 32768-token prefill and the 3277-token tail, 1% on packed tails).
     __builtin_amdgcn_s_setprio(3);
     if (more) {
-      issue_dma(b ^ 1, t0 + CH, slot + 1, true, WANT_O ? 0 : -1);
-      load_alpha(t0 + CH, L1);
-      load_norms(slot + 1, L1);
+      issue_dma(b ^ 1, nt0, nslot, true, WANT_O ? 0 : -1);
+      load_alpha(nt0, L1);
+      load_norms(nslot, L1);
     }
     query_norms(b);   // (raw inputs with outputs; read when this chunk's outputs are stored)
     const char *buf = smem + b * C::BUF;
@@ -939,7 +1021,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
           finish_o(b ^ 1);
           stash_o();
         }
-        if (more) issue_dma(b ^ 1, t0 + CH, slot + 1, true, 1);
+        if (more) issue_dma(b ^ 1, nt0, nslot, true, 1);
       }
 
       if (active) {
@@ -1028,13 +1110,51 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
     __builtin_amdgcn_s_setprio(0);
     if (WANT_O) build_p(b);
     // ---- hand over to the next chunk ----
-    if (more) gates(b ^ 1, L1, t0 + 2 * CH >= tend);
+    if (more) gates(b ^ 1, L1, nt0 + CH >= ntend);
     wait_vmem();
     if (WANT_O && active && Ls > 0) store_s(b ^ 1);   // the previous chunk's outputs
+    if constexpr (MULTI) {
+      if (t0 + CH >= tend) {
+        // this item's operator out (the stores drain during the next
+        // steps), the registers back to their start, the stream on to item nit
+        if (active) {
+          float *ob = op_base(n, h);
+          // the start values from the lane's diagonal positions (kept opaque,
+          // so that the compiler does not hold all 64 of them in registers
+          // across the loop)
+          int dg[RT];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const int c = row0 + 16 * rt + jl;   // the diagonal element's column
+            dg[rt] = (is_T && g4 == (c & 31) >> 3) ? 4 * (2 * (c >> 5) + ((c & 7) >> 2)) + (c & 3) : -1;
+            asm volatile("" : "+v"(dg[rt]));
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int d = 0; d < C::NSB; ++d) {
+              *reinterpret_cast<f32x4 *>(ob + op_off(rt, d)) = st[rt][d];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) st[rt][d][e] = dg[rt] == 4 * d + e ? 1.f : 0.f;
+            }
+        }
+        if (more) {
+          n = nn;
+          h = hn;
+          tend = ntend;
+          t0 = nt0 - CH;     // (the loop's increments then land on the next chunk)
+          slot = nslot - 1;
+        }
+      }
+    }
     lds_barrier();
     if (more) read_v(b ^ 1);
   }
 
+  if constexpr (MULTI) {
+    wait_vmem();   // (the last operator's stores, before the workgroup ends)
+    return;        // (every item's operator was written in the loop)
+  }
   // ---------------- epilogue: final rows ----------------
   if (WANT_O && active && Lp > 0) {
     finish_o(b ^ 1);   // the last chunk's set (b has moved past it)
@@ -1098,12 +1218,20 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, const int n, co
 // The launch: one workgroup per (sequence, head, segment, row-tile group).
 // With LEAD (segment launch of the lead layout) segment 0 runs the output
 // recurrence, one row tile per wave, and the other segments this body.
-template <int DK, bool WANT_O, int NW, int RT, bool FUSED, bool LEAD = false, bool QN = false>
+template <int DK, bool WANT_O, int NW, int RT, bool FUSED, bool LEAD = false, bool QN = false, bool MULTI = false>
 __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int n_items) {
   using C = Cfg<DK, WANT_O, NW, RT, FUSED>;
   using CL = Cfg<DK, true, NW, 1, FUSED>;
   constexpr size_t SM = (LEAD && CL::SMEM > C::SMEM) ? CL::SMEM : C::SMEM;
   __shared__ __attribute__((aligned(16))) char smem[SM];
+  if constexpr (MULTI) {
+    // block b: items b per .. (b + 1) per - 1 (one (sequence, head) each)
+    const int per = (n_items + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int i0 = (int)blockIdx.x * per, i1 = min(n_items, i0 + per);
+    if (i0 >= i1) return;
+    chain_body<DK, WANT_O, NW, RT, FUSED, false, true>(p, i0 / p.H, i0 % p.H, 0, 0, smem, i0, i1);
+    return;
+  }
   const SegGroups sg = seg_groups(p, C::TW, LEAD ? NW : C::TW);
   // One workgroup per (sequence, head) with a longest-first sequence order:
   // items in block order (the dispatcher deals blocks round-robin over the
@@ -1131,7 +1259,8 @@ __global__ void __launch_bounds__(NW * 64) chain_bf16_kernel(ChainLaunch p, int 
   chain_body<DK, WANT_O, NW, RT, FUSED, WANT_O && QN>(p, n, h, seg, grp, smem);
 }
 
-template <int DK, bool WANT_O, int NW, int RT, bool FUSED = false, bool LEAD = false, bool QN = false>
+template <int DK, bool WANT_O, int NW, int RT, bool FUSED = false, bool LEAD = false, bool QN = false,
+          bool MULTI = false>
 hipError_t launch_b(const ChainLaunch &p, hipStream_t stream) {
   constexpr int TW = NW * RT;
   if (p.tiles_T % RT != 0 || p.tiles_S % RT != 0 || p.tiles_T > 8 || p.tiles_S > 8) return hipErrorInvalidValue;
@@ -1139,9 +1268,10 @@ hipError_t launch_b(const ChainLaunch &p, hipStream_t stream) {
   const SegGroups sg = seg_groups(p, TW, LEAD ? NW : TW);
   const int64_t items = (int64_t)p.n_seqs * p.H * sg.per_nh;
   if (items <= 0) return hipSuccess;
-  const int64_t grid = (items + 7) / 8 * 8;
-  return launch_kernel(chain_bf16_kernel<DK, WANT_O, NW, RT, FUSED, LEAD, QN>, dim3((unsigned)grid), dim3(NW * 64),
-                       0, stream, p, (int)items);
+  if (MULTI && (sg.per_nh != 1 || p.multi_wgs <= 0)) return hipErrorInvalidValue;
+  const int64_t grid = MULTI ? (items < p.multi_wgs ? items : p.multi_wgs) : (items + 7) / 8 * 8;
+  return launch_kernel(chain_bf16_kernel<DK, WANT_O, NW, RT, FUSED, LEAD, QN, MULTI>, dim3((unsigned)grid),
+                       dim3(NW * 64), 0, stream, p, (int)items);
 }
 
 template <int DK>
@@ -1179,6 +1309,14 @@ hipError_t launch_dk(const ChainLaunch &p, hipStream_t stream) {
   if (p.tiles_T > 0) {
     // one workgroup per (sequence, segment, head): it may build its own
     // segment's records first
+    if (p.multi_wgs > 0) {
+      // chunk operators in several rounds of workgroups: one stream of items
+      // per workgroup
+      if (!p.fuse_prep || p.n_segs != 1 || p.T_frags || p.S0 || p.S0_seg || p.S_last || tilesA <= 8 ||
+          tilesA > 16)
+        return hipErrorInvalidValue;
+      return launch_b<DK, false, 8, 2, true, false, false, true>(p, stream);
+    }
     if (tilesA <= 8)
       return p.fuse_prep ? launch_b<DK, false, 4, 2, true>(p, stream) : launch_b<DK, false, 4, 2>(p, stream);
     if (tilesA <= 16)

@@ -144,6 +144,11 @@ struct ChainLaunch {
   // [n_seqs] longest-first sequence order (PrepLaunch::order), or null;
   // used by the bf16 recurrence when each (sequence, head) is one workgroup
   const int32_t *order;
+  // bf16 chunk operators (fuse_prep, one workgroup per (sequence, head), no
+  // time split): > 0 runs that many workgroups, each over a contiguous run
+  // of the (sequence, head) items as one stream of chunks; 0: one
+  // workgroup per item
+  int multi_wgs;
   // raw inputs (kNormFloats): alpha holds log-gates, beta logits, k and q
   // raw projections; norms [n_slots, H, kNormFloats] come from the record
   // builder (written by the fused prologue, read by the recurrence)
