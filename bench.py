@@ -108,13 +108,41 @@ def uninstrumented_ms(fn, steps, torch):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def code_text(src):
+    """C/C++/HIP source without its comments and whitespace (string and
+    character literals kept as written): what the compiler sees as code."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            if not c.isspace():
+                out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def sources_sha256():
+    """Hash of the kernel and library sources as code (comments and
+    whitespace left out): the counter summaries in profiles/ carry it, and
+    their traffic figures count only while it matches."""
     import glob
     import hashlib
     h = hashlib.sha256()
     for src in sorted(glob.glob(os.path.join(ROOT, "gated_deltanet_state_amd", "csrc", "*"))):
-        with open(src, "rb") as f:
-            h.update(f.read())
+        with open(src, encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode("utf-8"))
     return h.hexdigest()
 
 

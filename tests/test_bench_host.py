@@ -29,3 +29,15 @@ def test_measured_traffic_follows_the_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("other") is None
     monkeypatch.setattr(bench, "sources_sha256", lambda: "y")
     assert bench.measured_traffic("w") is None
+
+
+def test_source_hash_ignores_comments_and_whitespace():
+    # the counter summaries stay valid across comment edits, not across code edits
+    import bench
+    a = 'int f(int x) { // twice\n  return 2 * x; /* doubled */ }\nconst char *s = "a // b";\n'
+    b = 'int  f(int x)\n{\n  return 2*x;\n}\nconst char *s = "a // b";  // the same code\n'
+    c = 'int f(int x) { return 3 * x; }\nconst char *s = "a // b";\n'
+    d = 'int f(int x) { return 2 * x; }\nconst char *s = "a /* b";\n'
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
+    assert bench.code_text(a) != bench.code_text(d)    # string contents are code
