@@ -254,10 +254,10 @@ __host__ __device__ inline SegGroups seg_groups(const ChainLaunch &p, int tw, in
 // MULTI (chunk operators without a time split, state and transition rows in
 // one workgroup per (sequence, head)): the workgroup runs the items it ..
 // it_end - 1 (item i: sequence i / H, head i % H) as one stream of chunks.
-// Its prologue builds the records of all of them; the copies of an item's
-// first chunk go out during the previous item's last chunk, whose operator
-// is written as the registers start over.  An empty item's operator
-// (identity, zero) is written as the stream passes it.
+// Its prologue writes the operators of the empty items (identity, zero)
+// and builds the records of all the others; the copies of an item's first
+// chunk go out during the previous item's last chunk, whose operator is
+// written as the registers start over.
 template <int DK, bool WANT_O, int NW, int RT, bool FUSED, bool QN = false, bool MULTI = false>
 __device__ __forceinline__ void chain_body(const ChainLaunch &p, int n, int h, const int seg, const int grp,
                                            char *smem, int it = 0, const int it_end = 0) {
