@@ -561,19 +561,19 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, int n, int h, c
         }
       }
     } else {
-    for (int c = w; c < nch + nx && w < C::NPW; c += C::NPW) {
-      const bool own = c < nch;
-      const int tc = own ? tbeg + c * CH : cbeg + (xb + c - nch) * CH;
-      const int64_t sl = (int64_t)(cbeg / CH) + n + (tc - cbeg) / CH;
-      char *rec = const_cast<char *>(grec) + (sl * H + h) * (int64_t)(kRecFloats * 4);
-      char *lrec = (own && c == 0) ? smem + C::bTF * 1024 : nullptr;
-      if (p.raw)
-        prep_chunk_wave<DK, true>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta),
-                                  H, h, tc, min(CH, cend - tc), rec, scr, lrec, p.norms + (sl * H + h) * kNormFloats);
-      else
-        prep_chunk_wave<DK>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta), H,
-                            h, tc, min(CH, cend - tc), rec, scr, lrec);
-    }
+      for (int c = w; c < nch + nx && w < C::NPW; c += C::NPW) {
+        const bool own = c < nch;
+        const int tc = own ? tbeg + c * CH : cbeg + (xb + c - nch) * CH;
+        const int64_t sl = (int64_t)(cbeg / CH) + n + (tc - cbeg) / CH;
+        char *rec = const_cast<char *>(grec) + (sl * H + h) * (int64_t)(kRecFloats * 4);
+        char *lrec = (own && c == 0) ? smem + C::bTF * 1024 : nullptr;
+        if (p.raw)
+          prep_chunk_wave<DK, true>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta),
+                                    H, h, tc, min(CH, cend - tc), rec, scr, lrec, p.norms + (sl * H + h) * kNormFloats);
+        else
+          prep_chunk_wave<DK>(gk, reinterpret_cast<const bf16 *>(p.alpha), reinterpret_cast<const bf16 *>(p.beta), H,
+                              h, tc, min(CH, cend - tc), rec, scr, lrec);
+      }
     }
     wait_vmem();
     __syncthreads();
