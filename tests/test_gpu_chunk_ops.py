@@ -64,7 +64,8 @@ def test_transition_only():
     check_T("T_C only", to_np(TC), TC_ref, "bf16")
 
 
-def test_chunk_operator_item_streams():
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
+def test_chunk_operator_item_streams(dk, dv):
     # more (chunk, head) items than two per compute unit (40 chunks x 16
     # heads): each workgroup runs a run of items as one stream of chunks,
     # with runs that start and end inside a chunk's heads; ragged chunks and
@@ -76,15 +77,15 @@ def test_chunk_operator_item_streams():
     lengths[12] = 64
     bounds = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     H, heads = 16, [0, 3, 9, 15]
-    inp = workloads.generate([int(bounds[-1])], H=H, dk=128, dv=128, dtype="bf16", seed=46)
+    inp = workloads.generate([int(bounds[-1])], H=H, dk=dk, dv=dv, dtype="bf16", seed=46)
     TC, SL = gpu_ops(inp, bounds)
     f = inp.f64
     TC_ref, SL_ref = oracle.chunk_operator(f["k"][:, heads], f["alpha"][:, heads], f["beta"][:, heads], bounds,
                                            v=f["v"][:, heads])
-    check_T("T_C item streams", to_np(TC)[:, heads], TC_ref, "bf16")
-    check_state("S_local item streams", to_np(SL)[:, heads], SL_ref, "bf16")
+    check_T("T_C item streams %dx%d" % (dk, dv), to_np(TC)[:, heads], TC_ref, "bf16")
+    check_state("S_local item streams %dx%d" % (dk, dv), to_np(SL)[:, heads], SL_ref, "bf16")
     for c in (0, 7, 8, 9, 39):   # empty chunks, every head: identity and zero
-        assert np.array_equal(to_np(TC)[c], np.broadcast_to(np.eye(128), (H, 128, 128)))
+        assert np.array_equal(to_np(TC)[c], np.broadcast_to(np.eye(dk), (H, dk, dk)))
         assert not np.any(to_np(SL)[c])
 
 
