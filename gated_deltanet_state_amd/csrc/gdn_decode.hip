@@ -15,7 +15,7 @@
 // 32-byte contiguous pieces, so a wave reads four whole rows per step), a
 // wave loads all of its rows before it updates any (its reads are then in
 // flight together), the two dot products are reduced across the 16 lanes
-// with xor shuffles, and each updated row is written back in place (S_out
+// by DPP, and each updated row is written back in place (S_out
 // may alias S_in).  All arithmetic is fp32.
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -32,12 +32,6 @@ template <>
 __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ float to_f32<bf16>(bf16 x) { return (float)x; }
-
-__device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) x += __shfl_xor(x, m, 16);
-  return x;
-}
 
 template <int DK, int DV, typename TI>
 __global__ void __launch_bounds__(DNW * 64) decode_kernel(DecodeLaunch p) {
@@ -94,7 +88,7 @@ __global__ void __launch_bounds__(DNW * 64) decode_kernel(DecodeLaunch p) {
       float y = 0.f;
 #pragma unroll
       for (int i = 0; i < PER; ++i) y += s[it][i] * kk[i];
-      y = sum16(y);
+      y = row16_sum(y);
       const float coef = beta * (vr[it] - alpha * y);
       float o = 0.f;
 #pragma unroll
@@ -106,7 +100,7 @@ __global__ void __launch_bounds__(DNW * 64) decode_kernel(DecodeLaunch p) {
       for (int i = 0; i < PER; i += 4)
         *reinterpret_cast<f32x4 *>(p.S_out + off + i) = f32x4{s[it][i], s[it][i + 1], s[it][i + 2], s[it][i + 3]};
       if (p.o) {
-        o = sum16(o);
+        o = row16_sum(o);
         if (c == 0) {
           if (p.o_bf16)
             reinterpret_cast<bf16 *>(p.o)[(int64_t)nh * DV + row] = (bf16)o;

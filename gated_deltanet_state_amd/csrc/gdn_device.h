@@ -227,6 +227,23 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
   x += dpp_src<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
   return x;
 }
+// Sum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15): the quad
+// pairs (lane ^ 1), the quads' halves (lane ^ 2), the two quads of each
+// half-row (mirror in 8), the two half-rows (mirror in 16).  Every step adds
+// the same two partial sums in both lanes of a pair, so all 16 lanes end
+// with the same bits.  (DPP moves stay in the VALU; a shuffle by
+// ds_bpermute is an LDS round trip per step.)
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_row<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x += dpp_row<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x += dpp_row<0x141>(x);   // row_half_mirror
+  x += dpp_row<0x140>(x);   // row_mirror
+  return x;
+}
 __device__ __forceinline__ float lane_value(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }

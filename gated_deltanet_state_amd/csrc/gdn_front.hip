@@ -14,10 +14,10 @@
 //
 // One pass over the tensors, bound by HBM bandwidth: 16 lanes share a row
 // (dk / 16 contiguous values each), a lane loads its values of FU rows before
-// it reduces any, the squared norm is summed across the 16 lanes with xor
-// shuffles, and each lane writes back only the values it read, so the
-// outputs may alias the inputs.  The gates are one element per lane in a
-// grid-stride loop of their own.
+// it reduces any, the squared norm is summed across the 16 lanes by DPP and
+// its reciprocal square root scales the row, and each lane writes back only
+// the values it read, so the outputs may alias the inputs.  The gates are
+// one element per lane in a grid-stride loop of their own.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -29,12 +29,6 @@ constexpr int FNT = 256;   // threads per workgroup
 constexpr int FU = 2;      // rows a 16-lane group loads before reducing (1, 2 and 4 measured
                            // with unconditional loads: 22.6, 20.7 and 21.7 us on 3277 x 32 rows
                            // of q and k, against 22.2-23.8 us for one row loaded under a branch)
-
-__device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) x += __shfl_xor(x, m, 16);
-  return x;
-}
 
 template <typename TI>
 __device__ __forceinline__ TI from_f32(float x);
@@ -115,10 +109,10 @@ __global__ void __launch_bounds__(FNT) front_kernel(FrontLaunch p) {
         float s = 0.f;
 #pragma unroll
         for (int i = 0; i < PER; ++i) s += x[u][i] * x[u][i];
-        s = sum16(s);
-        const float nrm = sqrtf(s);
+        s = row16_sum(s);
+        const float inv = s > 0.f ? rsqrtf(s) : 0.f;   // (a zero row stays zero)
 #pragma unroll
-        for (int i = 0; i < PER; ++i) x[u][i] = s > 0.f ? x[u][i] / nrm : 0.f;
+        for (int i = 0; i < PER; ++i) x[u][i] *= inv;
         const bool is_q = p.q_in && r < rows;
         TI *dst = reinterpret_cast<TI *>(is_q ? p.q_out : p.k_out);
         store_row<PER>(dst + (is_q ? r : r - (p.q_in ? rows : 0)) * DK + PER * c, x[u]);
