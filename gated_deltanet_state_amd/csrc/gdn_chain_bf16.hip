@@ -519,7 +519,10 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, int n, int h, c
         const int u = min(2 * (vtile + rt), C::VU - 2) + ((jl & 3) >> 1);
         const uint2 x = ds_read_tr16(reinterpret_cast<const bf16 *>(
             buf + C::bV * 1024 + rr0 * (C::VU * 16) + 16 * (u ^ vswz<C::VU>(rr0)) + 8 * (jl & 1)));
-        vt[rt][bt] = uint2{x.x & vmask, x.y & vmask};
+        if constexpr (WANT_O)   // (no transition tiles; an idle wave never reads vt)
+          vt[rt][bt] = x;
+        else
+          vt[rt][bt] = uint2{x.x & vmask, x.y & vmask};
       }
   };
 
@@ -649,10 +652,13 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, int n, int h, c
       *reinterpret_cast<bf16x4 *>(sP + kTauFragPlane + (f * 64 + l) * 8 + 4 * half) = lo;
     }
   };
-  // the pending outputs: add (M o Q K^T) D from set b, then store
-  auto finish_o = [&](int b) {
+  // the pending outputs: zp plus (M o Q K^T) D from set b, into dst (the
+  // first product of each block reads zp and writes dst, so finished outputs
+  // move to the stash without copies; dst may be zp)
+  auto finish_o = [&](int b, f32x4 (&dst)[RT][4]) {
     const bf16 *sP = reinterpret_cast<const bf16 *>(smem + C::oP + b * C::PSET);
     constexpr int ford[kTauFrags] = {0, 2, 4, 1, 3, 5};
+    constexpr bool first[kTauFrags] = {true, true, true, true, false, false};   // token blocks 0, 2, 3, 1, 2, 3
     bf16x8 ph[kTauFrags], pl[kTauFrags];
 #pragma unroll
     for (int f = 0; f < kTauFrags; ++f) {
@@ -668,7 +674,8 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, int n, int h, c
           const int f = ford[i];
           const int bt = f < 2 ? f : (f - 2) / 2 + 2;
           const int m = f < 2 ? 0 : (f - 2) % 2;
-          zp[rt][bt] = mfma_bf16(pass == 1 ? dpl[rt][m] : dph[rt][m], pass == 2 ? pl[f] : ph[f], zp[rt][bt]);
+          dst[rt][bt] = mfma_bf16(pass == 1 ? dpl[rt][m] : dph[rt][m], pass == 2 ? pl[f] : ph[f],
+                                  pass == 0 && first[i] ? zp[rt][bt] : dst[rt][bt]);
         }
   };
   // Finished outputs wait in zs (tokens ts .. ts + Ls - 1) until the end of
@@ -681,11 +688,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, int n, int h, c
   // finished, in the middle of the step.)
   f32x4 zs[RT][4];
   int ts = 0, Ls = 0;
-  auto stash_o = [&]() {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int bt = 0; bt < 4; ++bt) zs[rt][bt] = zp[rt][bt];
+  auto stash_o = [&]() {   // (the outputs themselves went to zs in finish_o)
     ts = tp;
     Ls = Lp;
     Lp = 0;
@@ -1018,7 +1021,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, int n, int h, c
         // the previous chunk's outputs (its M o Q K^T became visible at the
         // hand-over barrier), then the second half of the next chunk's copies
         if (active && Lp > 0) {
-          finish_o(b ^ 1);
+          finish_o(b ^ 1, zs);
           stash_o();
         }
         if (more) issue_dma(b ^ 1, nt0, nslot, true, 1);
@@ -1157,7 +1160,7 @@ __device__ __forceinline__ void chain_body(const ChainLaunch &p, int n, int h, c
   }
   // ---------------- epilogue: final rows ----------------
   if (WANT_O && active && Lp > 0) {
-    finish_o(b ^ 1);   // the last chunk's set (b has moved past it)
+    finish_o(b ^ 1, zp);   // the last chunk's set (b has moved past it)
     store_o(b ^ 1);
   }
   const int64_t unit = ((int64_t)n * p.n_segs + seg) * H + h;
