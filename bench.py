@@ -329,7 +329,7 @@ def summarize_counters(wid, stats_dir, fetch_dir, write_dir, cal_fetch_dir, cal_
     print("wrote profiles/%s.md and profiles/traffic_%s.json" % (wname, wname))
 
 
-def cpu_baseline(inp, want_o, wid, min_seconds=3.0):
+def cpu_baseline(inp, want_o, wid, min_seconds=10.0):
     """fp64 oracle on the same workload: whole heads, repeated to >= min_seconds,
     or a subset of heads when one full pass would be long."""
     import oracle
