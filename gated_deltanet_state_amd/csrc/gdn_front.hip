@@ -102,8 +102,8 @@ __global__ void __launch_bounds__(FNT) front_kernel(FrontLaunch p) {
     }
 #pragma unroll
     for (int u = 0; u < FU; ++u) {
-      // live[u] is the same for the 16 lanes of a row, so the shuffles below
-      // only combine lanes of rows that are all live
+      // live[u] is the same for the 16 lanes of a row, so the row sum below
+      // only combines lanes of rows that are all live
       if (live[u]) {
         const int64_t r = r0 + u * groups;
         float s = 0.f;
