@@ -87,6 +87,16 @@ def test_chunk_operator_item_streams(dk, dv):
     for c in (0, 7, 8, 9, 39):   # empty chunks, every head: identity and zero
         assert np.array_equal(to_np(TC)[c], np.broadcast_to(np.eye(dk), (H, dk, dk)))
         assert not np.any(to_np(SL)[c])
+    # one head alone (40 items: one workgroup per item) gives the same bits:
+    # the streams change the schedule, not the arithmetic
+    gdn, torch = _gdn()
+    d = dev(inp)
+    cu = torch.from_numpy(bounds).cuda()
+    for h in (0, 9):
+        one = {key: d[key][:, h:h + 1].contiguous() for key in ("k", "v", "alpha", "beta")}
+        TC1, SL1 = gdn.chunk_operator(one["k"], one["alpha"], one["beta"], cu, v=one["v"])
+        torch.cuda.synchronize()
+        assert torch.equal(TC1[:, 0], TC[:, h]) and torch.equal(SL1[:, 0], SL[:, h])
 
 
 @pytest.mark.parametrize("gate", ["one", "slow", "workload"])
